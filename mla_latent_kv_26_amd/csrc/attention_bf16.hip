@@ -1,0 +1,539 @@
+// Latent attention on MFMA (gfx950), bf16 cache rows, float32 accumulate.
+//
+// For one query row and 64 heads (modeldna "MLA" module, "Under the hood":
+// W_UK absorbed into the query, attention run on the cached latent):
+//   s[h, j]  = q_full[h] . row_j          (q_full = scale*log2e*[q_lat | q_rope])
+//   o_lat[h] = sum_j 2^(s[h,j] - m[h]) c_j / sum_j 2^(s[h,j] - m[h]).
+// The rows are dense bf16 [c (512) | k_rope (64)], 1152 B each, shared by
+// every head, so both contractions are matrix products:
+//   S^T [64 tok x 64 h] = T [64 tok x 576] * Q^T [576 x 64 h]
+//   O   [64 h x 512]   += P [64 h x 64 tok] * T[:, :512]
+// and one LDS copy of each 64-token tile serves both: T is read row-wise
+// for S (16-byte LDS reads) and column-wise for P*C (transposing LDS reads),
+// so every cached byte leaves HBM once.
+//
+// Workgroup: 256 threads = 4 waves, 64 heads.  For S each wave takes 16
+// heads and all 64 tokens of the tile (its 16 heads' queries stay in
+// registers, and each head's row max and row sum stay inside one wave); for
+// P*C each wave owns a 128-column quarter of O for all 64 heads.  Tiles stream HBM -> LDS
+// with asynchronous direct-to-LDS loads into two buffers: tile j+1 is in
+// flight while tile j is multiplied.
+//
+// Tile layout in LDS: chunk-major.  The 16-byte chunk k (of 72) of row t
+// (of 64) sits at slot k*64 + (t ^ 4*(k&1)).  One direct-to-LDS load
+// instruction then moves chunk k of all 64 rows (a lane per row), row-wise
+// fragment reads (8 consecutive rows, one chunk) hit 8 consecutive slots,
+// and a transposing read (4 rows x 2 neighbouring chunks) hits 8 distinct
+// slot positions: neither access pattern has bank conflicts.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int kR = 512, kDr = 64, kW = kR + kDr;       // row width 576
+constexpr int kTok = 64;                                // tokens per tile
+constexpr int kCh = kW * 2 / 16;                        // 72 chunks per row
+constexpr int kTileBytes = kTok * kW * 2;               // 73728
+constexpr int kHG = 64;                                 // heads per workgroup
+constexpr int kLoads = kTok * kCh / (64 * 4);           // 18 loads per wave per tile
+constexpr int kPStride = 72;                            // bf16 per P row (64 + 8)
+constexpr int kMaxBatch = 1024;
+
+constexpr int kOffP = 2 * kTileBytes;
+constexpr int kOffAlpha = kOffP + kHG * kPStride * 2;  // float [64] rescale factors
+constexpr int kOffFlag = kOffAlpha + kHG * 4;           // int [4] per-wave rescale flags
+constexpr int kOffLsum = kOffFlag + 16;                 // float [64] row sums
+constexpr int kOffRed = kOffLsum + kHG * 4;             // scratch for the prefix scan
+constexpr int kOffPrefix = kOffRed + 64;                // int [kMaxBatch + 1]
+constexpr int kLdsBytes = kOffPrefix + (kMaxBatch + 1) * 4;
+// A head's running max only moves when a tile exceeds it by more than this
+// (log2 units): probabilities stay below 2^8 and O is rescaled rarely.
+constexpr float kRescaleSlack = 8.0f;
+static_assert(kLdsBytes <= 163840, "LDS budget");
+
+__device__ __forceinline__ uint32_t toff(uint32_t t, uint32_t k) {
+  return (k * kTok + (t ^ ((k & 1u) << 2))) * 16u;
+}
+
+// Issue the asynchronous loads of one tile: `valid` rows (1..64) starting at
+// row pointer `rows`.  Wave w loads chunks 18w .. 18w+17 of every row; lane l
+// carries row l (even chunks) or row l^4 (odd chunks).  Rows past `valid`
+// repeat the last valid row so the tile holds finite data (their
+// probabilities are zero).
+__device__ __forceinline__ void issue_tile(const bf16* rows, int valid, uint32_t buf, int wave,
+                                           int lane) {
+  const int te = min(lane, valid - 1), to = min(lane ^ 4, valid - 1);
+  const bf16* pe = rows + te * kW + wave * kLoads * 8;
+  const bf16* po = rows + to * kW + wave * kLoads * 8;
+  const uint32_t dst = buf + (uint32_t)(wave * kLoads) * 1024u;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) g2lds16((i & 1 ? po : pe) + i * 8, dst + i * 1024u);
+}
+
+struct SegState {
+  f32x16 o[2][4];   // O[32 hb + ..][128 wave + 32 cb + ..]
+  float m;          // reference max of head 16 wave + lane%16, log2 units
+  float l;          // lane-partial running sum for that head
+};
+
+// Attend one query row (64 heads at q_rows, row stride kW) over tiles
+// [tile0, tile1) of one sequence (len rows, page table `table`).
+__device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
+                                            const bf16* __restrict__ pool,
+                                            const int* __restrict__ table, int shift, int len,
+                                            int tile0, int tile1, uint32_t lds, SegState& st,
+                                            int wave, int lane) {
+  const uint32_t p_lds = lds + kOffP, alp = lds + kOffAlpha, flags = lds + kOffFlag;
+  const int h = 16 * wave + (lane & 15);   // this lane's head in the S phase
+  const uint32_t kq = lane >> 4;           // 0..3
+
+  // Per-lane LDS bases; every other offset below is a compile-time constant.
+  // S phase (16x16x32): row 16 tb + lane%16, chunk 4 ks + kq -> s_base + 256 tb + 4096 ks.
+  const uint32_t s_base = (kq * 64u + ((lane & 15) ^ ((kq & 1u) << 2))) * 16u;
+  // P*C phase, transposing reads: lane (16 g + li) of the fragment for token
+  // block ks and column block cb reads row 16 ks + x (+4), chunk kb + 4 cb.
+  const uint32_t g = lane >> 4, li = lane & 15;
+  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u;
+  const uint32_t kb = 16u * wave + 2u * (g & 1) + b1;
+  const uint32_t tr_lo = (kb * 64u + x + 4u * b1) * 16u + 8u * (li & 1);
+  const uint32_t tr_hi = (kb * 64u + x + 4u * (1u - b1)) * 16u + 8u * (li & 1);
+  // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
+  const uint32_t pa_base = p_lds + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
+  const uint32_t pw_base = p_lds + (h * kPStride + 4 * kq) * 2;
+  const uint32_t al_base = alp + 16 * (lane >> 5);
+
+  // queries of this wave's 16 heads: B operand of S^T = T Q^T (16x16x32)
+  bf16x8 qf[kW / 32];
+  {
+    const bf16* q = q_rows + h * kW + 8 * kq;
+#pragma unroll
+    for (int ks = 0; ks < kW / 32; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) st.o[a][b] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  const int mask = (1 << shift) - 1;
+  auto rows_of = [&](int tile) {
+    const int tok = tile * kTok;
+    const int page = table[tok >> shift];
+    return pool + ((long)page * (mask + 1) + (tok & mask)) * kW;
+  };
+
+  issue_tile(rows_of(tile0), min(kTok, len - tile0 * kTok), lds, wave, lane);
+
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const uint32_t buf = lds + (uint32_t)((tile - tile0) & 1) * kTileBytes;
+    wait_vmcnt<0>();
+    lds_barrier();  // tile visible to all waves; previous tile fully consumed
+    if (tile + 1 < tile1)
+      issue_tile(rows_of(tile + 1), min(kTok, len - (tile + 1) * kTok),
+                 lds + (uint32_t)((tile + 1 - tile0) & 1) * kTileBytes, wave, lane);
+
+    // ---- S^T for tokens [0, 64) x heads [16 wave, +16), K = 576:
+    // four 16-token blocks, fragments read one k-step ahead.
+    f32x4 sacc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    {
+      const uint32_t sa = buf + s_base;
+      bf16x8 a[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) a[tb] = lds_read_b128(sa + tb * 256u);
+#pragma unroll
+      for (int ks = 0; ks < kW / 32; ++ks) {
+        bf16x8 n[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          n[tb] = (ks + 1 < kW / 32) ? lds_read_b128(sa + (uint32_t)(ks + 1) * 4096u + tb * 256u) : a[tb];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) sacc[tb] = mfma16(a[tb], qf[ks], sacc[tb]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) a[tb] = n[tb];
+      }
+    }
+    // register v of block tb <-> token 16 tb + 4 kq + v, head h
+    const int valid = len - tile * kTok;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
+        tmax = fmaxf(tmax, sacc[tb][v]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const bool grow = tmax > st.m + kRescaleSlack;
+    const float m_new = grow ? tmax : st.m;
+    const float alpha = grow ? exp2f(st.m - m_new) : 1.0f;
+    const bool any = __ballot(grow) != 0ull;
+    float psum = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      bf16x4 pk;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bf16 pb = (bf16)exp2f(sacc[tb][v] - m_new);
+        pk[v] = pb;
+        psum += (float)pb;
+      }
+      lds_st(pw_base + tb * 32, pk);
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    if (lane < 16) lds_st(alp + h * 4, alpha);
+    if (lane == 0) lds_st(flags + wave * 4, any ? 1.0f : 0.0f);
+    lds_barrier();
+
+    // ---- O[64 h, 128 wave + (0..127)] = O * alpha + P T
+    const f32x4 fl = lds_ld4(flags);
+    if (fl[0] + fl[1] + fl[2] + fl[3] != 0.0f) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 a4 = lds_ld4(al_base + hb * 128 + q * 32);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.o[hb][cb][4 * q + r] *= a4[r];
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < kTok / 16; ++ks) {
+      const bf16x8 pa0 = lds_read_b128(pa_base + ks * 32);
+      const bf16x8 pa1 = lds_read_b128(pa_base + 32 * kPStride * 2 + ks * 32);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint32_t off = buf + (uint32_t)(cb * 4096 + ks * 256);
+        const bf16x8 bv = cat(lds_read_tr(off + tr_lo), lds_read_tr(off + tr_hi));
+        st.o[0][cb] = mfma32(pa0, bv, st.o[0][cb]);
+        st.o[1][cb] = mfma32(pa1, bv, st.o[1][cb]);
+      }
+    }
+  }
+}
+
+// Row sums of the segment into LDS (a barrier must follow before use).
+__device__ __forceinline__ void publish_sums(const SegState& st, uint32_t lds, int wave, int lane) {
+  float lt = st.l + __shfl_xor(st.l, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (lane < 16) lds_st(lds + kOffLsum + (16 * wave + lane) * 4, lt);
+}
+__device__ __forceinline__ float head_sum(uint32_t lds, int h) {
+  return lds_ld(lds + kOffLsum + h * 4);
+}
+
+// Store O / l for the 64 heads of this workgroup: dst[h * 512 + c] (bf16).
+__device__ __forceinline__ void store_normalised(const SegState& st, uint32_t lds, bf16* dst,
+                                                 long head_stride, int wave, int lane) {
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int h = 32 * hb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const float inv = 1.0f / head_sum(lds, h);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int c = 128 * wave + 32 * cb + (lane & 31);
+        dst[h * head_stride + c] = (bf16)(st.o[hb][cb][v] * inv);
+      }
+    }
+}
+
+// Workgroup -> (head group, stream index); the head groups of one stream
+// index sit 8 workgroups apart, so round-robin dispatch puts them on the
+// same XCD and the second group reads each tile from that XCD's L2.
+__device__ __forceinline__ void map_block(int hgc, int& hg, int& w) {
+  const int b = blockIdx.x;
+  const int per = 8 * hgc;
+  hg = (b % per) / 8;
+  w = (b / per) * 8 + (b % 8);
+}
+
+}  // namespace
+
+// Which workgroup of the stream owns tile x (ranges [w*T/n, (w+1)*T/n)).
+__host__ __device__ inline int owner_of(long x, long T, int n) {
+  int w = (int)((x * n) / T);
+  while (w + 1 < n && ((long)(w + 1) * T) / n <= x) ++w;
+  while (w > 0 && ((long)w * T) / n > x) --w;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Decode: each workgroup takes an equal share of the concatenated tile stream
+// of all sequences; every (workgroup, sequence) piece writes one partial
+// into slot w + b (unique: w + b grows along the stream).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
+    const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
+    const int* __restrict__ block_table, int max_blocks, int shift,
+    const int* __restrict__ seq_lens, int batch, int H, int n_wg, int* __restrict__ prefix_out,
+    float* __restrict__ part_ml, bf16* __restrict__ part_o) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const uint32_t lds = lds_addr(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hgc = H / kHG;
+  int hg, w;
+  map_block(hgc, hg, w);
+  int* prefix = (int*)(smem + kOffPrefix);
+
+  // prefix sums of tiles per sequence (4 sequences per thread, then a scan)
+  {
+    int cnt[4], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid * 4 + i;
+      cnt[i] = b < batch ? (seq_lens[b] + kTok - 1) / kTok : 0;
+      tot += cnt[i];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int* wsum = (int*)(smem + kOffRed);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += wsum[i];
+    int run = base + incl - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid * 4 + i;
+      if (b < batch) {
+        if (b == 0) prefix[0] = 0;
+        run += cnt[i];
+        prefix[b + 1] = run;
+      }
+    }
+    __syncthreads();
+  }
+  const long T = prefix[batch];
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= batch; b += 256) prefix_out[b] = prefix[b];
+
+  long x0 = ((long)w * T) / n_wg, x1 = ((long)(w + 1) * T) / n_wg;
+  if (x0 >= x1) return;
+  // first sequence touching x0
+  int b = 0;
+  {
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= x0) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const long n_slots = (long)n_wg + batch;
+  SegState st;
+  while (x0 < x1) {
+    const long seg_end = min(x1, (long)prefix[b + 1]);
+    const int len = seq_lens[b];
+    const int tile0 = (int)(x0 - prefix[b]), tile1 = (int)(seg_end - prefix[b]);
+    if (tile1 <= tile0) {  // a sequence without rows (invalid input): nothing to attend
+      ++b;
+      continue;
+    }
+    run_segment(q_full + ((long)b * H + hg * kHG) * kW, pool, block_table + (long)b * max_blocks,
+                shift, len, tile0, tile1, lds, st, wave, lane);
+    publish_sums(st, lds, wave, lane);
+    lds_barrier();
+    const long slot = (long)hg * n_slots + w + b;
+    store_normalised(st, lds, part_o + slot * kHG * kR, kR, wave, lane);
+    if (lane < 16) {
+      const int h = 16 * wave + lane;
+      part_ml[(slot * kHG + h) * 2 + 0] = st.m;
+      part_ml[(slot * kHG + h) * 2 + 1] = head_sum(lds, h);
+    }
+    lds_barrier();
+    x0 = seg_end;
+    ++b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup per (query row, head group); whole causal range.
+// Rows are processed longest first.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256, 1) attn_prefill_kernel(
+    const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
+    const int* __restrict__ block_table, int max_blocks, int shift,
+    const int* __restrict__ start_pos, int T_len, int n_rows, int H, bf16* __restrict__ o_lat) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const uint32_t lds = lds_addr(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hgc = H / kHG;
+  const int hg = blockIdx.x % hgc;
+  const int r = blockIdx.x / hgc;
+  // longest rows first: t descending, sequences interleaved
+  const int nb = n_rows / T_len;
+  const int t = T_len - 1 - r / nb;
+  const int b = r % nb;
+  const int n = b * T_len + t;
+  const int len = start_pos[b] + t + 1;
+  SegState st;
+  run_segment(q_full + ((long)n * H + hg * kHG) * kW, pool, block_table + (long)b * max_blocks,
+              shift, len, 0, (len + kTok - 1) / kTok, lds, st, wave, lane);
+  publish_sums(st, lds, wave, lane);
+  lds_barrier();
+  store_normalised(st, lds, o_lat + ((long)n * H + hg * kHG) * kR, kR, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Combine (+ optional W_UV projection).  Workgroup = (head, 16 sequences).
+// o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kCRows = 16;
+constexpr int kOStride = kR + 8;        // bf16 per o_lat row in LDS
+constexpr int kWChunk = 128;            // W_UV rows per LDS chunk
+constexpr int kWStride = 128 + 16;      // bf16 per W_UV row in LDS (Dv <= 128)
+}
+
+__global__ void __launch_bounds__(256) combine_kernel(
+    const int* __restrict__ prefix, const float* __restrict__ part_ml,
+    const bf16* __restrict__ part_o, int batch, int H, int n_wg, const bf16* __restrict__ w_uv,
+    int Dv, bf16* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) bf16 olds[kCRows * kOStride];
+  __shared__ __attribute__((aligned(16))) bf16 wlds[kWChunk * kWStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b0 = blockIdx.y * kCRows;
+  const int hg = h / kHG, hl = h % kHG;
+  const long T = prefix[batch];
+  const long n_slots = (long)n_wg + batch;
+
+  // merge: thread -> (row tid/16, 32 columns)
+  {
+    const int rr = tid >> 4, c0 = (tid & 15) * 32;
+    const int b = b0 + rr;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    if (b < batch && prefix[b + 1] > prefix[b]) {
+      const long x0 = prefix[b], x1 = prefix[b + 1] - 1;
+      const int wf = owner_of(x0, T, n_wg), wl = owner_of(x1, T, n_wg);
+      float M = -INFINITY;
+      for (int w = wf; w <= wl; ++w)
+        M = fmaxf(M, part_ml[(((long)hg * n_slots + w + b) * kHG + hl) * 2]);
+      float den = 0.f;
+      for (int w = wf; w <= wl; ++w) {
+        const long slot = (long)hg * n_slots + w + b;
+        const float e = exp2f(part_ml[(slot * kHG + hl) * 2] - M) * part_ml[(slot * kHG + hl) * 2 + 1];
+        den += e;
+        const bf16* src = part_o + (slot * kHG + hl) * kR + c0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 v = *(const bf16x8*)(src + 8 * q);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[8 * q + i] += e * (float)v[i];
+        }
+      }
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[i] *= inv;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8 v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (bf16)acc[8 * q + i];
+      if (w_uv == nullptr) {
+        if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + c0 + 8 * q) = v;
+      } else {
+        *(bf16x8*)(olds + rr * kOStride + c0 + 8 * q) = v;
+      }
+    }
+  }
+  if (w_uv == nullptr) return;
+
+  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows x Dv, K = 512, 16x16x32 MFMAs.
+  // Wave w owns 16-column blocks w, w + 4 (Dv <= 128).
+  const bf16* W = w_uv + (long)h * kR * Dv;
+  const int nblk = Dv / 16;
+  f32x4 acc[2] = {f32x4{}, f32x4{}};
+  const uint32_t ob = lds_addr(olds), wb = lds_addr(wlds);
+  const int g = lane >> 4, li = lane & 15;
+  for (int k0 = 0; k0 < kR; k0 += kWChunk) {
+    __syncthreads();
+    const int chunks = kWChunk * Dv / 8;
+    for (int c = tid; c < chunks; c += 256) {
+      const int r = c / (Dv / 8), cc = (c % (Dv / 8)) * 8;
+      *(bf16x8*)(wlds + r * kWStride + cc) = *(const bf16x8*)(W + (long)(k0 + r) * Dv + cc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kWChunk / 32; ++ks) {
+      const bf16x8 a = lds_read_b128(ob + ((lane & 15) * kOStride + k0 + 32 * ks + 8 * (lane >> 4)) * 2);
+      // 16x16x32 B operand: lane (16g + i) needs column i of rows 8g .. 8g+7
+      const uint32_t row = 32 * ks + 8 * g + (li >> 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int nb = wave + 4 * j;
+        if (nb < nblk) {
+          const uint32_t col = 16 * nb + 4 * (li & 3);
+          const bf16x4 lo = lds_read_tr(wb + (row * kWStride + col) * 2);
+          const bf16x4 hi = lds_read_tr(wb + ((row + 4) * kWStride + col) * 2);
+          acc[j] = mfma16(a, cat(lo, hi), acc[j]);
+        }
+      }
+    }
+  }
+  // register v of lane l: row 4(l/16) + v, column l%16
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int nb = wave + 4 * j;
+    if (nb >= nblk) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int b = b0 + 4 * (lane >> 4) + v;
+      if (b < batch) out[((long)b * H + h) * Dv + 16 * nb + (lane & 15)] = (bf16)acc[j][v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+size_t decode_partial_slots(int batch, int n_wg) { return (size_t)n_wg + (size_t)batch; }
+
+int decode_num_wg(int batch, int max_seq_len, int head_groups, int num_cus) {
+  // one workgroup per CU in total; a multiple of 8 per head group (XCD pairing)
+  (void)batch;
+  (void)max_seq_len;
+  int n = num_cus / head_groups;
+  n = (n / 8) * 8;
+  return n < 8 ? 8 : n;
+}
+
+void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
+                                    int max_blocks, int block_shift, const int* seq_lens,
+                                    int batch, int H, int n_wg, int* prefix, float* part_ml,
+                                    void* part_o, hipStream_t st) {
+  const int hgc = H / kHG;
+  attn_decode_partials_kernel<<<n_wg * hgc, 256, 0, st>>>(
+      (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, seq_lens,
+      batch, H, n_wg, prefix, part_ml, (bf16*)part_o);
+}
+
+void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
+                    int n_wg, const void* w_uv, int Dv, void* out, hipStream_t st) {
+  dim3 grid(H, (batch + kCRows - 1) / kCRows);
+  combine_kernel<<<grid, 256, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H, n_wg,
+                                       (const bf16*)w_uv, Dv, (bf16*)out);
+}
+
+void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
+                                   int max_blocks, int block_shift, const int* start_pos, int T,
+                                   int batch, int H, void* o_lat, hipStream_t st) {
+  const int hgc = H / kHG;
+  const int n_rows = batch * T;
+  attn_prefill_kernel<<<n_rows * hgc, 256, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
+                                                     block_table, max_blocks, block_shift,
+                                                     start_pos, T, n_rows, H, (bf16*)o_lat);
+}
+
+}  // namespace mla

@@ -1,0 +1,96 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// log2(e): scores are pre-multiplied by it so the softmax uses exp2.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 32x32x16 bf16 MFMA.  Lane l holds A[l%32][8(l/32)+j] and B[8(l/32)+j][l%32];
+// accumulator register v of lane l is C[8(v/4) + 4(l/32) + v%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x32 bf16 MFMA.  Lane l holds A[l%16][8(l/16)+j] and B[8(l/16)+j][l%16];
+// accumulator register v of lane l is C[4(l/16) + v][l%16].
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each group of 16 lanes, output lane i element j
+// is element (i % 4) of the 8 bytes read by lane 4j + i/4 of that group.  If
+// lane 4a + b of a group reads row (r0 + a), columns (c0 + 4b .. c0 + 4b + 3)
+// of a row-major 16-bit matrix, lane i receives column c0 + i, rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 lds_read_tr(uint32_t byte_addr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(uintptr_t)byte_addr);
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t byte_addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)byte_addr;
+}
+
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ float lds_ld(uint32_t a) { return *(lds_f32*)(uintptr_t)a; }
+__device__ __forceinline__ f32x4 lds_ld4(uint32_t a) { return *(lds_f32x4*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st(uint32_t a, float v) { *(lds_f32*)(uintptr_t)a = v; }
+__device__ __forceinline__ void lds_st(uint32_t a, const bf16x4& v) { *(lds_bf16x4*)(uintptr_t)a = v; }
+
+// Address of a __shared__ object in the LDS aperture.
+template <typename T> __device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+}
+
+// Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes land at
+// lds_base + 16 * l (lds_base is wave-uniform).
+__device__ __forceinline__ void g2lds16(const void* gptr, uint32_t lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)(uintptr_t)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]; expcnt [6:4]; lgkmcnt [11:8]).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a fenced __syncthreads
+// would also wait for in-flight direct-to-LDS prefetches).  Callers wait for
+// the direct-to-LDS loads they depend on themselves (wait_vmcnt).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace mla

@@ -1,0 +1,176 @@
+// bf16 GEMM on MFMA (gfx950): C[b] = alpha * A[b] * B[b], float32 accumulate.
+//
+// A is [M, K] row-major (K contiguous) and B is [K, N] row-major (N
+// contiguous), the layout of every weight in this library (x W with W
+// [in, out]).  The MFMA B operand wants 8 consecutive k per lane, so the B
+// tile is kept in LDS in its natural [k][n] layout and read with the gfx950
+// transposing LDS load, which hands each lane one column of a 4 x 16 block.
+//
+// Tile: BM x 128 x 32 per 256-thread workgroup, 4 waves, 32x32x16 MFMAs.
+// Global loads for the next K-tile are in flight (in registers) while the
+// current one is multiplied.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int kBN = 128, kBK = 32;
+constexpr int kAStride = kBK + 8;    // bf16 per A row in LDS (80 B: conflict-free b128 reads)
+constexpr int kBStride = kBN + 16;   // bf16 per B row in LDS (288 B: conflict-free tr reads)
+
+template <int BM>
+struct Cfg {
+  static constexpr int WAVES_M = BM >= 64 ? 2 : 1;
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int FM = BM / (32 * WAVES_M);
+  static constexpr int FN = kBN / (32 * WAVES_N);
+  static constexpr int A_CHUNKS = BM * kBK / 8;    // 16-byte chunks per A tile
+  static constexpr int B_CHUNKS = kBK * kBN / 8;
+  static constexpr int A_PER_T = (A_CHUNKS + 255) / 256;
+  static constexpr int B_PER_T = B_CHUNKS / 256;
+};
+
+template <int BM, bool kOutF32>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__ A,
+                                                        const bf16* __restrict__ B,
+                                                        void* __restrict__ Cv, int M, int N, int K,
+                                                        long lda, long ldb, long ldc, long sA,
+                                                        long sB, long sC, float alpha) {
+  using C_ = Cfg<BM>;
+  __shared__ __attribute__((aligned(16))) bf16 As[BM * kAStride];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[kBK * kBStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C_::WAVES_N, wn = wave % C_::WAVES_N;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kBN;
+  A += blockIdx.z * sA;
+  B += blockIdx.z * sB;
+
+  bf16x8 ra[C_::A_PER_T], rb[C_::B_PER_T];
+  const bf16x8 zero8 = {};
+
+  auto load_tiles = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C_::A_PER_T; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+      const int gr = m0 + r, gk = k0 + kc;
+      ra[i] = (c < C_::A_CHUNKS && gr < M && gk < K)
+                  ? *(const bf16x8*)(A + (long)gr * lda + gk) : zero8;
+    }
+#pragma unroll
+    for (int i = 0; i < C_::B_PER_T; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (kBN / 8), nc = (c % (kBN / 8)) * 8;
+      const int gk = k0 + r, gn = n0 + nc;
+      rb[i] = (gk < K && gn < N) ? *(const bf16x8*)(B + (long)gk * ldb + gn) : zero8;
+    }
+  };
+  auto store_tiles = [&]() {
+#pragma unroll
+    for (int i = 0; i < C_::A_PER_T; ++i) {
+      const int c = tid + 256 * i;
+      if (c < C_::A_CHUNKS) {
+        const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+        *(bf16x8*)(As + r * kAStride + kc) = ra[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C_::B_PER_T; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (kBN / 8), nc = (c % (kBN / 8)) * 8;
+      *(bf16x8*)(Bs + r * kBStride + nc) = rb[i];
+    }
+  };
+
+  f32x16 acc[C_::FM][C_::FN];
+#pragma unroll
+  for (int i = 0; i < C_::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C_::FN; ++j) acc[i][j] = f32x16{};
+
+  const uint32_t as_base = lds_addr(As), bs_base = lds_addr(Bs);
+  // transposed-read coordinates of this lane inside a 32x32x16 B fragment
+  const int g = lane >> 4, li = lane & 15;
+  const int tr_row = 8 * (g >> 1) + (li >> 2);           // + 16 * ks (+ 4 for the high half)
+  const int tr_col = 16 * (g & 1) + 4 * (li & 3);        // + fragment column base
+
+  load_tiles(0);
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+    store_tiles();
+    __syncthreads();
+    if (k0 + kBK < K) load_tiles(k0 + kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8 af[C_::FM], bfr[C_::FN];
+#pragma unroll
+      for (int i = 0; i < C_::FM; ++i) {
+        const int r = (wm * C_::FM + i) * 32 + (lane & 31);
+        af[i] = lds_read_b128(as_base + (r * kAStride + 16 * ks + 8 * (lane >> 5)) * 2);
+      }
+#pragma unroll
+      for (int j = 0; j < C_::FN; ++j) {
+        const int col = (wn * C_::FN + j) * 32 + tr_col;
+        const int row = 16 * ks + tr_row;
+        const bf16x4 lo = lds_read_tr(bs_base + (row * kBStride + col) * 2);
+        const bf16x4 hi = lds_read_tr(bs_base + ((row + 4) * kBStride + col) * 2);
+        bfr[j] = cat(lo, hi);
+      }
+#pragma unroll
+      for (int i = 0; i < C_::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C_::FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: register v of lane l is row 8(v/4) + 4(l/32) + v%4, column l%32
+#pragma unroll
+  for (int i = 0; i < C_::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C_::FN; ++j) {
+      const int col = n0 + (wn * C_::FN + j) * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + (wm * C_::FM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < M) {
+          const float x = alpha * acc[i][j][v];
+          if constexpr (kOutF32)
+            ((float*)Cv)[blockIdx.z * sC + (long)row * ldc + col] = x;
+          else
+            ((bf16*)Cv)[blockIdx.z * sC + (long)row * ldc + col] = (bf16)x;
+        }
+      }
+    }
+}
+
+template <int BM>
+void launch_bm(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
+               long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32,
+               hipStream_t st) {
+  dim3 grid((N + kBN - 1) / kBN, (M + BM - 1) / BM, batch);
+  if (c_f32)
+    gemm_bf16_kernel<BM, true><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M, N, K,
+                                                     lda, ldb, ldc, sA, sB, sC, alpha);
+  else
+    gemm_bf16_kernel<BM, false><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M, N, K,
+                                                      lda, ldb, ldc, sA, sB, sC, alpha);
+}
+
+}  // namespace
+
+void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda,
+                      long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                      int c_f32, hipStream_t st) {
+  if (M <= 0 || N <= 0 || batch <= 0) return;
+  if (M <= 32)
+    launch_bm<32>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, st);
+  else if (M <= 64)
+    launch_bm<64>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, st);
+  else
+    launch_bm<128>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, st);
+}
+
+}  // namespace mla

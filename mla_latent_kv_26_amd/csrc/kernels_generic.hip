@@ -1,0 +1,269 @@
+// Generic kernels: the float32 VALU path and the dtype-templated epilogues
+// (RMSNorm, RoPE, paged row store) used by both dtypes.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// float32 GEMM, 16x16 output tile per 256-thread block, K staged through LDS.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A,
+                                                       const float* __restrict__ B,
+                                                       float* __restrict__ C, int M, int N, int K,
+                                                       long lda, long ldb, long ldc, long sA,
+                                                       long sB, long sC, float alpha) {
+  __shared__ float As[16][17];
+  __shared__ float Bs[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int row = blockIdx.y * 16 + ty, col = blockIdx.x * 16 + tx;
+  A += blockIdx.z * sA;
+  B += blockIdx.z * sB;
+  C += blockIdx.z * sC;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const int ka = k0 + tx, kb = k0 + ty;
+    As[ty][tx] = (row < M && ka < K) ? A[(long)row * lda + ka] : 0.f;
+    Bs[ty][tx] = (kb < K && col < N) ? B[(long)kb * ldb + col] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc = fmaf(As[ty][k], Bs[k][tx], acc);
+    __syncthreads();
+  }
+  if (row < M && col < N) C[(long)row * ldc + col] = alpha * acc;
+}
+
+void launch_gemm_f32(const float* A, const float* B, float* C, int M, int N, int K, long lda,
+                     long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                     hipStream_t st) {
+  dim3 grid((N + 15) / 16, (M + 15) / 16, batch);
+  gemm_f32_kernel<<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, alpha);
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide sum over 256 threads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_sum_256(float v, float* red /* [4] */) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+// RMSNorm of float32 rows into dtype T.  One block per row.
+template <typename T>
+__global__ void __launch_bounds__(256) rms_norm_rows_kernel(const float* __restrict__ in, long ld_in,
+                                                            const float* __restrict__ gain,
+                                                            T* __restrict__ out, long ld_out, int K,
+                                                            float eps) {
+  __shared__ float red[4];
+  const float* x = in + (long)blockIdx.x * ld_in;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < K; k += 256) ss = fmaf(x[k], x[k], ss);
+  ss = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+  T* y = out + (long)blockIdx.x * ld_out;
+  for (int k = threadIdx.x; k < K; k += 256) y[k] = from_f32<T>(x[k] * inv * gain[k]);
+}
+
+void launch_rms_norm_rows(const float* in, long ld_in, const float* gain, void* out, long ld_out,
+                          int n, int K, float eps, int dtype, hipStream_t st) {
+  if (n <= 0) return;
+  if (dtype == 1)
+    rms_norm_rows_kernel<bf16><<<n, 256, 0, st>>>(in, ld_in, gain, (bf16*)out, ld_out, K, eps);
+  else
+    rms_norm_rows_kernel<float><<<n, 256, 0, st>>>(in, ld_in, gain, (float*)out, ld_out, K, eps);
+}
+
+// ---------------------------------------------------------------------------
+// Cache rows: [RMSNorm(z[:R]) * g | RoPE(z[R:], pos)] -> pool slot.  One
+// block per token.  The RoPE table row for position p holds cos in its first
+// Dr/2 entries and sin in the rest; element i pairs with i + Dr/2.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void store_row(const float* z, const float* gain, const float* rope_row,
+                                          T* dst, int R, int Dr, float eps, float* red) {
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < R; k += 256) ss = fmaf(z[k], z[k], ss);
+  ss = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)R + eps);
+  for (int k = threadIdx.x; k < R; k += 256) dst[k] = from_f32<T>(z[k] * inv * gain[k]);
+  const int half = Dr >> 1;
+  for (int i = threadIdx.x; i < half; i += 256) {
+    const float c = rope_row[i], s = rope_row[half + i];
+    const float a = z[R + i], b = z[R + half + i];
+    dst[R + i] = from_f32<T>(a * c - b * s);
+    dst[R + half + i] = from_f32<T>(b * c + a * s);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) append_rows_kernel(const float* __restrict__ z, long ld_z,
+                                                          const float* __restrict__ gain,
+                                                          const float* __restrict__ rope,
+                                                          const int* __restrict__ pos,
+                                                          const int* __restrict__ slot,
+                                                          T* __restrict__ pool, int R, int Dr,
+                                                          float eps) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int s = slot[t];
+  if (s < 0) return;  // uniform across the block
+  store_row<T>(z + (long)t * ld_z, gain, rope + (long)pos[t] * Dr, pool + (long)s * (R + Dr), R,
+               Dr, eps, red);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) append_rows_paged_kernel(
+    const float* __restrict__ z, long ld_z, const float* __restrict__ gain,
+    const float* __restrict__ rope, const int* __restrict__ start_pos,
+    const int* __restrict__ block_table, int max_blocks, int block_size, T* __restrict__ pool,
+    int T_len, int R, int Dr, float eps) {
+  __shared__ float red[4];
+  const int n = blockIdx.x;
+  const int b = n / T_len, t = n - b * T_len;
+  const int p = start_pos[b] + t;
+  const long s = (long)block_table[(long)b * max_blocks + p / block_size] * block_size + p % block_size;
+  store_row<T>(z + (long)n * ld_z, gain, rope + (long)p * Dr, pool + s * (R + Dr), R, Dr, eps, red);
+}
+
+void launch_append_rows(const float* z, long ld_z, const float* gain, const float* rope,
+                        const int* pos, const int* slot, void* pool, int n, int R, int Dr,
+                        float eps, int dtype, hipStream_t st) {
+  if (n <= 0) return;
+  if (dtype == 1)
+    append_rows_kernel<bf16><<<n, 256, 0, st>>>(z, ld_z, gain, rope, pos, slot, (bf16*)pool, R, Dr, eps);
+  else
+    append_rows_kernel<float><<<n, 256, 0, st>>>(z, ld_z, gain, rope, pos, slot, (float*)pool, R, Dr, eps);
+}
+
+void launch_append_rows_paged(const float* z, long ld_z, const float* gain, const float* rope,
+                              const int* start_pos, const int* block_table, int max_blocks,
+                              int block_size, void* pool, int batch, int T, int R, int Dr,
+                              float eps, int dtype, hipStream_t st) {
+  const int n = batch * T;
+  if (n <= 0) return;
+  if (dtype == 1)
+    append_rows_paged_kernel<bf16><<<n, 256, 0, st>>>(z, ld_z, gain, rope, start_pos, block_table,
+                                                      max_blocks, block_size, (bf16*)pool, T, R,
+                                                      Dr, eps);
+  else
+    append_rows_paged_kernel<float><<<n, 256, 0, st>>>(z, ld_z, gain, rope, start_pos,
+                                                       block_table, max_blocks, block_size,
+                                                       (float*)pool, T, R, Dr, eps);
+}
+
+// ---------------------------------------------------------------------------
+// Rope part of the query into q_full[n, h, R:R+Dr], scaled by alpha.
+// One block per token row; threads over (head, pair).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) q_rope_kernel(const T* __restrict__ q, long ld_q,
+                                                     int head_stride, int rope_off,
+                                                     const float* __restrict__ rope,
+                                                     const int* __restrict__ start_pos, int T_len,
+                                                     T* __restrict__ q_full, int H, int R, int Dr,
+                                                     float alpha) {
+  const int n = blockIdx.x;
+  const int half = Dr >> 1;
+  const T* src = q + (long)n * ld_q + rope_off;
+  T* dst = q_full + (long)n * H * (R + Dr) + R;
+  const float* rr = nullptr;
+  if (start_pos) {
+    const int b = n / T_len;
+    rr = rope + (long)(start_pos[b] + (n - b * T_len)) * Dr;
+  }
+  for (int idx = threadIdx.x; idx < H * half; idx += 256) {
+    const int h = idx / half, i = idx - h * half;
+    const float a = to_f32(src[(long)h * head_stride + i]);
+    const float b = to_f32(src[(long)h * head_stride + half + i]);
+    float ya = a, yb = b;
+    if (rr) {
+      const float c = rr[i], s = rr[half + i];
+      ya = a * c - b * s;
+      yb = b * c + a * s;
+    }
+    dst[(long)h * (R + Dr) + i] = from_f32<T>(alpha * ya);
+    dst[(long)h * (R + Dr) + half + i] = from_f32<T>(alpha * yb);
+  }
+}
+
+void launch_q_rope(const void* q, long ld_q, int head_stride, int rope_off, const float* rope,
+                   const int* start_pos, int T, void* q_full, int n, int H, int R, int Dr,
+                   float alpha, int dtype, hipStream_t st) {
+  if (n <= 0) return;
+  if (dtype == 1)
+    q_rope_kernel<bf16><<<n, 256, 0, st>>>((const bf16*)q, ld_q, head_stride, rope_off, rope,
+                                           start_pos, T, (bf16*)q_full, H, R, Dr, alpha);
+  else
+    q_rope_kernel<float><<<n, 256, 0, st>>>((const float*)q, ld_q, head_stride, rope_off, rope,
+                                            start_pos, T, (float*)q_full, H, R, Dr, alpha);
+}
+
+// ---------------------------------------------------------------------------
+// float32 latent attention: one 64-lane workgroup per (query row, head).
+// Scores are already in log2 units (q_full carries scale * log2 e).  Lane r
+// owns latent entries r, r + 64, ... (at most kMaxPer of them).
+// ---------------------------------------------------------------------------
+constexpr int kMaxPer = 16;  // R <= 1024
+
+__global__ void __launch_bounds__(64) attention_f32_kernel(
+    const float* __restrict__ q_full, const float* __restrict__ pool,
+    const int* __restrict__ block_table, int max_blocks, int block_size,
+    const int* __restrict__ seq_lens, const int* __restrict__ start_pos, int T_len,
+    float* __restrict__ o_lat, int H, int R, int Dr) {
+  const int n = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  int seq, len;
+  if (seq_lens) {
+    seq = n;
+    len = seq_lens[n];
+  } else {
+    seq = n / T_len;
+    len = start_pos[seq] + (n - seq * T_len) + 1;
+  }
+  const int W = R + Dr;
+  const float* q = q_full + ((long)n * H + h) * W;
+  const int* table = block_table + (long)seq * max_blocks;
+  float m = -INFINITY, l = 0.f;
+  float o[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) o[i] = 0.f;
+  for (int j = 0; j < len; ++j) {
+    const float* row = pool + ((long)table[j / block_size] * block_size + j % block_size) * W;
+    float part = 0.f;
+    for (int d = lane; d < W; d += 64) part = fmaf(q[d], row[d], part);
+    const float s = wave_sum(part);
+    const float m_new = fmaxf(m, s);
+    const float alpha = exp2f(m - m_new);
+    const float p = exp2f(s - m_new);
+    l = l * alpha + p;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int r = lane + 64 * i;
+      if (r < R) o[i] = o[i] * alpha + p * row[r];
+    }
+    m = m_new;
+  }
+  float* dst = o_lat + ((long)n * H + h) * R;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int r = lane + 64 * i;
+    if (r < R) dst[r] = o[i] * inv;
+  }
+}
+
+void launch_attention_f32(const float* q_full, const float* pool, const int* block_table,
+                          int max_blocks, int block_size, const int* seq_lens,
+                          const int* start_pos, int T, float* o_lat, int n, int H, int R, int Dr,
+                          hipStream_t st) {
+  if (n <= 0) return;
+  attention_f32_kernel<<<dim3(n, H), 64, 0, st>>>(q_full, pool, block_table, max_blocks,
+                                                  block_size, seq_lens, start_pos, T, o_lat, H, R,
+                                                  Dr);
+}
+
+}  // namespace mla

@@ -1,0 +1,88 @@
+// Internal launch interface between the host dispatch and the kernels.
+// Not part of the public ABI (see include/mla.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---- generic kernels (any dtype where templated; float32 VALU otherwise) ----
+
+// C[b] = alpha * A[b] (M x K, row stride lda) * B[b] (K x N, row stride ldb),
+// float32 everywhere.  Batch strides in elements.
+void launch_gemm_f32(const float* A, const float* B, float* C, int M, int N, int K, long lda,
+                     long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                     hipStream_t st);
+
+// out[n, k] = in[n, k] / sqrt(mean_k(in[n, :]^2) + eps) * gain[k]; in float32.
+// dtype selects out's type (0 f32, 1 bf16).
+void launch_rms_norm_rows(const float* in, long ld_in, const float* gain, void* out, long ld_out,
+                          int n, int K, float eps, int dtype, hipStream_t st);
+
+// Cache rows from z = x W_DKV (float32 [n, R + Dr], row stride ld_z):
+// pool[slot[t]] = [RMSNorm(z[t, :R]) * gain | RoPE(z[t, R:], pos[t])].
+// Tokens with slot < 0 are skipped.  dtype: 0 f32, 1 bf16 pool.
+void launch_append_rows(const float* z, long ld_z, const float* gain, const float* rope,
+                        const int* pos, const int* slot, void* pool, int n, int R, int Dr,
+                        float eps, int dtype, hipStream_t st);
+
+// Same, but positions and slots derived from a page table: token t of
+// sequence b (n = b * T + t) sits at start_pos[b] + t.
+void launch_append_rows_paged(const float* z, long ld_z, const float* gain, const float* rope,
+                              const int* start_pos, const int* block_table, int max_blocks,
+                              int block_size, void* pool, int batch, int T, int R, int Dr,
+                              float eps, int dtype, hipStream_t st);
+
+// q_full[n, h, R + i] = alpha * RoPE(q[n, h, Dn + :], pos)[i]   (i < Dr),
+// q of dtype `dtype` with row stride ld_q (per token) and head stride
+// Dn + Dr; q_full row stride H * (R + Dr).  pos = start_pos[n / T] + n % T
+// when start_pos != NULL, else no rotation (decode: q_rope already rotated,
+// then q points at q_rope with Dn = 0 and head stride Dr).
+void launch_q_rope(const void* q, long ld_q, int head_stride, int rope_off, const float* rope,
+                   const int* start_pos, int T, void* q_full, int n, int H, int R, int Dr,
+                   float alpha, int dtype, hipStream_t st);
+
+// float32 latent attention, one workgroup per (query row, head):
+// o_lat[n, h] = softmax over keys 0..len-1 of 2^(q_full[n,h] . row_j) applied to c_j.
+// len = seq_lens[n] (decode) or start_pos[n / T] + n % T + 1 (prefill,
+// seq_lens == NULL); sequence = n (decode) or n / T.
+void launch_attention_f32(const float* q_full, const float* pool, const int* block_table,
+                          int max_blocks, int block_size, const int* seq_lens,
+                          const int* start_pos, int T, float* o_lat, int n, int H, int R, int Dr,
+                          hipStream_t st);
+
+// ---- bf16 MFMA kernels (gfx950) ----
+
+// C[b] = alpha * A[b] * B[b]; A, B bf16 row-major; C bf16 (c_f32 == 0) or
+// float32.  Requires K % 8 == 0, N % 8 == 0, lda/ldb % 8 == 0, 16-B aligned
+// bases and batch strides.
+void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda,
+                      long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                      int c_f32, hipStream_t st);
+
+// Decode attention over a paged bf16 pool, R = 512, Dr = 64, 64 heads per
+// workgroup, block_size a power of two >= 64.  Writes split partials (bf16
+// O normalised by its own sum, float32 (m, l) in log2 units) and the tile
+// prefix sums, for launch_combine.
+
+size_t decode_partial_slots(int batch, int n_wg);
+int decode_num_wg(int batch, int max_seq_len, int head_groups, int num_cus);
+
+void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
+                                    int max_blocks, int block_shift, const int* seq_lens,
+                                    int batch, int H, int n_wg, int* prefix, float* part_ml,
+                                    void* part_o, hipStream_t st);
+
+// Merge the partials of each (sequence, head) into o_lat (bf16 [batch, H, R])
+// or, when w_uv != NULL, project directly: out[b, h] = o_lat[b, h] W_UV[h].
+void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
+                    int n_wg, const void* w_uv, int Dv, void* out, hipStream_t st);
+
+// Prefill attention: query row n = b * T + t at position start_pos[b] + t
+// attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].
+void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
+                                   int max_blocks, int block_shift, const int* start_pos, int T,
+                                   int batch, int H, void* o_lat, hipStream_t st);
+
+}  // namespace mla

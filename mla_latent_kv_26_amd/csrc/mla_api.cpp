@@ -1,0 +1,631 @@
+// Host side of the C ABI: validation, workspace layout and kernel dispatch.
+// Every check runs before anything is enqueued; see include/mla.h.
+#include "mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+struct Dims {
+  int H, R, Dr, Dn, Dv, M, Rq, bs, dt, W, shift;
+  float scale, eps, theta;
+  size_t esz;
+};
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mla_status check_cfg(const mla_config* c, Dims* d) {
+  if (!c) return fail(MLA_ERR_INVALID_ARG, "config pointer is NULL");
+  if (c->num_heads <= 0 || c->kv_lora_rank <= 0 || c->rope_dim <= 0 || c->qk_nope_dim <= 0 ||
+      c->v_dim <= 0)
+    return fail(MLA_ERR_INVALID_ARG,
+                "num_heads, kv_lora_rank, rope_dim, qk_nope_dim and v_dim must be positive "
+                "(got %d, %d, %d, %d, %d)",
+                c->num_heads, c->kv_lora_rank, c->rope_dim, c->qk_nope_dim, c->v_dim);
+  if (c->rope_dim % 2) return fail(MLA_ERR_INVALID_ARG, "rope_dim must be even (got %d)", c->rope_dim);
+  if (c->d_model < 0 || c->q_lora_rank < 0)
+    return fail(MLA_ERR_INVALID_ARG, "d_model and q_lora_rank must be >= 0");
+  if (c->d_model > 0 && c->kv_lora_rank >= c->d_model)
+    return fail(MLA_ERR_INVALID_ARG, "kv_lora_rank (%d) must be smaller than d_model (%d)",
+                c->kv_lora_rank, c->d_model);
+  if (c->d_model > 0 && c->q_lora_rank >= c->d_model)
+    return fail(MLA_ERR_INVALID_ARG, "q_lora_rank (%d) must be smaller than d_model (%d)",
+                c->q_lora_rank, c->d_model);
+  if (c->block_size <= 0) return fail(MLA_ERR_INVALID_ARG, "block_size must be positive");
+  if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(MLA_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta))
+    return fail(MLA_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (c->dtype != MLA_DTYPE_F32 && c->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (d) {
+    d->H = c->num_heads;
+    d->R = c->kv_lora_rank;
+    d->Dr = c->rope_dim;
+    d->Dn = c->qk_nope_dim;
+    d->Dv = c->v_dim;
+    d->M = c->d_model;
+    d->Rq = c->q_lora_rank;
+    d->bs = c->block_size;
+    d->dt = c->dtype;
+    d->W = d->R + d->Dr;
+    d->shift = pow2(d->bs) ? ilog2(d->bs) : -1;
+    d->scale = c->softmax_scale > 0.f ? c->softmax_scale
+                                      : (float)(1.0 / std::sqrt((double)(d->Dn + d->Dr)));
+    d->eps = c->rms_eps;
+    d->theta = c->rope_theta;
+    d->esz = d->dt == MLA_DTYPE_BF16 ? 2 : 4;
+  }
+  return MLA_OK;
+}
+
+// Shape support of the kernels (after the config itself is valid).
+mla_status check_decode_kernels(const Dims& d, int batch) {
+  if (d.dt == MLA_DTYPE_F32) {
+    if (d.R > 1024)
+      return fail(MLA_ERR_UNSUPPORTED, "float32 path supports kv_lora_rank <= 1024 (got %d)", d.R);
+    return MLA_OK;
+  }
+  if (d.R != 512 || d.Dr != 64)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "bf16 attention kernels are built for kv_lora_rank 512 and rope_dim 64 (got %d, %d)",
+                d.R, d.Dr);
+  if (d.H % 64)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs num_heads a multiple of 64 (got %d)", d.H);
+  if (d.shift < 6)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs block_size a power of two >= 64 (got %d)",
+                d.bs);
+  if (d.Dn % 8 || d.Dv % 16 || d.Dv > 128)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "bf16 projections need qk_nope_dim % 8 == 0 and v_dim % 16 == 0, v_dim <= 128");
+  if (batch > 1024)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 decode handles at most 1024 sequences per call (got %d)",
+                batch);
+  return MLA_OK;
+}
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+mla_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+// ---- decode workspace layout ----
+struct DecodeWs {
+  size_t prefix, part_ml, part_o, q_full, o_lat, total;
+  int n_wg, hgc;
+};
+DecodeWs decode_ws(const Dims& d, int batch) {
+  DecodeWs w{};
+  size_t off = 256;  // reserved
+  if (d.dt == MLA_DTYPE_BF16) {
+    w.hgc = d.H / 64;
+    w.n_wg = mla::decode_num_wg(batch, 0, w.hgc, num_cus());
+    const size_t slots = mla::decode_partial_slots(batch, w.n_wg);
+    w.prefix = off;
+    off = up256(off + (size_t)(batch + 1) * 4);
+    w.part_ml = off;
+    off = up256(off + (size_t)w.hgc * slots * 64 * 2 * 4);
+    w.part_o = off;
+    off = up256(off + (size_t)w.hgc * slots * 64 * 512 * 2);
+  }
+  w.q_full = off;
+  off = up256(off + (size_t)batch * d.H * d.W * d.esz);
+  if (d.dt == MLA_DTYPE_F32) {
+    w.o_lat = off;
+    off = up256(off + (size_t)batch * d.H * d.R * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+// ---- prefill workspace layout ----
+struct PrefillWs {
+  size_t z, cq32, cq, q, q_full, o_lat, total;
+};
+PrefillWs prefill_ws(const Dims& d, long n) {
+  PrefillWs w{};
+  size_t off = 256;
+  w.z = off;
+  off = up256(off + (size_t)n * d.W * 4);
+  if (d.Rq > 0) {
+    w.cq32 = off;
+    off = up256(off + (size_t)n * d.Rq * 4);
+    w.cq = off;
+    off = up256(off + (size_t)n * d.Rq * d.esz);
+  }
+  w.q = off;
+  off = up256(off + (size_t)n * d.H * (d.Dn + d.Dr) * d.esz);
+  w.q_full = off;
+  off = up256(off + (size_t)n * d.H * d.W * d.esz);
+  w.o_lat = off;
+  off = up256(off + (size_t)n * d.H * d.R * (d.dt == MLA_DTYPE_BF16 ? 2 : 4));
+  w.total = off;
+  return w;
+}
+
+char* at(void* base, size_t off) { return (char*)base + off; }
+
+// dtype-dispatched GEMM: C = alpha * A B (batched, strided); out_f32 selects
+// a float32 C for bf16 inputs (float32 inputs always give float32).
+void gemm(const Dims& d, const void* A, const void* B, void* C, int M, int N, int K, long lda,
+          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha, bool out_f32,
+          hipStream_t st) {
+  if (d.dt == MLA_DTYPE_BF16)
+    mla::launch_gemm_bf16(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, out_f32 ? 1 : 0,
+                          st);
+  else
+    mla::launch_gemm_f32((const float*)A, (const float*)B, (float*)C, M, N, K, lda, ldb, ldc, sA, sB,
+                         sC, batch, alpha, st);
+}
+
+// Stage 1 (shared by decode entry points).
+void enqueue_absorb(const Dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
+                    int n_rows, void* q_full, hipStream_t st) {
+  const float alpha = d.scale * 1.4426950408889634f;
+  gemm(d, q_nope, w_uk, q_full, n_rows, d.R, d.Dn, (long)d.H * d.Dn, d.R, (long)d.H * d.W, d.Dn,
+       (long)d.Dn * d.R, d.W, d.H, alpha, false, st);
+  mla::launch_q_rope(q_rope, (long)d.H * d.Dr, d.Dr, 0, nullptr, nullptr, 1, q_full, n_rows, d.H,
+                     d.R, d.Dr, alpha, d.dt, st);
+}
+
+mla_status check_pool(const Dims& d, const void* pool, int num_blocks, const int32_t* table,
+                      int max_blocks) {
+  if (!pool || !table) return fail(MLA_ERR_INVALID_ARG, "kv_pool and block_table must be non-NULL");
+  if (num_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (max_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (d.dt == MLA_DTYPE_BF16 && !al16(pool))
+    return fail(MLA_ERR_INVALID_ARG, "kv_pool must be 16-byte aligned");
+  return MLA_OK;
+}
+
+mla_status check_ptrs16(const Dims& d, std::initializer_list<const void*> ps, const char* names) {
+  for (const void* p : ps) {
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "NULL pointer among %s", names);
+    if (d.dt == MLA_DTYPE_BF16 && !al16(p))
+      return fail(MLA_ERR_INVALID_ARG, "%s must be 16-byte aligned", names);
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+mla_status mla_validate_config(const mla_config* cfg) {
+  g_err.clear();
+  return check_cfg(cfg, nullptr);
+}
+
+int64_t mla_cache_row_elems(const mla_config* cfg) {
+  Dims d;
+  g_err.clear();
+  if (check_cfg(cfg, &d) != MLA_OK) return -1;
+  return d.W;
+}
+
+int64_t mla_cache_bytes_per_token(const mla_config* cfg) {
+  Dims d;
+  g_err.clear();
+  if (check_cfg(cfg, &d) != MLA_OK) return -1;
+  return (int64_t)d.W * (int64_t)d.esz;
+}
+
+mla_status mla_rope_table(const mla_config* cfg, int32_t num_positions, float* host_table) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (num_positions <= 0) return fail(MLA_ERR_INVALID_ARG, "num_positions must be positive");
+  if (!host_table) return fail(MLA_ERR_INVALID_ARG, "host_table is NULL");
+  const int half = d.Dr / 2;
+  for (int p = 0; p < num_positions; ++p) {
+    for (int i = 0; i < half; ++i) {
+      const double inv_freq = std::pow((double)d.theta, -2.0 * i / (double)d.Dr);
+      const double a = (double)p * inv_freq;
+      host_table[(size_t)p * d.Dr + i] = (float)std::cos(a);
+      host_table[(size_t)p * d.Dr + half + i] = (float)std::sin(a);
+    }
+  }
+  return MLA_OK;
+}
+
+// ---------------------------------------------------------------------------
+mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32_t max_seq_len,
+                                     size_t* bytes) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be positive (got %d)", batch);
+  if (max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be positive");
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = decode_ws(d, batch).total;
+  return MLA_OK;
+}
+
+static mla_status check_decode_common(const Dims& d, const void* pool, int32_t num_blocks,
+                                      const int32_t* table, int32_t max_blocks,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len) {
+  if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be positive (got %d)", batch);
+  if (max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be positive (got %d)", max_seq_len);
+  mla_status s = check_pool(d, pool, num_blocks, table, max_blocks);
+  if (s != MLA_OK) return s;
+  if (!seq_lens) return fail(MLA_ERR_INVALID_ARG, "seq_lens is NULL");
+  if ((long)max_seq_len > (long)max_blocks * d.bs)
+    return fail(MLA_ERR_INVALID_ARG,
+                "max_seq_len %d exceeds the page table capacity %ld (max_blocks_per_seq %d x block_size %d)",
+                max_seq_len, (long)max_blocks * d.bs, max_blocks, d.bs);
+  return check_decode_kernels(d, batch);
+}
+
+static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* pool,
+                                 const int32_t* table, int32_t max_blocks, const int32_t* seq_lens,
+                                 int32_t batch, const void* w_uv, void* dst, void* ws,
+                                 hipStream_t st) {
+  const DecodeWs w = decode_ws(d, batch);
+  if (d.dt == MLA_DTYPE_BF16) {
+    mla::launch_attention_partials_bf16(q_full, pool, table, max_blocks, d.shift, seq_lens, batch,
+                                        d.H, w.n_wg, (int*)at(ws, w.prefix),
+                                        (float*)at(ws, w.part_ml), at(ws, w.part_o), st);
+    mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
+                        at(ws, w.part_o), batch, d.H, w.n_wg, w_uv, d.Dv, dst, st);
+  } else {
+    float* o_lat = w_uv ? (float*)at(ws, w.o_lat) : (float*)dst;
+    mla::launch_attention_f32((const float*)q_full, (const float*)pool, table, max_blocks, d.bs,
+                              seq_lens, nullptr, 1, o_lat, batch, d.H, d.R, d.Dr, st);
+    if (w_uv)
+      gemm(d, o_lat, w_uv, dst, batch, d.Dv, d.R, (long)d.H * d.R, d.Dv, (long)d.H * d.Dv, d.R,
+           (long)d.R * d.Dv, d.Dv, d.H, 1.0f, false, st);
+  }
+  return MLA_OK;
+}
+
+mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                      const void* w_uk, const void* w_uv, const void* kv_pool, int32_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  s = check_decode_common(d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                          max_seq_len);
+  if (s != MLA_OK) return s;
+  s = check_ptrs16(d, {q_nope, q_rope, w_uk, w_uv, out}, "q_nope, q_rope, w_uk, w_uv, out");
+  if (s != MLA_OK) return s;
+  const DecodeWs w = decode_ws(d, batch);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  void* q_full = at(workspace, w.q_full);
+  enqueue_absorb(d, q_nope, q_rope, w_uk, batch, q_full, st);
+  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, w_uv, out,
+                 workspace, st);
+  return launched("mla_decode");
+}
+
+mla_status mla_absorb_query(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                            const void* w_uk, int32_t n_rows, void* q_full, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (n_rows <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be positive (got %d)", n_rows);
+  s = check_ptrs16(d, {q_nope, q_rope, w_uk, q_full}, "q_nope, q_rope, w_uk, q_full");
+  if (s != MLA_OK) return s;
+  if (d.dt == MLA_DTYPE_BF16 && d.Dn % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorption needs qk_nope_dim % 8 == 0");
+  enqueue_absorb(d, q_nope, q_rope, w_uk, n_rows, q_full, (hipStream_t)stream);
+  return launched("mla_absorb_query");
+}
+
+mla_status mla_latent_attention(const mla_config* cfg, const void* q_full, const void* kv_pool,
+                                int32_t num_blocks, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, void* o_lat, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  s = check_decode_common(d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                          max_seq_len);
+  if (s != MLA_OK) return s;
+  s = check_ptrs16(d, {q_full, o_lat}, "q_full, o_lat");
+  if (s != MLA_OK) return s;
+  const DecodeWs w = decode_ws(d, batch);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, nullptr,
+                 o_lat, workspace, (hipStream_t)stream);
+  return launched("mla_latent_attention");
+}
+
+static mla_status check_ws(const DecodeWs& w, void* workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return MLA_OK;
+}
+
+mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, const void* kv_pool,
+                                  int32_t num_blocks, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t batch, int32_t max_seq_len, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (d.dt != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "split partials exist for bf16 only; use mla_latent_attention");
+  s = check_decode_common(d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                          max_seq_len);
+  if (s != MLA_OK) return s;
+  s = check_ptrs16(d, {q_full}, "q_full");
+  if (s != MLA_OK) return s;
+  const DecodeWs w = decode_ws(d, batch);
+  s = check_ws(w, workspace, workspace_bytes);
+  if (s != MLA_OK) return s;
+  mla::launch_attention_partials_bf16(q_full, kv_pool, block_table, max_blocks_per_seq, d.shift,
+                                      seq_lens, batch, d.H, w.n_wg, (int*)at(workspace, w.prefix),
+                                      (float*)at(workspace, w.part_ml), at(workspace, w.part_o),
+                                      (hipStream_t)stream);
+  return launched("mla_attention_partials");
+}
+
+mla_status mla_combine_output(const mla_config* cfg, const void* w_uv, int32_t batch,
+                              int32_t max_seq_len, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (d.dt != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "split partials exist for bf16 only; use mla_latent_attention");
+  if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be positive (got %d)", batch);
+  if (max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be positive");
+  s = check_decode_kernels(d, batch);
+  if (s != MLA_OK) return s;
+  if (!out || !al16(out)) return fail(MLA_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
+  if (w_uv && !al16(w_uv)) return fail(MLA_ERR_INVALID_ARG, "w_uv must be 16-byte aligned");
+  const DecodeWs w = decode_ws(d, batch);
+  s = check_ws(w, workspace, workspace_bytes);
+  if (s != MLA_OK) return s;
+  mla::launch_combine((const int*)at(workspace, w.prefix), (const float*)at(workspace, w.part_ml),
+                      at(workspace, w.part_o), batch, d.H, w.n_wg, w_uv, d.Dv, out,
+                      (hipStream_t)stream);
+  return launched("mla_combine_output");
+}
+
+mla_status mla_output_projection(const mla_config* cfg, const void* o_lat, const void* w_uv,
+                                 int32_t n_rows, void* out, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (n_rows <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be positive (got %d)", n_rows);
+  s = check_ptrs16(d, {o_lat, w_uv, out}, "o_lat, w_uv, out");
+  if (s != MLA_OK) return s;
+  if (d.dt == MLA_DTYPE_BF16 && (d.R % 8 || d.Dv % 8))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 projection needs kv_lora_rank and v_dim multiples of 8");
+  gemm(d, o_lat, w_uv, out, n_rows, d.Dv, d.R, (long)d.H * d.R, d.Dv, (long)d.H * d.Dv, d.R,
+       (long)d.R * d.Dv, d.Dv, d.H, 1.0f, false, (hipStream_t)stream);
+  return launched("mla_output_projection");
+}
+
+// ---------------------------------------------------------------------------
+mla_status mla_cache_append_workspace_size(const mla_config* cfg, int32_t n_tokens, size_t* bytes) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (n_tokens <= 0) return fail(MLA_ERR_INVALID_ARG, "n_tokens must be positive");
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = up256(256 + (size_t)n_tokens * d.W * 4);
+  return MLA_OK;
+}
+
+mla_status mla_cache_append(const mla_config* cfg, const void* x, const void* w_dkv,
+                            const float* kv_norm_w, const float* rope_table, int32_t rope_table_len,
+                            const int32_t* positions, const int32_t* slot_mapping, int32_t n_tokens,
+                            void* kv_pool, int32_t num_blocks, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (d.M <= 0) return fail(MLA_ERR_INVALID_ARG, "cache append needs d_model > 0");
+  if (n_tokens <= 0) return fail(MLA_ERR_INVALID_ARG, "n_tokens must be positive (got %d)", n_tokens);
+  if (rope_table_len <= 0) return fail(MLA_ERR_INVALID_ARG, "rope_table_len must be positive");
+  if (!kv_norm_w || !rope_table || !positions || !slot_mapping)
+    return fail(MLA_ERR_INVALID_ARG, "kv_norm_w, rope_table, positions and slot_mapping must be non-NULL");
+  if (!kv_pool || num_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "kv_pool NULL or num_blocks <= 0");
+  s = check_ptrs16(d, {x, w_dkv, kv_pool}, "x, w_dkv, kv_pool");
+  if (s != MLA_OK) return s;
+  if (d.dt == MLA_DTYPE_BF16 && (d.M % 8 || d.W % 8))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 append needs d_model and kv_lora_rank + rope_dim multiples of 8");
+  size_t need = 0;
+  mla_cache_append_workspace_size(cfg, n_tokens, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  float* z = (float*)at(workspace, 256);
+  gemm(d, x, w_dkv, z, n_tokens, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
+  mla::launch_append_rows(z, d.W, kv_norm_w, rope_table, positions, slot_mapping, kv_pool, n_tokens,
+                          d.R, d.Dr, d.eps, d.dt, st);
+  return launched("mla_cache_append");
+}
+
+// ---------------------------------------------------------------------------
+mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int32_t q_len,
+                                      int32_t max_context, size_t* bytes) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  (void)max_context;
+  if (batch <= 0 || q_len <= 0) return fail(MLA_ERR_INVALID_ARG, "batch and q_len must be positive");
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = prefill_ws(d, (long)batch * q_len).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, const void* w_dq,
+                       const float* q_norm_w, const void* w_uq, const void* w_dkv,
+                       const float* kv_norm_w, const void* w_uk, const void* w_uv,
+                       const float* rope_table, int32_t rope_table_len, void* kv_pool,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* start_pos, int32_t max_start_pos, int32_t batch,
+                       int32_t q_len, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (d.M <= 0) return fail(MLA_ERR_INVALID_ARG, "prefill needs d_model > 0");
+  if (batch <= 0 || q_len <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "batch and q_len must be positive (got %d, %d)", batch, q_len);
+  if (max_start_pos < 0) return fail(MLA_ERR_INVALID_ARG, "max_start_pos must be >= 0");
+  if (!start_pos || !kv_norm_w || !rope_table)
+    return fail(MLA_ERR_INVALID_ARG, "start_pos, kv_norm_w and rope_table must be non-NULL");
+  if ((long)rope_table_len < (long)max_start_pos + q_len)
+    return fail(MLA_ERR_INVALID_ARG, "rope_table_len %d must exceed the last position %ld",
+                rope_table_len, (long)max_start_pos + q_len - 1);
+  s = check_pool(d, kv_pool, num_blocks, block_table, max_blocks_per_seq);
+  if (s != MLA_OK) return s;
+  if ((long)max_start_pos + q_len > (long)max_blocks_per_seq * d.bs)
+    return fail(MLA_ERR_INVALID_ARG, "max_start_pos + q_len (%ld) exceeds the page table capacity %ld",
+                (long)max_start_pos + q_len, (long)max_blocks_per_seq * d.bs);
+  if (d.Rq > 0) {
+    s = check_ptrs16(d, {w_dq, w_uq, (const void*)q_norm_w}, "w_dq, w_uq, q_norm_w");
+    if (s != MLA_OK) return s;
+  } else {
+    s = check_ptrs16(d, {w_q}, "w_q");
+    if (s != MLA_OK) return s;
+  }
+  s = check_ptrs16(d, {x, w_dkv, w_uk, w_uv, out}, "x, w_dkv, w_uk, w_uv, out");
+  if (s != MLA_OK) return s;
+  if (d.dt == MLA_DTYPE_BF16) {
+    s = check_decode_kernels(d, 1);
+    if (s != MLA_OK) return s;
+    if (d.M % 8 || d.Rq % 8)
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill needs d_model and q_lora_rank multiples of 8");
+  } else if (d.R > 1024) {
+    return fail(MLA_ERR_UNSUPPORTED, "float32 path supports kv_lora_rank <= 1024");
+  }
+  const long n = (long)batch * q_len;
+  if (n > (1L << 30)) return fail(MLA_ERR_INVALID_ARG, "batch * q_len too large");
+  const PrefillWs w = prefill_ws(d, n);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  const int QW = d.H * (d.Dn + d.Dr);
+  const float alpha = d.scale * 1.4426950408889634f;
+  // 1. cache rows
+  float* z = (float*)at(workspace, w.z);
+  gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
+  mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
+                                max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
+                                d.dt, st);
+  // 2. queries
+  void* q = at(workspace, w.q);
+  if (d.Rq > 0) {
+    float* cq32 = (float*)at(workspace, w.cq32);
+    void* cq = at(workspace, w.cq);
+    gemm(d, x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 0, 0, 0, 1, 1.0f, true, st);
+    mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
+    gemm(d, cq, w_uq, q, (int)n, QW, d.Rq, d.Rq, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
+  } else {
+    gemm(d, x, w_q, q, (int)n, QW, d.M, d.M, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
+  }
+  // 3. absorbed query: q_full = alpha * [q_nope W_UK | RoPE(q_pe)]
+  void* q_full = at(workspace, w.q_full);
+  mla::launch_q_rope(q, QW, d.Dn + d.Dr, d.Dn, rope_table, start_pos, q_len, q_full, (int)n, d.H,
+                     d.R, d.Dr, alpha, d.dt, st);
+  gemm(d, q, w_uk, q_full, (int)n, d.R, d.Dn, QW, d.R, (long)d.H * d.W, d.Dn + d.Dr,
+       (long)d.Dn * d.R, d.W, d.H, alpha, false, st);
+  // 4. causal attention on the latent rows
+  void* o_lat = at(workspace, w.o_lat);
+  if (d.dt == MLA_DTYPE_BF16)
+    mla::launch_attention_prefill_bf16(q_full, kv_pool, block_table, max_blocks_per_seq, d.shift,
+                                       start_pos, q_len, batch, d.H, o_lat, st);
+  else
+    mla::launch_attention_f32((const float*)q_full, (const float*)kv_pool, block_table,
+                              max_blocks_per_seq, d.bs, nullptr, start_pos, q_len, (float*)o_lat,
+                              (int)n, d.H, d.R, d.Dr, st);
+  // 5. output up-projection
+  gemm(d, o_lat, w_uv, out, (int)n, d.Dv, d.R, (long)d.H * d.R, d.Dv, (long)d.H * d.Dv, d.R,
+       (long)d.R * d.Dv, d.Dv, d.H, 1.0f, false, st);
+  return launched("mla_prefill");
+}
+
+}  // extern "C"

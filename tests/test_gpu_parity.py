@@ -1,0 +1,355 @@
+"""Parity of the HIP library with the CPU oracle, on seeded inputs.
+
+Every workload runs at its full size through the C ABI; where the oracle
+would take too long on everything it checks a stated sample of sequences or
+query rows, computed one by one.  Tolerances: float32 max abs <= 1e-5;
+bf16 storage relative L2 <= 5e-3 and max abs <= 2e-2 (plus the cosine floor
+printed by the tutorial's bf16 run).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import to_f64
+from gpu_util import (to_dev, to_host_f64, assert_f32, assert_bf16, compact_sequences,
+                      errors)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import torch  # noqa: F401
+    import mla_latent_kv_26_amd as m
+    return m
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+def gpu_decode(m, cfg, inp):
+    mc = m.MLAConfig.from_dict(cfg)
+    out = m.mla_decode(mc, to_dev(inp.q_nope), to_dev(inp.q_rope), to_dev(inp.w_uk),
+                       to_dev(inp.w_uv), to_dev(inp.pool), to_dev(inp.block_table),
+                       to_dev(inp.seq_lens), int(inp.seq_lens.max()))
+    sync()
+    return to_host_f64(out)
+
+
+def oracle_decode(cfg, inp, ids):
+    outs = []
+    for b, (pages, table, lens) in zip(ids, compact_sequences(inp, ids)):
+        o, _ = oracle.decode(to_f64(inp.q_nope[b:b + 1]), to_f64(inp.q_rope[b:b + 1]),
+                             to_f64(inp.w_uk), to_f64(inp.w_uv), pages, table, lens, cfg)
+        outs.append(o[0])
+    return np.stack(outs)
+
+
+def bf16_decode_cfg(**over):
+    base = dict(workloads.WORKLOADS["paged_ragged_h128_b64"])
+    base.update(dict(num_heads=64, lengths="explicit", paged=True, seed=11))
+    base.update(over)
+    return base
+
+
+def check_decode(m, cfg, lengths, sample=None, seed=None):
+    inp = workloads.decode_inputs(cfg, seed=seed, lengths=np.asarray(lengths, np.int32))
+    got = gpu_decode(m, cfg, inp)
+    ids = list(range(len(lengths))) if sample is None else list(sample)
+    ref = oracle_decode(cfg, inp, ids)
+    if cfg["dtype"] == "f32":
+        return assert_f32(got[ids], ref, str(lengths[:8]))
+    return assert_bf16(got[ids], ref, str(lengths[:8]), per_row_axis=0)
+
+
+# ---------------------------------------------------------------------------
+# tiny float32 layer: full forward, incremental decode, append
+# ---------------------------------------------------------------------------
+def tiny_setup(m, gain_jitter=0.1):
+    seq = workloads.tiny_sequence(gain_jitter=gain_jitter)
+    cfg = seq.cfg
+    mc = m.MLAConfig.from_dict(cfg)
+    w = {k: to_dev(v) for k, v in vars(seq.weights).items() if v is not None}
+    w64 = {k: (None if v is None else to_f64(v)) for k, v in vars(seq.weights).items()}
+    return seq, cfg, mc, w, w64
+
+
+def test_tiny_fp32_full_forward(m):
+    import torch
+    seq, cfg, mc, w, w64 = tiny_setup(m)
+    pool = torch.zeros((2, 64, mc.row), dtype=torch.float32, device="cuda")
+    table = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    out = m.mla_prefill(mc, to_dev(seq.x), w, pool, table,
+                        torch.zeros(1, dtype=torch.int32, device="cuda"), 0)
+    sync()
+    ref, rows = oracle.layer_forward(to_f64(seq.x[0]), w64, cfg, storage="f32")
+    assert_f32(to_host_f64(out)[0], ref, "tiny full forward")
+    got_rows = to_host_f64(pool).reshape(-1, mc.row)[:65]
+    assert_f32(got_rows, rows, "tiny cache rows")
+
+
+def test_tiny_fp32_incremental_equals_full(m):
+    """Ticket acceptance criterion on the GPU: decode of token 64 after a
+    64-token prefill equals row 64 of the 65-token forward within 1e-5."""
+    import torch
+    seq, cfg, mc, w, w64 = tiny_setup(m)
+    table = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    pool_a = torch.zeros((2, 64, mc.row), dtype=torch.float32, device="cuda")
+    full = m.mla_prefill(mc, to_dev(seq.x), w, pool_a, table,
+                         torch.zeros(1, dtype=torch.int32, device="cuda"), 0)
+    pool_b = torch.zeros_like(pool_a)
+    x = to_dev(seq.x)
+    m.mla_prefill(mc, x[:, :64].contiguous(), w, pool_b, table,
+                  torch.zeros(1, dtype=torch.int32, device="cuda"), 0)
+    step = m.mla_prefill(mc, x[:, 64:].contiguous(), w, pool_b, table,
+                         torch.full((1,), 64, dtype=torch.int32, device="cuda"), 64)
+    sync()
+    assert_f32(to_host_f64(step)[0, 0], to_host_f64(full)[0, 64], "incremental vs full (gpu)")
+    ref, _ = oracle.layer_forward(to_f64(seq.x[0]), w64, cfg, storage="f32")
+    assert_f32(to_host_f64(step)[0, 0], ref[64], "incremental vs oracle")
+    np.testing.assert_array_equal(to_host_f64(pool_a), to_host_f64(pool_b))
+
+
+def test_tiny_fp32_decode_ragged(m):
+    cfg = dict(workloads.WORKLOADS["tiny_fp32"], batch=5, lengths="explicit", paged=True,
+               block_size=16, seed=21)
+    check_decode(m, cfg, [1, 5, 64, 65, 200])
+
+
+def test_tiny_fp32_cache_append_with_skip(m):
+    import torch
+    seq, cfg, mc, w, w64 = tiny_setup(m)
+    mc16 = dataclasses.replace(mc, block_size=16)
+    pool = torch.full((8, 16, mc.row), 7.0, dtype=torch.float32, device="cuda")
+    pos = np.array([3, 0, 50, 64, 9], np.int32)
+    slots = np.array([5, 17, -1, 127, 40], np.int32)
+    x = to_dev(seq.x[0, :5].copy())
+    m.mla_cache_append(mc16, x, w["w_dkv"], w["kv_norm_w"], to_dev(pos), to_dev(slots), pool,
+                       rope_table=m.mla_rope_table(mc16, 65).cuda())
+    sync()
+    ref = oracle.append_rows(to_f64(seq.x[0, :5]), pos, w64, cfg, storage="f32")
+    flat = to_host_f64(pool).reshape(-1, mc.row)
+    for i, s in enumerate(slots):
+        if s >= 0:
+            assert_f32(flat[s], ref[i], f"append slot {s}")
+    untouched = np.setdiff1d(np.arange(flat.shape[0]), slots[slots >= 0])
+    assert np.all(flat[untouched] == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# bf16 decode
+# ---------------------------------------------------------------------------
+def test_decode_h64_b32_l4096_full(m):
+    """Kimi-scale decode, contiguous cache, every sequence checked."""
+    cfg = workloads.WORKLOADS["decode_h64_b32_l4096"]
+    inp = workloads.decode_inputs(cfg)
+    got = gpu_decode(m, cfg, inp)
+    ref = oracle_decode(cfg, inp, range(cfg["batch"]))
+    e = assert_bf16(got, ref, "decode_h64_b32_l4096", per_row_axis=0)
+    print("decode_h64_b32_l4096", e)
+
+
+def test_decode_edge_lengths(m):
+    check_decode(m, bf16_decode_cfg(), [1, 2, 63, 64, 65, 127, 128, 129, 1000, 4097])
+
+
+def test_decode_more_sequences_than_workgroups(m):
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 300, size=300)
+    check_decode(m, bf16_decode_cfg(), lens, sample=[0, 1, 2, 150, 298, 299])
+
+
+def test_decode_max_batch_1024(m):
+    lens = (np.arange(1024) % 97) + 1
+    check_decode(m, bf16_decode_cfg(seed=12), lens, sample=[0, 96, 500, 1023])
+
+
+def test_decode_single_long_sequence(m):
+    check_decode(m, bf16_decode_cfg(), [20000])
+
+
+def test_decode_h128_ragged(m):
+    check_decode(m, bf16_decode_cfg(num_heads=128, seed=13), [1, 100, 4096, 5000, 16384])
+
+
+def test_paged_ragged_h128_b64_full(m):
+    cfg = workloads.WORKLOADS["paged_ragged_h128_b64"]
+    inp = workloads.decode_inputs(cfg)
+    got = gpu_decode(m, cfg, inp)
+    L = inp.seq_lens
+    ids = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 17, 40, 63})
+    ref = oracle_decode(cfg, inp, ids)
+    e = assert_bf16(got[ids], ref, "paged_ragged_h128_b64", per_row_axis=0)
+    print("paged_ragged_h128_b64 sample", ids, e)
+
+
+def test_longctx_h64_b4_l131072_full(m):
+    cfg = workloads.WORKLOADS["longctx_h64_b4_l131072"]
+    inp = workloads.decode_inputs(cfg)
+    got = gpu_decode(m, cfg, inp)
+    ids = [0, 3]
+    ref = oracle_decode(cfg, inp, ids)
+    e = assert_bf16(got[ids], ref, "longctx_h64_b4_l131072", per_row_axis=0)
+    print("longctx_h64_b4_l131072 sample", ids, e)
+
+
+def test_decode_zero_query_is_mean_of_latents(m):
+    cfg = bf16_decode_cfg(seed=14)
+    lens = np.array([1, 77, 3000], np.int32)
+    inp = workloads.decode_inputs(cfg, lengths=lens)
+    inp.q_nope[:] = 0
+    inp.q_rope[:] = 0
+    mc = m.MLAConfig.from_dict(cfg)
+    o_lat = m.mla_latent_attention(
+        mc, m.mla_absorb_query(mc, to_dev(inp.q_nope), to_dev(inp.q_rope), to_dev(inp.w_uk)),
+        to_dev(inp.pool), to_dev(inp.block_table), to_dev(inp.seq_lens), int(lens.max()))
+    sync()
+    got = to_host_f64(o_lat)
+    for b, (pages, table, L) in enumerate(compact_sequences(inp, range(3))):
+        rows = oracle.gather_sequence(pages, table[0], int(L[0]))
+        mean = rows[:, :cfg["kv_lora_rank"]].mean(axis=0)
+        assert_bf16(got[b], np.broadcast_to(mean, got[b].shape), f"uniform mean b={b}")
+
+
+def test_staged_calls_match_decode_and_oracle_latent(m):
+    cfg = bf16_decode_cfg(seed=15)
+    lens = np.array([5, 64, 700, 2500], np.int32)
+    inp = workloads.decode_inputs(cfg, lengths=lens)
+    mc = m.MLAConfig.from_dict(cfg)
+    qf = m.mla_absorb_query(mc, to_dev(inp.q_nope), to_dev(inp.q_rope), to_dev(inp.w_uk))
+    o_lat = m.mla_latent_attention(mc, qf, to_dev(inp.pool), to_dev(inp.block_table),
+                                   to_dev(inp.seq_lens), int(lens.max()))
+    out = m.mla_output_projection(mc, o_lat, to_dev(inp.w_uv))
+    sync()
+    full = gpu_decode(m, cfg, inp)
+    assert_bf16(to_host_f64(out), full, "staged vs fused")
+    # o_lat against the oracle's absorbed latent output
+    for b, (pages, table, L) in enumerate(compact_sequences(inp, range(len(lens)))):
+        _, ol = oracle.decode(to_f64(inp.q_nope[b:b + 1]), to_f64(inp.q_rope[b:b + 1]),
+                              to_f64(inp.w_uk), to_f64(inp.w_uv), pages, table, L, cfg)
+        assert_bf16(to_host_f64(o_lat)[b], ol[0], f"o_lat b={b}")
+    # absorbed query: scale * log2(e) * [q_nope W_UK | q_rope]
+    alpha = oracle.softmax_scale(cfg) / np.log(2.0)
+    ql = oracle.absorb_query(to_f64(inp.q_nope), to_f64(inp.w_uk))
+    want = alpha * np.concatenate([ql, to_f64(inp.q_rope)], axis=-1)
+    assert_bf16(to_host_f64(qf), want, "q_full")
+
+
+def test_page_permutation_invariance_and_determinism(m):
+    """Same logical rows in two physical page orders give bitwise-equal
+    outputs, and a repeated call is bitwise identical."""
+    cfg = bf16_decode_cfg(seed=16)
+    lens = np.array([130, 3000, 64, 1], np.int32)
+    inp = workloads.decode_inputs(cfg, lengths=lens)
+    a = gpu_decode(m, cfg, inp)
+    a2 = gpu_decode(m, cfg, inp)
+    np.testing.assert_array_equal(a, a2)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(inp.pool.shape[0])       # new physical index of each page
+    pool2 = np.empty_like(inp.pool)
+    pool2[perm] = inp.pool
+    table2 = inp.block_table.copy()
+    for b, L in enumerate(lens):
+        n = -(-int(L) // 64)
+        table2[b, :n] = perm[inp.block_table[b, :n]]
+    inp2 = dataclasses.replace(inp, pool=pool2, block_table=table2)
+    b_ = gpu_decode(m, cfg, inp2)
+    np.testing.assert_array_equal(a, b_)
+
+
+def test_garbage_beyond_sequence_end_is_ignored(m):
+    """Unused slots of a sequence's last page hold NaN; they must not leak."""
+    cfg = bf16_decode_cfg(seed=17)
+    lens = np.array([65, 1, 200], np.int32)
+    inp = workloads.decode_inputs(cfg, lengths=lens)
+    ref = oracle_decode(cfg, inp, range(3))
+    nan_bits = np.uint16(0x7FC0)
+    for b, L in enumerate(lens):
+        last = inp.block_table[b, (int(L) - 1) // 64]
+        inp.pool[last, (int(L) - 1) % 64 + 1:] = nan_bits
+    got = gpu_decode(m, cfg, inp)
+    assert_bf16(got, ref, "NaN padding")
+
+
+# ---------------------------------------------------------------------------
+# bf16 prefill
+# ---------------------------------------------------------------------------
+def _pool_rows(pool_np, table, L):
+    bs = pool_np.shape[1]
+    j = np.arange(L)
+    return pool_np[table[j // bs], j % bs]
+
+
+def check_rows(got, ref, what):
+    """Stored bf16 rows: each element within one bf16 step of the oracle's
+    stored value (2^-7 relative covers one ulp anywhere in a binade; the two
+    sides round different float32/float64 sums, so a value next to a rounding
+    boundary can land one step apart), or within 1e-4 absolute where the
+    value is near zero (the float32 sum over d_model products carries ~1e-5
+    absolute error before the store); plus the bf16 relative-L2 bar."""
+    bound = np.maximum(2.0 ** -7 * np.abs(ref), 1e-4)
+    worst = np.max(np.abs(got - ref) / bound)
+    assert worst <= 1.0, f"{what}: worst element at {worst:.2f} of its bound"
+    e = assert_bf16(got, ref, what)
+    print(what, "exact fraction", float(np.mean(got == ref)), e)
+
+
+def test_prefill_small_bf16_with_query_rank_and_continuation(m):
+    import torch
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=128,
+               seed=31)
+    mc = m.MLAConfig.from_dict(cfg)
+    inp = workloads.prefill_inputs(cfg, q_len=150, batch=2, gain_jitter=0.1)
+    w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+    w64 = {k: (None if v is None else to_f64(v)) for k, v in vars(inp.weights).items()}
+    pool = torch.zeros((inp.num_blocks, 64, mc.row), dtype=torch.bfloat16, device="cuda")
+    table = to_dev(inp.block_table)
+    x = to_dev(inp.x)
+    # first 100 tokens, then 50 more continuing at position 100
+    out1 = m.mla_prefill(mc, x[:, :100].contiguous(), w, pool, table,
+                         torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+    out2 = m.mla_prefill(mc, x[:, 100:].contiguous(), w, pool, table,
+                         torch.full((2,), 100, dtype=torch.int32, device="cuda"), 100)
+    sync()
+    got = np.concatenate([to_host_f64(out1), to_host_f64(out2)], axis=1)
+    pool_np = to_host_f64(pool)
+    for b in range(2):
+        ref, rows = oracle.layer_forward(to_f64(inp.x[b]), w64, cfg, storage="bf16")
+        g_rows = _pool_rows(pool_np, inp.block_table[b], 150)
+        check_rows(g_rows, rows, f"small prefill rows b={b}")
+        assert_bf16(got[b], ref, f"small prefill b={b}", per_row_axis=0)
+
+
+def test_prefill_d7168_b2_t4096_full(m):
+    """Full-size prefill: every appended cache row checked, outputs on a
+    sample of query rows (first, block edges, last) of both sequences."""
+    import torch
+    cfg = workloads.WORKLOADS["prefill_d7168_b2_t4096"]
+    mc = m.MLAConfig.from_dict(cfg)
+    inp = workloads.prefill_inputs(cfg)
+    w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+    pool = torch.zeros((inp.num_blocks, 64, mc.row), dtype=torch.bfloat16, device="cuda")
+    out = m.mla_prefill(mc, to_dev(inp.x), w, pool, to_dev(inp.block_table),
+                        torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+    sync()
+    w64 = {k: (None if v is None else to_f64(v)) for k, v in vars(inp.weights).items()}
+    pool_np = to_host_f64(pool)
+    T = cfg["q_len"]
+    sample = [0, 1, 63, 64, 65, 1000, 2047, 4095]
+    for b in range(2):
+        x64 = to_f64(inp.x[b])
+        rows = oracle.append_rows(x64, np.arange(T), w64, cfg, storage="bf16")
+        g_rows = _pool_rows(pool_np, inp.block_table[b], T)
+        check_rows(g_rows, rows, f"cache rows b={b}")
+        ref = oracle.attend_tokens(x64[sample], np.array(sample), w64, cfg, rows, q_block=1)
+        got = to_host_f64(out[b, sample])
+        e = assert_bf16(got, ref, f"prefill b={b}", per_row_axis=0)
+        print("prefill_d7168_b2_t4096", b, e)
