@@ -1,0 +1,238 @@
+"""Benchmark: one MLA decode step (query absorption, split-KV latent attention,
+combine + W_UV projection) at H=64, B=32, L=4096 on one MI355X.
+
+Prints one JSON line.  `value` is the step's algorithmic HBM traffic divided
+by its time (TB/s); `ms_per_step` gives the step time.  Inputs are synthetic
+(seeded, shapes and distributions of the workload) and resident in HBM; the
+timed steps rotate over several independently drawn input sets whose total
+size exceeds the 256 MB Infinity Cache, so repeats are served from HBM.
+
+Timing: the step's kernels are captured in a HIP graph (one replay launches
+every step of one rotation), and HIP events on the launching stream bracket
+the replays.  The split-KV attention kernel is timed the same way on its own
+for the roofline entry.  The oracle is timed on the host cores on a bounded
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "MLA latent decode: µs/step, HBM TB/s, MFMA TFLOP/s at H=64 B=32 L=4096"
+ATTN_SRC = os.path.join(ROOT, "mla_latent_kv_26_amd", "csrc", "attention_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_traffic.json")
+
+
+def algorithmic(cfg, lens):
+    """Bytes and FLOPs a decode step must move/do (cache rows once, weights
+    once, queries in, outputs out) and the attention kernel's share."""
+    H, R, Dr, Dn, Dv = (cfg[k] for k in ("num_heads", "kv_lora_rank", "rope_dim",
+                                         "qk_nope_dim", "v_dim"))
+    B = len(lens)
+    tokens = int(np.sum(lens))
+    row_bytes = (R + Dr) * 2
+    cache = tokens * row_bytes
+    weights = 2 * H * R * (Dn + Dv)
+    io = 2 * B * H * (Dn + Dr + Dv)
+    flops_attn = 2 * H * (R + Dr + R) * tokens
+    flops_proj = 2 * B * H * R * (Dn + Dv)
+    return dict(step_bytes=cache + weights + io, attn_bytes=cache, tokens=tokens,
+                step_flops=flops_attn + flops_proj, attn_flops=flops_attn)
+
+
+def cpu_baseline(cfg, seconds):
+    """Time the oracle's decode (float64 numpy, as it stands) on whole steps of
+    the same workload until about `seconds` of work; report TB/s of
+    algorithmic bytes like the GPU line."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    inp = workloads.decode_inputs(cfg)
+    args = [workloads.to_f64(a) for a in (inp.q_nope, inp.q_rope, inp.w_uk, inp.w_uv, inp.pool)]
+    alg = algorithmic(cfg, inp.seq_lens)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode(*args, inp.block_table, inp.seq_lens, cfg)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > seconds:
+            break
+    t = float(np.median(times))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": alg["step_bytes"] / t / 1e12, "unit": "TB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(times)} full decode steps of {cfg['batch']}x{cfg['context']} tokens, "
+                      f"absorbed path in float64 numpy, median {t * 1e3:.1f} ms/step",
+            "ms_per_step": t * 1e3}
+
+
+def traffic_entry():
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def graph_time(torch, fn, reps, stream):
+    """Capture fn() once in a graph, replay `reps` times between two events."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    a.record(cur)
+    for _ in range(reps):
+        g.replay()
+    b.record(cur)
+    b.synchronize()
+    return a.elapsed_time(b) / reps  # ms per replay
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default=workloads.HEADLINE,
+                    choices=[k for k, v in workloads.WORKLOADS.items() if "q_len" not in v
+                             and v["dtype"] == "bf16"])
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MB (10 times), as the "
+                         "known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 10}))
+        return
+    import mla_latent_kv_26_amd as m
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = workloads.WORKLOADS[args.workload]
+    mc = m.MLAConfig.from_dict(cfg)
+    lens0 = workloads.decode_lengths(cfg, np.random.Generator(np.random.PCG64(cfg["seed"])))
+    sets = [workloads.decode_inputs_torch(cfg, cfg["seed"] + 1000 * i, dev, lengths=lens0)
+            for i in range(args.rotate)]
+    B, H = len(lens0), cfg["num_heads"]
+    max_len = int(lens0.max())
+    alg = algorithmic(cfg, lens0)
+    ws = [torch.zeros(m.mla_decode_workspace_size(mc, B, max_len), dtype=torch.uint8, device=dev)
+          for _ in sets]
+    out = torch.empty((B, H, cfg["v_dim"]), dtype=torch.bfloat16, device=dev)
+    qf = [m.mla_absorb_query(mc, s["q_nope"], s["q_rope"], s["w_uk"]) for s in sets]
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i]
+        m.mla_decode(mc, s["q_nope"], s["q_rope"], s["w_uk"], s["w_uv"], s["pool"],
+                     s["block_table"], s["seq_lens"], max_len, out=out, workspace=ws[i])
+
+    def attn(i):
+        s = sets[i]
+        m.mla_attention_partials(mc, qf[i], s["pool"], s["block_table"], s["seq_lens"], max_len,
+                                 ws[i])
+
+    R = len(sets)
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    # eager: python issues every call
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        step(i % R)
+    b.record()
+    b.synchronize()
+    eager_ms = a.elapsed_time(b) / args.steps
+
+    # graph: one replay = one step on each input set
+    side = torch.cuda.Stream()
+    reps = max(1, args.steps // R)
+    step_ms = graph_time(torch, lambda: [step(i) for i in range(R)], reps, side) / R
+    attn_ms = graph_time(torch, lambda: [attn(i) for i in range(R)], reps, side) / R
+    steps_timed = reps * R
+
+    value = alg["step_bytes"] / (step_ms * 1e-3) / 1e12
+    achieved = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": steps_timed,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "us_per_step": round(step_ms * 1e3, 3),
+        "tflops": round(alg["step_flops"] / (step_ms * 1e-3) / 1e12, 2),
+        "cached_tokens_per_s": round(alg["tokens"] / (step_ms * 1e-3), 1),
+        "eager_us_per_step": round(eager_ms * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "context": max_len,
+                   "cached_tokens": alg["tokens"], "heads": H,
+                   "kv_lora_rank": cfg["kv_lora_rank"], "rope_dim": cfg["rope_dim"],
+                   "qk_nope_dim": cfg["qk_nope_dim"], "v_dim": cfg["v_dim"],
+                   "block_size": cfg["block_size"], "input_sets_rotated": R,
+                   "timing": "hip graph replay, events on the launching stream"},
+        "roofline": {
+            "kernel": "attn_decode_partials_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_entry(),
+            "kernel_us": round(attn_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": alg["attn_bytes"],
+            "mfma_tflops": round(alg["attn_flops"] / (attn_ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(alg["attn_flops"] / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline and args.workload == workloads.HEADLINE:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

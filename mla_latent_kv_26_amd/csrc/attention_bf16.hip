@@ -12,16 +12,16 @@
 // for S (16-byte LDS reads) and column-wise for P*C (transposing LDS reads),
 // so every cached byte leaves HBM once.
 //
-// Workgroup: 256 threads = 4 waves, 64 heads.  For S each wave takes 16
-// heads and all 64 tokens of the tile (its 16 heads' queries stay in
-// registers, and each head's row max and row sum stay inside one wave); for
-// P*C each wave owns a 128-column quarter of O for all 64 heads.  Tiles stream HBM -> LDS
-// with asynchronous direct-to-LDS loads into two buffers: tile j+1 is in
-// flight while tile j is multiplied.
+// Workgroup: 512 threads = 8 waves (two per SIMD, so one wave's LDS waits
+// overlap the other's MFMAs), 64 heads.  For S, wave w takes heads
+// 16 (w%4) .. +16 and tokens 32 (w/4) .. +32 of the tile (its heads' queries
+// stay in registers); for P*C, wave w owns columns 64 w .. +64 of O for all
+// 64 heads.  Tiles stream HBM -> LDS with asynchronous direct-to-LDS loads
+// into two buffers: tile j+1 is in flight while tile j is multiplied.
 //
 // Tile layout in LDS: chunk-major.  The 16-byte chunk k (of 72) of row t
 // (of 64) sits at slot k*64 + (t ^ 4*(k&1)).  One direct-to-LDS load
-// instruction then moves chunk k of all 64 rows (a lane per row), row-wise
+// instruction moves chunk k of all 64 rows (a lane per row), row-wise
 // fragment reads (8 consecutive rows, one chunk) hit 8 consecutive slots,
 // and a transposing read (4 rows x 2 neighbouring chunks) hits 8 distinct
 // slot positions: neither access pattern has bank conflicts.
@@ -36,44 +36,45 @@ constexpr int kTok = 64;                                // tokens per tile
 constexpr int kCh = kW * 2 / 16;                        // 72 chunks per row
 constexpr int kTileBytes = kTok * kW * 2;               // 73728
 constexpr int kHG = 64;                                 // heads per workgroup
-constexpr int kLoads = kTok * kCh / (64 * 4);           // 18 loads per wave per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoads = kCh / kWaves;                    // 9 chunk loads per wave per tile
 constexpr int kPStride = 72;                            // bf16 per P row (64 + 8)
+constexpr int kOStride = kR + 8;                        // bf16 per staged output row
 constexpr int kMaxBatch = 1024;
 
-constexpr int kOffP = 2 * kTileBytes;
-constexpr int kOffAlpha = kOffP + kHG * kPStride * 2;  // float [64] rescale factors
-constexpr int kOffFlag = kOffAlpha + kHG * 4;           // int [4] per-wave rescale flags
-constexpr int kOffLsum = kOffFlag + 16;                 // float [64] row sums
-constexpr int kOffRed = kOffLsum + kHG * 4;             // scratch for the prefix scan
-constexpr int kOffPrefix = kOffRed + 64;                // int [kMaxBatch + 1]
+constexpr int kOffP = 2 * kTileBytes;                   // bf16 [64][72]
+constexpr int kOffRed = kOffP + kHG * kPStride * 2;     // float [2][64] half-tile maxima
+constexpr int kOffAlpha = kOffRed + 2 * kHG * 4;        // float [64] rescale factors
+constexpr int kOffFlag = kOffAlpha + kHG * 4;           // float [8] per-wave rescale flags
+constexpr int kOffLsum = kOffFlag + 32;                 // float [2][64] row sums
+constexpr int kOffInv = kOffLsum + 2 * kHG * 4;         // float [64] 1 / row sum
+constexpr int kOffScan = kOffInv + kHG * 4;             // int [8] scan scratch
+constexpr int kOffPrefix = kOffScan + 32;               // int [kMaxBatch + 1]
 constexpr int kLdsBytes = kOffPrefix + (kMaxBatch + 1) * 4;
-// A head's running max only moves when a tile exceeds it by more than this
+static_assert(kLdsBytes <= 163840, "LDS budget");
+static_assert(kHG * kOStride * 2 <= 2 * kTileBytes, "output staging fits the tile buffers");
+// A head's reference max only moves when a tile exceeds it by more than this
 // (log2 units): probabilities stay below 2^8 and O is rescaled rarely.
 constexpr float kRescaleSlack = 8.0f;
-static_assert(kLdsBytes <= 163840, "LDS budget");
-
-__device__ __forceinline__ uint32_t toff(uint32_t t, uint32_t k) {
-  return (k * kTok + (t ^ ((k & 1u) << 2))) * 16u;
-}
 
 // Issue the asynchronous loads of one tile: `valid` rows (1..64) starting at
-// row pointer `rows`.  Wave w loads chunks 18w .. 18w+17 of every row; lane l
-// carries row l (even chunks) or row l^4 (odd chunks).  Rows past `valid`
-// repeat the last valid row so the tile holds finite data (their
-// probabilities are zero).
+// row pointer `rows`.  Wave w loads chunks w, w+8, ..., w+64 of every row
+// (all of one parity, so a lane carries row lane or lane^4 throughout).
+// Rows past `valid` repeat the last valid row so the tile holds finite data
+// (their probabilities are zero).
 __device__ __forceinline__ void issue_tile(const bf16* rows, int valid, uint32_t buf, int wave,
                                            int lane) {
-  const int te = min(lane, valid - 1), to = min(lane ^ 4, valid - 1);
-  const bf16* pe = rows + te * kW + wave * kLoads * 8;
-  const bf16* po = rows + to * kW + wave * kLoads * 8;
-  const uint32_t dst = buf + (uint32_t)(wave * kLoads) * 1024u;
+  const int t = lane ^ ((wave & 1) << 2);
+  const bf16* p = rows + min(t, valid - 1) * kW + wave * 8;
+  const uint32_t dst = buf + (uint32_t)wave * 1024u;
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) g2lds16((i & 1 ? po : pe) + i * 8, dst + i * 1024u);
+  for (int i = 0; i < kLoads; ++i) g2lds16(p + i * 64, dst + i * 8192u);
 }
 
 struct SegState {
-  f32x16 o[2][4];   // O[32 hb + ..][128 wave + 32 cb + ..]
-  float m;          // reference max of head 16 wave + lane%16, log2 units
+  f32x16 o[2][2];   // O[32 hb + ..][64 wave + 32 cb + ..]
+  float m;          // reference max of this lane's S head, log2 units
   float l;          // lane-partial running sum for that head
 };
 
@@ -84,23 +85,25 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
                                             const int* __restrict__ table, int shift, int len,
                                             int tile0, int tile1, uint32_t lds, SegState& st,
                                             int wave, int lane) {
-  const uint32_t p_lds = lds + kOffP, alp = lds + kOffAlpha, flags = lds + kOffFlag;
-  const int h = 16 * wave + (lane & 15);   // this lane's head in the S phase
+  const uint32_t p_lds = lds + kOffP, alp = lds + kOffAlpha, red = lds + kOffRed;
+  const int hq = wave & 3, th = wave >> 2;
+  const int h = 16 * hq + (lane & 15);     // this lane's head in the S phase
   const uint32_t kq = lane >> 4;           // 0..3
 
   // Per-lane LDS bases; every other offset below is a compile-time constant.
-  // S phase (16x16x32): row 16 tb + lane%16, chunk 4 ks + kq -> s_base + 256 tb + 4096 ks.
-  const uint32_t s_base = (kq * 64u + ((lane & 15) ^ ((kq & 1u) << 2))) * 16u;
-  // P*C phase, transposing reads: lane (16 g + li) of the fragment for token
-  // block ks and column block cb reads row 16 ks + x (+4), chunk kb + 4 cb.
+  // S: row 32 th + 16 tb + lane%16, chunk 4 ks + kq -> s_base + 256 tb + 4096 ks.
+  const uint32_t s_base =
+      (kq * 64u + ((32u * th + (lane & 15)) ^ ((kq & 1u) << 2))) * 16u;
+  // P*C transposing reads: lane (16 g + li) of the fragment for token block
+  // ks and column block cb reads row 16 ks + x (+4), chunk kb + 4 cb.
   const uint32_t g = lane >> 4, li = lane & 15;
   const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u;
-  const uint32_t kb = 16u * wave + 2u * (g & 1) + b1;
+  const uint32_t kb = 8u * wave + 2u * (g & 1) + b1;
   const uint32_t tr_lo = (kb * 64u + x + 4u * b1) * 16u + 8u * (li & 1);
   const uint32_t tr_hi = (kb * 64u + x + 4u * (1u - b1)) * 16u + 8u * (li & 1);
   // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
   const uint32_t pa_base = p_lds + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
-  const uint32_t pw_base = p_lds + (h * kPStride + 4 * kq) * 2;
+  const uint32_t pw_base = p_lds + (h * kPStride + 32 * th + 4 * kq) * 2;
   const uint32_t al_base = alp + 16 * (lane >> 5);
 
   // queries of this wave's 16 heads: B operand of S^T = T Q^T (16x16x32)
@@ -113,66 +116,71 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) st.o[a][b] = f32x16{};
+    for (int b = 0; b < 2; ++b) st.o[a][b] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
 
   const int mask = (1 << shift) - 1;
-  auto rows_of = [&](int tile) {
-    const int tok = tile * kTok;
-    const int page = table[tok >> shift];
-    return pool + ((long)page * (mask + 1) + (tok & mask)) * kW;
+  auto rows_at = [&](int tile, int page) {
+    return pool + ((long)page * (mask + 1) + ((tile * kTok) & mask)) * kW;
   };
-
-  issue_tile(rows_of(tile0), min(kTok, len - tile0 * kTok), lds, wave, lane);
+  int page = table[(tile0 * kTok) >> shift];
+  issue_tile(rows_at(tile0, page), min(kTok, len - tile0 * kTok), lds, wave, lane);
+  int next_page = (tile0 + 1 < tile1) ? table[((tile0 + 1) * kTok) >> shift] : 0;
 
   for (int tile = tile0; tile < tile1; ++tile) {
     const uint32_t buf = lds + (uint32_t)((tile - tile0) & 1) * kTileBytes;
     wait_vmcnt<0>();
     lds_barrier();  // tile visible to all waves; previous tile fully consumed
-    if (tile + 1 < tile1)
-      issue_tile(rows_of(tile + 1), min(kTok, len - (tile + 1) * kTok),
+    if (tile + 1 < tile1) {
+      issue_tile(rows_at(tile + 1, next_page), min(kTok, len - (tile + 1) * kTok),
                  lds + (uint32_t)((tile + 1 - tile0) & 1) * kTileBytes, wave, lane);
+      if (tile + 2 < tile1) next_page = table[((tile + 2) * kTok) >> shift];
+    }
 
-    // ---- S^T for tokens [0, 64) x heads [16 wave, +16), K = 576:
-    // four 16-token blocks, fragments read one k-step ahead.
-    f32x4 sacc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    // ---- S^T for tokens 32 th + (0..31) x heads 16 hq + (0..15), K = 576
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
       const uint32_t sa = buf + s_base;
-      bf16x8 a[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) a[tb] = lds_read_b128(sa + tb * 256u);
+      bf16x8 a0 = lds_read_b128(sa), a1 = lds_read_b128(sa + 256u);
+      bf16x8 b0 = lds_read_b128(sa + 4096u), b1v = lds_read_b128(sa + 4096u + 256u);
 #pragma unroll
       for (int ks = 0; ks < kW / 32; ++ks) {
-        bf16x8 n[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          n[tb] = (ks + 1 < kW / 32) ? lds_read_b128(sa + (uint32_t)(ks + 1) * 4096u + tb * 256u) : a[tb];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) sacc[tb] = mfma16(a[tb], qf[ks], sacc[tb]);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) a[tb] = n[tb];
+        bf16x8 n0 = a0, n1 = a1;
+        if (ks + 2 < kW / 32) {
+          n0 = lds_read_b128(sa + (uint32_t)(ks + 2) * 4096u);
+          n1 = lds_read_b128(sa + (uint32_t)(ks + 2) * 4096u + 256u);
+        }
+        sacc[0] = mfma16(a0, qf[ks], sacc[0]);
+        sacc[1] = mfma16(a1, qf[ks], sacc[1]);
+        a0 = b0;
+        a1 = b1v;
+        b0 = n0;
+        b1v = n1;
       }
     }
-    // register v of block tb <-> token 16 tb + 4 kq + v, head h
+    // register v of block tb <-> token 32 th + 16 tb + 4 kq + v, head h
     const int valid = len - tile * kTok;
-    float tmax = -INFINITY;
+    float hmax = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        if (16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
-        tmax = fmaxf(tmax, sacc[tb][v]);
+        if (32 * th + 16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
+        hmax = fmaxf(hmax, sacc[tb][v]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    hmax = fmaxf(hmax, __shfl_xor(hmax, 16, 64));
+    hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+    if (lane < 16) lds_st(red + (th * kHG + h) * 4, hmax);
+    lds_barrier();
+    const float tmax = fmaxf(lds_ld(red + h * 4), lds_ld(red + (kHG + h) * 4));
     const bool grow = tmax > st.m + kRescaleSlack;
     const float m_new = grow ? tmax : st.m;
     const float alpha = grow ? exp2f(st.m - m_new) : 1.0f;
     const bool any = __ballot(grow) != 0ull;
     float psum = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < 2; ++tb) {
       bf16x4 pk;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -184,20 +192,20 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
     }
     st.l = st.l * alpha + psum;
     st.m = m_new;
-    if (lane < 16) lds_st(alp + h * 4, alpha);
-    if (lane == 0) lds_st(flags + wave * 4, any ? 1.0f : 0.0f);
+    if (th == 0 && lane < 16) lds_st(alp + h * 4, alpha);
+    if (lane == 0) lds_st(lds + kOffFlag + wave * 4, any ? 1.0f : 0.0f);
     lds_barrier();
 
-    // ---- O[64 h, 128 wave + (0..127)] = O * alpha + P T
-    const f32x4 fl = lds_ld4(flags);
-    if (fl[0] + fl[1] + fl[2] + fl[3] != 0.0f) {
+    // ---- O[64 h, 64 wave + (0..63)] = O * alpha + P T
+    const f32x4 f0 = lds_ld4(lds + kOffFlag), f1 = lds_ld4(lds + kOffFlag + 16);
+    if (f0[0] + f0[1] + f0[2] + f0[3] + f1[0] + f1[1] + f1[2] + f1[3] != 0.0f) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4 a4 = lds_ld4(al_base + hb * 128 + q * 32);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
+          for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) st.o[hb][cb][4 * q + r] *= a4[r];
         }
@@ -207,7 +215,7 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
       const bf16x8 pa0 = lds_read_b128(pa_base + ks * 32);
       const bf16x8 pa1 = lds_read_b128(pa_base + 32 * kPStride * 2 + ks * 32);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < 2; ++cb) {
         const uint32_t off = buf + (uint32_t)(cb * 4096 + ks * 256);
         const bf16x8 bv = cat(lds_read_tr(off + tr_lo), lds_read_tr(off + tr_hi));
         st.o[0][cb] = mfma32(pa0, bv, st.o[0][cb]);
@@ -217,31 +225,53 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
   }
 }
 
-// Row sums of the segment into LDS (a barrier must follow before use).
-__device__ __forceinline__ void publish_sums(const SegState& st, uint32_t lds, int wave, int lane) {
+// Row sums of the segment: per-wave partial sums into LDS, then the S-phase
+// waves of the first token half combine them into 1/l per head.  Returns the
+// head's full sum in lanes 0..15 of waves 0..3 (the lanes that hold its m).
+// Ends with a barrier.
+__device__ __forceinline__ float finish_sums(const SegState& st, uint32_t lds, int wave, int lane) {
   float lt = st.l + __shfl_xor(st.l, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
-  if (lane < 16) lds_st(lds + kOffLsum + (16 * wave + lane) * 4, lt);
-}
-__device__ __forceinline__ float head_sum(uint32_t lds, int h) {
-  return lds_ld(lds + kOffLsum + h * 4);
+  if (lane < 16) lds_st(lds + kOffLsum + ((wave >> 2) * kHG + 16 * (wave & 3) + lane) * 4, lt);
+  lds_barrier();
+  float tot = 0.f;
+  if (wave < 4 && lane < 16) {
+    const int h = 16 * wave + lane;
+    tot = lds_ld(lds + kOffLsum + h * 4) + lds_ld(lds + kOffLsum + (kHG + h) * 4);
+    lds_st(lds + kOffInv + h * 4, 1.0f / tot);
+  }
+  lds_barrier();
+  return tot;
 }
 
-// Store O / l for the 64 heads of this workgroup: dst[h * 512 + c] (bf16).
+// Store O / l for the 64 heads of this workgroup to dst[h * head_stride + c]
+// (bf16): normalise into an LDS staging area (the tile buffers, free by
+// now), then copy out with 16-byte coalesced stores.  Call after
+// finish_sums; ends with a barrier.
 __device__ __forceinline__ void store_normalised(const SegState& st, uint32_t lds, bf16* dst,
                                                  long head_stride, int wave, int lane) {
+  typedef __attribute__((address_space(3))) bf16 lds_bf16;
+  // one per-lane base; (head, column-block) offsets are constants below 64 KiB
+  const uint32_t st_base = lds + ((4 * (lane >> 5)) * kOStride + 64 * wave + (lane & 31)) * 2;
+  const uint32_t inv_base = lds + kOffInv + 16 * (lane >> 5);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int h = 32 * hb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const float inv = 1.0f / head_sum(lds, h);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 inv = lds_ld4(inv_base + (32 * hb + 8 * q) * 4);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int c = 128 * wave + 32 * cb + (lane & 31);
-        dst[h * head_stride + c] = (bf16)(st.o[hb][cb][v] * inv);
-      }
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *(lds_bf16*)(uintptr_t)(st_base + ((32 * hb + 8 * q + r) * kOStride + 32 * cb) * 2) =
+              (bf16)(st.o[hb][cb][4 * q + r] * inv[r]);
     }
+  lds_barrier();
+  for (int i = threadIdx.x; i < kHG * kR / 8; i += kThreads) {
+    const int hh = i / (kR / 8), c8 = (i % (kR / 8)) * 8;
+    *(bf16x8*)(dst + hh * head_stride + c8) = lds_read_b128(lds + (hh * kOStride + c8) * 2);
+  }
+  lds_barrier();
 }
 
 // Workgroup -> (head group, stream index); the head groups of one stream
@@ -269,7 +299,7 @@ __host__ __device__ inline int owner_of(long x, long T, int n) {
 // of all sequences; every (workgroup, sequence) piece writes one partial
 // into slot w + b (unique: w + b grows along the stream).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
+__global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int shift,
     const int* __restrict__ seq_lens, int batch, int H, int n_wg, int* __restrict__ prefix_out,
@@ -282,12 +312,12 @@ __global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
   map_block(hgc, hg, w);
   int* prefix = (int*)(smem + kOffPrefix);
 
-  // prefix sums of tiles per sequence (4 sequences per thread, then a scan)
+  // prefix sums of tiles per sequence (2 sequences per thread, then a scan)
   {
-    int cnt[4], tot = 0;
+    int cnt[2], tot = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = tid * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int b = tid * 2 + i;
       cnt[i] = b < batch ? (seq_lens[b] + kTok - 1) / kTok : 0;
       tot += cnt[i];
     }
@@ -297,17 +327,17 @@ __global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
       const int y = __shfl_up(incl, o, 64);
       if (lane >= o) incl += y;
     }
-    int* wsum = (int*)(smem + kOffRed);
+    int* wsum = (int*)(smem + kOffScan);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int base = 0;
     for (int i = 0; i < wave; ++i) base += wsum[i];
     int run = base + incl - tot;
+    if (tid == 0) prefix[0] = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = tid * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int b = tid * 2 + i;
       if (b < batch) {
-        if (b == 0) prefix[0] = 0;
         run += cnt[i];
         prefix[b + 1] = run;
       }
@@ -316,7 +346,7 @@ __global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
   }
   const long T = prefix[batch];
   if (blockIdx.x == 0)
-    for (int b = tid; b <= batch; b += 256) prefix_out[b] = prefix[b];
+    for (int b = tid; b <= batch; b += kThreads) prefix_out[b] = prefix[b];
 
   long x0 = ((long)w * T) / n_wg, x1 = ((long)(w + 1) * T) / n_wg;
   if (x0 >= x1) return;
@@ -342,16 +372,14 @@ __global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
     }
     run_segment(q_full + ((long)b * H + hg * kHG) * kW, pool, block_table + (long)b * max_blocks,
                 shift, len, tile0, tile1, lds, st, wave, lane);
-    publish_sums(st, lds, wave, lane);
-    lds_barrier();
+    const float tot = finish_sums(st, lds, wave, lane);
     const long slot = (long)hg * n_slots + w + b;
-    store_normalised(st, lds, part_o + slot * kHG * kR, kR, wave, lane);
-    if (lane < 16) {
+    if (wave < 4 && lane < 16) {
       const int h = 16 * wave + lane;
       part_ml[(slot * kHG + h) * 2 + 0] = st.m;
-      part_ml[(slot * kHG + h) * 2 + 1] = head_sum(lds, h);
+      part_ml[(slot * kHG + h) * 2 + 1] = tot;
     }
-    lds_barrier();
+    store_normalised(st, lds, part_o + slot * kHG * kR, kR, wave, lane);
     x0 = seg_end;
     ++b;
   }
@@ -361,7 +389,7 @@ __global__ void __launch_bounds__(256, 1) attn_decode_partials_kernel(
 // Prefill: one workgroup per (query row, head group); whole causal range.
 // Rows are processed longest first.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256, 1) attn_prefill_kernel(
+__global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int shift,
     const int* __restrict__ start_pos, int T_len, int n_rows, int H, bf16* __restrict__ o_lat) {
@@ -377,53 +405,102 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(
   const int b = r % nb;
   const int n = b * T_len + t;
   const int len = start_pos[b] + t + 1;
+  (void)tid;
   SegState st;
   run_segment(q_full + ((long)n * H + hg * kHG) * kW, pool, block_table + (long)b * max_blocks,
               shift, len, 0, (len + kTok - 1) / kTok, lds, st, wave, lane);
-  publish_sums(st, lds, wave, lane);
-  lds_barrier();
+  finish_sums(st, lds, wave, lane);
   store_normalised(st, lds, o_lat + ((long)n * H + hg * kHG) * kR, kR, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
 // Combine (+ optional W_UV projection).  Workgroup = (head, 16 sequences).
 // o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
+// All global loads of a phase are issued before any is used.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kCRows = 16;
-constexpr int kOStride = kR + 8;        // bf16 per o_lat row in LDS
-constexpr int kWChunk = 128;            // W_UV rows per LDS chunk
-constexpr int kWStride = 128 + 16;      // bf16 per W_UV row in LDS (Dv <= 128)
+constexpr int kCOStride = kR + 8;       // bf16 per o_lat row in LDS
+// W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
+// position c ^ 2(r&3), so the 4 rows x 2 chunks of a transposing read fall
+// on 8 distinct bank groups.
+__device__ __forceinline__ uint32_t w_off(uint32_t r, uint32_t c) {
+  return (r * 16u + (c ^ ((r & 3u) << 1))) * 16u;
+}
+constexpr int kMaxSeg = 64;             // pieces per (sequence, head) with weights kept in LDS
 }
 
 __global__ void __launch_bounds__(256) combine_kernel(
     const int* __restrict__ prefix, const float* __restrict__ part_ml,
     const bf16* __restrict__ part_o, int batch, int H, int n_wg, const bf16* __restrict__ w_uv,
     int Dv, bf16* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) bf16 olds[kCRows * kOStride];
-  __shared__ __attribute__((aligned(16))) bf16 wlds[kWChunk * kWStride];
+  __shared__ __attribute__((aligned(16))) bf16 olds[kCRows * kCOStride];
+  __shared__ __attribute__((aligned(16))) bf16 wlds[kR * 128];
+  __shared__ float wts[kCRows][kMaxSeg];
+  __shared__ int seg0[kCRows], nseg[kCRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b0 = blockIdx.y * kCRows;
   const int hg = h / kHG, hl = h % kHG;
   const long T = prefix[batch];
   const long n_slots = (long)n_wg + batch;
+  const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
 
-  // merge: thread -> (row tid/16, 32 columns)
+  // W_UV[h] -> LDS: every load of the matrix is issued up front
+  if (W) {
+    const int chunks = kR * Dv / 8;
+    const uint32_t wb0 = lds_addr(wlds);
+    for (int c = tid; c < chunks; c += 256) {
+      const int r = c / (Dv / 8), cc = c % (Dv / 8);
+      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(wb0 + w_off(r, cc)) =
+          *(const bf16x8*)(W + (long)r * Dv + cc * 8);
+    }
+  }
+  // segment ranges of the 16 sequences
+  if (tid < kCRows) {
+    const int b = b0 + tid;
+    int f = 0, n = 0;
+    if (b < batch && prefix[b + 1] > prefix[b]) {
+      f = owner_of(prefix[b], T, n_wg);
+      n = owner_of(prefix[b + 1] - 1, T, n_wg) - f + 1;
+    }
+    seg0[tid] = f;
+    nseg[tid] = n;
+  }
+  __syncthreads();
+  // merge weights e_s / sum e_s, 16 threads per row
+  {
+    const int rr = tid >> 4, sl = tid & 15;
+    const int b = b0 + rr, f = seg0[rr], n = nseg[rr];
+    float m_loc = -INFINITY;
+    for (int s = sl; s < n; s += 16)
+      m_loc = fmaxf(m_loc, part_ml[(((long)hg * n_slots + f + s + b) * kHG + hl) * 2]);
+    for (int o = 1; o < 16; o <<= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, o, 64));
+    float d_loc = 0.f;
+    for (int s = sl; s < n; s += 16) {
+      const long slot = (long)hg * n_slots + f + s + b;
+      const float e = exp2f(part_ml[(slot * kHG + hl) * 2] - m_loc) * part_ml[(slot * kHG + hl) * 2 + 1];
+      if (s < kMaxSeg) wts[rr][s] = e;
+      d_loc += e;
+    }
+    for (int o = 1; o < 16; o <<= 1) d_loc += __shfl_xor(d_loc, o, 64);
+    __syncthreads();
+    for (int s = sl; s < min(n, kMaxSeg); s += 16) wts[rr][s] /= d_loc;
+  }
+  __syncthreads();
+  // weighted sum: thread -> (row tid/16, 32 columns); four pieces in flight at a time
   {
     const int rr = tid >> 4, c0 = (tid & 15) * 32;
-    const int b = b0 + rr;
+    const int b = b0 + rr, f = seg0[rr], n = nseg[rr];
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-    if (b < batch && prefix[b + 1] > prefix[b]) {
-      const long x0 = prefix[b], x1 = prefix[b + 1] - 1;
-      const int wf = owner_of(x0, T, n_wg), wl = owner_of(x1, T, n_wg);
-      float M = -INFINITY;
-      for (int w = wf; w <= wl; ++w)
-        M = fmaxf(M, part_ml[(((long)hg * n_slots + w + b) * kHG + hl) * 2]);
-      float den = 0.f;
-      for (int w = wf; w <= wl; ++w) {
-        const long slot = (long)hg * n_slots + w + b;
+    if (n > kMaxSeg) {
+      // long merges recompute their weights on the fly (more than 64 pieces)
+      float M = -INFINITY, den = 0.f;
+      for (int s = 0; s < n; ++s)
+        M = fmaxf(M, part_ml[(((long)hg * n_slots + f + s + b) * kHG + hl) * 2]);
+      for (int s = 0; s < n; ++s) {
+        const long slot = (long)hg * n_slots + f + s + b;
         const float e = exp2f(part_ml[(slot * kHG + hl) * 2] - M) * part_ml[(slot * kHG + hl) * 2 + 1];
         den += e;
         const bf16* src = part_o + (slot * kHG + hl) * kR + c0;
@@ -434,53 +511,72 @@ __global__ void __launch_bounds__(256) combine_kernel(
           for (int i = 0; i < 8; ++i) acc[8 * q + i] += e * (float)v[i];
         }
       }
-      const float inv = 1.0f / den;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] *= inv;
+      for (int i = 0; i < 32; ++i) acc[i] /= den;
+    } else {
+      int s = 0;
+      for (; s + 4 <= n; s += 4) {
+        bf16x8 v[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16* src = part_o + (((long)hg * n_slots + f + s + u + b) * kHG + hl) * kR + c0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[u][q] = *(const bf16x8*)(src + 8 * q);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float e = wts[rr][s + u];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[8 * q + i] += e * (float)v[u][q][i];
+        }
+      }
+      for (; s < n; ++s) {
+        const bf16* src = part_o + (((long)hg * n_slots + f + s + b) * kHG + hl) * kR + c0;
+        const float e = wts[rr][s];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 v = *(const bf16x8*)(src + 8 * q);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[8 * q + i] += e * (float)v[i];
+        }
+      }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       bf16x8 v;
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = (bf16)acc[8 * q + i];
-      if (w_uv == nullptr) {
+      if (!W) {
         if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + c0 + 8 * q) = v;
       } else {
-        *(bf16x8*)(olds + rr * kOStride + c0 + 8 * q) = v;
+        *(bf16x8*)(olds + rr * kCOStride + c0 + 8 * q) = v;
       }
     }
   }
-  if (w_uv == nullptr) return;
+  if (!W) return;
+  __syncthreads();
 
   // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows x Dv, K = 512, 16x16x32 MFMAs.
   // Wave w owns 16-column blocks w, w + 4 (Dv <= 128).
-  const bf16* W = w_uv + (long)h * kR * Dv;
   const int nblk = Dv / 16;
   f32x4 acc[2] = {f32x4{}, f32x4{}};
   const uint32_t ob = lds_addr(olds), wb = lds_addr(wlds);
   const int g = lane >> 4, li = lane & 15;
-  for (int k0 = 0; k0 < kR; k0 += kWChunk) {
-    __syncthreads();
-    const int chunks = kWChunk * Dv / 8;
-    for (int c = tid; c < chunks; c += 256) {
-      const int r = c / (Dv / 8), cc = (c % (Dv / 8)) * 8;
-      *(bf16x8*)(wlds + r * kWStride + cc) = *(const bf16x8*)(W + (long)(k0 + r) * Dv + cc);
-    }
-    __syncthreads();
+#pragma unroll 4
+  for (int ks = 0; ks < kR / 32; ++ks) {
+    const bf16x8 a = lds_read_b128(ob + ((lane & 15) * kCOStride + 32 * ks + 8 * (lane >> 4)) * 2);
+    // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
+    const uint32_t row = 32 * ks + 8 * g + (li >> 2);
 #pragma unroll
-    for (int ks = 0; ks < kWChunk / 32; ++ks) {
-      const bf16x8 a = lds_read_b128(ob + ((lane & 15) * kOStride + k0 + 32 * ks + 8 * (lane >> 4)) * 2);
-      // 16x16x32 B operand: lane (16g + i) needs column i of rows 8g .. 8g+7
-      const uint32_t row = 32 * ks + 8 * g + (li >> 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int nb = wave + 4 * j;
-        if (nb < nblk) {
-          const uint32_t col = 16 * nb + 4 * (li & 3);
-          const bf16x4 lo = lds_read_tr(wb + (row * kWStride + col) * 2);
-          const bf16x4 hi = lds_read_tr(wb + ((row + 4) * kWStride + col) * 2);
-          acc[j] = mfma16(a, cat(lo, hi), acc[j]);
-        }
+    for (int j = 0; j < 2; ++j) {
+      const int nb = wave + 4 * j;
+      if (nb < nblk) {
+        const uint32_t c = 2 * nb + ((li & 3) >> 1), sub = 8 * (li & 1);
+        const bf16x4 lo = lds_read_tr(wb + w_off(row, c) + sub);
+        const bf16x4 hi = lds_read_tr(wb + w_off(row + 4, c) + sub);
+        acc[j] = mfma16(a, cat(lo, hi), acc[j]);
       }
     }
   }
@@ -514,7 +610,7 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, const 
                                     int batch, int H, int n_wg, int* prefix, float* part_ml,
                                     void* part_o, hipStream_t st) {
   const int hgc = H / kHG;
-  attn_decode_partials_kernel<<<n_wg * hgc, 256, 0, st>>>(
+  attn_decode_partials_kernel<<<n_wg * hgc, kThreads, 0, st>>>(
       (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, seq_lens,
       batch, H, n_wg, prefix, part_ml, (bf16*)part_o);
 }
@@ -531,9 +627,9 @@ void launch_attention_prefill_bf16(const void* q_full, const void* pool, const i
                                    int batch, int H, void* o_lat, hipStream_t st) {
   const int hgc = H / kHG;
   const int n_rows = batch * T;
-  attn_prefill_kernel<<<n_rows * hgc, 256, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
-                                                     block_table, max_blocks, block_shift,
-                                                     start_pos, T, n_rows, H, (bf16*)o_lat);
+  attn_prefill_kernel<<<n_rows * hgc, kThreads, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
+                                                          block_table, max_blocks, block_shift,
+                                                          start_pos, T, n_rows, H, (bf16*)o_lat);
 }
 
 }  // namespace mla
