@@ -19,12 +19,14 @@
 // 64 heads.  Tiles stream HBM -> LDS with asynchronous direct-to-LDS loads
 // into two buffers: tile j+1 is in flight while tile j is multiplied.
 //
-// Tile layout in LDS: chunk-major.  The 16-byte chunk k (of 72) of row t
-// (of 64) sits at slot k*64 + (t ^ 4*(k&1)).  One direct-to-LDS load
-// instruction moves chunk k of all 64 rows (a lane per row), row-wise
-// fragment reads (8 consecutive rows, one chunk) hit 8 consecutive slots,
-// and a transposing read (4 rows x 2 neighbouring chunks) hits 8 distinct
-// slot positions: neither access pattern has bank conflicts.
+// Tile layout in LDS: row-major, row t (1152 B = 72 chunks of 16 B) at
+// t*1152, with its chunk k stored at position k ^ swz(t) (a permutation
+// inside each aligned group of 8 chunks).  A direct-to-LDS load instruction
+// fills 64 consecutive slots; its lanes read the matching 1 KB of global
+// memory in that permuted order, so every instruction stays fully coalesced.
+// swz(t) = 2(t%4) + (t/4)%2 puts 8 consecutive rows (row-wise fragment
+// reads) and the 4 rows x 2 neighbouring chunks of a transposing read on 8
+// distinct bank groups: neither access pattern has bank conflicts.
 #include "device_common.h"
 #include "launch.h"
 
@@ -58,18 +60,24 @@ static_assert(kHG * kOStride * 2 <= 2 * kTileBytes, "output staging fits the til
 // (log2 units): probabilities stay below 2^8 and O is rescaled rarely.
 constexpr float kRescaleSlack = 8.0f;
 
+__device__ __forceinline__ uint32_t swz(uint32_t t) { return ((t & 3u) << 1) | ((t >> 2) & 1u); }
+
 // Issue the asynchronous loads of one tile: `valid` rows (1..64) starting at
-// row pointer `rows`.  Wave w loads chunks w, w+8, ..., w+64 of every row
-// (all of one parity, so a lane carries row lane or lane^4 throughout).
-// Rows past `valid` repeat the last valid row so the tile holds finite data
-// (their probabilities are zero).
+// row pointer `rows` (consecutive rows of one page).  Wave w fills slots
+// [64 j, 64 j + 64) for j = w, w+8, ..., w+64.  Rows past `valid` repeat
+// the last valid row so the tile holds finite data (their probabilities are
+// zero).
 __device__ __forceinline__ void issue_tile(const bf16* rows, int valid, uint32_t buf, int wave,
                                            int lane) {
-  const int t = lane ^ ((wave & 1) << 2);
-  const bf16* p = rows + min(t, valid - 1) * kW + wave * 8;
-  const uint32_t dst = buf + (uint32_t)wave * 1024u;
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) g2lds16(p + i * 64, dst + i * 8192u);
+  for (int i = 0; i < kLoads; ++i) {
+    const uint32_t j = (uint32_t)wave + 8u * i;
+    const uint32_t s = 64u * j + (uint32_t)lane;
+    const uint32_t t = s / kCh;
+    const uint32_t k = (s - t * kCh) ^ swz(t);
+    const uint32_t tt = min(t, (uint32_t)(valid - 1));
+    g2lds16(rows + tt * kW + k * 8, buf + j * 1024u);
+  }
 }
 
 struct SegState {
@@ -91,16 +99,24 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
   const uint32_t kq = lane >> 4;           // 0..3
 
   // Per-lane LDS bases; every other offset below is a compile-time constant.
-  // S: row 32 th + 16 tb + lane%16, chunk 4 ks + kq -> s_base + 256 tb + 4096 ks.
-  const uint32_t s_base =
-      (kq * 64u + ((32u * th + (lane & 15)) ^ ((kq & 1u) << 2))) * 16u;
+  // S: row tr = 32 th + 16 tb + lane%16, chunk k = 4 ks + kq at position
+  // 8 (ks/2) + ((4 (ks%2) + kq) ^ swz(tr)); swz(tr) depends on lane%16 only.
+  const uint32_t tr0 = 32u * th + (lane & 15);
+  const uint32_t s_even = (tr0 * kCh + (kq ^ swz(tr0))) * 16u;
+  const uint32_t s_odd = (tr0 * kCh + ((4u + kq) ^ swz(tr0))) * 16u;
   // P*C transposing reads: lane (16 g + li) of the fragment for token block
-  // ks and column block cb reads row 16 ks + x (+4), chunk kb + 4 cb.
+  // ks and column block cb reads row 16 ks + x + 4 hi, chunk 8 wave + cc,
+  // cc = 4 cb + 2 (g%2) + b1, at position 8 wave + (cc ^ (2 a + hi)), a = li/4.
   const uint32_t g = lane >> 4, li = lane & 15;
-  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u;
-  const uint32_t kb = 8u * wave + 2u * (g & 1) + b1;
-  const uint32_t tr_lo = (kb * 64u + x + 4u * b1) * 16u + 8u * (li & 1);
-  const uint32_t tr_hi = (kb * 64u + x + 4u * (1u - b1)) * 16u + 8u * (li & 1);
+  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u, a2 = 2u * (li >> 2);
+  uint32_t tr_off[2][2];  // [cb][hi]
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const uint32_t cc = 4u * cb + 2u * (g & 1) + b1;
+      tr_off[cb][hi] = ((x + 4u * hi) * kCh + 8u * wave + (cc ^ (a2 + hi))) * 16u + 8u * (li & 1);
+    }
   // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
   const uint32_t pa_base = p_lds + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
   const uint32_t pw_base = p_lds + (h * kPStride + 32 * th + 4 * kq) * 2;
@@ -141,15 +157,19 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
     // ---- S^T for tokens 32 th + (0..31) x heads 16 hq + (0..15), K = 576
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
-      const uint32_t sa = buf + s_base;
-      bf16x8 a0 = lds_read_b128(sa), a1 = lds_read_b128(sa + 256u);
-      bf16x8 b0 = lds_read_b128(sa + 4096u), b1v = lds_read_b128(sa + 4096u + 256u);
+      // fragment (ks, tb): row tr0 + 16 tb -> + tb * 16 * 1152 bytes
+      auto frag = [&](int ks, int tb) {
+        return lds_read_b128(buf + ((ks & 1) ? s_odd : s_even) +
+                             (uint32_t)((ks >> 1) * 128 + tb * 16 * kCh * 16));
+      };
+      bf16x8 a0 = frag(0, 0), a1 = frag(0, 1);
+      bf16x8 b0 = frag(1, 0), b1v = frag(1, 1);
 #pragma unroll
       for (int ks = 0; ks < kW / 32; ++ks) {
         bf16x8 n0 = a0, n1 = a1;
         if (ks + 2 < kW / 32) {
-          n0 = lds_read_b128(sa + (uint32_t)(ks + 2) * 4096u);
-          n1 = lds_read_b128(sa + (uint32_t)(ks + 2) * 4096u + 256u);
+          n0 = frag(ks + 2, 0);
+          n1 = frag(ks + 2, 1);
         }
         sacc[0] = mfma16(a0, qf[ks], sacc[0]);
         sacc[1] = mfma16(a1, qf[ks], sacc[1]);
@@ -216,8 +236,8 @@ __device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
       const bf16x8 pa1 = lds_read_b128(pa_base + 32 * kPStride * 2 + ks * 32);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const uint32_t off = buf + (uint32_t)(cb * 4096 + ks * 256);
-        const bf16x8 bv = cat(lds_read_tr(off + tr_lo), lds_read_tr(off + tr_hi));
+        const uint32_t off = buf + (uint32_t)(ks * 16 * kCh * 16);
+        const bf16x8 bv = cat(lds_read_tr(off + tr_off[cb][0]), lds_read_tr(off + tr_off[cb][1]));
         st.o[0][cb] = mfma32(pa0, bv, st.o[0][cb]);
         st.o[1][cb] = mfma32(pa1, bv, st.o[1][cb]);
       }
@@ -447,12 +467,20 @@ __global__ void __launch_bounds__(256) combine_kernel(
 
   // W_UV[h] -> LDS: every load of the matrix is issued up front
   if (W) {
+    // at most 32 chunks per thread (Dv <= 128): all loads issued, then stored
     const int chunks = kR * Dv / 8;
     const uint32_t wb0 = lds_addr(wlds);
-    for (int c = tid; c < chunks; c += 256) {
-      const int r = c / (Dv / 8), cc = c % (Dv / 8);
-      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(wb0 + w_off(r, cc)) =
-          *(const bf16x8*)(W + (long)r * Dv + cc * 8);
+    bf16x8 wv[kR * 128 / 8 / 256];
+#pragma unroll
+    for (int i = 0; i < kR * 128 / 8 / 256; ++i) {
+      const int c = tid + 256 * i;
+      if (c < chunks) wv[i] = *(const bf16x8*)(W + (long)(c / (Dv / 8)) * Dv + (c % (Dv / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kR * 128 / 8 / 256; ++i) {
+      const int c = tid + 256 * i;
+      if (c < chunks)
+        *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(wb0 + w_off(c / (Dv / 8), c % (Dv / 8))) = wv[i];
     }
   }
   // segment ranges of the 16 sequences

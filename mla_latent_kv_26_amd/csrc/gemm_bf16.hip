@@ -6,21 +6,34 @@
 // tile is kept in LDS in its natural [k][n] layout and read with the gfx950
 // transposing LDS load, which hands each lane one column of a 4 x 16 block.
 //
-// Tile: BM x 128 x 32 per 256-thread workgroup, 4 waves, 32x32x16 MFMAs.
+// Tile: BM x 128 x BK per 256-thread workgroup, 4 waves, 32x32x16 MFMAs.
 // Global loads for the next K-tile are in flight (in registers) while the
-// current one is multiplied.
+// current one is multiplied; BK = 128 covers short contractions in one pass.
+//
+// Optional side job (used by query absorption): the workgroups of the first
+// column tile also copy side_cols values per row, scaled by alpha, from
+// side_src (row stride side_ld, batch stride side_sb) to side_dst (row stride
+// ldc, batch stride sC), i.e. next to their rows of C (side_cols % 8 == 0,
+// 16-byte aligned rows).
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
 namespace {
 
-constexpr int kBN = 128, kBK = 32;
-constexpr int kAStride = kBK + 8;    // bf16 per A row in LDS (80 B: conflict-free b128 reads)
+constexpr int kBN = 128;
 constexpr int kBStride = kBN + 16;   // bf16 per B row in LDS (288 B: conflict-free tr reads)
 
-template <int BM>
+struct Side {
+  const bf16* src;
+  long ld, sb;
+  bf16* dst;
+  int cols;
+};
+
+template <int BM, int kBK>
 struct Cfg {
+  static constexpr int A_STRIDE = kBK + 8;   // bf16 per A row in LDS (conflict-free b128 reads)
   static constexpr int WAVES_M = BM >= 64 ? 2 : 1;
   static constexpr int WAVES_N = 4 / WAVES_M;
   static constexpr int FM = BM / (32 * WAVES_M);
@@ -31,13 +44,14 @@ struct Cfg {
   static constexpr int B_PER_T = B_CHUNKS / 256;
 };
 
-template <int BM, bool kOutF32>
+template <int BM, int kBK, bool kOutF32>
 __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__ A,
                                                         const bf16* __restrict__ B,
                                                         void* __restrict__ Cv, int M, int N, int K,
                                                         long lda, long ldb, long ldc, long sA,
-                                                        long sB, long sC, float alpha) {
-  using C_ = Cfg<BM>;
+                                                        long sB, long sC, float alpha, Side side) {
+  using C_ = Cfg<BM, kBK>;
+  constexpr int kAStride = C_::A_STRIDE;
   __shared__ __attribute__((aligned(16))) bf16 As[BM * kAStride];
   __shared__ __attribute__((aligned(16))) bf16 Bs[kBK * kBStride];
 
@@ -97,6 +111,21 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
   const int tr_col = 16 * (g & 1) + 4 * (li & 3);        // + fragment column base
 
   load_tiles(0);
+  if (side.src && blockIdx.x == 0) {
+    // side job: scaled copy of side_cols values for each of this tile's rows
+    const bf16* ss = side.src + blockIdx.z * side.sb;
+    bf16* sd = side.dst + blockIdx.z * sC;
+    const int cc = side.cols / 8;  // 16-byte chunks per row
+    for (int i = tid; i < BM * cc; i += 256) {
+      const int r = i / cc, c = (i % cc) * 8;
+      if (m0 + r < M) {
+        bf16x8 v = *(const bf16x8*)(ss + (long)(m0 + r) * side.ld + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)(alpha * (float)v[e]);
+        *(bf16x8*)(sd + (long)(m0 + r) * ldc + c) = v;
+      }
+    }
+  }
   for (int k0 = 0; k0 < K; k0 += kBK) {
     store_tiles();
     __syncthreads();
@@ -146,31 +175,44 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
     }
 }
 
-template <int BM>
+template <int BM, int BK>
 void launch_bm(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
-               long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32,
+               long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, Side side,
                hipStream_t st) {
   dim3 grid((N + kBN - 1) / kBN, (M + BM - 1) / BM, batch);
   if (c_f32)
-    gemm_bf16_kernel<BM, true><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M, N, K,
-                                                     lda, ldb, ldc, sA, sB, sC, alpha);
+    gemm_bf16_kernel<BM, BK, true><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M, N,
+                                                         K, lda, ldb, ldc, sA, sB, sC, alpha, side);
   else
-    gemm_bf16_kernel<BM, false><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M, N, K,
-                                                      lda, ldb, ldc, sA, sB, sC, alpha);
+    gemm_bf16_kernel<BM, BK, false><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M,
+                                                          N, K, lda, ldb, ldc, sA, sB, sC, alpha,
+                                                          side);
+}
+
+template <int BK>
+void launch_bk(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
+               long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, Side side,
+               hipStream_t st) {
+  if (M <= 32)
+    launch_bm<32, BK>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+  else if (M <= 64)
+    launch_bm<64, BK>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+  else
+    launch_bm<128, BK>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
 }
 
 }  // namespace
 
 void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda,
                       long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
-                      int c_f32, hipStream_t st) {
+                      int c_f32, hipStream_t st, const void* side_src, long side_ld,
+                      long side_sb, void* side_dst, int side_cols) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
-  if (M <= 32)
-    launch_bm<32>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, st);
-  else if (M <= 64)
-    launch_bm<64>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, st);
+  const Side side{(const bf16*)side_src, side_ld, side_sb, (bf16*)side_dst, side_cols};
+  if (K <= 128)
+    launch_bk<128>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
   else
-    launch_bm<128>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, st);
+    launch_bk<32>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
 }
 
 }  // namespace mla

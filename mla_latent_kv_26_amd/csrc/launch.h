@@ -56,10 +56,14 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 
 // C[b] = alpha * A[b] * B[b]; A, B bf16 row-major; C bf16 (c_f32 == 0) or
 // float32.  Requires K % 8 == 0, N % 8 == 0, lda/ldb % 8 == 0, 16-B aligned
-// bases and batch strides.
+// bases and batch strides.  When side_src is set (bf16 C only), also
+// C_b[r, c] = alpha * side_src[b * side_sb + r * side_ld + c] into
+// side_dst (same ldc / sC as C) for c < side_cols.
 void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda,
                       long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
-                      int c_f32, hipStream_t st);
+                      int c_f32, hipStream_t st, const void* side_src = nullptr,
+                      long side_ld = 0, long side_sb = 0, void* side_dst = nullptr,
+                      int side_cols = 0);
 
 // Decode attention over a paged bf16 pool, R = 512, Dr = 64, 64 heads per
 // workgroup, block_size a power of two >= 64.  Writes split partials (bf16

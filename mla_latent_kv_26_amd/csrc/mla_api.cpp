@@ -205,6 +205,13 @@ void gemm(const Dims& d, const void* A, const void* B, void* C, int M, int N, in
 void enqueue_absorb(const Dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
                     int n_rows, void* q_full, hipStream_t st) {
   const float alpha = d.scale * 1.4426950408889634f;
+  if (d.dt == MLA_DTYPE_BF16) {
+    // one launch: q_lat = alpha * q_nope W_UK, plus the scaled copy of q_rope
+    mla::launch_gemm_bf16(q_nope, w_uk, q_full, n_rows, d.R, d.Dn, (long)d.H * d.Dn, d.R,
+                          (long)d.H * d.W, d.Dn, (long)d.Dn * d.R, d.W, d.H, alpha, 0, st, q_rope,
+                          (long)d.H * d.Dr, d.Dr, (char*)q_full + (size_t)d.R * d.esz, d.Dr);
+    return;
+  }
   gemm(d, q_nope, w_uk, q_full, n_rows, d.R, d.Dn, (long)d.H * d.Dn, d.R, (long)d.H * d.W, d.Dn,
        (long)d.Dn * d.R, d.W, d.H, alpha, false, st);
   mla::launch_q_rope(q_rope, (long)d.H * d.Dr, d.Dr, 0, nullptr, nullptr, 1, q_full, n_rows, d.H,
@@ -374,8 +381,9 @@ mla_status mla_absorb_query(const mla_config* cfg, const void* q_nope, const voi
   if (n_rows <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be positive (got %d)", n_rows);
   s = check_ptrs16(d, {q_nope, q_rope, w_uk, q_full}, "q_nope, q_rope, w_uk, q_full");
   if (s != MLA_OK) return s;
-  if (d.dt == MLA_DTYPE_BF16 && d.Dn % 8)
-    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorption needs qk_nope_dim % 8 == 0");
+  if (d.dt == MLA_DTYPE_BF16 && (d.Dn % 8 || d.Dr % 8 || d.W % 8))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "bf16 absorption needs qk_nope_dim, rope_dim and kv_lora_rank + rope_dim multiples of 8");
   enqueue_absorb(d, q_nope, q_rope, w_uk, n_rows, q_full, (hipStream_t)stream);
   return launched("mla_absorb_query");
 }
