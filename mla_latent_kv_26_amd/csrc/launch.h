@@ -65,23 +65,24 @@ void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K
                       long side_ld = 0, long side_sb = 0, void* side_dst = nullptr,
                       int side_cols = 0);
 
-// Decode attention over a paged bf16 pool, R = 512, Dr = 64, 64 heads per
-// workgroup, block_size a power of two >= 64.  Writes split partials (bf16
-// O normalised by its own sum, float32 (m, l) in log2 units) and the tile
-// prefix sums, for launch_combine.
-
+// Decode attention over a paged bf16 pool, R = 512, Dr = 64, 32 or 64 heads
+// per workgroup, block_size a power of two >= 64.  Writes split partials
+// (bf16 O normalised by its own sum, float32 (m, l) in log2 units) and the
+// tile prefix sums, for launch_combine.
 size_t decode_partial_slots(int batch, int n_wg);
-int decode_num_wg(int batch, int max_seq_len, int head_groups, int num_cus);
+int decode_heads_per_wg(int H, int batch, int max_seq_len, int num_cus);
+int decode_num_wg(int head_groups, int num_cus);
 
 void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
                                     int max_blocks, int block_shift, const int* seq_lens,
-                                    int batch, int H, int n_wg, int* prefix, float* part_ml,
-                                    void* part_o, hipStream_t st);
+                                    int batch, int H, int heads_per_wg, int n_wg, int* prefix,
+                                    float* part_ml, void* part_o, hipStream_t st);
 
 // Merge the partials of each (sequence, head) into o_lat (bf16 [batch, H, R])
 // or, when w_uv != NULL, project directly: out[b, h] = o_lat[b, h] W_UV[h].
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
-                    int n_wg, const void* w_uv, int Dv, void* out, hipStream_t st);
+                    int heads_per_wg, int n_wg, const void* w_uv, int Dv, void* out,
+                    hipStream_t st);
 
 // Prefill attention: query row n = b * T + t at position start_pos[b] + t
 // attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].

@@ -99,8 +99,8 @@ mla_status check_decode_kernels(const Dims& d, int batch) {
     return fail(MLA_ERR_UNSUPPORTED,
                 "bf16 attention kernels are built for kv_lora_rank 512 and rope_dim 64 (got %d, %d)",
                 d.R, d.Dr);
-  if (d.H % 64)
-    return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs num_heads a multiple of 64 (got %d)", d.H);
+  if (d.H % 32)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs num_heads a multiple of 32 (got %d)", d.H);
   if (d.shift < 6)
     return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs block_size a power of two >= 64 (got %d)",
                 d.bs);
@@ -135,21 +135,23 @@ mla_status launched(const char* what) {
 // ---- decode workspace layout ----
 struct DecodeWs {
   size_t prefix, part_ml, part_o, q_full, o_lat, total;
-  int n_wg, hgc;
+  int n_wg, hgc, heads;
 };
-DecodeWs decode_ws(const Dims& d, int batch) {
+DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
   DecodeWs w{};
   size_t off = 256;  // reserved
   if (d.dt == MLA_DTYPE_BF16) {
-    w.hgc = d.H / 64;
-    w.n_wg = mla::decode_num_wg(batch, 0, w.hgc, num_cus());
+    const int cus = num_cus();
+    w.heads = mla::decode_heads_per_wg(d.H, batch, max_seq_len, cus);
+    w.hgc = d.H / w.heads;
+    w.n_wg = mla::decode_num_wg(w.hgc, cus);
     const size_t slots = mla::decode_partial_slots(batch, w.n_wg);
     w.prefix = off;
     off = up256(off + (size_t)(batch + 1) * 4);
     w.part_ml = off;
-    off = up256(off + (size_t)w.hgc * slots * 64 * 2 * 4);
+    off = up256(off + (size_t)w.hgc * slots * w.heads * 2 * 4);
     w.part_o = off;
-    off = up256(off + (size_t)w.hgc * slots * 64 * 512 * 2);
+    off = up256(off + (size_t)w.hgc * slots * w.heads * 512 * 2);
   }
   w.q_full = off;
   off = up256(off + (size_t)batch * d.H * d.W * d.esz);
@@ -304,7 +306,7 @@ mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32
   if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be positive (got %d)", batch);
   if (max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be positive");
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = decode_ws(d, batch).total;
+  *bytes = decode_ws(d, batch, max_seq_len).total;
   return MLA_OK;
 }
 
@@ -325,15 +327,15 @@ static mla_status check_decode_common(const Dims& d, const void* pool, int32_t n
 
 static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* pool,
                                  const int32_t* table, int32_t max_blocks, const int32_t* seq_lens,
-                                 int32_t batch, const void* w_uv, void* dst, void* ws,
-                                 hipStream_t st) {
-  const DecodeWs w = decode_ws(d, batch);
+                                 int32_t batch, int32_t max_seq_len, const void* w_uv, void* dst,
+                                 void* ws, hipStream_t st) {
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
   if (d.dt == MLA_DTYPE_BF16) {
     mla::launch_attention_partials_bf16(q_full, pool, table, max_blocks, d.shift, seq_lens, batch,
-                                        d.H, w.n_wg, (int*)at(ws, w.prefix),
+                                        d.H, w.heads, w.n_wg, (int*)at(ws, w.prefix),
                                         (float*)at(ws, w.part_ml), at(ws, w.part_o), st);
     mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
-                        at(ws, w.part_o), batch, d.H, w.n_wg, w_uv, d.Dv, dst, st);
+                        at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, w_uv, d.Dv, dst, st);
   } else {
     float* o_lat = w_uv ? (float*)at(ws, w.o_lat) : (float*)dst;
     mla::launch_attention_f32((const float*)q_full, (const float*)pool, table, max_blocks, d.bs,
@@ -359,7 +361,7 @@ mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_r
   if (s != MLA_OK) return s;
   s = check_ptrs16(d, {q_nope, q_rope, w_uk, w_uv, out}, "q_nope, q_rope, w_uk, w_uv, out");
   if (s != MLA_OK) return s;
-  const DecodeWs w = decode_ws(d, batch);
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
   if (!workspace || workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
                 workspace ? "" : ", NULL");
@@ -367,8 +369,8 @@ mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_r
   hipStream_t st = (hipStream_t)stream;
   void* q_full = at(workspace, w.q_full);
   enqueue_absorb(d, q_nope, q_rope, w_uk, batch, q_full, st);
-  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, w_uv, out,
-                 workspace, st);
+  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                 w_uv, out, workspace, st);
   return launched("mla_decode");
 }
 
@@ -402,13 +404,13 @@ mla_status mla_latent_attention(const mla_config* cfg, const void* q_full, const
   if (s != MLA_OK) return s;
   s = check_ptrs16(d, {q_full, o_lat}, "q_full, o_lat");
   if (s != MLA_OK) return s;
-  const DecodeWs w = decode_ws(d, batch);
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
   if (!workspace || workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
                 workspace ? "" : ", NULL");
   if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, nullptr,
-                 o_lat, workspace, (hipStream_t)stream);
+  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                 nullptr, o_lat, workspace, (hipStream_t)stream);
   return launched("mla_latent_attention");
 }
 
@@ -436,11 +438,12 @@ mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, con
   if (s != MLA_OK) return s;
   s = check_ptrs16(d, {q_full}, "q_full");
   if (s != MLA_OK) return s;
-  const DecodeWs w = decode_ws(d, batch);
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
   s = check_ws(w, workspace, workspace_bytes);
   if (s != MLA_OK) return s;
   mla::launch_attention_partials_bf16(q_full, kv_pool, block_table, max_blocks_per_seq, d.shift,
-                                      seq_lens, batch, d.H, w.n_wg, (int*)at(workspace, w.prefix),
+                                      seq_lens, batch, d.H, w.heads, w.n_wg,
+                                      (int*)at(workspace, w.prefix),
                                       (float*)at(workspace, w.part_ml), at(workspace, w.part_o),
                                       (hipStream_t)stream);
   return launched("mla_attention_partials");
@@ -461,11 +464,11 @@ mla_status mla_combine_output(const mla_config* cfg, const void* w_uv, int32_t b
   if (s != MLA_OK) return s;
   if (!out || !al16(out)) return fail(MLA_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
   if (w_uv && !al16(w_uv)) return fail(MLA_ERR_INVALID_ARG, "w_uv must be 16-byte aligned");
-  const DecodeWs w = decode_ws(d, batch);
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
   s = check_ws(w, workspace, workspace_bytes);
   if (s != MLA_OK) return s;
   mla::launch_combine((const int*)at(workspace, w.prefix), (const float*)at(workspace, w.part_ml),
-                      at(workspace, w.part_o), batch, d.H, w.n_wg, w_uv, d.Dv, out,
+                      at(workspace, w.part_o), batch, d.H, w.heads, w.n_wg, w_uv, d.Dv, out,
                       (hipStream_t)stream);
   return launched("mla_combine_output");
 }
