@@ -70,22 +70,36 @@ def cpu_baseline(cfg, seconds):
         if time.perf_counter() - t_start > seconds:
             break
     t = float(np.median(times))
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    blas = ",".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
+                            if p.get("user_api") == "blas"})) or "unknown"
     return {"value": alg["step_bytes"] / t / 1e12, "unit": "TB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(times)} full decode steps of {cfg['batch']}x{cfg['context']} tokens, "
-                      f"absorbed path in float64 numpy, median {t * 1e3:.1f} ms/step",
+                      f"absorbed path in float64 numpy, median {t * 1e3:.1f} ms/step; "
+                      f"CPU {cpu_model()}, BLAS {blas}",
             "ms_per_step": t * 1e3}
 
 
-def traffic_entry():
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def traffic_entry(workload):
     """HBM bytes per launch measured with rocprofv3 counters, if they were
-    taken on the current kernel source; else None."""
+    taken on this workload and on the current kernel source; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -222,7 +236,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_entry(),
+            "traffic": traffic_entry(args.workload),
             "kernel_us": round(attn_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": alg["attn_bytes"],
             "mfma_tflops": round(alg["attn_flops"] / (attn_ms * 1e-3) / 1e12, 2),

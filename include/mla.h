@@ -147,7 +147,7 @@ mla_status mla_absorb_query(const mla_config* cfg, const void* q_nope, const voi
  * ([batch, H, R + Dr]); o_lat [batch, H, R] (written) is
  * sum_j P[h, j] c_j with P the softmax over the sequence's seq_lens[b] rows.
  * Pool, table and lengths as in mla_decode.  Uses the workspace for split
- * partials (size from mla_decode_workspace_size; counter rule there). */
+ * partials (size from mla_decode_workspace_size). */
 mla_status mla_latent_attention(const mla_config* cfg, const void* q_full, const void* kv_pool,
                                 int32_t num_blocks, const int32_t* block_table,
                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
@@ -226,7 +226,8 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int3
  *   start_pos int32 [batch] (device, trusted, each <= max_start_pos);
  *   max_start_pos (host); (max_start_pos + q_len) <= max_blocks_per_seq * block_size;
  *   out [batch, q_len, H, Dv] (written).
- * q_len == 1 runs the decode kernels after the append. */
+ * Every q_len (1 included) runs the same causal attention kernel: one
+ * workgroup per (query row, head group) over all of that row's keys. */
 mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, const void* w_dq,
                        const float* q_norm_w, const void* w_uq, const void* w_dkv,
                        const float* kv_norm_w, const void* w_uk, const void* w_uv,
