@@ -1,25 +1,25 @@
 // Latent attention on MFMA (gfx950), bf16 cache rows, float32 accumulate.
 //
-// For one query row and 64 heads (modeldna "MLA" module, "Under the hood":
-// W_UK absorbed into the query, attention run on the cached latent):
+// For one query row and up to 64 heads (modeldna "MLA" module, "Under the
+// hood": W_UK absorbed into the query, attention run on the cached latent):
 //   s[h, j]  = q_full[h] . row_j          (q_full = scale*log2e*[q_lat | q_rope])
 //   o_lat[h] = sum_j 2^(s[h,j] - m[h]) c_j / sum_j 2^(s[h,j] - m[h]).
 // The rows are dense bf16 [c (512) | k_rope (64)], 1152 B each, shared by
 // every head, so both contractions are matrix products:
-//   S^T [64 tok x 64 h] = T [64 tok x 576] * Q^T [576 x 64 h]
-//   O   [64 h x 512]   += P [64 h x 64 tok] * T[:, :512]
-// and one LDS copy of each 64-token tile serves both: T is read row-wise
-// for S (16-byte LDS reads) and column-wise for P*C (transposing LDS reads),
-// so every cached byte leaves HBM once.
+//   S^T [32 tok x 16 h] = T [32 tok x 576] * Q^T [576 x 16 h]   (per score wave)
+//   O   [H x 128]      += P [H x 32 tok] * T[:, 128 w .. +128]   (per P*C wave)
+// and one LDS copy of each 32-token tile serves both: T is read row-wise for
+// S (16-byte LDS reads) and column-wise for P*C (transposing LDS reads), so
+// every cached byte leaves HBM once.
 //
-// Workgroup: 512 threads = 8 waves (two per SIMD, so one wave's LDS waits
-// overlap the other's MFMAs) and HEADS = 64 or 32 heads.  For S, each wave
-// takes 16 heads and 32 (HEADS = 64) or 16 (HEADS = 32) tokens of the tile
-// (its heads' queries stay in registers); for P*C, wave w owns columns
-// 64 w .. +64 of O for all HEADS heads.  Tiles stream HBM -> LDS with
-// asynchronous direct-to-LDS loads into two buffers: tile j+1 is in flight
-// while tile j is multiplied.  With HEADS = 32, two workgroups share each
-// tile; they are placed on the same XCD so the second read hits its L2.
+// Workgroup: 512 threads = 8 waves, one "score" wave and one "P*C" wave per
+// SIMD, working on consecutive tiles at once.  In step k the score waves
+// compute S, the softmax and P for tile k (each owns 16 heads and all 32
+// tokens, so row maxima need no exchange between waves) while the P*C waves
+// fold P of tile k-1 into O (each owns 128 columns of O for all heads, fp32
+// in registers).  One barrier per step hands P from one group to the other.
+// Tiles stream HBM -> LDS with asynchronous direct-to-LDS loads into four
+// buffers: tiles k-1 and k are being read, k+1 and k+2 are in flight.
 //
 // Tile layout in LDS: row-major, row t (1152 B = 72 chunks of 16 B) at
 // t*1152, with its chunk k stored at position k ^ swz(t) (a permutation
@@ -36,38 +36,37 @@ namespace mla {
 namespace {
 
 constexpr int kR = 512, kDr = 64, kW = kR + kDr;       // row width 576
-constexpr int kTok = 64;                                // tokens per tile
+constexpr int kTok = 32;                                // tokens per tile
 constexpr int kCh = kW * 2 / 16;                        // 72 chunks per row
-constexpr int kTileBytes = kTok * kW * 2;               // 73728
+constexpr int kTileBytes = kTok * kW * 2;               // 36864
+constexpr int kNBuf = 4;                                // tile buffers
+constexpr int kTileLoads = kTileBytes / 1024;           // 36 1-KB load instructions
+constexpr int kSLoads = 4, kPLoads = 5;                 // per score wave / per P*C wave
+static_assert(4 * kSLoads + 4 * kPLoads == kTileLoads, "every slot loaded once");
 constexpr int kMaxHG = 64;                              // heads per workgroup, at most
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLoads = kCh / kWaves;                    // 9 chunk loads per wave per tile
-constexpr int kPStride = 72;                            // bf16 per P row (64 + 8)
+constexpr int kPStride = kTok + 8;                      // bf16 per P row (80 B)
 constexpr int kOStride = kR + 8;                        // bf16 per staged output row
 constexpr int kMaxBatch = 1024;
 
-constexpr int kOffP = 2 * kTileBytes;                   // bf16 [64][72]
-constexpr int kOffRed = kOffP + kMaxHG * kPStride * 2;  // float [4][64] per-token-group maxima
-constexpr int kOffAlpha = kOffRed + 4 * kMaxHG * 4;     // float [64] rescale factors
-constexpr int kOffFlag = kOffAlpha + kMaxHG * 4;        // float [8] per-wave rescale flags
-constexpr int kOffLsum = kOffFlag + 32;                 // float [4][64] row sums
-constexpr int kOffInv = kOffLsum + 4 * kMaxHG * 4;      // float [64] 1 / row sum
+constexpr int kOffP = kNBuf * kTileBytes;               // bf16 [2][64][40]
+constexpr int kOffAlpha = kOffP + 2 * kMaxHG * kPStride * 2;  // float [2][64]
+constexpr int kOffFlag = kOffAlpha + 2 * kMaxHG * 4;    // float [2][4] rescale flags
+constexpr int kOffInv = kOffFlag + 2 * 4 * 4;           // float [64] 1 / row sum
 constexpr int kOffScan = kOffInv + kMaxHG * 4;          // int [8] scan scratch
 constexpr int kOffPrefix = kOffScan + 32;               // int [kMaxBatch + 1]
-constexpr int kLdsBytes = kOffPrefix + (kMaxBatch + 1) * 4;
+constexpr int kOffLenLo = kOffPrefix + (kMaxBatch + 1) * 4;  // uint8 [kMaxBatch]
+constexpr int kLdsBytes = kOffLenLo + kMaxBatch;
 static_assert(kLdsBytes <= 163840, "LDS budget");
-static_assert(kMaxHG * kOStride * 2 <= 2 * kTileBytes, "output staging fits the tile buffers");
+static_assert(kMaxHG * kOStride * 2 <= kNBuf * kTileBytes, "output staging fits the tile buffers");
 
-// Per-HEADS geometry: HQ 16-head blocks x TQ token groups = 8 waves for S;
-// HB 32-head row blocks of O per wave for P*C.
+// Per-HEADS geometry: SW score waves of 16 heads; HB 32-head row blocks of O
+// per P*C wave.
 template <int HEADS>
 struct Geo {
   static_assert(HEADS == 32 || HEADS == 64, "32 or 64 heads per workgroup");
-  static constexpr int HQ = HEADS / 16;
-  static constexpr int TQ = kWaves / HQ;
-  static constexpr int TPW = kTok / TQ;   // tokens per wave in S
-  static constexpr int TB = TPW / 16;     // 16-token blocks per wave in S
+  static constexpr int SW = HEADS / 16;
   static constexpr int HB = HEADS / 32;
 };
 // A head's reference max only moves when a tile exceeds it by more than this
@@ -76,16 +75,46 @@ constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ uint32_t swz(uint32_t t) { return ((t & 3u) << 1) | ((t >> 2) & 1u); }
 
-// Issue the asynchronous loads of one tile: `valid` rows (1..64) starting at
-// row pointer `rows` (consecutive rows of one page).  Wave w fills slots
-// [64 j, 64 j + 64) for j = w, w+8, ..., w+64.  Rows past `valid` repeat
-// the last valid row so the tile holds finite data (their probabilities are
-// zero).
-__device__ __forceinline__ void issue_tile(const bf16* rows, int valid, uint32_t buf, int wave,
+// Page ids of one sequence, 64 at a time in a register (lane i holds the id
+// of page index base + i), the following 64 loaded ahead.  Loads are plain
+// vector loads issued before the tile loads of the same step, so waiting for
+// a tile also retires them.  Indices are clamped to the table row.
+struct PageCursor {
+  const int* row;
+  int max_blocks, base, cur, nxt;
+
+  __device__ __forceinline__ int fetch(int first, int lane) const {
+    return row[min(first + lane, max_blocks - 1)];
+  }
+  __device__ __forceinline__ void start(const int* r, int mb, int page0, int lane) {
+    row = r;
+    max_blocks = mb;
+    base = page0;
+    cur = fetch(base, lane);
+    nxt = fetch(base + 64, lane);
+  }
+  // page id of page index p (p >= base, p < base + 128, non-decreasing)
+  __device__ __forceinline__ int page(int p, int lane) {
+    if (p - base >= 64) {
+      cur = nxt;
+      base += 64;
+      nxt = fetch(base + 64, lane);
+    }
+    return __builtin_amdgcn_readlane(cur, p - base);
+  }
+};
+
+// Issue this wave's share of the asynchronous loads of one tile: NL
+// instructions j = j0 .. j0+NL-1, each filling LDS slots [64 j, 64 j + 64)
+// of the buffer.  `valid` rows (1..32) start at row pointer `rows`
+// (consecutive rows of one page); rows past `valid` repeat the last valid
+// row so the tile holds finite data (their probabilities are zero).
+template <int NL>
+__device__ __forceinline__ void issue_part(const bf16* rows, int valid, uint32_t buf, uint32_t j0,
                                            int lane) {
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const uint32_t j = (uint32_t)wave + 8u * i;
+  for (int i = 0; i < NL; ++i) {
+    const uint32_t j = j0 + i;
     const uint32_t s = 64u * j + (uint32_t)lane;
     const uint32_t t = s / kCh;
     const uint32_t k = (s - t * kCh) ^ swz(t);
@@ -94,244 +123,311 @@ __device__ __forceinline__ void issue_tile(const bf16* rows, int valid, uint32_t
   }
 }
 
-template <int HEADS>
-struct SegState {
-  f32x16 o[Geo<HEADS>::HB][2];  // O[32 hb + ..][64 wave + 32 cb + ..]
-  float m;                      // reference max of this lane's S head, log2 units
-  float l;                      // lane-partial running sum for that head
+// One segment: a query row (HEADS heads at q_rows, row stride kW) against
+// tiles [tile0, tile1) of one sequence of `len` rows (page table `table`).
+struct SegArgs {
+  const bf16* q_rows;
+  const bf16* pool;
+  const int* table;
+  int max_blocks, shift, len, tile0, tile1;
 };
 
-// Attend one query row (HEADS heads at q_rows, row stride kW) over tiles
-// [tile0, tile1) of one sequence (len rows, page table `table`).
+__device__ __forceinline__ const bf16* tile_rows(const SegArgs& a, PageCursor& pc, int tile,
+                                                 int lane) {
+  const int tok = tile * kTok;
+  const int page = pc.page(tok >> a.shift, lane);
+  const int mask = (1 << a.shift) - 1;
+  return a.pool + ((long)page * (mask + 1) + (tok & mask)) * kW;
+}
+
+// Segment prologue shared by both wave roles: the page ids, then this
+// wave's share of tile 0 (the caller issues its queries, then tile 1).
+template <int NL>
+__device__ __forceinline__ void seg_start(const SegArgs& a, PageCursor& pc, uint32_t lds,
+                                          uint32_t j0, int lane) {
+  pc.start(a.table, a.max_blocks, (a.tile0 * kTok) >> a.shift, lane);
+  issue_part<NL>(tile_rows(a, pc, a.tile0, lane), min(kTok, a.len - a.tile0 * kTok), lds, j0, lane);
+}
+
+// Step-top synchronisation shared by both wave roles: wait for this wave's
+// loads of tile k (tile k+1 may stay in flight), barrier, then issue tile
+// k+2 into the buffer tile k-2 used.
+template <int NL>
+__device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint32_t lds,
+                                          uint32_t j0, int k, int n, int lane) {
+  if (k < n) {
+    if (k + 1 < n)
+      wait_vmcnt<NL>();
+    else
+      wait_vmcnt<0>();
+  }
+  lds_barrier();
+  if (k + 2 < n) {
+    const int tile = a.tile0 + k + 2;
+    issue_part<NL>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
+                   lds + (uint32_t)((k + 2) % kNBuf) * kTileBytes, j0, lane);
+  }
+}
+
+// Score wave `sw` (heads 16 sw .. 16 sw + 15): runs the segment's steps and
+// returns (in lanes 0..15) the reference max and full row sum of head
+// 16 sw + lane.  Inactive score waves (sw >= SW) only take part in loads and
+// barriers.
 template <int HEADS>
-__device__ __forceinline__ void run_segment(const bf16* __restrict__ q_rows,
-                                            const bf16* __restrict__ pool,
-                                            const int* __restrict__ table, int shift, int len,
-                                            int tile0, int tile1, uint32_t lds,
-                                            SegState<HEADS>& st, int wave, int lane) {
+__device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int sw, int lane,
+                                           float& m_out, float& l_out) {
   using G = Geo<HEADS>;
-  const uint32_t p_lds = lds + kOffP, alp = lds + kOffAlpha, red = lds + kOffRed;
-  const int hq = wave % G::HQ, tq = wave / G::HQ;
-  const int h = 16 * hq + (lane & 15);     // this lane's head in the S phase
-  const uint32_t kq = lane >> 4;           // 0..3
+  const bool active = sw < G::SW;
+  const int n = a.tile1 - a.tile0;
+  const uint32_t j0 = (uint32_t)sw * kSLoads;
+  PageCursor pc;
+  seg_start<kSLoads>(a, pc, lds, j0, lane);
 
-  // Per-lane LDS bases; every other offset below is a compile-time constant.
-  // S: row tr = TPW tq + 16 tb + lane%16, chunk k = 4 ks + kq at position
-  // 8 (ks/2) + ((4 (ks%2) + kq) ^ swz(tr)); swz(tr) depends on lane%16 only.
-  const uint32_t tr0 = (uint32_t)(G::TPW * tq) + (lane & 15);
-  const uint32_t s_even = (tr0 * kCh + (kq ^ swz(tr0))) * 16u;
-  const uint32_t s_odd = (tr0 * kCh + ((4u + kq) ^ swz(tr0))) * 16u;
-  // P*C transposing reads: lane (16 g + li) of the fragment for token block
-  // ks and column block cb reads row 16 ks + x + 4 hi, chunk 8 wave + cc,
-  // cc = 4 cb + 2 (g%2) + b1, at position 8 wave + (cc ^ (2 a + hi)), a = li/4.
-  const uint32_t g = lane >> 4, li = lane & 15;
-  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u, a2 = 2u * (li >> 2);
-  uint32_t tr_off[2][2];  // [cb][hi]
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const uint32_t cc = 4u * cb + 2u * (g & 1) + b1;
-      tr_off[cb][hi] = ((x + 4u * hi) * kCh + 8u * wave + (cc ^ (a2 + hi))) * 16u + 8u * (li & 1);
-    }
-  // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
-  const uint32_t pa_base = p_lds + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
-  const uint32_t pw_base = p_lds + (h * kPStride + G::TPW * tq + 4 * kq) * 2;
-  const uint32_t al_base = alp + 16 * (lane >> 5);
-
-  // queries of this wave's 16 heads: B operand of S^T = T Q^T (16x16x32)
+  const int h = 16 * sw + (lane & 15);
+  const uint32_t kq = lane >> 4;
   bf16x8 qf[kW / 32];
-  {
-    const bf16* q = q_rows + h * kW + 8 * kq;
+  if (active) {
+    const bf16* q = a.q_rows + h * kW + 8 * kq;
 #pragma unroll
     for (int ks = 0; ks < kW / 32; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
   }
-#pragma unroll
-  for (int a = 0; a < G::HB; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) st.o[a][b] = f32x16{};
-  st.m = -INFINITY;
-  st.l = 0.f;
-
-  const int mask = (1 << shift) - 1;
-  auto rows_at = [&](int tile, int page) {
-    return pool + ((long)page * (mask + 1) + ((tile * kTok) & mask)) * kW;
-  };
-  int page = table[(tile0 * kTok) >> shift];
-  issue_tile(rows_at(tile0, page), min(kTok, len - tile0 * kTok), lds, wave, lane);
-  int next_page = (tile0 + 1 < tile1) ? table[((tile0 + 1) * kTok) >> shift] : 0;
-
-  for (int tile = tile0; tile < tile1; ++tile) {
-    const uint32_t buf = lds + (uint32_t)((tile - tile0) & 1) * kTileBytes;
+  if (n > 1) {
+    const int tile = a.tile0 + 1;
+    issue_part<kSLoads>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
+                        lds + kTileBytes, j0, lane);
+    wait_vmcnt<kSLoads>();
+  } else {
     wait_vmcnt<0>();
-    lds_barrier();  // tile visible to all waves; previous tile fully consumed
-    if (tile + 1 < tile1) {
-      issue_tile(rows_at(tile + 1, next_page), min(kTok, len - (tile + 1) * kTok),
-                 lds + (uint32_t)((tile + 1 - tile0) & 1) * kTileBytes, wave, lane);
-      if (tile + 2 < tile1) next_page = table[((tile + 2) * kTok) >> shift];
-    }
-
-    // ---- S^T for tokens TPW tq + (0..TPW-1) x heads 16 hq + (0..15), K = 576
-    f32x4 sacc[G::TB];
+  }
+  // The queries have landed (only tile 1 may still be in flight).  Hand them
+  // on as plain register values, so that no wait inside the loop is tied to
+  // their loads.
 #pragma unroll
-    for (int tb = 0; tb < G::TB; ++tb) sacc[tb] = f32x4{};
+  for (int ks = 0; ks < kW / 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+
+  // S fragment (ks, tb): row tr0 + 16 tb, chunk 4 ks + kq at position
+  // 8 (ks/2) + ((4 (ks%2) + kq) ^ swz(tr0)); swz depends on lane%16 only.
+  const uint32_t tr0 = lane & 15;
+  const uint32_t s_even = (tr0 * kCh + (kq ^ swz(tr0))) * 16u;
+  const uint32_t s_odd = (tr0 * kCh + ((4u + kq) ^ swz(tr0))) * 16u;
+  const uint32_t pw_base = lds + kOffP + (h * kPStride + 4 * kq) * 2;
+
+  float m = -INFINITY, l = 0.f;
+  for (int k = 0; k <= n; ++k) {
+    step_sync<kSLoads>(a, pc, lds, j0, k, n, lane);
+    if (k == n || !active) continue;
+    const uint32_t buf = lds + (uint32_t)(k % kNBuf) * kTileBytes;
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
-      // fragment (ks, tb): row tr0 + 16 tb -> + tb * 16 * 1152 bytes
       auto frag = [&](int ks, int tb) {
         return lds_read_b128(buf + ((ks & 1) ? s_odd : s_even) +
                              (uint32_t)((ks >> 1) * 128 + tb * 16 * kCh * 16));
       };
-      constexpr int D = G::TB == 1 ? 3 : 1;  // k-steps read ahead
-      bf16x8 fr[D + 1][G::TB];
-#pragma unroll
-      for (int d = 0; d < D; ++d)
-#pragma unroll
-        for (int tb = 0; tb < G::TB; ++tb) fr[d][tb] = frag(d, tb);
+      bf16x8 fr[2][2];
+      fr[0][0] = frag(0, 0);
+      fr[0][1] = frag(0, 1);
 #pragma unroll
       for (int ks = 0; ks < kW / 32; ++ks) {
-        if (ks + D < kW / 32) {
-#pragma unroll
-          for (int tb = 0; tb < G::TB; ++tb) fr[(ks + D) % (D + 1)][tb] = frag(ks + D, tb);
+        if (ks + 1 < kW / 32) {
+          fr[(ks + 1) & 1][0] = frag(ks + 1, 0);
+          fr[(ks + 1) & 1][1] = frag(ks + 1, 1);
         }
-#pragma unroll
-        for (int tb = 0; tb < G::TB; ++tb)
-          sacc[tb] = mfma16(fr[ks % (D + 1)][tb], qf[ks], sacc[tb]);
+        sacc[0] = mfma16(fr[ks & 1][0], qf[ks], sacc[0]);
+        sacc[1] = mfma16(fr[ks & 1][1], qf[ks], sacc[1]);
       }
     }
-    // register v of block tb <-> token TPW tq + 16 tb + 4 kq + v, head h
-    const int valid = len - tile * kTok;
+    // register v of block tb <-> token 16 tb + 4 kq + v, head h
+    const int valid = a.len - (a.tile0 + k) * kTok;
     float hmax = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < G::TB; ++tb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        if (G::TPW * tq + 16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
+        if (16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
         hmax = fmaxf(hmax, sacc[tb][v]);
       }
     hmax = fmaxf(hmax, __shfl_xor(hmax, 16, 64));
     hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-    if (lane < 16) lds_st(red + (tq * kMaxHG + h) * 4, hmax);
-    lds_barrier();
-    float tmax = lds_ld(red + h * 4);
-#pragma unroll
-    for (int t2 = 1; t2 < G::TQ; ++t2) tmax = fmaxf(tmax, lds_ld(red + (t2 * kMaxHG + h) * 4));
-    const bool grow = tmax > st.m + kRescaleSlack;
-    const float m_new = grow ? tmax : st.m;
-    const float alpha = grow ? exp2f(st.m - m_new) : 1.0f;
+    const bool grow = hmax > m + kRescaleSlack;
+    const float m_new = grow ? hmax : m;
+    const float alpha = grow ? exp2f(m - m_new) : 1.0f;
     const bool any = __ballot(grow) != 0ull;
+    const uint32_t pb = pw_base + (uint32_t)(k & 1) * (kMaxHG * kPStride * 2);
     float psum = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < G::TB; ++tb) {
+    for (int tb = 0; tb < 2; ++tb) {
       bf16x4 pk;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const bf16 pb = (bf16)exp2f(sacc[tb][v] - m_new);
-        pk[v] = pb;
-        psum += (float)pb;
+        const bf16 p = (bf16)exp2f(sacc[tb][v] - m_new);
+        pk[v] = p;
+        psum += (float)p;
       }
-      lds_st(pw_base + tb * 32, pk);
+      lds_st(pb + tb * 32, pk);
     }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-    if (tq == 0 && lane < 16) lds_st(alp + h * 4, alpha);
-    if (lane == 0) lds_st(lds + kOffFlag + wave * 4, any ? 1.0f : 0.0f);
-    lds_barrier();
+    l = l * alpha + psum;
+    m = m_new;
+    if (lane < 16) lds_st(lds + kOffAlpha + ((k & 1) * kMaxHG + h) * 4, alpha);
+    if (lane == 0) lds_st(lds + kOffFlag + ((k & 1) * 4 + sw) * 4, any ? 1.0f : 0.0f);
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  m_out = m;
+  l_out = l;
+}
 
-    // ---- O[HEADS h, 64 wave + (0..63)] = O * alpha + P T
-    const f32x4 f0 = lds_ld4(lds + kOffFlag), f1 = lds_ld4(lds + kOffFlag + 16);
-    if (f0[0] + f0[1] + f0[2] + f0[3] + f1[0] + f1[1] + f1[2] + f1[3] != 0.0f) {
+// P*C wave `pw` (columns 128 pw .. 128 pw + 127 of O, all HEADS heads).
+template <int HEADS>
+struct OAcc {
+  f32x16 o[Geo<HEADS>::HB][4];  // O[32 hb + ..][128 pw + 32 cb + ..]
+};
+
+template <int HEADS>
+__device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, int lane,
+                                        OAcc<HEADS>& acc) {
+  using G = Geo<HEADS>;
+  const int n = a.tile1 - a.tile0;
+  const uint32_t j0 = 4u * kSLoads + (uint32_t)pw * kPLoads;
+  PageCursor pc;
+  seg_start<kPLoads>(a, pc, lds, j0, lane);
+  if (n > 1) {
+    const int tile = a.tile0 + 1;
+    issue_part<kPLoads>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
+                        lds + kTileBytes, j0, lane);
+  }
+#pragma unroll
+  for (int hb = 0; hb < G::HB; ++hb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc.o[hb][cb] = f32x16{};
+
+  // Transposing reads: lane (16 g + li) of the fragment for token block ks
+  // and column block cb reads row 16 ks + x + 4 hi, chunk 16 pw + 4 cb +
+  // 2 (g%2) + b1, stored at 8 (2 pw + cb/2) + ((4 (cb%2) + 2 (g%2) + b1) ^ (2 a + hi)),
+  // a = li/4 (the row's swizzle), plus 8 bytes for odd li.
+  const uint32_t g = lane >> 4, li = lane & 15;
+  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u, a2 = 2u * (li >> 2);
+  uint32_t tr_off[4][2];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const uint32_t cc = 4u * (cb & 1) + 2u * (g & 1) + b1;
+      tr_off[cb][hi] = ((x + 4u * hi) * kCh + 8u * (2u * pw + (cb >> 1)) + (cc ^ (a2 + hi))) * 16u +
+                       8u * (li & 1);
+    }
+  // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
+  const uint32_t pa_base = lds + kOffP + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
+  const uint32_t al_base = lds + kOffAlpha + 16 * (lane >> 5);
+
+  for (int k = 0; k <= n; ++k) {
+    step_sync<kPLoads>(a, pc, lds, j0, k, n, lane);
+    if (k == 0) continue;
+    const int kp = k - 1;  // tile whose P is ready
+    const uint32_t buf = lds + (uint32_t)(kp % kNBuf) * kTileBytes;
+    const uint32_t par = (uint32_t)(kp & 1);
+    const f32x4 f = lds_ld4(lds + kOffFlag + par * 16);
+    float fs = f[0] + f[1];
+    if (G::SW > 2) fs += f[2] + f[3];
+    if (fs != 0.0f) {
 #pragma unroll
       for (int hb = 0; hb < G::HB; ++hb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 a4 = lds_ld4(al_base + hb * 128 + q * 32);
+          const f32x4 a4 = lds_ld4(al_base + (par * kMaxHG + 32 * hb + 8 * q) * 4);
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st.o[hb][cb][4 * q + r] *= a4[r];
+            for (int r = 0; r < 4; ++r) acc.o[hb][cb][4 * q + r] *= a4[r];
         }
     }
+    const uint32_t pbase = pa_base + par * (kMaxHG * kPStride * 2);
+    uint32_t ta[8];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) ta[2 * cb + hi] = buf + tr_off[cb][hi];
 #pragma unroll
     for (int ks = 0; ks < kTok / 16; ++ks) {
       bf16x8 pa[G::HB];
 #pragma unroll
       for (int hb = 0; hb < G::HB; ++hb)
-        pa[hb] = lds_read_b128(pa_base + hb * 32 * kPStride * 2 + ks * 32);
+        pa[hb] = lds_read_b128(pbase + hb * 32 * kPStride * 2 + ks * 32);
+      bf16x4 t[8];
+      if (ks == 0)
+        lds_read_tr_x8<0>(ta, t);
+      else
+        lds_read_tr_x8<16 * kCh * 16>(ta, t);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const uint32_t off = buf + (uint32_t)(ks * 16 * kCh * 16);
-        const bf16x8 bv = cat(lds_read_tr(off + tr_off[cb][0]), lds_read_tr(off + tr_off[cb][1]));
+      for (int cb = 0; cb < 4; ++cb) {
+        const bf16x8 bv = cat(t[2 * cb], t[2 * cb + 1]);
 #pragma unroll
-        for (int hb = 0; hb < G::HB; ++hb) st.o[hb][cb] = mfma32(pa[hb], bv, st.o[hb][cb]);
+        for (int hb = 0; hb < G::HB; ++hb) acc.o[hb][cb] = mfma32(pa[hb], bv, acc.o[hb][cb]);
       }
     }
   }
 }
 
-// Row sums of the segment: per-wave partial sums into LDS, then the S-phase
-// waves of the first token group combine them into 1/l per head.  Returns the
-// head's full sum in lanes 0..15 of waves 0..HQ-1 (the lanes that hold its m).
-// Ends with a barrier.
+// A whole segment plus its normalised output: score waves publish 1/l per
+// head, P*C waves stage O/l in LDS (the tile buffers, idle by then), all
+// waves copy it out with 16-byte stores.  m and the sum come back in lanes
+// 0..15 of the active score waves (for the split statistics).  Ends with a
+// barrier, so the next segment may refill the buffers.
 template <int HEADS>
-__device__ __forceinline__ float finish_sums(const SegState<HEADS>& st, uint32_t lds, int wave,
-                                             int lane) {
+__device__ __forceinline__ void attend_segment(const SegArgs& a, uint32_t lds, bf16* dst,
+                                               int wave, int lane, float& m_out, float& l_out) {
   using G = Geo<HEADS>;
-  float lt = st.l + __shfl_xor(st.l, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  const int h = 16 * (wave % G::HQ) + (lane & 15);
-  if (lane < 16) lds_st(lds + kOffLsum + ((wave / G::HQ) * kMaxHG + h) * 4, lt);
-  lds_barrier();
-  float tot = 0.f;
-  if (wave < G::HQ && lane < 16) {
-#pragma unroll
-    for (int t2 = 0; t2 < G::TQ; ++t2) tot += lds_ld(lds + kOffLsum + (t2 * kMaxHG + h) * 4);
-    lds_st(lds + kOffInv + h * 4, 1.0f / tot);
-  }
-  lds_barrier();
-  return tot;
-}
-
-// Store O / l for the HEADS heads of this workgroup to dst[h * head_stride + c]
-// (bf16): normalise into an LDS staging area (the tile buffers, free by
-// now), then copy out with 16-byte coalesced stores.  Call after
-// finish_sums; ends with a barrier.
-template <int HEADS>
-__device__ __forceinline__ void store_normalised(const SegState<HEADS>& st, uint32_t lds,
-                                                 bf16* dst, long head_stride, int wave, int lane) {
   typedef __attribute__((address_space(3))) bf16 lds_bf16;
-  // one per-lane base; (head, column-block) offsets are constants below 64 KiB
-  const uint32_t st_base = lds + ((4 * (lane >> 5)) * kOStride + 64 * wave + (lane & 31)) * 2;
-  const uint32_t inv_base = lds + kOffInv + 16 * (lane >> 5);
+  if (wave < 4) {
+    score_role<HEADS>(a, lds, wave, lane, m_out, l_out);
+    if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
+    lds_barrier();
+    lds_barrier();
+  } else {
+    const int pw = wave - 4;
+    OAcc<HEADS> acc;
+    pv_role<HEADS>(a, lds, pw, lane, acc);
+    lds_barrier();
+    // register v of o[hb][cb] <-> head 32 hb + 8 (v/4) + 4 (lane/32) + v%4,
+    // column 128 pw + 32 cb + lane%32
+    const uint32_t st_base = lds + ((4 * (lane >> 5)) * kOStride + 128 * pw + (lane & 31)) * 2;
+    const uint32_t inv_base = lds + kOffInv + 16 * (lane >> 5);
 #pragma unroll
-  for (int hb = 0; hb < Geo<HEADS>::HB; ++hb)
+    for (int hb = 0; hb < G::HB; ++hb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 inv = lds_ld4(inv_base + (32 * hb + 8 * q) * 4);
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 inv = lds_ld4(inv_base + (32 * hb + 8 * q) * 4);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *(lds_bf16*)(uintptr_t)(st_base + ((32 * hb + 8 * q + r) * kOStride + 32 * cb) * 2) =
-              (bf16)(st.o[hb][cb][4 * q + r] * inv[r]);
-    }
-  lds_barrier();
+          for (int r = 0; r < 4; ++r)
+            *(lds_bf16*)(uintptr_t)(st_base + ((32 * hb + 8 * q + r) * kOStride + 32 * cb) * 2) =
+                (bf16)(acc.o[hb][cb][4 * q + r] * inv[r]);
+      }
+    lds_barrier();
+    m_out = 0.f;
+    l_out = 0.f;
+  }
 #pragma unroll
   for (int i0 = 0; i0 < HEADS * kR / 8; i0 += kThreads) {
-    const int i = i0 + threadIdx.x;
+    const int i = i0 + (int)threadIdx.x;
     const int hh = i / (kR / 8), c8 = (i % (kR / 8)) * 8;
-    *(bf16x8*)(dst + hh * head_stride + c8) = lds_read_b128(lds + (hh * kOStride + c8) * 2);
+    __builtin_nontemporal_store(lds_read_b128(lds + (hh * kOStride + c8) * 2),
+                                (bf16x8*)(dst + hh * kR + c8));
   }
   lds_barrier();
 }
 
-// Workgroup -> (head group, stream index); the head groups of one stream
-// index sit 8 workgroups apart, so round-robin dispatch puts them on the
-// same XCD and the second group reads each tile from that XCD's L2.
-__device__ __forceinline__ void map_block(int hgc, int& hg, int& w) {
+// Workgroup -> (head group, stream index).  Blocks go round-robin over the
+// 8 XCDs, so block b runs on XCD b % 8; each XCD gets a contiguous run of
+// stream indices (consecutive pieces of the same sequences share its
+// queries in that XCD's L2), and the head groups of one stream index sit 8
+// blocks apart on the same XCD (the second group reads each tile from L2).
+// n_wg is a multiple of 8.
+__device__ __forceinline__ void map_block(int hgc, int n_wg, int& hg, int& w) {
   const int b = blockIdx.x;
-  const int per = 8 * hgc;
-  hg = (b % per) / 8;
-  w = (b / per) * 8 + (b % 8);
+  const int x = b & 7, j = b >> 3;
+  hg = j % hgc;
+  w = x * (n_wg >> 3) + j / hgc;
 }
 
 }  // namespace
@@ -360,16 +456,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hgc = H / HEADS;
   int hg, w;
-  map_block(hgc, hg, w);
+  map_block(hgc, n_wg, hg, w);
   int* prefix = (int*)(smem + kOffPrefix);
+  unsigned char* lenlo = (unsigned char*)(smem + kOffLenLo);
 
-  // prefix sums of tiles per sequence (2 sequences per thread, then a scan)
+  // prefix sums of tiles per sequence (2 sequences per thread, then a scan);
+  // (len - 1) % kTok kept beside them, so a sequence's length needs no
+  // further global read
   {
     int cnt[2], tot = 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int b = tid * 2 + i;
-      cnt[i] = b < batch ? (seq_lens[b] + kTok - 1) / kTok : 0;
+      const int len = b < batch ? seq_lens[b] : 0;
+      cnt[i] = len > 0 ? (len + kTok - 1) / kTok : 0;
+      if (b < batch) lenlo[b] = (unsigned char)((len - 1) & (kTok - 1));
       tot += cnt[i];
     }
     int incl = tot;
@@ -412,26 +513,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     b = lo;
   }
   const long n_slots = (long)n_wg + batch;
-  SegState<HEADS> st;
   while (x0 < x1) {
-    const long seg_end = min(x1, (long)prefix[b + 1]);
-    const int len = seq_lens[b];
-    const int tile0 = (int)(x0 - prefix[b]), tile1 = (int)(seg_end - prefix[b]);
+    const int p0 = prefix[b], p1 = prefix[b + 1];
+    const long seg_end = min(x1, (long)p1);
+    const int tile0 = (int)(x0 - p0), tile1 = (int)(seg_end - p0);
     if (tile1 <= tile0) {  // a sequence without rows (invalid input): nothing to attend
       ++b;
       continue;
     }
-    run_segment<HEADS>(q_full + ((long)b * H + hg * HEADS) * kW, pool,
-                       block_table + (long)b * max_blocks, shift, len, tile0, tile1, lds, st,
-                       wave, lane);
-    const float tot = finish_sums<HEADS>(st, lds, wave, lane);
+    const int len = (p1 - p0 - 1) * kTok + lenlo[b] + 1;
     const long slot = (long)hg * n_slots + w + b;
-    if (wave < Geo<HEADS>::HQ && lane < 16) {
+    SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
+              max_blocks, shift, len, tile0, tile1};
+    float m, tot;
+    attend_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane, m, tot);
+    if (wave < Geo<HEADS>::SW && lane < 16) {
       const int h = 16 * wave + lane;
-      part_ml[(slot * HEADS + h) * 2 + 0] = st.m;
-      part_ml[(slot * HEADS + h) * 2 + 1] = tot;
+      const f32x2 ml = {m, tot};
+      __builtin_nontemporal_store(ml, (f32x2*)(part_ml + (slot * HEADS + h) * 2));
     }
-    store_normalised<HEADS>(st, lds, part_o + slot * HEADS * kR, kR, wave, lane);
     x0 = seg_end;
     ++b;
   }
@@ -459,12 +559,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
   const int n = b * T_len + t;
   const int len = start_pos[b] + t + 1;
   (void)tid;
-  SegState<HEADS> st;
-  run_segment<HEADS>(q_full + ((long)n * H + hg * HEADS) * kW, pool,
-                     block_table + (long)b * max_blocks, shift, len, 0, (len + kTok - 1) / kTok,
-                     lds, st, wave, lane);
-  finish_sums<HEADS>(st, lds, wave, lane);
-  store_normalised<HEADS>(st, lds, o_lat + ((long)n * H + hg * HEADS) * kR, kR, wave, lane);
+  SegArgs a{q_full + ((long)n * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
+            max_blocks, shift, len, 0, (len + kTok - 1) / kTok};
+  float m, tot;
+  attend_segment<HEADS>(a, lds, o_lat + ((long)n * H + hg * HEADS) * kR, wave, lane, m, tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -613,6 +711,7 @@ __global__ void __launch_bounds__(kCThreads) combine_kernel(
     if (bb < batch) out[((long)bb * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[v];
   }
 }
+
 
 // ---------------------------------------------------------------------------
 size_t decode_partial_slots(int batch, int n_wg) { return (size_t)n_wg + (size_t)batch; }

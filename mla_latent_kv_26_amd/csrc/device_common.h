@@ -9,6 +9,7 @@ typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -41,6 +42,28 @@ __device__ __forceinline__ bf16x4 lds_read_tr(uint32_t byte_addr) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(uintptr_t)byte_addr);
   return __builtin_bit_cast(bf16x4, v);
+}
+// Eight transposing LDS reads at a[i] + OFF, finished before the block ends
+// (the wait is inside the asm block, so the outputs are valid when it
+// returns).  Unlike the builtin, this does not make the compiler wait for
+// in-flight direct-to-LDS loads into other buffers first.
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr_x8(const uint32_t (&a)[8], bf16x4 (&o)[8]) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "i"(OFF));
 }
 __device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
