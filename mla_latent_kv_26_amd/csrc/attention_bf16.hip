@@ -566,18 +566,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Combine (+ optional W_UV projection).  Workgroup = (head, 16 sequences),
-// 512 threads; thread (row tid/32, 16 columns).
+// Combine (+ optional W_UV projection).  Workgroup = (head, 8 sequences),
+// one wave per sequence; lane l holds columns 8 l .. 8 l + 7 of o_lat.
 // o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
 // Dependent global round trips are kept to two: the prefix sums, then every
-// piece's statistics and values at once.  W_UV[h] streams into LDS with
-// direct-to-LDS loads issued first.
+// piece's statistics and the first pieces' values at once.  W_UV[h] streams
+// into LDS with direct-to-LDS loads issued first; the workgroups of one head
+// sit 64 blocks apart, i.e. on one XCD, and share it through that L2.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kCRows = 16;
-constexpr int kCThreads = 512;
+constexpr int kCRows = 8;               // sequences per workgroup
+constexpr int kCThreads = 64 * kCRows;  // one wave per sequence
 constexpr int kCOStride = kR + 8;       // bf16 per o_lat row in LDS
-constexpr int kSegChunk = 8;            // pieces whose values are in flight together
+constexpr int kPieceChunk = 8;          // pieces whose values are in flight together
 
 // W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
 // position c ^ 2(r&3), so the 4 rows x 2 chunks of a transposing read fall
@@ -591,30 +592,33 @@ __global__ void __launch_bounds__(kCThreads) combine_kernel(
     const int* __restrict__ prefix, const float* __restrict__ part_ml,
     const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg,
     const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) bf16 olds[kCRows * kCOStride];
+  // o_lat rows for the projection: 16 (the MFMA height); rows 8..15 are zero
+  __shared__ __attribute__((aligned(16))) bf16 olds[16 * kCOStride];
   __shared__ __attribute__((aligned(16))) bf16 wlds[kR * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b0 = blockIdx.y * kCRows;
   const int hg = h / hg_heads, hl = h % hg_heads;
   const long n_slots = (long)n_wg + batch;
   const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
-  const uint32_t wb = lds_addr(wlds);
+  const uint32_t wb = lds_addr(wlds), ob = lds_addr(olds);
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
   // W_UV[h] -> LDS (asynchronous): slot s = 64 j + lane holds row s/16,
   // chunk (s%16) ^ 2(row&3); chunks past Dv/8 load the row's chunk 0 (unused).
   if (W) {
 #pragma unroll
-    for (int i = 0; i < kR * 16 / 64 / 8; ++i) {
-      const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / 8) + i;
+    for (int i = 0; i < kR * 16 / 64 / kCRows; ++i) {
+      const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCRows) + i;
       const uint32_t s = 64u * j + lane, r = s >> 4;
       uint32_t c = (s & 15u) ^ ((r & 3u) << 1);
       if ((int)c >= Dv / 8) c = 0;
       g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
     }
+    // zero padding rows 8..15 (one 16-byte chunk per thread)
+    *(lds_bf16x8*)(uintptr_t)(ob + ((kCRows + (tid >> 6)) * kCOStride + 8 * lane) * 2) = bf16x8{};
   }
 
-  const int rr = tid >> 5, sl = tid & 31, c0 = sl * 16;
-  const int b = b0 + rr;
+  const int b = b0 + wave;
   const long T = prefix[batch];
   int f = 0, n = 0;
   if (b < batch) {
@@ -625,74 +629,72 @@ __global__ void __launch_bounds__(kCThreads) combine_kernel(
     }
   }
   const long slot0 = (long)hg * n_slots + f + b;
-  // statistics: thread sl holds pieces sl and sl + 32 (n <= 64 here; longer
-  // merges loop over groups of 64)
-  float acc[16];
+  auto piece_o = [&](int s) {
+    return *(const bf16x8*)(part_o + ((slot0 + s) * hg_heads + hl) * kR + 8 * lane);
+  };
+  auto piece_ml = [&](int s) {
+    return *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2);
+  };
+  // the first pieces' values, in flight together with the statistics
+  bf16x8 v[kPieceChunk];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int u = 0; u < kPieceChunk; ++u)
+    if (u < n) v[u] = piece_o(u);
+  f32x2 ml0 = {-INFINITY, 0.f};
   float M = -INFINITY;
-  for (int s = sl; s < n; s += 32) M = fmaxf(M, part_ml[((slot0 + s) * hg_heads + hl) * 2]);
+  for (int s = lane; s < n; s += 64) {
+    const f32x2 t = piece_ml(s);
+    if (s == lane) ml0 = t;
+    M = fmaxf(M, t[0]);
+  }
+  M = wave_max(M);
+
+  float acc[8];
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float den = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 32) {
-    // weight of piece s0 + sl, then all of this group's values, kSegChunk at a time
-    const int sw = s0 + sl;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int sw = s0 + lane;
     float e = 0.f;
     if (sw < n) {
-      const float2 ml = *(const float2*)(part_ml + ((slot0 + sw) * hg_heads + hl) * 2);
-      e = exp2f(ml.x - M) * ml.y;
+      const f32x2 t = s0 == 0 ? ml0 : piece_ml(sw);
+      e = exp2f(t[0] - M) * t[1];
     }
     den += e;
-    const int m = min(32, n - s0);
-    for (int u0 = 0; u0 < m; u0 += kSegChunk) {
-      bf16x8 v[kSegChunk][2];
+    const int m = min(64, n - s0);
+    for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
+      if (s0 + u0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kSegChunk; ++u)
-        if (u0 + u < m) {
-          const bf16* src = part_o + ((slot0 + s0 + u0 + u) * hg_heads + hl) * kR + c0;
-          v[u][0] = *(const bf16x8*)src;
-          v[u][1] = *(const bf16x8*)(src + 8);
-        }
+        for (int u = 0; u < kPieceChunk; ++u)
+          if (u0 + u < m) v[u] = piece_o(s0 + u0 + u);
+      }
 #pragma unroll
-      for (int u = 0; u < kSegChunk; ++u) {
-        const float eu = __shfl(e, (lane & 32) + u0 + u, 64);
+      for (int u = 0; u < kPieceChunk; ++u) {
+        const float eu = __shfl(e, u0 + u, 64);
         if (u0 + u < m) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            acc[i] += eu * (float)v[u][0][i];
-            acc[8 + i] += eu * (float)v[u][1][i];
-          }
+          for (int i = 0; i < 8; ++i) acc[i] += eu * (float)v[u][i];
         }
       }
     }
   }
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) den += __shfl_xor(den, o, 64);
+  den = wave_sum(den);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  bf16x8 o0, o1;
+  bf16x8 o;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    o0[i] = (bf16)(acc[i] * inv);
-    o1[i] = (bf16)(acc[8 + i] * inv);
-  }
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)(acc[i] * inv);
   if (!W) {
-    if (b < batch) {
-      *(bf16x8*)(out + ((long)b * H + h) * kR + c0) = o0;
-      *(bf16x8*)(out + ((long)b * H + h) * kR + c0 + 8) = o1;
-    }
+    if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
     return;
   }
-  *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(lds_addr(olds) + (rr * kCOStride + c0) * 2) = o0;
-  *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(lds_addr(olds) + (rr * kCOStride + c0 + 8) * 2) = o1;
+  *(lds_bf16x8*)(uintptr_t)(ob + (wave * kCOStride + 8 * lane) * 2) = o;
   wait_vmcnt<0>();
   __syncthreads();
 
-  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows x Dv, K = 512, 16x16x32 MFMAs;
-  // wave w owns the 16-column block w (Dv <= 128).
+  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows (8 used) x Dv, K = 512,
+  // 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
   if (16 * wave >= Dv) return;
   f32x4 pacc = {};
-  const uint32_t ob = lds_addr(olds);
   const int g = lane >> 4, li = lane & 15;
 #pragma unroll 4
   for (int ks = 0; ks < kR / 32; ++ks) {
@@ -706,12 +708,12 @@ __global__ void __launch_bounds__(kCThreads) combine_kernel(
   }
   // register v of lane l: row 4(l/16) + v, column l%16
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int bb = b0 + 4 * (lane >> 4) + v;
-    if (bb < batch) out[((long)bb * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[v];
+  for (int v4 = 0; v4 < 4; ++v4) {
+    const int r = 4 * (lane >> 4) + v4;
+    if (r < kCRows && b0 + r < batch)
+      out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[v4];
   }
 }
-
 
 // ---------------------------------------------------------------------------
 size_t decode_partial_slots(int batch, int n_wg) { return (size_t)n_wg + (size_t)batch; }
