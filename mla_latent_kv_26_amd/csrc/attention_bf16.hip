@@ -130,6 +130,7 @@ struct SegArgs {
   const bf16* pool;
   const int* table;
   int max_blocks, shift, len, tile0, tile1;
+  const PageCursor* pre;  // page ids already loaded for tile0's page, or null
 };
 
 __device__ __forceinline__ const bf16* tile_rows(const SegArgs& a, PageCursor& pc, int tile,
@@ -145,7 +146,10 @@ __device__ __forceinline__ const bf16* tile_rows(const SegArgs& a, PageCursor& p
 template <int NL>
 __device__ __forceinline__ void seg_start(const SegArgs& a, PageCursor& pc, uint32_t lds,
                                           uint32_t j0, int lane) {
-  pc.start(a.table, a.max_blocks, (a.tile0 * kTok) >> a.shift, lane);
+  if (a.pre)
+    pc = *a.pre;
+  else
+    pc.start(a.table, a.max_blocks, (a.tile0 * kTok) >> a.shift, lane);
   issue_part<NL>(tile_rows(a, pc, a.tile0, lane), min(kTok, a.len - a.tile0 * kTok), lds, j0, lane);
 }
 
@@ -449,8 +453,8 @@ template <int HEADS>
 __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int shift,
-    const int* __restrict__ seq_lens, int batch, int H, int n_wg, int* __restrict__ prefix_out,
-    float* __restrict__ part_ml, bf16* __restrict__ part_o) {
+    const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
+    int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   const uint32_t lds = lds_addr(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -459,6 +463,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
   map_block(hgc, n_wg, hg, w);
   int* prefix = (int*)(smem + kOffPrefix);
   unsigned char* lenlo = (unsigned char*)(smem + kOffLenLo);
+
+  // Where this workgroup's range would start if every sequence had
+  // guess_tiles tiles (the common equal-length batch): load that page-id
+  // chunk now, in parallel with the lengths, and keep it if the guess holds.
+  const long tg = (long)batch * guess_tiles;
+  const long xg = ((long)w * tg) / n_wg;
+  const int bg = min((int)(xg / guess_tiles), batch - 1);
+  const int pg0 = (int)((xg - (long)bg * guess_tiles) * kTok) >> shift;
+  PageCursor spec;
+  spec.start(block_table + (long)bg * max_blocks, max_blocks, pg0, lane);
 
   // prefix sums of tiles per sequence (2 sequences per thread, then a scan);
   // (len - 1) % kTok kept beside them, so a sequence's length needs no
@@ -523,8 +537,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     }
     const int len = (p1 - p0 - 1) * kTok + lenlo[b] + 1;
     const long slot = (long)hg * n_slots + w + b;
+    const bool guessed = b == bg && ((tile0 * kTok) >> shift) == pg0;
     SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
-              max_blocks, shift, len, tile0, tile1};
+              max_blocks, shift, len, tile0, tile1, guessed ? &spec : nullptr};
     float m, tot;
     attend_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane, m, tot);
     if (wave < Geo<HEADS>::SW && lane < 16) {
@@ -560,25 +575,33 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
   const int len = start_pos[b] + t + 1;
   (void)tid;
   SegArgs a{q_full + ((long)n * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
-            max_blocks, shift, len, 0, (len + kTok - 1) / kTok};
+            max_blocks, shift, len, 0, (len + kTok - 1) / kTok, nullptr};
   float m, tot;
   attend_segment<HEADS>(a, lds, o_lat + ((long)n * H + hg * HEADS) * kR, wave, lane, m, tot);
 }
 
 // ---------------------------------------------------------------------------
-// Combine (+ optional W_UV projection).  Workgroup = (head, 8 sequences),
-// one wave per sequence; lane l holds columns 8 l .. 8 l + 7 of o_lat.
+// Combine (+ optional W_UV projection).  Workgroup = (head, 8 RPW sequences),
+// 8 waves, each merging RPW sequences; lane l holds columns 8 l .. 8 l + 7
+// of o_lat.  (RPW = 1 is used: measured, the combine is bound by per-CU
+// bandwidth, and 4 sequences per wave on a quarter of the workgroups ran
+// the decode step 8 us slower at 32 sequences.)
 // o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
 // Dependent global round trips are kept to two: the prefix sums, then every
 // piece's statistics and the first pieces' values at once.  W_UV[h] streams
-// into LDS with direct-to-LDS loads issued first; the workgroups of one head
-// sit 64 blocks apart, i.e. on one XCD, and share it through that L2.
+// into LDS with direct-to-LDS loads issued after those (a wave's loads
+// complete in issue order, so the merge never waits behind W_UV).
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kCRows = 8;               // sequences per workgroup
-constexpr int kCThreads = 64 * kCRows;  // one wave per sequence
-constexpr int kCOStride = kR + 8;       // bf16 per o_lat row in LDS
+constexpr int kCWaves = 8;
+constexpr int kCThreads = 64 * kCWaves;
 constexpr int kPieceChunk = 8;          // pieces whose values are in flight together
+
+// o_lat rows in LDS: 1 KB each, 16-byte chunk c of row r at position
+// c ^ (r % 16), so the 16 rows of a fragment read hit distinct bank groups.
+__device__ __forceinline__ uint32_t o_off(uint32_t r, uint32_t c) {
+  return (r * (kR / 8) + (c ^ (r & 15u))) * 16u;
+}
 
 // W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
 // position c ^ 2(r&3), so the 4 rows x 2 chunks of a transposing read fall
@@ -588,131 +611,152 @@ __device__ __forceinline__ uint32_t w_off(uint32_t r, uint32_t c) {
 }
 }  // namespace
 
+template <int RPW>
 __global__ void __launch_bounds__(kCThreads) combine_kernel(
     const int* __restrict__ prefix, const float* __restrict__ part_ml,
     const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg,
     const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
-  // o_lat rows for the projection: 16 (the MFMA height); rows 8..15 are zero
-  __shared__ __attribute__((aligned(16))) bf16 olds[16 * kCOStride];
+  constexpr int ROWS = kCWaves * RPW;           // sequences per workgroup
+  constexpr int MROWS = ROWS < 16 ? 16 : ROWS;  // rows of the projection (MFMA height)
+  __shared__ __attribute__((aligned(16))) bf16 olds[MROWS * kR];
   __shared__ __attribute__((aligned(16))) bf16 wlds[kR * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x, b0 = blockIdx.y * kCRows;
+  const int h = blockIdx.x, b0 = blockIdx.y * ROWS;
   const int hg = h / hg_heads, hl = h % hg_heads;
   const long n_slots = (long)n_wg + batch;
   const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
   const uint32_t wb = lds_addr(wlds), ob = lds_addr(olds);
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
+  // rows of this wave: r = wave + 8 i, sequence b0 + r
+  const long T = prefix[batch];
+  int f[RPW], n[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int b = b0 + wave + kCWaves * i;
+    const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
+    f[i] = 0;
+    n[i] = 0;
+    if (p1 > p0) {
+      f[i] = owner_of(p0, T, n_wg);
+      n[i] = owner_of(p1 - 1, T, n_wg) - f[i] + 1;
+    }
+  }
+  auto slot0 = [&](int i) { return (long)hg * n_slots + f[i] + b0 + wave + kCWaves * i; };
+  auto piece_o = [&](int i, int s) {
+    return *(const bf16x8*)(part_o + ((slot0(i) + s) * hg_heads + hl) * kR + 8 * lane);
+  };
+  auto piece_ml = [&](int i, int s) {
+    return *(const f32x2*)(part_ml + ((slot0(i) + s) * hg_heads + hl) * 2);
+  };
+  // statistics and the first pieces' values of every row, all in flight
+  f32x2 ml0[RPW];
+  bf16x8 v[RPW][kPieceChunk];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    ml0[i] = f32x2{-INFINITY, 0.f};
+    if (lane < n[i]) ml0[i] = piece_ml(i, lane);
+#pragma unroll
+    for (int u = 0; u < kPieceChunk; ++u)
+      if (u < n[i]) v[i][u] = piece_o(i, u);
+  }
+
   // W_UV[h] -> LDS (asynchronous): slot s = 64 j + lane holds row s/16,
   // chunk (s%16) ^ 2(row&3); chunks past Dv/8 load the row's chunk 0 (unused).
   if (W) {
 #pragma unroll
-    for (int i = 0; i < kR * 16 / 64 / kCRows; ++i) {
-      const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCRows) + i;
+    for (int i = 0; i < kR * 16 / 64 / kCWaves; ++i) {
+      const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCWaves) + i;
       const uint32_t s = 64u * j + lane, r = s >> 4;
       uint32_t c = (s & 15u) ^ ((r & 3u) << 1);
       if ((int)c >= Dv / 8) c = 0;
       g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
     }
-    // zero padding rows 8..15 (one 16-byte chunk per thread)
-    *(lds_bf16x8*)(uintptr_t)(ob + ((kCRows + (tid >> 6)) * kCOStride + 8 * lane) * 2) = bf16x8{};
+    // zero padding rows ROWS .. MROWS-1
+    for (int r = ROWS + wave; r < MROWS; r += kCWaves)
+      *(lds_bf16x8*)(uintptr_t)(ob + o_off(r, lane)) = bf16x8{};
   }
 
-  const int b = b0 + wave;
-  const long T = prefix[batch];
-  int f = 0, n = 0;
-  if (b < batch) {
-    const int p0 = prefix[b], p1 = prefix[b + 1];
-    if (p1 > p0) {
-      f = owner_of(p0, T, n_wg);
-      n = owner_of(p1 - 1, T, n_wg) - f + 1;
-    }
-  }
-  const long slot0 = (long)hg * n_slots + f + b;
-  auto piece_o = [&](int s) {
-    return *(const bf16x8*)(part_o + ((slot0 + s) * hg_heads + hl) * kR + 8 * lane);
-  };
-  auto piece_ml = [&](int s) {
-    return *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2);
-  };
-  // the first pieces' values, in flight together with the statistics
-  bf16x8 v[kPieceChunk];
 #pragma unroll
-  for (int u = 0; u < kPieceChunk; ++u)
-    if (u < n) v[u] = piece_o(u);
-  f32x2 ml0 = {-INFINITY, 0.f};
-  float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) {
-    const f32x2 t = piece_ml(s);
-    if (s == lane) ml0 = t;
-    M = fmaxf(M, t[0]);
-  }
-  M = wave_max(M);
-
-  float acc[8];
+  for (int i = 0; i < RPW; ++i) {
+    const int b = b0 + wave + kCWaves * i;
+    float M = ml0[i][0];
+    for (int s = 64 + lane; s < n[i]; s += 64) M = fmaxf(M, piece_ml(i, s)[0]);
+    M = wave_max(M);
+    float acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  float den = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int sw = s0 + lane;
-    float e = 0.f;
-    if (sw < n) {
-      const f32x2 t = s0 == 0 ? ml0 : piece_ml(sw);
-      e = exp2f(t[0] - M) * t[1];
-    }
-    den += e;
-    const int m = min(64, n - s0);
-    for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
-      if (s0 + u0 > 0) {
-#pragma unroll
-        for (int u = 0; u < kPieceChunk; ++u)
-          if (u0 + u < m) v[u] = piece_o(s0 + u0 + u);
+    for (int e8 = 0; e8 < 8; ++e8) acc[e8] = 0.f;
+    float den = 0.f;
+    for (int s0 = 0; s0 < n[i]; s0 += 64) {
+      const int sw = s0 + lane;
+      float e = 0.f;
+      if (sw < n[i]) {
+        const f32x2 t = s0 == 0 ? ml0[i] : piece_ml(i, sw);
+        e = exp2f(t[0] - M) * t[1];
       }
+      den += e;
+      const int m = min(64, n[i] - s0);
+      for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
+        if (s0 + u0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kPieceChunk; ++u) {
-        const float eu = __shfl(e, u0 + u, 64);
-        if (u0 + u < m) {
+          for (int u = 0; u < kPieceChunk; ++u)
+            if (u0 + u < m) v[i][u] = piece_o(i, s0 + u0 + u);
+        }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += eu * (float)v[u][i];
+        for (int u = 0; u < kPieceChunk; ++u) {
+          const float eu = __shfl(e, u0 + u, 64);
+          if (u0 + u < m) {
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[i][u][e8];
+          }
         }
       }
     }
-  }
-  den = wave_sum(den);
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  bf16x8 o;
+    den = wave_sum(den);
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    bf16x8 o;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = (bf16)(acc[i] * inv);
-  if (!W) {
-    if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
-    return;
+    for (int e8 = 0; e8 < 8; ++e8) o[e8] = (bf16)(acc[e8] * inv);
+    if (!W) {
+      if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
+    } else {
+      *(lds_bf16x8*)(uintptr_t)(ob + o_off(wave + kCWaves * i, lane)) = o;
+    }
   }
-  *(lds_bf16x8*)(uintptr_t)(ob + (wave * kCOStride + 8 * lane) * 2) = o;
+  if (!W) return;
   wait_vmcnt<0>();
   __syncthreads();
 
-  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows (8 used) x Dv, K = 512,
+  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: MROWS rows x Dv, K = 512,
   // 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
   if (16 * wave >= Dv) return;
-  f32x4 pacc = {};
+  f32x4 pacc[MROWS / 16];
+#pragma unroll
+  for (int rb = 0; rb < MROWS / 16; ++rb) pacc[rb] = f32x4{};
   const int g = lane >> 4, li = lane & 15;
 #pragma unroll 4
   for (int ks = 0; ks < kR / 32; ++ks) {
-    const bf16x8 a = lds_read_b128(ob + ((lane & 15) * kCOStride + 32 * ks + 8 * (lane >> 4)) * 2);
     // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
     const uint32_t row = 32 * ks + 8 * g + (li >> 2);
     const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
     const bf16x4 lo = lds_read_tr(wb + w_off(row, c) + sub);
     const bf16x4 hi = lds_read_tr(wb + w_off(row + 4, c) + sub);
-    pacc = mfma16(a, cat(lo, hi), pacc);
-  }
-  // register v of lane l: row 4(l/16) + v, column l%16
+    const bf16x8 bw = cat(lo, hi);
 #pragma unroll
-  for (int v4 = 0; v4 < 4; ++v4) {
-    const int r = 4 * (lane >> 4) + v4;
-    if (r < kCRows && b0 + r < batch)
-      out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[v4];
+    for (int rb = 0; rb < MROWS / 16; ++rb) {
+      const bf16x8 a = lds_read_b128(ob + o_off(16 * rb + (lane & 15), 4 * ks + (lane >> 4)));
+      pacc[rb] = mfma16(a, bw, pacc[rb]);
+    }
   }
+  // register v of lane l: row 16 rb + 4(l/16) + v, column l%16
+#pragma unroll
+  for (int rb = 0; rb < MROWS / 16; ++rb)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int r = 16 * rb + 4 * (lane >> 4) + v4;
+      if (r < ROWS && b0 + r < batch)
+        out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[rb][v4];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -738,25 +782,27 @@ int decode_num_wg(int head_groups, int num_cus) {
 
 void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
                                     int max_blocks, int block_shift, const int* seq_lens,
-                                    int batch, int H, int heads_per_wg, int n_wg, int* prefix,
-                                    float* part_ml, void* part_o, hipStream_t st) {
+                                    int batch, int max_seq_len, int H, int heads_per_wg, int n_wg,
+                                    int* prefix, float* part_ml, void* part_o, hipStream_t st) {
   const int hgc = H / heads_per_wg;
+  const int guess_tiles = (max_seq_len + kTok - 1) / kTok;
   if (heads_per_wg == 64)
     attn_decode_partials_kernel<64><<<n_wg * hgc, kThreads, 0, st>>>(
         (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, seq_lens,
-        batch, H, n_wg, prefix, part_ml, (bf16*)part_o);
+        batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
   else
     attn_decode_partials_kernel<32><<<n_wg * hgc, kThreads, 0, st>>>(
         (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, seq_lens,
-        batch, H, n_wg, prefix, part_ml, (bf16*)part_o);
+        batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
 }
 
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
                     int heads_per_wg, int n_wg, const void* w_uv, int Dv, void* out,
                     hipStream_t st) {
-  dim3 grid(H, (batch + kCRows - 1) / kCRows);
-  combine_kernel<<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
-                                       heads_per_wg, n_wg, (const bf16*)w_uv, Dv, (bf16*)out);
+  dim3 grid(H, (batch + kCWaves - 1) / kCWaves);
+  combine_kernel<1><<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
+                                             heads_per_wg, n_wg, (const bf16*)w_uv, Dv,
+                                             (bf16*)out);
 }
 
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,

@@ -75,8 +75,8 @@ int decode_num_wg(int head_groups, int num_cus);
 
 void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
                                     int max_blocks, int block_shift, const int* seq_lens,
-                                    int batch, int H, int heads_per_wg, int n_wg, int* prefix,
-                                    float* part_ml, void* part_o, hipStream_t st);
+                                    int batch, int max_seq_len, int H, int heads_per_wg, int n_wg,
+                                    int* prefix, float* part_ml, void* part_o, hipStream_t st);
 
 // Merge the partials of each (sequence, head) into o_lat (bf16 [batch, H, R])
 // or, when w_uv != NULL, project directly: out[b, h] = o_lat[b, h] W_UV[h].

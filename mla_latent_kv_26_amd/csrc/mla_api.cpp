@@ -332,7 +332,7 @@ static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* 
   const DecodeWs w = decode_ws(d, batch, max_seq_len);
   if (d.dt == MLA_DTYPE_BF16) {
     mla::launch_attention_partials_bf16(q_full, pool, table, max_blocks, d.shift, seq_lens, batch,
-                                        d.H, w.heads, w.n_wg, (int*)at(ws, w.prefix),
+                                        max_seq_len, d.H, w.heads, w.n_wg, (int*)at(ws, w.prefix),
                                         (float*)at(ws, w.part_ml), at(ws, w.part_o), st);
     mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
                         at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, w_uv, d.Dv, dst, st);
@@ -442,7 +442,7 @@ mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, con
   s = check_ws(w, workspace, workspace_bytes);
   if (s != MLA_OK) return s;
   mla::launch_attention_partials_bf16(q_full, kv_pool, block_table, max_blocks_per_seq, d.shift,
-                                      seq_lens, batch, d.H, w.heads, w.n_wg,
+                                      seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
                                       (int*)at(workspace, w.prefix),
                                       (float*)at(workspace, w.part_ml), at(workspace, w.part_o),
                                       (hipStream_t)stream);
