@@ -109,7 +109,9 @@ mla_status mla_rope_table(const mla_config* cfg, int32_t num_positions, float* h
 
 /* Workspace bytes needed by the decode calls (mla_decode,
  * mla_latent_attention, mla_attention_partials, mla_combine_output) for this
- * batch and maximum length.  Scratch only: no initial contents required. */
+ * batch and maximum length.  Scratch only: no initial contents required,
+ * and a call reads only what it wrote itself.  Do not share one workspace
+ * between calls that may run concurrently. */
 mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32_t max_seq_len,
                                      size_t* bytes /* host out */);
 
@@ -143,7 +145,7 @@ mla_status mla_absorb_query(const mla_config* cfg, const void* q_nope, const voi
                             const void* w_uk, int32_t n_rows, void* q_full, void* stream);
 
 /* Stage 2 of decode: attention on the latent rows, split over KV chunks
- * and merged in the same launch.  q_full as written by mla_absorb_query
+ * and merged in the same call.  q_full as written by mla_absorb_query
  * ([batch, H, R + Dr]); o_lat [batch, H, R] (written) is
  * sum_j P[h, j] c_j with P the softmax over the sequence's seq_lens[b] rows.
  * Pool, table and lengths as in mla_decode.  Uses the workspace for split

@@ -427,8 +427,7 @@ __device__ __forceinline__ void attend_segment(const SegArgs& a, uint32_t lds, b
 // queries in that XCD's L2), and the head groups of one stream index sit 8
 // blocks apart on the same XCD (the second group reads each tile from L2).
 // n_wg is a multiple of 8.
-__device__ __forceinline__ void map_block(int hgc, int n_wg, int& hg, int& w) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ void map_block(int b, int hgc, int n_wg, int& hg, int& w) {
   const int x = b & 7, j = b >> 3;
   hg = j % hgc;
   w = x * (n_wg >> 3) + j / hgc;
@@ -444,23 +443,61 @@ __host__ __device__ inline int owner_of(long x, long T, int n) {
   return w;
 }
 
-// ---------------------------------------------------------------------------
-// Decode: each workgroup takes an equal share of the concatenated tile stream
-// of all sequences; every (workgroup, sequence) piece writes one partial
-// into slot w + b (unique: w + b grows along the stream).
-// ---------------------------------------------------------------------------
+namespace {
+
+// Prefix sums of tiles per sequence into LDS prefix[0..batch] (2 sequences
+// per thread, then a scan); optionally (len - 1) % kTok per sequence into
+// lenlo, so a length needs no further global read.  All kThreads threads
+// call it; ends with a barrier.
+__device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, int batch,
+                                            int* prefix, int* scan, unsigned char* lenlo) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt[2], tot = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = tid * 2 + i;
+    const int len = b < batch ? seq_lens[b] : 0;
+    cnt[i] = len > 0 ? (len + kTok - 1) / kTok : 0;
+    if (lenlo && b < batch) lenlo[b] = (unsigned char)((len - 1) & (kTok - 1));
+    tot += cnt[i];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wave; ++i) base += scan[i];
+  int run = base + incl - tot;
+  if (tid == 0) prefix[0] = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = tid * 2 + i;
+    if (b < batch) {
+      run += cnt[i];
+      prefix[b + 1] = run;
+    }
+  }
+  __syncthreads();
+}
+
+// One decode workgroup of the tile stream (block `blk`): every (workgroup,
+// sequence) piece writes one partial into slot w + b (unique: w + b grows
+// along the stream).  Returns whether this workgroup wrote any piece.
 template <int HEADS>
-__global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
-    const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
+__device__ __forceinline__ bool decode_attention_wg(
+    char* smem, int blk, const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int shift,
     const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
     int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   const uint32_t lds = lds_addr(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hgc = H / HEADS;
   int hg, w;
-  map_block(hgc, n_wg, hg, w);
+  map_block(blk, hgc, n_wg, hg, w);
   int* prefix = (int*)(smem + kOffPrefix);
   unsigned char* lenlo = (unsigned char*)(smem + kOffLenLo);
 
@@ -474,48 +511,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
   PageCursor spec;
   spec.start(block_table + (long)bg * max_blocks, max_blocks, pg0, lane);
 
-  // prefix sums of tiles per sequence (2 sequences per thread, then a scan);
-  // (len - 1) % kTok kept beside them, so a sequence's length needs no
-  // further global read
-  {
-    int cnt[2], tot = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int b = tid * 2 + i;
-      const int len = b < batch ? seq_lens[b] : 0;
-      cnt[i] = len > 0 ? (len + kTok - 1) / kTok : 0;
-      if (b < batch) lenlo[b] = (unsigned char)((len - 1) & (kTok - 1));
-      tot += cnt[i];
-    }
-    int incl = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    int* wsum = (int*)(smem + kOffScan);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < wave; ++i) base += wsum[i];
-    int run = base + incl - tot;
-    if (tid == 0) prefix[0] = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int b = tid * 2 + i;
-      if (b < batch) {
-        run += cnt[i];
-        prefix[b + 1] = run;
-      }
-    }
-    __syncthreads();
-  }
+  tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo);
   const long T = prefix[batch];
-  if (blockIdx.x == 0)
+  if (blk == 0)
     for (int b = tid; b <= batch; b += kThreads) prefix_out[b] = prefix[b];
 
   long x0 = ((long)w * T) / n_wg, x1 = ((long)(w + 1) * T) / n_wg;
-  if (x0 >= x1) return;
+  if (x0 >= x1) return false;
   // first sequence touching x0
   int b = 0;
   {
@@ -550,6 +552,196 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     x0 = seg_end;
     ++b;
   }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Combine (+ optional W_UV projection) of 8 sequences for one head: 8 waves,
+// one sequence each; lane l holds columns 8 l .. 8 l + 7 of o_lat.
+//   o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
+// Global round trips after the prefix sums: every piece's statistics and
+// the first pieces' values at once.  A wave's loads complete in issue order,
+// so W_UV (streamed into LDS with direct-to-LDS loads) is issued after them,
+// A piece is read only if its workgroup's range is non-empty (with fewer
+// tiles than workgroups some write nothing), so stale workspace contents
+// never enter the merge.
+// Measured: the combine is bound by per-CU bandwidth, so more workgroups of
+// fewer sequences beat fewer larger ones (4 sequences per wave on a quarter
+// of the workgroups ran the step 8 us slower at 32 sequences).
+// ---------------------------------------------------------------------------
+constexpr int kCWaves = 8;
+constexpr int kCThreads = 64 * kCWaves;
+constexpr int kCRows = kCWaves;           // sequences per workgroup
+constexpr int kPieceChunk = 8;            // pieces whose values are in flight together
+constexpr int kCOBytes = 16 * kR * 2;     // o_lat rows (16: the MFMA height; 8..15 zero)
+constexpr int kCWBytes = kR * 128 * 2;    // W_UV[h] (Dv <= 128)
+
+// W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
+// position c ^ 2(r&3), so the 4 rows x 2 chunks of a transposing read fall
+// on 8 distinct bank groups.
+__device__ __forceinline__ uint32_t w_off(uint32_t r, uint32_t c) {
+  return (r * 16u + (c ^ ((r & 3u) << 1))) * 16u;
+}
+// o_lat rows in LDS: 1 KB each, 16-byte chunk c of row r at position
+// c ^ (r % 16), so the 16 rows of a fragment read hit distinct bank groups.
+__device__ __forceinline__ uint32_t o_off(uint32_t r, uint32_t c) {
+  return (r * (kR / 8) + (c ^ (r & 15u))) * 16u;
+}
+
+__device__ __forceinline__ void issue_w_uv(const bf16* W, int Dv, uint32_t wb, uint32_t ob) {
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // slot s = 64 j + lane holds row s/16, chunk (s%16) ^ 2(row&3); chunks
+  // past Dv/8 load the row's chunk 0 (unused)
+#pragma unroll
+  for (int i = 0; i < kR * 16 / 64 / kCWaves; ++i) {
+    const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCWaves) + i;
+    const uint32_t s = 64u * j + lane, r = s >> 4;
+    uint32_t c = (s & 15u) ^ ((r & 3u) << 1);
+    if ((int)c >= Dv / 8) c = 0;
+    g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
+  }
+  // zero rows kCRows .. 15 of o_lat (one 16-byte chunk per thread)
+  *(lds_bf16x8*)(uintptr_t)(ob + o_off(kCRows + wave, lane)) = bf16x8{};
+}
+
+__device__ __forceinline__ void combine_rows(const int* prefix, const float* __restrict__ part_ml,
+                                             const bf16* __restrict__ part_o, int batch, int H,
+                                             int hg_heads, int n_wg, const bf16* __restrict__ w_uv,
+                                             int Dv, bf16* __restrict__ out, int h, int b0,
+                                             uint32_t wb, uint32_t ob) {
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = h / hg_heads, hl = h % hg_heads;
+  const long n_slots = (long)n_wg + batch;
+  const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
+
+  const int b = b0 + wave;
+  const long T = prefix[batch];
+  const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
+  int f = 0, n = 0;
+  if (p1 > p0) {
+    f = owner_of(p0, T, n_wg);
+    n = owner_of(p1 - 1, T, n_wg) - f + 1;
+  }
+  // Pieces f .. f+n-1 come from workgroups f .. f+n-1 of the stream; one
+  // whose range is empty (fewer tiles than workgroups) wrote nothing.
+  auto has_piece = [&](int s) {
+    const long w = f + s;
+    return (w * T) / n_wg < ((w + 1) * T) / n_wg;
+  };
+  const long slot0 = (long)hg * n_slots + f + b;
+  auto piece_o = [&](int s) {
+    return has_piece(s) ? *(const bf16x8*)(part_o + ((slot0 + s) * hg_heads + hl) * kR + 8 * lane)
+                        : bf16x8{};
+  };
+  auto piece_ml = [&](int s) {
+    return has_piece(s) ? *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2)
+                        : f32x2{-INFINITY, 0.f};
+  };
+  // statistics and the first pieces' values, all in flight
+  f32x2 ml0 = {-INFINITY, 0.f};
+  if (lane < n) ml0 = piece_ml(lane);
+  bf16x8 v[kPieceChunk];
+#pragma unroll
+  for (int u = 0; u < kPieceChunk; ++u)
+    if (u < n) v[u] = piece_o(u);
+  if (W) issue_w_uv(W, Dv, wb, ob);
+
+  float M = ml0[0];
+  for (int s = 64 + lane; s < n; s += 64) M = fmaxf(M, piece_ml(s)[0]);
+  M = wave_max(M);
+  float acc[8];
+#pragma unroll
+  for (int e8 = 0; e8 < 8; ++e8) acc[e8] = 0.f;
+  float den = 0.f;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int sw = s0 + lane;
+    float e = 0.f;
+    if (sw < n) {
+      const f32x2 t = s0 == 0 ? ml0 : piece_ml(sw);
+      if (t[1] > 0.f) e = exp2f(t[0] - M) * t[1];
+    }
+    den += e;
+    const int m = min(64, n - s0);
+    for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
+      if (s0 + u0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kPieceChunk; ++u)
+          if (u0 + u < m) v[u] = piece_o(s0 + u0 + u);
+      }
+#pragma unroll
+      for (int u = 0; u < kPieceChunk; ++u) {
+        const float eu = __shfl(e, u0 + u, 64);
+        if (u0 + u < m) {
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
+        }
+      }
+    }
+  }
+  den = wave_sum(den);
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  bf16x8 o;
+#pragma unroll
+  for (int e8 = 0; e8 < 8; ++e8) o[e8] = (bf16)(acc[e8] * inv);
+  if (!W) {
+    if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
+    return;
+  }
+  *(lds_bf16x8*)(uintptr_t)(ob + o_off(wave, lane)) = o;
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows (8 used) x Dv, K = 512,
+  // 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
+  if (16 * wave >= Dv) return;
+  f32x4 pacc = {};
+  const int g = lane >> 4, li = lane & 15;
+#pragma unroll 4
+  for (int ks = 0; ks < kR / 32; ++ks) {
+    // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
+    const uint32_t row = 32 * ks + 8 * g + (li >> 2);
+    const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
+    const bf16x4 lo = lds_read_tr(wb + w_off(row, c) + sub);
+    const bf16x4 hi = lds_read_tr(wb + w_off(row + 4, c) + sub);
+    const bf16x8 a = lds_read_b128(ob + o_off(lane & 15, 4 * ks + (lane >> 4)));
+    pacc = mfma16(a, cat(lo, hi), pacc);
+  }
+  // register v of lane l: row 4(l/16) + v, column l%16
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) {
+    const int r = 4 * (lane >> 4) + v4;
+    if (r < kCRows && b0 + r < batch)
+      out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[v4];
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Split-KV attention partials only (the staged call).
+// ---------------------------------------------------------------------------
+template <int HEADS>
+__global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
+    const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
+    const int* __restrict__ block_table, int max_blocks, int shift,
+    const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
+    int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  decode_attention_wg<HEADS>(smem, blockIdx.x, q_full, pool, block_table, max_blocks, shift,
+                             seq_lens, batch, H, n_wg, guess_tiles, prefix_out, part_ml, part_o);
+}
+
+// Combine of the partials (the staged call): grid (H, ceil(batch / 8)).
+__global__ void __launch_bounds__(kCThreads) combine_kernel(
+    const int* __restrict__ prefix, const float* __restrict__ part_ml,
+    const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg,
+    const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char smem[kCWBytes + kCOBytes];
+  const uint32_t wb = lds_addr(smem), ob = wb + kCWBytes;
+  combine_rows(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, w_uv, Dv, out, blockIdx.x,
+               blockIdx.y * kCRows, wb, ob);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,185 +770,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
             max_blocks, shift, len, 0, (len + kTok - 1) / kTok, nullptr};
   float m, tot;
   attend_segment<HEADS>(a, lds, o_lat + ((long)n * H + hg * HEADS) * kR, wave, lane, m, tot);
-}
-
-// ---------------------------------------------------------------------------
-// Combine (+ optional W_UV projection).  Workgroup = (head, 8 RPW sequences),
-// 8 waves, each merging RPW sequences; lane l holds columns 8 l .. 8 l + 7
-// of o_lat.  (RPW = 1 is used: measured, the combine is bound by per-CU
-// bandwidth, and 4 sequences per wave on a quarter of the workgroups ran
-// the decode step 8 us slower at 32 sequences.)
-// o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
-// Dependent global round trips are kept to two: the prefix sums, then every
-// piece's statistics and the first pieces' values at once.  W_UV[h] streams
-// into LDS with direct-to-LDS loads issued after those (a wave's loads
-// complete in issue order, so the merge never waits behind W_UV).
-// ---------------------------------------------------------------------------
-namespace {
-constexpr int kCWaves = 8;
-constexpr int kCThreads = 64 * kCWaves;
-constexpr int kPieceChunk = 8;          // pieces whose values are in flight together
-
-// o_lat rows in LDS: 1 KB each, 16-byte chunk c of row r at position
-// c ^ (r % 16), so the 16 rows of a fragment read hit distinct bank groups.
-__device__ __forceinline__ uint32_t o_off(uint32_t r, uint32_t c) {
-  return (r * (kR / 8) + (c ^ (r & 15u))) * 16u;
-}
-
-// W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
-// position c ^ 2(r&3), so the 4 rows x 2 chunks of a transposing read fall
-// on 8 distinct bank groups.
-__device__ __forceinline__ uint32_t w_off(uint32_t r, uint32_t c) {
-  return (r * 16u + (c ^ ((r & 3u) << 1))) * 16u;
-}
-}  // namespace
-
-template <int RPW>
-__global__ void __launch_bounds__(kCThreads) combine_kernel(
-    const int* __restrict__ prefix, const float* __restrict__ part_ml,
-    const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg,
-    const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
-  constexpr int ROWS = kCWaves * RPW;           // sequences per workgroup
-  constexpr int MROWS = ROWS < 16 ? 16 : ROWS;  // rows of the projection (MFMA height)
-  __shared__ __attribute__((aligned(16))) bf16 olds[MROWS * kR];
-  __shared__ __attribute__((aligned(16))) bf16 wlds[kR * 128];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x, b0 = blockIdx.y * ROWS;
-  const int hg = h / hg_heads, hl = h % hg_heads;
-  const long n_slots = (long)n_wg + batch;
-  const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
-  const uint32_t wb = lds_addr(wlds), ob = lds_addr(olds);
-  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-
-  // rows of this wave: r = wave + 8 i, sequence b0 + r
-  const long T = prefix[batch];
-  int f[RPW], n[RPW];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int b = b0 + wave + kCWaves * i;
-    const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
-    f[i] = 0;
-    n[i] = 0;
-    if (p1 > p0) {
-      f[i] = owner_of(p0, T, n_wg);
-      n[i] = owner_of(p1 - 1, T, n_wg) - f[i] + 1;
-    }
-  }
-  auto slot0 = [&](int i) { return (long)hg * n_slots + f[i] + b0 + wave + kCWaves * i; };
-  auto piece_o = [&](int i, int s) {
-    return *(const bf16x8*)(part_o + ((slot0(i) + s) * hg_heads + hl) * kR + 8 * lane);
-  };
-  auto piece_ml = [&](int i, int s) {
-    return *(const f32x2*)(part_ml + ((slot0(i) + s) * hg_heads + hl) * 2);
-  };
-  // statistics and the first pieces' values of every row, all in flight
-  f32x2 ml0[RPW];
-  bf16x8 v[RPW][kPieceChunk];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    ml0[i] = f32x2{-INFINITY, 0.f};
-    if (lane < n[i]) ml0[i] = piece_ml(i, lane);
-#pragma unroll
-    for (int u = 0; u < kPieceChunk; ++u)
-      if (u < n[i]) v[i][u] = piece_o(i, u);
-  }
-
-  // W_UV[h] -> LDS (asynchronous): slot s = 64 j + lane holds row s/16,
-  // chunk (s%16) ^ 2(row&3); chunks past Dv/8 load the row's chunk 0 (unused).
-  if (W) {
-#pragma unroll
-    for (int i = 0; i < kR * 16 / 64 / kCWaves; ++i) {
-      const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCWaves) + i;
-      const uint32_t s = 64u * j + lane, r = s >> 4;
-      uint32_t c = (s & 15u) ^ ((r & 3u) << 1);
-      if ((int)c >= Dv / 8) c = 0;
-      g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
-    }
-    // zero padding rows ROWS .. MROWS-1
-    for (int r = ROWS + wave; r < MROWS; r += kCWaves)
-      *(lds_bf16x8*)(uintptr_t)(ob + o_off(r, lane)) = bf16x8{};
-  }
-
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int b = b0 + wave + kCWaves * i;
-    float M = ml0[i][0];
-    for (int s = 64 + lane; s < n[i]; s += 64) M = fmaxf(M, piece_ml(i, s)[0]);
-    M = wave_max(M);
-    float acc[8];
-#pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) acc[e8] = 0.f;
-    float den = 0.f;
-    for (int s0 = 0; s0 < n[i]; s0 += 64) {
-      const int sw = s0 + lane;
-      float e = 0.f;
-      if (sw < n[i]) {
-        const f32x2 t = s0 == 0 ? ml0[i] : piece_ml(i, sw);
-        e = exp2f(t[0] - M) * t[1];
-      }
-      den += e;
-      const int m = min(64, n[i] - s0);
-      for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
-        if (s0 + u0 > 0) {
-#pragma unroll
-          for (int u = 0; u < kPieceChunk; ++u)
-            if (u0 + u < m) v[i][u] = piece_o(i, s0 + u0 + u);
-        }
-#pragma unroll
-        for (int u = 0; u < kPieceChunk; ++u) {
-          const float eu = __shfl(e, u0 + u, 64);
-          if (u0 + u < m) {
-#pragma unroll
-            for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[i][u][e8];
-          }
-        }
-      }
-    }
-    den = wave_sum(den);
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    bf16x8 o;
-#pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) o[e8] = (bf16)(acc[e8] * inv);
-    if (!W) {
-      if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
-    } else {
-      *(lds_bf16x8*)(uintptr_t)(ob + o_off(wave + kCWaves * i, lane)) = o;
-    }
-  }
-  if (!W) return;
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: MROWS rows x Dv, K = 512,
-  // 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
-  if (16 * wave >= Dv) return;
-  f32x4 pacc[MROWS / 16];
-#pragma unroll
-  for (int rb = 0; rb < MROWS / 16; ++rb) pacc[rb] = f32x4{};
-  const int g = lane >> 4, li = lane & 15;
-#pragma unroll 4
-  for (int ks = 0; ks < kR / 32; ++ks) {
-    // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
-    const uint32_t row = 32 * ks + 8 * g + (li >> 2);
-    const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
-    const bf16x4 lo = lds_read_tr(wb + w_off(row, c) + sub);
-    const bf16x4 hi = lds_read_tr(wb + w_off(row + 4, c) + sub);
-    const bf16x8 bw = cat(lo, hi);
-#pragma unroll
-    for (int rb = 0; rb < MROWS / 16; ++rb) {
-      const bf16x8 a = lds_read_b128(ob + o_off(16 * rb + (lane & 15), 4 * ks + (lane >> 4)));
-      pacc[rb] = mfma16(a, bw, pacc[rb]);
-    }
-  }
-  // register v of lane l: row 16 rb + 4(l/16) + v, column l%16
-#pragma unroll
-  for (int rb = 0; rb < MROWS / 16; ++rb)
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int r = 16 * rb + 4 * (lane >> 4) + v4;
-      if (r < ROWS && b0 + r < batch)
-        out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[rb][v4];
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -799,10 +812,10 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, const 
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
                     int heads_per_wg, int n_wg, const void* w_uv, int Dv, void* out,
                     hipStream_t st) {
-  dim3 grid(H, (batch + kCWaves - 1) / kCWaves);
-  combine_kernel<1><<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
-                                             heads_per_wg, n_wg, (const bf16*)w_uv, Dv,
-                                             (bf16*)out);
+  dim3 grid(H, (batch + kCRows - 1) / kCRows);
+  combine_kernel<<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
+                                           heads_per_wg, n_wg, (const bf16*)w_uv, Dv,
+                                           (bf16*)out);
 }
 
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,

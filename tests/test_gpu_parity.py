@@ -35,11 +35,17 @@ def sync():
 # ---------------------------------------------------------------------------
 # helpers
 # ---------------------------------------------------------------------------
-def gpu_decode(m, cfg, inp):
+def gpu_decode(m, cfg, inp, workspace=None):
+    """mla_decode through the C ABI (workspace: reuse a buffer across calls)."""
+    import torch
     mc = m.MLAConfig.from_dict(cfg)
+    B, L = len(inp.seq_lens), int(inp.seq_lens.max())
+    if workspace is None:
+        workspace = torch.zeros(m.mla_decode_workspace_size(mc, B, L), dtype=torch.uint8,
+                                device="cuda")
     out = m.mla_decode(mc, to_dev(inp.q_nope), to_dev(inp.q_rope), to_dev(inp.w_uk),
                        to_dev(inp.w_uv), to_dev(inp.pool), to_dev(inp.block_table),
-                       to_dev(inp.seq_lens), int(inp.seq_lens.max()))
+                       to_dev(inp.seq_lens), L, workspace=workspace)
     sync()
     return to_host_f64(out)
 
@@ -155,6 +161,24 @@ def test_decode_h64_b32_l4096_full(m):
     ref = oracle_decode(cfg, inp, range(cfg["batch"]))
     e = assert_bf16(got, ref, "decode_h64_b32_l4096", per_row_axis=0)
     print("decode_h64_b32_l4096", e)
+
+
+def test_decode_workspace_reused_across_calls(m):
+    """One workspace, several consecutive decode calls with different inputs:
+    each call must merge only the partials it wrote itself (with fewer tiles
+    than workgroups, some workgroups write none), so every result matches
+    the oracle although the workspace holds the previous call's values."""
+    import torch
+    cfg = bf16_decode_cfg()
+    lens = np.array([700, 64, 3000, 1, 129, 2048, 511, 900], np.int32)
+    mc = m.MLAConfig.from_dict(cfg)
+    ws = torch.zeros(m.mla_decode_workspace_size(mc, len(lens), int(lens.max())),
+                     dtype=torch.uint8, device="cuda")
+    for seed in (21, 22, 23):
+        inp = workloads.decode_inputs(cfg, seed=seed, lengths=lens)
+        got = gpu_decode(m, cfg, inp, workspace=ws)
+        ref = oracle_decode(cfg, inp, range(len(lens)))
+        assert_bf16(got, ref, f"reused workspace, seed {seed}", per_row_axis=0)
 
 
 def test_decode_edge_lengths(m):
