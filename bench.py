@@ -52,6 +52,63 @@ def algorithmic(cfg, lens):
                 step_flops=flops_attn + flops_proj, attn_flops=flops_attn)
 
 
+def prefill_algorithmic(cfg):
+    """FLOPs and bytes of one prefill call (T new tokens per sequence, causal,
+    absorbed path): projections, cache append, attention on the latent rows,
+    W_UV."""
+    B, T, M, H = cfg["batch"], cfg["q_len"], cfg["d_model"], cfg["num_heads"]
+    R, Dr, Dn, Dv = (cfg[k] for k in ("kv_lora_rank", "rope_dim", "qk_nope_dim", "v_dim"))
+    Rq = cfg.get("q_lora_rank", 0)
+    n = B * T
+    qw = H * (Dn + Dr)
+    proj = 2 * n * M * (R + Dr) + (2 * n * M * Rq + 2 * n * Rq * qw if Rq else 2 * n * M * qw)
+    absorb = 2 * n * H * Dn * R
+    pairs = B * T * (T + 1) // 2                        # causal (query, key) pairs
+    attn = 2 * H * (R + Dr + R) * pairs
+    out = 2 * n * H * R * Dv
+    weights = 2 * (M * (R + Dr) + (M * Rq + Rq * qw if Rq else M * qw) + H * R * (Dn + Dv))
+    bytes_ = 2 * n * M + weights + 2 * n * (R + Dr) + 2 * n * H * Dv
+    return dict(flops=proj + absorb + attn + out, attn_flops=attn, bytes=bytes_)
+
+
+def prefill_main(args, torch, m):
+    """Time mla_prefill on the prefill workload (MFMA-bound)."""
+    dev = torch.device("cuda", 0)
+    cfg = workloads.WORKLOADS[args.workload]
+    mc = m.MLAConfig.from_dict(cfg)
+    inp = workloads.prefill_inputs_torch(cfg, cfg["seed"], dev)
+    B, T = cfg["batch"], cfg["q_len"]
+    rope = m.mla_rope_table(mc, T).to(dev)
+    ws = torch.zeros(m.mla_prefill_workspace_size(mc, B, T), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, cfg["num_heads"], cfg["v_dim"]), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        m.mla_prefill(mc, inp["x"], inp["weights"], inp["pool"], inp["block_table"],
+                      inp["start_pos"], 0, rope_table=rope, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    ms = graph_time(torch, call, args.steps, side)
+    alg = prefill_algorithmic(cfg)
+    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "MLA prefill with cache append: ms per call, bf16 MFMA TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "q_len": T, "d_model": cfg["d_model"],
+                   "q_lora_rank": cfg.get("q_lora_rank", 0), "heads": cfg["num_heads"],
+                   "algorithmic_flops": alg["flops"], "attention_flops": alg["attn_flops"],
+                   "timing": "hip graph replay, events on the launching stream"},
+        "roofline": {"kernel": "mla_prefill (whole call)", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(cfg, seconds):
     """Time the oracle's decode (float64 numpy, as it stands) on whole steps of
     the same workload until about `seconds` of work; report TB/s of
@@ -129,8 +186,7 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=workloads.HEADLINE,
-                    choices=[k for k, v in workloads.WORKLOADS.items() if "q_len" not in v
-                             and v["dtype"] == "bf16"])
+                    choices=[k for k, v in workloads.WORKLOADS.items() if v["dtype"] == "bf16"])
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,6 +212,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 10}))
         return
     import mla_latent_kv_26_amd as m
+    if "q_len" in workloads.WORKLOADS[args.workload]:
+        return prefill_main(args, torch, m)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

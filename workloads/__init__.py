@@ -275,3 +275,40 @@ def decode_inputs_torch(cfg: dict, seed: int, device, lengths=None):
         q_nope=n((B, H, Dn)), q_rope=n((B, H, Dr)),
         w_uk=n((H, Dn, R), 1.0 / math.sqrt(R)), w_uv=n((H, R, Dv), 1.0 / math.sqrt(R)),
     )
+
+
+def prefill_inputs_torch(cfg: dict, seed: int, device):
+    """Same shapes and distributions as ``prefill_inputs`` (fresh tokens at
+    positions 0..T-1, gains 1, block-64 pool with permuted pages), drawn on
+    the device for the benchmark.  Returns a dict of torch tensors."""
+    import torch
+    rng = _rng(seed)
+    B, T = cfg["batch"], cfg["q_len"]
+    M, H = cfg["d_model"], cfg["num_heads"]
+    R, Dr, Dn, Dv = cfg["kv_lora_rank"], cfg["rope_dim"], cfg["qk_nope_dim"], cfg["v_dim"]
+    Rq, bs = cfg.get("q_lora_rank", 0), cfg["block_size"]
+    table, nblocks = page_table(rng, np.full(B, T), bs, True)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+
+    def n(shape, std=1.0):
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return t.to(dt)
+
+    qw = H * (Dn + Dr)
+    w = dict(w_dkv=n((M, R + Dr), 1.0 / math.sqrt(M)),
+             kv_norm_w=torch.ones(R, dtype=torch.float32, device=device),
+             w_uk=n((H, Dn, R), 1.0 / math.sqrt(R)), w_uv=n((H, R, Dv), 1.0 / math.sqrt(R)))
+    if Rq:
+        w.update(w_dq=n((M, Rq), 1.0 / math.sqrt(M)),
+                 q_norm_w=torch.ones(Rq, dtype=torch.float32, device=device),
+                 w_uq=n((Rq, qw), 1.0 / math.sqrt(Rq)))
+    else:
+        w.update(w_q=n((M, qw), 1.0 / math.sqrt(M)))
+    return dict(x=n((B, T, M)), weights=w,
+                pool=torch.zeros((nblocks, bs, R + Dr), dtype=dt, device=device),
+                block_table=torch.from_numpy(table).to(device),
+                start_pos=torch.zeros(B, dtype=torch.int32, device=device))
