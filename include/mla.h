@@ -207,6 +207,9 @@ mla_status mla_cache_append(const mla_config* cfg, const void* x, const void* w_
 
 /* ---- prefill (T new tokens per sequence, causal) ------------------------- */
 
+/* Workspace bytes for mla_prefill with this batch and q_len; max_context is
+ * the largest start_pos + q_len the call will see (values below q_len count
+ * as q_len).  Scratch only: no initial contents required. */
 mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int32_t q_len,
                                       int32_t max_context, size_t* bytes /* host out */);
 
@@ -227,9 +230,16 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int3
  *     positions 0 .. start_pos[b] + q_len - 1 of each sequence;
  *   start_pos int32 [batch] (device, trusted, each <= max_start_pos);
  *   max_start_pos (host); (max_start_pos + q_len) <= max_blocks_per_seq * block_size;
- *   out [batch, q_len, H, Dv] (written).
- * Every q_len (1 included) runs the same causal attention kernel: one
- * workgroup per (query row, head group) over all of that row's keys. */
+ *   out [batch, q_len, H, Dv] (written); workspace as sized by
+ *   mla_prefill_workspace_size with max_context = max_start_pos + q_len.
+ * Attention takes one of two equivalent forms (same result up to rounding):
+ * on the latent rows (q_full = [q_nope W_UK | q_rope], P V on c, then W_UV),
+ * or through per-head keys and values rebuilt for the context (K_h =
+ * [c W_UK[h]^T | k_rope], V_h = c W_UV[h], "GatedMLA" docs, "Build per-head
+ * Q, K and V").  bf16 with R = 512, Dr = 64, Dn = Dv = 128 takes the second
+ * when it needs fewer FLOPs: 2H(Dn + Dr + Dv) per (query, key) pair plus
+ * 2H R (Dn + Dv) per context token, against 2H(2R + Dr) per pair (long new
+ * spans; continuations of a few tokens stay on the latent rows). */
 mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, const void* w_dq,
                        const float* q_norm_w, const void* w_uq, const void* w_dkv,
                        const float* kv_norm_w, const void* w_uk, const void* w_uv,

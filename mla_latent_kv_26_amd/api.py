@@ -334,7 +334,8 @@ def mla_prefill(cfg: MLAConfig, x, weights: dict, kv_pool, block_table, start_po
     if out is None:
         out = torch.empty((B, T, H, cfg.v_dim), dtype=dt, device=x.device)
     _dev(out, "out", dt, (B, T, H, cfg.v_dim))
-    ws = _workspace(workspace, mla_prefill_workspace_size(cfg, B, T), x.device)
+    ws = _workspace(workspace, mla_prefill_workspace_size(cfg, B, T, int(max_start_pos) + T),
+                    x.device)
     check(lib.mla_prefill(_ref(cfg), x.data_ptr(), p_wq, p_wdq, p_qn, p_wuq, p_wdkv, p_kvn, p_wuk,
                           p_wuv, rope_table.data_ptr(), rope_table.shape[0], kv_pool.data_ptr(),
                           nb, block_table.data_ptr(), mb, start_pos.data_ptr(),

@@ -7,6 +7,7 @@
 // transposing LDS load, which hands each lane one column of a 4 x 16 block.
 //
 // Tile: BM x 128 x BK per 256-thread workgroup, 4 waves, 32x32x16 MFMAs.
+// launch_gemm_bf16_bt takes B transposed ([N, K], K contiguous).
 // Global loads for the next K-tile are in flight (in registers) while the
 // current one is multiplied; BK = 128 covers short contractions in one pass.
 //
@@ -44,7 +45,10 @@ struct Cfg {
   static constexpr int B_PER_T = B_CHUNKS / 256;
 };
 
-template <int BM, int kBK, bool kOutF32>
+// kBT: B is given transposed, [N, K] row-major (K contiguous, row stride
+// ldb); its tile is then kept as [n][k] in LDS like A's and read with plain
+// 16-byte reads.
+template <int BM, int kBK, bool kOutF32, bool kBT>
 __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__ A,
                                                         const bf16* __restrict__ B,
                                                         void* __restrict__ Cv, int M, int N, int K,
@@ -52,8 +56,10 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
                                                         long sB, long sC, float alpha, Side side) {
   using C_ = Cfg<BM, kBK>;
   constexpr int kAStride = C_::A_STRIDE;
+  constexpr int kBRows = kBT ? kBN : kBK;
+  constexpr int kBCols = kBT ? kBK + 8 : kBStride;
   __shared__ __attribute__((aligned(16))) bf16 As[BM * kAStride];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[kBK * kBStride];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[kBRows * kBCols];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C_::WAVES_N, wn = wave % C_::WAVES_N;
@@ -76,9 +82,15 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
 #pragma unroll
     for (int i = 0; i < C_::B_PER_T; ++i) {
       const int c = tid + 256 * i;
-      const int r = c / (kBN / 8), nc = (c % (kBN / 8)) * 8;
-      const int gk = k0 + r, gn = n0 + nc;
-      rb[i] = (gk < K && gn < N) ? *(const bf16x8*)(B + (long)gk * ldb + gn) : zero8;
+      if constexpr (kBT) {
+        const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+        const int gn = n0 + r, gk = k0 + kc;
+        rb[i] = (gn < N && gk < K) ? *(const bf16x8*)(B + (long)gn * ldb + gk) : zero8;
+      } else {
+        const int r = c / (kBN / 8), nc = (c % (kBN / 8)) * 8;
+        const int gk = k0 + r, gn = n0 + nc;
+        rb[i] = (gk < K && gn < N) ? *(const bf16x8*)(B + (long)gk * ldb + gn) : zero8;
+      }
     }
   };
   auto store_tiles = [&]() {
@@ -93,8 +105,13 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
 #pragma unroll
     for (int i = 0; i < C_::B_PER_T; ++i) {
       const int c = tid + 256 * i;
-      const int r = c / (kBN / 8), nc = (c % (kBN / 8)) * 8;
-      *(bf16x8*)(Bs + r * kBStride + nc) = rb[i];
+      if constexpr (kBT) {
+        const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+        *(bf16x8*)(Bs + r * kBCols + kc) = rb[i];
+      } else {
+        const int r = c / (kBN / 8), nc = (c % (kBN / 8)) * 8;
+        *(bf16x8*)(Bs + r * kBStride + nc) = rb[i];
+      }
     }
   };
 
@@ -140,11 +157,17 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
       }
 #pragma unroll
       for (int j = 0; j < C_::FN; ++j) {
-        const int col = (wn * C_::FN + j) * 32 + tr_col;
-        const int row = 16 * ks + tr_row;
-        const bf16x4 lo = lds_read_tr(bs_base + (row * kBStride + col) * 2);
-        const bf16x4 hi = lds_read_tr(bs_base + ((row + 4) * kBStride + col) * 2);
-        bfr[j] = cat(lo, hi);
+        if constexpr (kBT) {
+          // lane l: column n = l%32 of the fragment, k = 16 ks + 8 (l/32) .. + 7
+          const int n = (wn * C_::FN + j) * 32 + (lane & 31);
+          bfr[j] = lds_read_b128(bs_base + (n * kBCols + 16 * ks + 8 * (lane >> 5)) * 2);
+        } else {
+          const int col = (wn * C_::FN + j) * 32 + tr_col;
+          const int row = 16 * ks + tr_row;
+          const bf16x4 lo = lds_read_tr(bs_base + (row * kBStride + col) * 2);
+          const bf16x4 hi = lds_read_tr(bs_base + ((row + 4) * kBStride + col) * 2);
+          bfr[j] = cat(lo, hi);
+        }
       }
 #pragma unroll
       for (int i = 0; i < C_::FM; ++i)
@@ -175,30 +198,34 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
     }
 }
 
-template <int BM, int BK>
+template <int BM, int BK, bool BT>
 void launch_bm(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
                long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, Side side,
                hipStream_t st) {
   dim3 grid((N + kBN - 1) / kBN, (M + BM - 1) / BM, batch);
   if (c_f32)
-    gemm_bf16_kernel<BM, BK, true><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M, N,
-                                                         K, lda, ldb, ldc, sA, sB, sC, alpha, side);
+    gemm_bf16_kernel<BM, BK, true, BT><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M,
+                                                             N, K, lda, ldb, ldc, sA, sB, sC, alpha,
+                                                             side);
   else
-    gemm_bf16_kernel<BM, BK, false><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C, M,
-                                                          N, K, lda, ldb, ldc, sA, sB, sC, alpha,
-                                                          side);
+    gemm_bf16_kernel<BM, BK, false, BT><<<grid, 256, 0, st>>>((const bf16*)A, (const bf16*)B, C,
+                                                              M, N, K, lda, ldb, ldc, sA, sB, sC,
+                                                              alpha, side);
 }
 
-template <int BK>
+template <int BK, bool BT>
 void launch_bk(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
                long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, Side side,
                hipStream_t st) {
   if (M <= 32)
-    launch_bm<32, BK>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+    launch_bm<32, BK, BT>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                          st);
   else if (M <= 64)
-    launch_bm<64, BK>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+    launch_bm<64, BK, BT>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                          st);
   else
-    launch_bm<128, BK>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+    launch_bm<128, BK, BT>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                           st);
 }
 
 }  // namespace
@@ -210,9 +237,24 @@ void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K
   if (M <= 0 || N <= 0 || batch <= 0) return;
   const Side side{(const bf16*)side_src, side_ld, side_sb, (bf16*)side_dst, side_cols};
   if (K <= 128)
-    launch_bk<128>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+    launch_bk<128, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                          st);
   else
-    launch_bk<32>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side, st);
+    launch_bk<32, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                         st);
+}
+
+void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, int K, long lda,
+                         long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                         int c_f32, hipStream_t st) {
+  if (M <= 0 || N <= 0 || batch <= 0) return;
+  const Side side{nullptr, 0, 0, nullptr, 0};
+  if (K <= 128)
+    launch_bk<128, true>(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                         st);
+  else
+    launch_bk<32, true>(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
+                        st);
 }
 
 }  // namespace mla

@@ -59,6 +59,11 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 // bases and batch strides.  When side_src is set (bf16 C only), also
 // C_b[r, c] = alpha * side_src[b * side_sb + r * side_ld + c] into
 // side_dst (same ldc / sC as C) for c < side_cols.
+// As launch_gemm_bf16 with B given transposed: Bt[b] is [N, K] row-major
+// (row stride ldb), C[b] = alpha * A[b] * Bt[b]^T.
+void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, int K, long lda,
+                         long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                         int c_f32, hipStream_t st);
 void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda,
                       long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
                       int c_f32, hipStream_t st, const void* side_src = nullptr,
@@ -86,6 +91,21 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
 
 // Prefill attention: query row n = b * T + t at position start_pos[b] + t
 // attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].
+// Prefill through per-head keys and values (bf16, R = 512, Dn = Dv = 128,
+// Dr = 64).  gather: dst [batch, ctx_pad, R + Dr] = each sequence's cache
+// rows 0 .. start_pos[b] + T - 1, zero after.  naive_q: qn [n, H, Dn + Dr] =
+// alpha * [q_nope | RoPE(q_pe)] from q [n, H (Dn + Dr)].  flash: out [batch,
+// T, H, Dv] = causal softmax(qn K^T) V with K = [kn | rope part of cg]
+// (kn, v: [batch, ctx_pad, H, 128]).
+void launch_gather_rows(const void* pool, const int* block_table, int max_blocks, int shift,
+                        const int* start_pos, int batch, int T, int ctx_pad, void* dst,
+                        hipStream_t st);
+void launch_naive_q(const void* q, long ld_q, const float* rope, const int* start_pos, int T,
+                    int n, int H, float alpha, void* qn, hipStream_t st);
+void launch_flash_prefill(const void* qn, const void* kn, const void* cg, const void* v,
+                          const int* start_pos, int batch, int T, int H, int ctx_pad, void* out,
+                          hipStream_t st);
+
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
                                    int max_blocks, int block_shift, const int* start_pos, int T,
                                    int batch, int H, void* o_lat, hipStream_t st);

@@ -163,12 +163,31 @@ DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
   return w;
 }
 
-// ---- prefill workspace layout ----
+// ---- prefill path choice and workspace layout ----
+// Per-head keys and values (the naive path) when they cost fewer FLOPs than
+// attending on the latent rows: per (query, key) pair 2H(Dn + Dr + Dv)
+// against 2H(2R + Dr), plus 2H R (Dn + Dv) per context token to build K and V
+// (context = max_start_pos + q_len).  bf16 with the shapes of its kernels.
+bool prefill_naive(const Dims& d, int q_len, int max_start_pos) {
+  if (d.dt != MLA_DTYPE_BF16 || d.R != 512 || d.Dr != 64 || d.Dn != 128 || d.Dv != 128)
+    return false;
+  const double T = q_len, S = max_start_pos;
+  const double pairs = T * (S + (T + 1) / 2);
+  const double latent = (2.0 * d.R + d.Dr) * pairs;
+  const double naive = (double)(d.Dn + d.Dr + d.Dv) * pairs + (double)d.R * (d.Dn + d.Dv) * (S + T);
+  return naive < latent;
+}
+
 struct PrefillWs {
-  size_t z, cq32, cq, q, q_full, o_lat, total;
+  size_t z, cq32, cq, q, q_full, o_lat, cg, kn, vv, total;
+  int ctx_pad;
+  bool naive;
 };
-PrefillWs prefill_ws(const Dims& d, long n) {
+PrefillWs prefill_ws(const Dims& d, int batch, int q_len, int max_start_pos) {
+  const long n = (long)batch * q_len;
   PrefillWs w{};
+  w.naive = prefill_naive(d, q_len, max_start_pos);
+  w.ctx_pad = (int)(((long)max_start_pos + q_len + 63) / 64 * 64);
   size_t off = 256;
   w.z = off;
   off = up256(off + (size_t)n * d.W * 4);
@@ -182,8 +201,18 @@ PrefillWs prefill_ws(const Dims& d, long n) {
   off = up256(off + (size_t)n * d.H * (d.Dn + d.Dr) * d.esz);
   w.q_full = off;
   off = up256(off + (size_t)n * d.H * d.W * d.esz);
-  w.o_lat = off;
-  off = up256(off + (size_t)n * d.H * d.R * (d.dt == MLA_DTYPE_BF16 ? 2 : 4));
+  if (w.naive) {
+    const size_t rows = (size_t)batch * w.ctx_pad;
+    w.cg = off;
+    off = up256(off + rows * d.W * 2);
+    w.kn = off;
+    off = up256(off + rows * d.H * d.Dn * 2);
+    w.vv = off;
+    off = up256(off + rows * d.H * d.Dv * 2);
+  } else {
+    w.o_lat = off;
+    off = up256(off + (size_t)n * d.H * d.R * (d.dt == MLA_DTYPE_BF16 ? 2 : 4));
+  }
   w.total = off;
   return w;
 }
@@ -540,10 +569,11 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int3
   g_err.clear();
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
-  (void)max_context;
   if (batch <= 0 || q_len <= 0) return fail(MLA_ERR_INVALID_ARG, "batch and q_len must be positive");
+  if (max_context < 0) return fail(MLA_ERR_INVALID_ARG, "max_context must be >= 0");
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = prefill_ws(d, (long)batch * q_len).total;
+  const int max_start = max_context > q_len ? max_context - q_len : 0;
+  *bytes = prefill_ws(d, batch, q_len, max_start).total;
   return MLA_OK;
 }
 
@@ -592,7 +622,7 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   }
   const long n = (long)batch * q_len;
   if (n > (1L << 30)) return fail(MLA_ERR_INVALID_ARG, "batch * q_len too large");
-  const PrefillWs w = prefill_ws(d, n);
+  const PrefillWs w = prefill_ws(d, batch, q_len, max_start_pos);
   if (!workspace || workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
                 workspace ? "" : ", NULL");
@@ -617,6 +647,28 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
     gemm(d, cq, w_uq, q, (int)n, QW, d.Rq, d.Rq, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
   } else {
     gemm(d, x, w_q, q, (int)n, QW, d.M, d.M, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
+  }
+  if (w.naive) {
+    // 3'. per-head keys and values over each sequence's context, then causal
+    //     attention straight to the output
+    void* qn = at(workspace, w.q_full);
+    mla::launch_naive_q(q, QW, rope_table, start_pos, q_len, (int)n, d.H, alpha, qn, st);
+    void* cg = at(workspace, w.cg);
+    mla::launch_gather_rows(kv_pool, block_table, max_blocks_per_seq, d.shift, start_pos, batch,
+                            q_len, w.ctx_pad, cg, st);
+    for (int b = 0; b < batch; ++b) {
+      const long r0 = (long)b * w.ctx_pad;
+      const uint16_t* a = (const uint16_t*)cg + r0 * d.W;
+      mla::launch_gemm_bf16_bt(a, w_uk, (uint16_t*)at(workspace, w.kn) + r0 * d.H * d.Dn, w.ctx_pad,
+                               d.Dn, d.R, d.W, d.R, (long)d.H * d.Dn, 0, (long)d.Dn * d.R, d.Dn,
+                               d.H, 1.0f, 0, st);
+      mla::launch_gemm_bf16(a, w_uv, (uint16_t*)at(workspace, w.vv) + r0 * d.H * d.Dv, w.ctx_pad,
+                            d.Dv, d.R, d.W, d.Dv, (long)d.H * d.Dv, 0, (long)d.R * d.Dv, d.Dv,
+                            d.H, 1.0f, 0, st);
+    }
+    mla::launch_flash_prefill(qn, at(workspace, w.kn), cg, at(workspace, w.vv), start_pos, batch,
+                              q_len, d.H, w.ctx_pad, out, st);
+    return launched("mla_prefill");
   }
   // 3. absorbed query: q_full = alpha * [q_nope W_UK | RoPE(q_pe)]
   void* q_full = at(workspace, w.q_full);

@@ -1,0 +1,348 @@
+// Prefill through per-head keys and values ("GatedMLA" docs, "Build per-head
+// Q, K and V": K_h = [c W_UK[h]^T | k_rope], the rope key shared by every
+// head, V_h = c W_UV[h]; "Observe logits, then compute causal attention").
+// For long new-token spans this costs far fewer FLOPs than attending on the
+// latent rows (scores over 192 instead of 576 values, P V over 128 instead
+// of 512), at the price of materialising K and V once per call (the
+// memory-for-compute trade named in the modeldna "MLA" module).
+//
+// Pieces: gather the cache rows of each sequence into a dense buffer (zero
+// past its length), two batched GEMMs for K_nope and V (in the GEMM file),
+// the scaled / rotated per-head queries, and a causal flash-attention
+// kernel whose output is the layer's per-head output directly.
+//
+// Attention kernel: workgroup = (sequence, head, 256 query rows), 8 waves of
+// 32 queries.  Per 64-key tile in LDS (K 64 x 192, V 64 x 128; three
+// buffers, two tiles in flight):
+//   S^T [64 keys x 32 q] = K_tile [64 x 192] Q^T          (32x32x16 MFMAs)
+//   O^T [128 x 32 q]    += V_tile^T [128 x 64] P^T [64 x 32 q]
+// Computing the transposes puts one query in each lane, so row maxima,
+// sums and rescales are per-lane values.  P goes through a per-wave LDS
+// buffer to change its layout for the second product.  Scores are in base 2
+// (the queries carry scale * log2 e).
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int kFW = 8;                        // waves per workgroup
+constexpr int kFThreads = 64 * kFW;
+constexpr int kFQ = 32 * kFW;                 // queries per workgroup
+constexpr int kFK = 64;                       // keys per tile
+constexpr int kNDn = 128, kNDr = 64, kNDk = kNDn + kNDr, kNDv = 128;
+constexpr int kKCh = kNDk * 2 / 16;           // 24 chunks per K row (384 B)
+constexpr int kVCh = kNDv * 2 / 16;           // 16 chunks per V row (256 B)
+constexpr int kKBytes = kFK * kNDk * 2;       // 24576
+constexpr int kVBytes = kFK * kNDv * 2;       // 16384
+constexpr int kTBytes = kKBytes + kVBytes;    // 40960
+constexpr int kFBuf = 3;
+constexpr int kTLoads = kTBytes / 1024;       // 40 one-KB load instructions per tile
+constexpr int kWLoads = kTLoads / kFW;        // 5 per wave
+static_assert(kWLoads * kFW == kTLoads, "tile loads split evenly");
+constexpr int kFPStride = kFK + 8;            // bf16 per P row
+constexpr int kFPWave = 32 * kFPStride * 2;   // 4608 B of P per wave
+constexpr int kFOffP = kFBuf * kTBytes;
+constexpr int kFLds = kFOffP + kFW * kFPWave;
+static_assert(kFLds <= 163840, "LDS budget");
+constexpr int kFSStride = kNDv + 8;           // bf16 per staged output row
+static_assert(kFW * 32 * kFSStride * 2 <= kFBuf * kTBytes, "output staging fits the tile buffers");
+constexpr float kFSlack = 8.0f;               // lazy rescale threshold (log2 units)
+
+// K row t: chunk k (24 per row) at position k ^ (t % 8) within its group of
+// 8; V row t: chunk k (16 per row) at position k ^ 4 (t % 4).
+__device__ __forceinline__ uint32_t k_pos(uint32_t t, uint32_t k) { return k ^ (t & 7u); }
+__device__ __forceinline__ uint32_t v_pos(uint32_t t, uint32_t k) { return k ^ ((t & 3u) << 2); }
+
+// This wave's share of one tile's loads: instruction j fills slots
+// [64 j, 64 j + 64); slots [0, 1536) are K (row t = s / 24), the rest V.
+// Each lane's source pointer for the first tile and its row stride are set
+// up once; issuing a tile advances them by 64 rows.  Keys past a sequence's
+// length are zero rows of the buffers, so every address is in bounds.
+struct KvSource {
+  const bf16* p[kWLoads];
+  uint32_t stride[kWLoads];  // elements per key row
+
+  __device__ __forceinline__ void setup(const bf16* kn, const bf16* cg, const bf16* vv, long row0,
+                                        int H, int h, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) {
+      const uint32_t j = (uint32_t)(wave * kWLoads + i);
+      const uint32_t s = 64u * j + (uint32_t)lane;
+      if (s < (uint32_t)(kFK * kKCh)) {
+        const uint32_t t = s / kKCh, k = k_pos(t, s % kKCh);
+        const long r = row0 + t;
+        if (k < 16) {
+          p[i] = kn + (r * H + h) * kNDn + k * 8;
+          stride[i] = (uint32_t)H * kNDn;
+        } else {
+          p[i] = cg + r * 576 + 512 + (k - 16) * 8;
+          stride[i] = 576;
+        }
+      } else {
+        const uint32_t sv = s - kFK * kKCh;
+        const uint32_t t = sv / kVCh, k = v_pos(t, sv % kVCh);
+        p[i] = vv + ((row0 + t) * H + h) * kNDv + k * 8;
+        stride[i] = (uint32_t)H * kNDv;
+      }
+    }
+  }
+  // issue the next tile into `buf`
+  __device__ __forceinline__ void issue(uint32_t buf, int wave) {
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) {
+      g2lds16(p[i], buf + (uint32_t)(wave * kWLoads + i) * 1024u);
+      p[i] += (size_t)kFK * stride[i];
+    }
+  }
+};
+
+__global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
+    const bf16* __restrict__ qn, const bf16* __restrict__ kn, const bf16* __restrict__ cg,
+    const bf16* __restrict__ vv, const int* __restrict__ start_pos, int B, int T, int H,
+    int ctx_pad, bf16* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char smem[kFLds];
+  const uint32_t lds = lds_addr(smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // longest query blocks first; a (sequence, head) stays on one XCD
+  const int nqb = (T + kFQ - 1) / kFQ;
+  const int bh = blockIdx.x % (B * H);
+  const int qb = nqb - 1 - blockIdx.x / (B * H);
+  const int b = bh / H, h = bh % H;
+  const int sp = start_pos[b];
+  const int q0 = qb * kFQ;
+  const int last = min(q0 + kFQ, T) - 1;                 // last query row of the block
+  const int n = (sp + last) / kFK + 1;                  // key tiles the block needs
+  const long row0 = (long)b * ctx_pad;
+
+  // this lane's query row (rows past T repeat the last one; not stored)
+  const int qw0 = q0 + 32 * wave;
+  const int tq = min(qw0 + (lane & 31), T - 1);
+  const int pos = sp + tq;                              // its absolute position
+  const int wave_last = sp + min(qw0 + 31, T - 1);      // largest position in the wave
+  const bool wave_live = qw0 < T;
+
+  KvSource src;
+  src.setup(kn, cg, vv, row0, H, h, wave, lane);
+  src.issue(lds, wave);
+  bf16x8 qf[kNDk / 16];
+  {
+    const bf16* q = qn + (((long)b * T + tq) * H + h) * kNDk + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kNDk / 16; ++ks) qf[ks] = *(const bf16x8*)(q + 16 * ks);
+  }
+  if (n > 1) src.issue(lds + kTBytes, wave);
+  if (n > 1)
+    wait_vmcnt<kWLoads>();
+  else
+    wait_vmcnt<0>();
+  // the queries have landed: plain register values from here on
+#pragma unroll
+  for (int ks = 0; ks < kNDk / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
+
+  // per-lane LDS offsets.  K fragment (S^T A operand): row 32 kb + lane%32,
+  // chunk 2 ks + lane/32 -> position 8 (ks/4) + ((2 (ks%4) + lane/32) ^ (lane%8)).
+  const uint32_t hi = lane >> 5, x7 = lane & 7;
+  uint32_t k_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) k_off[q] = ((lane & 31) * kKCh + ((2u * q + hi) ^ x7)) * 16u;
+  // V^T fragment (transposing reads): group g, lane li = 4a + bb reads key
+  // row 8 (g/2) + 4 hi + a (+ 16 ks), dv chunk 4 db + 2 (g%2) + bb/2 at
+  // position chunk ^ 4a, plus 8 bytes for odd bb.
+  const uint32_t g = lane >> 4, li = lane & 15, a4 = li >> 2, bb = li & 3;
+  uint32_t v_off[8];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t row = 8u * (g >> 1) + 4u * hh + a4;
+      const uint32_t ch = 4u * db + 2u * (g & 1) + (bb >> 1);
+      v_off[2 * db + hh] = kKBytes + (row * kVCh + (ch ^ (a4 << 2))) * 16u + 8u * (bb & 1);
+    }
+  const uint32_t pw = lds + kFOffP + wave * kFPWave;
+  const uint32_t p_wr = pw + ((lane & 31) * kFPStride + 4 * hi) * 2;
+  const uint32_t p_rd = pw + ((lane & 31) * kFPStride + 8 * hi) * 2;
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  for (int k = 0; k < n; ++k) {
+    if (k + 1 < n)
+      wait_vmcnt<kWLoads>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();  // tile k visible; tile k-1 fully consumed
+    if (k + 2 < n) src.issue(lds + (uint32_t)((k + 2) % kFBuf) * kTBytes, wave);
+    const int key0 = k * kFK;
+    if (!wave_live || key0 > wave_last) continue;  // every key of the tile is masked for the wave
+    const uint32_t buf = lds + (uint32_t)(k % kFBuf) * kTBytes;
+
+    // ---- S^T = K Q^T: two 32-key blocks, K = 192 (12 steps of 16)
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < kNDk / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = lds_read_b128(buf + k_off[ks & 3] + (uint32_t)((ks >> 2) * 128) +
+                                        (uint32_t)(kb * 32 * kKCh * 16));
+        s[kb] = mfma32(kf, qf[ks], s[kb]);
+      }
+    }
+    // register v of block kb <-> key key0 + 32 kb + 8 (v/4) + 4 hi + v%4, query lane%32
+    float hmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * (int)hi + (v & 3);
+        if (key > pos) s[kb][v] = -INFINITY;
+        hmax = fmaxf(hmax, s[kb][v]);
+      }
+    hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+    const bool grow = hmax > m + kFSlack;
+    const float m_new = grow ? hmax : m;
+    const float alpha = grow ? exp2f(m - m_new) : 1.0f;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 pk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bf16 p = (bf16)exp2f(s[kb][4 * q4 + r] - m_new);
+          pk[r] = p;
+          psum += (float)p;
+        }
+        lds_st(p_wr + (uint32_t)((32 * kb + 8 * q4) * 2), pk);
+      }
+    l = l * alpha + psum;
+    m = m_new;
+    if (__ballot(grow) != 0ull) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T: 4 steps of 16 keys
+    uint32_t ta[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ta[i] = buf + v_off[i];
+#pragma unroll
+    for (int ks = 0; ks < kFK / 16; ++ks) {
+      const bf16x8 pf = lds_read_b128(p_rd + ks * 32);
+      bf16x4 t[8];
+      if (ks == 0) lds_read_tr_x8<0>(ta, t);
+      else if (ks == 1) lds_read_tr_x8<16 * kVCh * 16>(ta, t);
+      else if (ks == 2) lds_read_tr_x8<32 * kVCh * 16>(ta, t);
+      else lds_read_tr_x8<48 * kVCh * 16>(ta, t);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma32(cat(t[2 * db], t[2 * db + 1]), pf, o[db]);
+    }
+  }
+
+  // ---- out[b, t, h, :] = O / l, staged per wave in the (idle) tile buffers
+  l += __shfl_xor(l, 32, 64);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  lds_barrier();  // every wave is done with the tile buffers
+  typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+  const uint32_t st = lds + wave * 32 * kFSStride * 2;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w4[r] = (bf16)(o[db][4 * q4 + r] * inv);
+      *(lds_b4*)(uintptr_t)(st + ((lane & 31) * kFSStride + 32 * db + 8 * q4 + 4 * hi) * 2) = w4;
+    }
+  // each wave writes its 32 rows (256 B each) with 16-byte stores
+#pragma unroll
+  for (int i = 0; i < 32 * kVCh / 64; ++i) {
+    const int c = i * 64 + lane;
+    const int r = c / kVCh, ch = c % kVCh;
+    const int t = qw0 + r;
+    const bf16x8 v8 = lds_read_b128(st + (r * kFSStride + 8 * ch) * 2);
+    if (t < T) *(bf16x8*)(out + (((long)b * T + t) * H + h) * kNDv + 8 * ch) = v8;
+  }
+}
+
+// Dense copy of each sequence's cache rows 0 .. start_pos + T - 1 (zero past
+// that, up to ctx_pad): one thread per 16-byte chunk.
+__global__ void __launch_bounds__(256) gather_rows_kernel(
+    const bf16* __restrict__ pool, const int* __restrict__ block_table, int max_blocks, int shift,
+    const int* __restrict__ start_pos, int T, int ctx_pad, long total, bf16* __restrict__ dst) {
+  constexpr int kChunks = 576 / 8;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long row = i / kChunks;
+  const int c = (int)(i - row * kChunks);
+  const int b = (int)(row / ctx_pad), j = (int)(row - (long)b * ctx_pad);
+  bf16x8 v = {};
+  if (j < start_pos[b] + T) {
+    const int page = block_table[(long)b * max_blocks + (j >> shift)];
+    const long r = ((long)page << shift) + (j & ((1 << shift) - 1));
+    v = *(const bf16x8*)(pool + r * 576 + c * 8);
+  }
+  *(bf16x8*)(dst + row * 576 + c * 8) = v;
+}
+
+// Per-head queries for the attention kernel: qn[n, h] = scale * log2(e) *
+// [q_nope | RoPE(q_pe, position)], from q [n, H (Dn + Dr)] (row stride ld_q).
+__global__ void __launch_bounds__(256) naive_q_kernel(const bf16* __restrict__ q, long ld_q,
+                                                      const float* __restrict__ rope,
+                                                      const int* __restrict__ start_pos, int T,
+                                                      int H, float alpha, bf16* __restrict__ qn) {
+  const int n = blockIdx.x;
+  const int b = n / T;
+  const float* rr = rope + (long)(start_pos[b] + (n - b * T)) * kNDr;
+  const bf16* src = q + (long)n * ld_q;
+  bf16* dst = qn + (long)n * H * kNDk;
+  constexpr int half = kNDr / 2;
+  for (int idx = threadIdx.x; idx < H * (kNDn + half); idx += 256) {
+    const int hh = idx / (kNDn + half), i = idx % (kNDn + half);
+    const bf16* s = src + hh * kNDk;
+    bf16* d = dst + hh * kNDk;
+    if (i < kNDn) {
+      d[i] = (bf16)(alpha * (float)s[i]);
+    } else {
+      const int p = i - kNDn;
+      const float x = (float)s[kNDn + p], y = (float)s[kNDn + half + p];
+      const float c = rr[p], sn = rr[half + p];
+      d[kNDn + p] = (bf16)(alpha * (x * c - y * sn));
+      d[kNDn + half + p] = (bf16)(alpha * (y * c + x * sn));
+    }
+  }
+}
+
+}  // namespace
+
+void launch_gather_rows(const void* pool, const int* block_table, int max_blocks, int shift,
+                        const int* start_pos, int batch, int T, int ctx_pad, void* dst,
+                        hipStream_t st) {
+  const long chunks = (long)batch * ctx_pad * (576 / 8);
+  gather_rows_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(
+      (const bf16*)pool, block_table, max_blocks, shift, start_pos, T, ctx_pad, chunks,
+      (bf16*)dst);
+}
+
+void launch_naive_q(const void* q, long ld_q, const float* rope, const int* start_pos, int T,
+                    int n, int H, float alpha, void* qn, hipStream_t st) {
+  if (n <= 0) return;
+  naive_q_kernel<<<n, 256, 0, st>>>((const bf16*)q, ld_q, rope, start_pos, T, H, alpha,
+                                    (bf16*)qn);
+}
+
+void launch_flash_prefill(const void* qn, const void* kn, const void* cg, const void* v,
+                          const int* start_pos, int batch, int T, int H, int ctx_pad, void* out,
+                          hipStream_t st) {
+  const int nqb = (T + kFQ - 1) / kFQ;
+  flash_prefill_kernel<<<batch * H * nqb, kFThreads, 0, st>>>(
+      (const bf16*)qn, (const bf16*)kn, (const bf16*)cg, (const bf16*)v, start_pos, batch, T, H,
+      ctx_pad, (bf16*)out);
+}
+
+}  // namespace mla

@@ -352,6 +352,34 @@ def test_prefill_small_bf16_with_query_rank_and_continuation(m):
         assert_bf16(got[b], ref, f"small prefill b={b}", per_row_axis=0)
 
 
+def test_prefill_per_head_path_with_continuation(m):
+    """Spans long enough for the per-head key/value path (600 new tokens,
+    then 300 more at position 600): partial query blocks, keys from earlier
+    calls through permuted pages, jittered gains; outputs and cache rows
+    against the oracle."""
+    import torch
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=128,
+               seed=41)
+    mc = m.MLAConfig.from_dict(cfg)
+    inp = workloads.prefill_inputs(cfg, q_len=900, batch=2, gain_jitter=0.1)
+    w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+    w64 = {k: (None if v is None else to_f64(v)) for k, v in vars(inp.weights).items()}
+    pool = torch.zeros((inp.num_blocks, 64, mc.row), dtype=torch.bfloat16, device="cuda")
+    table = to_dev(inp.block_table)
+    x = to_dev(inp.x)
+    out1 = m.mla_prefill(mc, x[:, :600].contiguous(), w, pool, table,
+                         torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+    out2 = m.mla_prefill(mc, x[:, 600:].contiguous(), w, pool, table,
+                         torch.full((2,), 600, dtype=torch.int32, device="cuda"), 600)
+    sync()
+    got = np.concatenate([to_host_f64(out1), to_host_f64(out2)], axis=1)
+    pool_np = to_host_f64(pool)
+    for b in range(2):
+        ref, rows = oracle.layer_forward(to_f64(inp.x[b]), w64, cfg, storage="bf16")
+        check_rows(_pool_rows(pool_np, inp.block_table[b], 900), rows, f"rows b={b}")
+        assert_bf16(got[b], ref, f"per-head path b={b}", per_row_axis=0)
+
+
 def test_prefill_d7168_b2_t4096_full(m):
     """Full-size prefill: every appended cache row checked, outputs on a
     sample of query rows (first, block edges, last) of both sequences."""
