@@ -93,18 +93,16 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
 // attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].
 // Prefill through per-head keys and values (bf16, R = 512, Dn = Dv = 128,
 // Dr = 64).  gather: dst [batch, ctx_pad, R + Dr] = each sequence's cache
-// rows 0 .. start_pos[b] + T - 1, zero after.  naive_q: qn [n, H, Dn + Dr] =
-// alpha * [q_nope | RoPE(q_pe)] from q [n, H (Dn + Dr)].  flash: out [batch,
-// T, H, Dv] = causal softmax(qn K^T) V with K = [kn | rope part of cg]
-// (kn, v: [batch, ctx_pad, H, 128]).
+// rows 0 .. start_pos[b] + T - 1, zero after.  flash: out [batch, T, H, Dv] =
+// causal softmax(Q K^T) V with Q = alpha [q_nope | RoPE(q_pe, position)] from
+// q [batch * T, H (Dn + Dr)], K = [kn | rope part of cg] (kn, v: [batch,
+// ctx_pad, H, 128]).
 void launch_gather_rows(const void* pool, const int* block_table, int max_blocks, int shift,
                         const int* start_pos, int batch, int T, int ctx_pad, void* dst,
                         hipStream_t st);
-void launch_naive_q(const void* q, long ld_q, const float* rope, const int* start_pos, int T,
-                    int n, int H, float alpha, void* qn, hipStream_t st);
-void launch_flash_prefill(const void* qn, const void* kn, const void* cg, const void* v,
-                          const int* start_pos, int batch, int T, int H, int ctx_pad, void* out,
-                          hipStream_t st);
+void launch_flash_prefill(const void* q, const float* rope, float alpha, const void* kn,
+                          const void* cg, const void* v, const int* start_pos, int batch, int T,
+                          int H, int ctx_pad, void* out, hipStream_t st);
 
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
                                    int max_blocks, int block_shift, const int* start_pos, int T,

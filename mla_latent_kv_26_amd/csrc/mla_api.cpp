@@ -199,8 +199,10 @@ PrefillWs prefill_ws(const Dims& d, int batch, int q_len, int max_start_pos) {
   }
   w.q = off;
   off = up256(off + (size_t)n * d.H * (d.Dn + d.Dr) * d.esz);
-  w.q_full = off;
-  off = up256(off + (size_t)n * d.H * d.W * d.esz);
+  if (!w.naive) {
+    w.q_full = off;
+    off = up256(off + (size_t)n * d.H * d.W * d.esz);
+  }
   if (w.naive) {
     const size_t rows = (size_t)batch * w.ctx_pad;
     w.cg = off;
@@ -651,8 +653,6 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   if (w.naive) {
     // 3'. per-head keys and values over each sequence's context, then causal
     //     attention straight to the output
-    void* qn = at(workspace, w.q_full);
-    mla::launch_naive_q(q, QW, rope_table, start_pos, q_len, (int)n, d.H, alpha, qn, st);
     void* cg = at(workspace, w.cg);
     mla::launch_gather_rows(kv_pool, block_table, max_blocks_per_seq, d.shift, start_pos, batch,
                             q_len, w.ctx_pad, cg, st);
@@ -666,8 +666,8 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
                             d.Dv, d.R, d.W, d.Dv, (long)d.H * d.Dv, 0, (long)d.R * d.Dv, d.Dv,
                             d.H, 1.0f, 0, st);
     }
-    mla::launch_flash_prefill(qn, at(workspace, w.kn), cg, at(workspace, w.vv), start_pos, batch,
-                              q_len, d.H, w.ctx_pad, out, st);
+    mla::launch_flash_prefill(q, rope_table, alpha, at(workspace, w.kn), cg, at(workspace, w.vv),
+                              start_pos, batch, q_len, d.H, w.ctx_pad, out, st);
     return launched("mla_prefill");
   }
   // 3. absorbed query: q_full = alpha * [q_nope W_UK | RoPE(q_pe)]

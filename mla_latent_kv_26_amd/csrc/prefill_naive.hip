@@ -8,8 +8,8 @@
 //
 // Pieces: gather the cache rows of each sequence into a dense buffer (zero
 // past its length), two batched GEMMs for K_nope and V (in the GEMM file),
-// the scaled / rotated per-head queries, and a causal flash-attention
-// kernel whose output is the layer's per-head output directly.
+// and a causal flash-attention kernel that scales and rotates the queries
+// as it loads them and whose output is the layer's per-head output.
 //
 // Attention kernel: workgroup = (sequence, head, 256 query rows), 8 waves of
 // 32 queries.  Per 64-key tile in LDS (K 64 x 192, V 64 x 128; three
@@ -98,9 +98,10 @@ struct KvSource {
 };
 
 __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
-    const bf16* __restrict__ qn, const bf16* __restrict__ kn, const bf16* __restrict__ cg,
-    const bf16* __restrict__ vv, const int* __restrict__ start_pos, int B, int T, int H,
-    int ctx_pad, bf16* __restrict__ out) {
+    const bf16* __restrict__ q, const float* __restrict__ rope, float alpha,
+    const bf16* __restrict__ kn, const bf16* __restrict__ cg, const bf16* __restrict__ vv,
+    const int* __restrict__ start_pos, int B, int T, int H, int ctx_pad,
+    bf16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char smem[kFLds];
   const uint32_t lds = lds_addr(smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -125,18 +126,59 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
   KvSource src;
   src.setup(kn, cg, vv, row0, H, h, wave, lane);
   src.issue(lds, wave);
+  // This lane's query fragments (B operand of S^T): dims 16 ks + 8 (lane/32)
+  // .. + 7 of head h, straight from the query projection; the rope dims
+  // (ks >= 8) are rotated here (dim i of the rope part pairs with i + 32,
+  // two steps further in the same lane) and all are scaled by alpha.
   bf16x8 qf[kNDk / 16];
+  f32x4 cs[4];  // cos (ks 8, 9) and sin (ks 8, 9) of the lane's 16 rope angles, 4 at a time
   {
-    const bf16* q = qn + (((long)b * T + tq) * H + h) * kNDk + 8 * (lane >> 5);
+    const bf16* qr = q + (((long)b * T + tq) * H + h) * kNDk + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kNDk / 16; ++ks) qf[ks] = *(const bf16x8*)(q + 16 * ks);
+    for (int ks = 0; ks < kNDk / 16; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
+  }
+  {
+    const float* rr = rope + (long)pos * kNDr + 8 * (lane >> 5);
+    float* c = (float*)cs;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {  // ks = 8 + e: angles 16 e + 8 (lane/32) + j
+      *(f32x4*)(c + 8 * e) = *(const f32x4*)(rr + 16 * e);
+      *(f32x4*)(c + 8 * e + 4) = *(const f32x4*)(rr + 16 * e + 4);
+    }
+  }
+  f32x4 sn[4];
+  {
+    const float* rr = rope + (long)pos * kNDr + kNDr / 2 + 8 * (lane >> 5);
+    float* c = (float*)sn;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      *(f32x4*)(c + 8 * e) = *(const f32x4*)(rr + 16 * e);
+      *(f32x4*)(c + 8 * e + 4) = *(const f32x4*)(rr + 16 * e + 4);
+    }
   }
   if (n > 1) src.issue(lds + kTBytes, wave);
   if (n > 1)
     wait_vmcnt<kWLoads>();
   else
     wait_vmcnt<0>();
-  // the queries have landed: plain register values from here on
+  {
+    const float* c = (const float*)cs;
+    const float* sv = (const float*)sn;
+#pragma unroll
+    for (int ks = 0; ks < kNDn / 16; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[ks][j] = (bf16)(alpha * (float)qf[ks][j]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (float)qf[8 + e][j], y = (float)qf[10 + e][j];
+        const float co = c[8 * e + j], si = sv[8 * e + j];
+        qf[8 + e][j] = (bf16)(alpha * (x * co - y * si));
+        qf[10 + e][j] = (bf16)(alpha * (y * co + x * si));
+      }
+  }
+  // the queries are plain register values from here on
 #pragma unroll
   for (int ks = 0; ks < kNDk / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
 
@@ -290,34 +332,6 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(
   *(bf16x8*)(dst + row * 576 + c * 8) = v;
 }
 
-// Per-head queries for the attention kernel: qn[n, h] = scale * log2(e) *
-// [q_nope | RoPE(q_pe, position)], from q [n, H (Dn + Dr)] (row stride ld_q).
-__global__ void __launch_bounds__(256) naive_q_kernel(const bf16* __restrict__ q, long ld_q,
-                                                      const float* __restrict__ rope,
-                                                      const int* __restrict__ start_pos, int T,
-                                                      int H, float alpha, bf16* __restrict__ qn) {
-  const int n = blockIdx.x;
-  const int b = n / T;
-  const float* rr = rope + (long)(start_pos[b] + (n - b * T)) * kNDr;
-  const bf16* src = q + (long)n * ld_q;
-  bf16* dst = qn + (long)n * H * kNDk;
-  constexpr int half = kNDr / 2;
-  for (int idx = threadIdx.x; idx < H * (kNDn + half); idx += 256) {
-    const int hh = idx / (kNDn + half), i = idx % (kNDn + half);
-    const bf16* s = src + hh * kNDk;
-    bf16* d = dst + hh * kNDk;
-    if (i < kNDn) {
-      d[i] = (bf16)(alpha * (float)s[i]);
-    } else {
-      const int p = i - kNDn;
-      const float x = (float)s[kNDn + p], y = (float)s[kNDn + half + p];
-      const float c = rr[p], sn = rr[half + p];
-      d[kNDn + p] = (bf16)(alpha * (x * c - y * sn));
-      d[kNDn + half + p] = (bf16)(alpha * (y * c + x * sn));
-    }
-  }
-}
-
 }  // namespace
 
 void launch_gather_rows(const void* pool, const int* block_table, int max_blocks, int shift,
@@ -329,20 +343,13 @@ void launch_gather_rows(const void* pool, const int* block_table, int max_blocks
       (bf16*)dst);
 }
 
-void launch_naive_q(const void* q, long ld_q, const float* rope, const int* start_pos, int T,
-                    int n, int H, float alpha, void* qn, hipStream_t st) {
-  if (n <= 0) return;
-  naive_q_kernel<<<n, 256, 0, st>>>((const bf16*)q, ld_q, rope, start_pos, T, H, alpha,
-                                    (bf16*)qn);
-}
-
-void launch_flash_prefill(const void* qn, const void* kn, const void* cg, const void* v,
-                          const int* start_pos, int batch, int T, int H, int ctx_pad, void* out,
-                          hipStream_t st) {
+void launch_flash_prefill(const void* q, const float* rope, float alpha, const void* kn,
+                          const void* cg, const void* v, const int* start_pos, int batch, int T,
+                          int H, int ctx_pad, void* out, hipStream_t st) {
   const int nqb = (T + kFQ - 1) / kFQ;
   flash_prefill_kernel<<<batch * H * nqb, kFThreads, 0, st>>>(
-      (const bf16*)qn, (const bf16*)kn, (const bf16*)cg, (const bf16*)v, start_pos, batch, T, H,
-      ctx_pad, (bf16*)out);
+      (const bf16*)q, rope, alpha, (const bf16*)kn, (const bf16*)cg, (const bf16*)v, start_pos,
+      batch, T, H, ctx_pad, (bf16*)out);
 }
 
 }  // namespace mla
