@@ -26,9 +26,12 @@
 // inside each aligned group of 8 chunks).  A direct-to-LDS load instruction
 // fills 64 consecutive slots; its lanes read the matching 1 KB of global
 // memory in that permuted order, so every instruction stays fully coalesced.
-// swz(t) = 2(t%4) + (t/4)%2 puts 8 consecutive rows (row-wise fragment
-// reads) and the 4 rows x 2 neighbouring chunks of a transposing read on 8
-// distinct bank groups: neither access pattern has bank conflicts.
+// The LDS serves a 16-byte read 16 lanes (256 bytes) at a time and an
+// 8-byte read 32 lanes at a time; rows are 1152 B (128 mod 256).  swz(t) =
+// 4 ((t/2) % 2) + (t/4) % 4 gives the 16 consecutive rows of a row-wise
+// fragment read 16 distinct 16-byte bank slots, and the 4 rows x 4 chunks
+// of a transposing read (rows 4-aligned, chunks 4-aligned) 16 distinct
+// slots too: neither access pattern has bank conflicts.
 #include "device_common.h"
 #include "launch.h"
 
@@ -73,7 +76,7 @@ struct Geo {
 // (log2 units): probabilities stay below 2^8 and O is rescaled rarely.
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ uint32_t swz(uint32_t t) { return ((t & 3u) << 1) | ((t >> 2) & 1u); }
+__device__ __forceinline__ uint32_t swz(uint32_t t) { return (((t >> 1) & 1u) << 2) | ((t >> 2) & 3u); }
 
 // Page ids of one sequence, 64 at a time in a register (lane i holds the id
 // of page index base + i), the following 64 loaded ahead.  Loads are plain
@@ -306,17 +309,18 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
 
   // Transposing reads: lane (16 g + li) of the fragment for token block ks
   // and column block cb reads row 16 ks + x + 4 hi, chunk 16 pw + 4 cb +
-  // 2 (g%2) + b1, stored at 8 (2 pw + cb/2) + ((4 (cb%2) + 2 (g%2) + b1) ^ (2 a + hi)),
-  // a = li/4 (the row's swizzle), plus 8 bytes for odd li.
+  // 2 (g%2) + b1, stored at 8 (2 pw + cb/2) + ((4 (cb%2) + 2 (g%2) + b1) ^ swz(row)),
+  // plus 8 bytes for odd li (16 ks does not change swz).
   const uint32_t g = lane >> 4, li = lane & 15;
-  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u, a2 = 2u * (li >> 2);
+  const uint32_t x = 8u * (g >> 1) + (li >> 2), b1 = (li >> 1) & 1u;
   uint32_t tr_off[4][2];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
       const uint32_t cc = 4u * (cb & 1) + 2u * (g & 1) + b1;
-      tr_off[cb][hi] = ((x + 4u * hi) * kCh + 8u * (2u * pw + (cb >> 1)) + (cc ^ (a2 + hi))) * 16u +
+      const uint32_t row = x + 4u * hi;
+      tr_off[cb][hi] = (row * kCh + 8u * (2u * pw + (cb >> 1)) + (cc ^ swz(row))) * 16u +
                        8u * (li & 1);
     }
   // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
@@ -577,10 +581,11 @@ constexpr int kCOBytes = 16 * kR * 2;     // o_lat rows (16: the MFMA height; 8.
 constexpr int kCWBytes = kR * 128 * 2;    // W_UV[h] (Dv <= 128)
 
 // W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
-// position c ^ 2(r&3), so the 4 rows x 2 chunks of a transposing read fall
-// on 8 distinct bank groups.
+// position c ^ 2((r % 4) + 4 ((r / 8) % 2)), so the 8 rows (r0 .. r0+3 and
+// r0+8 .. r0+11) x 2 chunks that 32 lanes of a transposing read touch fall
+// on 16 distinct bank slots.
 __device__ __forceinline__ uint32_t w_off(uint32_t r, uint32_t c) {
-  return (r * 16u + (c ^ ((r & 3u) << 1))) * 16u;
+  return (r * 16u + (c ^ (((r & 3u) | ((r >> 1) & 4u)) << 1))) * 16u;
 }
 // o_lat rows in LDS: 1 KB each, 16-byte chunk c of row r at position
 // c ^ (r % 16), so the 16 rows of a fragment read hit distinct bank groups.
@@ -591,13 +596,13 @@ __device__ __forceinline__ uint32_t o_off(uint32_t r, uint32_t c) {
 __device__ __forceinline__ void issue_w_uv(const bf16* W, int Dv, uint32_t wb, uint32_t ob) {
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // slot s = 64 j + lane holds row s/16, chunk (s%16) ^ 2(row&3); chunks
+  // slot s = 64 j + lane holds row s/16, the chunk w_off puts at s%16; chunks
   // past Dv/8 load the row's chunk 0 (unused)
 #pragma unroll
   for (int i = 0; i < kR * 16 / 64 / kCWaves; ++i) {
     const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCWaves) + i;
     const uint32_t s = 64u * j + lane, r = s >> 4;
-    uint32_t c = (s & 15u) ^ ((r & 3u) << 1);
+    uint32_t c = (s & 15u) ^ (((r & 3u) | ((r >> 1) & 4u)) << 1);
     if ((int)c >= Dv / 8) c = 0;
     g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
   }

@@ -23,7 +23,9 @@ namespace mla {
 namespace {
 
 constexpr int kBN = 128;
-constexpr int kBStride = kBN + 16;   // bf16 per B row in LDS (288 B: conflict-free tr reads)
+// bf16 per B row in LDS: 320 B (64 mod 256), so the 4 rows x 64 bytes that
+// 32 lanes of a transposing read touch are 4 disjoint bank ranges
+constexpr int kBStride = kBN + 32;
 
 struct Side {
   const bf16* src;

@@ -49,9 +49,14 @@ constexpr int kFSStride = kNDv + 8;           // bf16 per staged output row
 static_assert(kFW * 32 * kFSStride * 2 <= kFBuf * kTBytes, "output staging fits the tile buffers");
 constexpr float kFSlack = 8.0f;               // lazy rescale threshold (log2 units)
 
-// K row t: chunk k (24 per row) at position k ^ (t % 8) within its group of
-// 8; V row t: chunk k (16 per row) at position k ^ 4 (t % 4).
-__device__ __forceinline__ uint32_t k_pos(uint32_t t, uint32_t k) { return k ^ (t & 7u); }
+// The LDS serves a 16-byte read 16 lanes (256 bytes) at a time and an
+// 8-byte read 32 lanes at a time.  K row t (384 B, 128 mod 256): chunk k
+// (24 per row) at position k ^ f(t) within its group of 8, f(t) = 4 ((t/2)
+// % 2) + (t/4) % 4, so 16 consecutive rows of a fragment read hit 16
+// distinct bank slots.  V row t (256 B): chunk k (16 per row) at position
+// k ^ 4 (t % 4), so the 4 rows x 4 chunks of a transposing read do.
+__device__ __forceinline__ uint32_t k_swz(uint32_t t) { return (((t >> 1) & 1u) << 2) | ((t >> 2) & 3u); }
+__device__ __forceinline__ uint32_t k_pos(uint32_t t, uint32_t k) { return k ^ k_swz(t); }
 __device__ __forceinline__ uint32_t v_pos(uint32_t t, uint32_t k) { return k ^ ((t & 3u) << 2); }
 
 // This wave's share of one tile's loads: instruction j fills slots
@@ -183,11 +188,11 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
   for (int ks = 0; ks < kNDk / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   // per-lane LDS offsets.  K fragment (S^T A operand): row 32 kb + lane%32,
-  // chunk 2 ks + lane/32 -> position 8 (ks/4) + ((2 (ks%4) + lane/32) ^ (lane%8)).
-  const uint32_t hi = lane >> 5, x7 = lane & 7;
+  // chunk 2 ks + lane/32 -> position 8 (ks/4) + ((2 (ks%4) + lane/32) ^ f(row)).
+  const uint32_t hi = lane >> 5, fk = k_swz(lane & 31);
   uint32_t k_off[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) k_off[q] = ((lane & 31) * kKCh + ((2u * q + hi) ^ x7)) * 16u;
+  for (int q = 0; q < 4; ++q) k_off[q] = ((lane & 31) * kKCh + ((2u * q + hi) ^ fk)) * 16u;
   // V^T fragment (transposing reads): group g, lane li = 4a + bb reads key
   // row 8 (g/2) + 4 hi + a (+ 16 ks), dv chunk 4 db + 2 (g%2) + bb/2 at
   // position chunk ^ 4a, plus 8 bytes for odd bb.
@@ -223,13 +228,31 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
 
     // ---- S^T = K Q^T: two 32-key blocks, K = 192 (12 steps of 16)
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      // fragments read two steps ahead of the MFMAs that use them
+      auto frag = [&](int ks, int kb) {
+        return lds_read_b128(buf + k_off[ks & 3] + (uint32_t)((ks >> 2) * 128) +
+                             (uint32_t)(kb * 32 * kKCh * 16));
+      };
+      constexpr int D = 2;
+      bf16x8 fr[D + 1][2];
 #pragma unroll
-    for (int ks = 0; ks < kNDk / 16; ++ks) {
+      for (int d = 0; d < D; ++d) {
+        fr[d][0] = frag(d, 0);
+        fr[d][1] = frag(d, 1);
+      }
+      // (the scheduling barriers keep the compiler from folding the reads
+      // back next to their MFMAs, which would expose every LDS latency)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = lds_read_b128(buf + k_off[ks & 3] + (uint32_t)((ks >> 2) * 128) +
-                                        (uint32_t)(kb * 32 * kKCh * 16));
-        s[kb] = mfma32(kf, qf[ks], s[kb]);
+      for (int ks = 0; ks < kNDk / 16; ++ks) {
+        if (ks + D < kNDk / 16) {
+          fr[(ks + D) % (D + 1)][0] = frag(ks + D, 0);
+          fr[(ks + D) % (D + 1)][1] = frag(ks + D, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = mfma32(fr[ks % (D + 1)][0], qf[ks], s[0]);
+        s[1] = mfma32(fr[ks % (D + 1)][1], qf[ks], s[1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // register v of block kb <-> key key0 + 32 kb + 8 (v/4) + 4 hi + v%4, query lane%32
