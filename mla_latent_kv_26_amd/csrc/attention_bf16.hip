@@ -45,6 +45,7 @@ constexpr int kTileBytes = kTok * kW * 2;               // 36864
 constexpr int kNBuf = 4;                                // tile buffers
 constexpr int kTileLoads = kTileBytes / 1024;           // 36 1-KB load instructions
 constexpr int kSLoads = 4, kPLoads = 5;                 // per score wave / per P*C wave
+constexpr int kSAhead = 4;  // score fragment pairs read ahead of their MFMAs
 static_assert(4 * kSLoads + 4 * kPLoads == kTileLoads, "every slot loaded once");
 constexpr int kMaxHG = 64;                              // heads per workgroup, at most
 constexpr int kWaves = 8;
@@ -134,6 +135,7 @@ struct SegArgs {
   const int* table;
   int max_blocks, shift, len, tile0, tile1;
   const PageCursor* pre;  // page ids already loaded for tile0's page, or null
+  bool tile0_issued;      // tile0's loads already in flight into buffer 0
 };
 
 __device__ __forceinline__ const bf16* tile_rows(const SegArgs& a, PageCursor& pc, int tile,
@@ -153,7 +155,9 @@ __device__ __forceinline__ void seg_start(const SegArgs& a, PageCursor& pc, uint
     pc = *a.pre;
   else
     pc.start(a.table, a.max_blocks, (a.tile0 * kTok) >> a.shift, lane);
-  issue_part<NL>(tile_rows(a, pc, a.tile0, lane), min(kTok, a.len - a.tile0 * kTok), lds, j0, lane);
+  if (!a.tile0_issued)
+    issue_part<NL>(tile_rows(a, pc, a.tile0, lane), min(kTok, a.len - a.tile0 * kTok), lds, j0,
+                   lane);
 }
 
 // Step-top synchronisation shared by both wave roles: wait for this wave's
@@ -230,17 +234,27 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
         return lds_read_b128(buf + ((ks & 1) ? s_odd : s_even) +
                              (uint32_t)((ks >> 1) * 128 + tb * 16 * kCh * 16));
       };
-      bf16x8 fr[2][2];
-      fr[0][0] = frag(0, 0);
-      fr[0][1] = frag(0, 1);
+      // Fragments are read kSAhead steps ahead of their MFMAs; the
+      // scheduling barriers keep the compiler from sinking the reads next
+      // to their uses (it otherwise waits for every pair in turn, and the
+      // loop runs at LDS latency instead of MFMA rate).
+      constexpr int NK = kW / 32;
+      bf16x8 fr[kSAhead + 1][2];
 #pragma unroll
-      for (int ks = 0; ks < kW / 32; ++ks) {
-        if (ks + 1 < kW / 32) {
-          fr[(ks + 1) & 1][0] = frag(ks + 1, 0);
-          fr[(ks + 1) & 1][1] = frag(ks + 1, 1);
+      for (int i = 0; i < kSAhead; ++i) {
+        fr[i][0] = frag(i, 0);
+        fr[i][1] = frag(i, 1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        if (ks + kSAhead < NK) {
+          fr[(ks + kSAhead) % (kSAhead + 1)][0] = frag(ks + kSAhead, 0);
+          fr[(ks + kSAhead) % (kSAhead + 1)][1] = frag(ks + kSAhead, 1);
         }
-        sacc[0] = mfma16(fr[ks & 1][0], qf[ks], sacc[0]);
-        sacc[1] = mfma16(fr[ks & 1][1], qf[ks], sacc[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[0] = mfma16(fr[ks % (kSAhead + 1)][0], qf[ks], sacc[0]);
+        sacc[1] = mfma16(fr[ks % (kSAhead + 1)][1], qf[ks], sacc[1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // register v of block tb <-> token 16 tb + 4 kq + v, head h
@@ -437,30 +451,51 @@ __device__ __forceinline__ void map_block(int b, int hgc, int n_wg, int& hg, int
   w = x * (n_wg >> 3) + j / hgc;
 }
 
-}  // namespace
-
-// Which workgroup of the stream owns tile x (ranges [w*T/n, (w+1)*T/n)).
-__host__ __device__ inline int owner_of(long x, long T, int n) {
-  int w = (int)((x * n) / T);
-  while (w + 1 < n && ((long)(w + 1) * T) / n <= x) ++w;
-  while (w > 0 && ((long)w * T) / n > x) --w;
-  return w;
-}
-
-namespace {
+// Equal shares of a stream of T tiles over n workgroups: workgroup w owns
+// [start(w), start(w + 1)), start(w) = floor(w T / n).  With T = q n + r
+// that is w q + floor(w r / n), which stays in 32 bits (T < 2^31, and
+// w r < n^2); a 64-bit division would cost hundreds of instructions.
+struct StreamSplit {
+  int n, q, r;
+  __device__ __forceinline__ StreamSplit(int T, int n_) : n(n_), q(T / n_), r(T % n_) {}
+  __device__ __forceinline__ int start(int w) const { return w * q + (w * r) / n; }
+  // Whether workgroup w's range holds a tile (all do once T >= n).
+  __device__ __forceinline__ bool nonempty(int w) const {
+    return q > 0 || ((w + 1) * r) / n > (w * r) / n;
+  }
+  // The workgroup whose range holds tile x (0 <= x < T): a float estimate
+  // of x n / T, then exact corrections.
+  __device__ __forceinline__ int owner(int x) const {
+    const float T = (float)q * (float)n + (float)r;
+    int w = min(n - 1, (int)((float)x * (float)n / T));
+    while (w + 1 < n && start(w + 1) <= x) ++w;
+    while (w > 0 && start(w) > x) --w;
+    return w;
+  }
+};
 
 // Prefix sums of tiles per sequence into LDS prefix[0..batch] (2 sequences
 // per thread, then a scan); optionally (len - 1) % kTok per sequence into
 // lenlo, so a length needs no further global read.  All kThreads threads
-// call it; ends with a barrier.
+// call it; ends with a barrier.  `early` runs once the lengths have landed
+// and before the scan: loads it issues overlap the rest (the barriers here
+// are LDS-only, so they do not wait for them).
+template <typename Early>
 __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, int batch,
-                                            int* prefix, int* scan, unsigned char* lenlo) {
+                                            int* prefix, int* scan, unsigned char* lenlo,
+                                            Early&& early) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int lens[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) lens[i] = tid * 2 + i < batch ? seq_lens[tid * 2 + i] : 0;
+  // the lengths are plain values from here on: no wait below is tied to them
+  asm volatile("" : "+v"(lens[0]), "+v"(lens[1]));
+  early();
   int cnt[2], tot = 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int b = tid * 2 + i;
-    const int len = b < batch ? seq_lens[b] : 0;
+    const int len = lens[i];
     cnt[i] = len > 0 ? (len + kTok - 1) / kTok : 0;
     if (lenlo && b < batch) lenlo[b] = (unsigned char)((len - 1) & (kTok - 1));
     tot += cnt[i];
@@ -472,7 +507,7 @@ __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, in
     if (lane >= o) incl += y;
   }
   if (lane == 63) scan[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int base = 0;
   for (int i = 0; i < wave; ++i) base += scan[i];
   int run = base + incl - tot;
@@ -485,7 +520,7 @@ __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, in
       prefix[b + 1] = run;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // One decode workgroup of the tile stream (block `blk`): every (workgroup,
@@ -494,7 +529,7 @@ __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, in
 template <int HEADS>
 __device__ __forceinline__ bool decode_attention_wg(
     char* smem, int blk, const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
-    const int* __restrict__ block_table, int max_blocks, int shift,
+    const int* __restrict__ block_table, int max_blocks, int shift, int num_blocks,
     const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
     int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   const uint32_t lds = lds_addr(smem);
@@ -508,20 +543,40 @@ __device__ __forceinline__ bool decode_attention_wg(
   // Where this workgroup's range would start if every sequence had
   // guess_tiles tiles (the common equal-length batch): load that page-id
   // chunk now, in parallel with the lengths, and keep it if the guess holds.
-  const long tg = (long)batch * guess_tiles;
-  const long xg = ((long)w * tg) / n_wg;
-  const int bg = min((int)(xg / guess_tiles), batch - 1);
-  const int pg0 = (int)((xg - (long)bg * guess_tiles) * kTok) >> shift;
+  // As soon as the ids land, the guessed first tile (as a full tile) goes
+  // in flight into buffer 0, overlapping the prefix sums and the range
+  // search; a page id outside the pool is never dereferenced.
+  const int xg = StreamSplit(batch * guess_tiles, n_wg).start(w);
+  const int bg = min(xg / guess_tiles, batch - 1);
+  const int tg0 = xg - bg * guess_tiles;
+  const int pg0 = (tg0 * kTok) >> shift;
   PageCursor spec;
   spec.start(block_table + (long)bg * max_blocks, max_blocks, pg0, lane);
+  bool spec_issued = false;
+  auto early = [&]() {
+    const int page = spec.page(pg0, lane);
+    if (page < 0 || page >= num_blocks) return;
+    const int tok = tg0 * kTok;
+    const bf16* rows = pool + ((long)page * (1 << shift) + (tok & ((1 << shift) - 1))) * kW;
+    if (wave < 4)
+      issue_part<kSLoads>(rows, kTok, lds, (uint32_t)wave * kSLoads, lane);
+    else
+      issue_part<kPLoads>(rows, kTok, lds, 4u * kSLoads + (uint32_t)(wave - 4) * kPLoads, lane);
+    spec_issued = true;
+  };
 
-  tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo);
-  const long T = prefix[batch];
+  tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo, early);
+  const int T = prefix[batch];
   if (blk == 0)
     for (int b = tid; b <= batch; b += kThreads) prefix_out[b] = prefix[b];
 
-  long x0 = ((long)w * T) / n_wg, x1 = ((long)(w + 1) * T) / n_wg;
-  if (x0 >= x1) return false;
+  const StreamSplit split(T, n_wg);
+  int x0 = split.start(w);
+  const int x1 = split.start(w + 1);
+  if (x0 >= x1) {
+    if (spec_issued) wait_vmcnt<0>();  // no load may land in LDS after the exit
+    return false;
+  }
   // first sequence touching x0
   int b = 0;
   {
@@ -535,8 +590,8 @@ __device__ __forceinline__ bool decode_attention_wg(
   const long n_slots = (long)n_wg + batch;
   while (x0 < x1) {
     const int p0 = prefix[b], p1 = prefix[b + 1];
-    const long seg_end = min(x1, (long)p1);
-    const int tile0 = (int)(x0 - p0), tile1 = (int)(seg_end - p0);
+    const int seg_end = min(x1, p1);
+    const int tile0 = x0 - p0, tile1 = seg_end - p0;
     if (tile1 <= tile0) {  // a sequence without rows (invalid input): nothing to attend
       ++b;
       continue;
@@ -544,8 +599,13 @@ __device__ __forceinline__ bool decode_attention_wg(
     const int len = (p1 - p0 - 1) * kTok + lenlo[b] + 1;
     const long slot = (long)hg * n_slots + w + b;
     const bool guessed = b == bg && ((tile0 * kTok) >> shift) == pg0;
+    // the speculative tile is this segment's tile 0 only if it is the same
+    // tile and a full one (a partial tile repeats its last row instead)
+    const bool reuse = spec_issued && guessed && tile0 == tg0 && (tile0 + 1) * kTok <= len;
+    if (spec_issued && !reuse) wait_vmcnt<0>();  // its loads land before buffer 0 is refilled
+    spec_issued = false;
     SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
-              max_blocks, shift, len, tile0, tile1, guessed ? &spec : nullptr};
+              max_blocks, shift, len, tile0, tile1, guessed ? &spec : nullptr, reuse};
     float m, tot;
     attend_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane, m, tot);
     if (wave < Geo<HEADS>::SW && lane < 16) {
@@ -556,6 +616,7 @@ __device__ __forceinline__ bool decode_attention_wg(
     x0 = seg_end;
     ++b;
   }
+  if (spec_issued) wait_vmcnt<0>();
   return true;
 }
 
@@ -593,18 +654,33 @@ __device__ __forceinline__ uint32_t o_off(uint32_t r, uint32_t c) {
   return (r * (kR / 8) + (c ^ (r & 15u))) * 16u;
 }
 
-__device__ __forceinline__ void issue_w_uv(const bf16* W, int Dv, uint32_t wb, uint32_t ob) {
-  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+// W_UV[h] goes through registers (16 chunks of 16 bytes per thread): plain
+// loads keep the compiler's per-load waits exact, where direct-to-LDS loads
+// in flight make it wait for everything before the first piece is used.
+constexpr int kWChunks = kR * 16 / 64 / kCWaves;
+
+__device__ __forceinline__ void load_w_uv(const bf16* W, int Dv, bf16x8 (&wr)[kWChunks]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // slot s = 64 j + lane holds row s/16, the chunk w_off puts at s%16; chunks
   // past Dv/8 load the row's chunk 0 (unused)
 #pragma unroll
-  for (int i = 0; i < kR * 16 / 64 / kCWaves; ++i) {
-    const uint32_t j = (uint32_t)wave * (kR * 16 / 64 / kCWaves) + i;
+  for (int i = 0; i < kWChunks; ++i) {
+    const uint32_t j = (uint32_t)wave * kWChunks + i;
     const uint32_t s = 64u * j + lane, r = s >> 4;
     uint32_t c = (s & 15u) ^ (((r & 3u) | ((r >> 1) & 4u)) << 1);
     if ((int)c >= Dv / 8) c = 0;
-    g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
+    wr[i] = *(const bf16x8*)(W + (long)r * Dv + c * 8);
+  }
+}
+
+__device__ __forceinline__ void store_w_uv(const bf16x8 (&wr)[kWChunks], uint32_t wb,
+                                           uint32_t ob) {
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < kWChunks; ++i) {
+    const uint32_t j = (uint32_t)wave * kWChunks + i;
+    *(lds_bf16x8*)(uintptr_t)(wb + (64u * j + lane) * 16u) = wr[i];
   }
   // zero rows kCRows .. 15 of o_lat (one 16-byte chunk per thread)
   *(lds_bf16x8*)(uintptr_t)(ob + o_off(kCRows + wave, lane)) = bf16x8{};
@@ -622,20 +698,17 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
   const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
 
   const int b = b0 + wave;
-  const long T = prefix[batch];
+  const StreamSplit split(prefix[batch], n_wg);
   const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
   int f = 0, n = 0;
   if (p1 > p0) {
-    f = owner_of(p0, T, n_wg);
-    n = owner_of(p1 - 1, T, n_wg) - f + 1;
+    f = split.owner(p0);
+    n = split.owner(p1 - 1) - f + 1;
   }
   // Pieces f .. f+n-1 come from workgroups f .. f+n-1 of the stream; one
   // whose range is empty (fewer tiles than workgroups) wrote nothing.
-  auto has_piece = [&](int s) {
-    const long w = f + s;
-    return (w * T) / n_wg < ((w + 1) * T) / n_wg;
-  };
-  const long slot0 = (long)hg * n_slots + f + b;
+  auto has_piece = [&](int s) { return split.nonempty(f + s); };
+  const long slot0 = (long)hg * n_slots + f + min(b, batch - 1);
   auto piece_o = [&](int s) {
     return has_piece(s) ? *(const bf16x8*)(part_o + ((slot0 + s) * hg_heads + hl) * kR + 8 * lane)
                         : bf16x8{};
@@ -644,14 +717,19 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
     return has_piece(s) ? *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2)
                         : f32x2{-INFINITY, 0.f};
   };
-  // statistics and the first pieces' values, all in flight
-  f32x2 ml0 = {-INFINITY, 0.f};
-  if (lane < n) ml0 = piece_ml(lane);
+  // Statistics and the first pieces' values, all in flight, then W_UV.  The
+  // loads are unconditional (piece index clamped to the last piece; what is
+  // not a piece is masked afterwards), so the compiler can wait for each in
+  // turn instead of for everything, W_UV included.
+  const int last = max(n, 1) - 1;
+  const f32x2 ml_raw = *(const f32x2*)(part_ml + ((slot0 + min(lane, last)) * hg_heads + hl) * 2);
   bf16x8 v[kPieceChunk];
 #pragma unroll
   for (int u = 0; u < kPieceChunk; ++u)
-    if (u < n) v[u] = piece_o(u);
-  if (W) issue_w_uv(W, Dv, wb, ob);
+    v[u] = *(const bf16x8*)(part_o + ((slot0 + min(u, last)) * hg_heads + hl) * kR + 8 * lane);
+  bf16x8 wr[kWChunks];
+  if (W) load_w_uv(W, Dv, wr);
+  const f32x2 ml0 = lane < n && has_piece(lane) ? ml_raw : f32x2{-INFINITY, 0.f};
 
   float M = ml0[0];
   for (int s = 64 + lane; s < n; s += 64) M = fmaxf(M, piece_ml(s)[0]);
@@ -660,27 +738,43 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
 #pragma unroll
   for (int e8 = 0; e8 < 8; ++e8) acc[e8] = 0.f;
   float den = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int sw = s0 + lane;
-    float e = 0.f;
-    if (sw < n) {
-      const f32x2 t = s0 == 0 ? ml0 : piece_ml(sw);
-      if (t[1] > 0.f) e = exp2f(t[0] - M) * t[1];
-    }
-    den += e;
-    const int m = min(64, n - s0);
-    for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
-      if (s0 + u0 > 0) {
+  if (n <= kPieceChunk) {
+    // the common case: every piece is already in registers.  A piece with
+    // zero weight (missing, or a clamped duplicate) is skipped, so its
+    // values never meet the sum.
+    const float e = ml0[1] > 0.f ? exp2f(ml0[0] - M) * ml0[1] : 0.f;
+    den = e;
 #pragma unroll
-        for (int u = 0; u < kPieceChunk; ++u)
-          if (u0 + u < m) v[u] = piece_o(s0 + u0 + u);
+    for (int u = 0; u < kPieceChunk; ++u) {
+      const float eu = lane_value(e, u);
+      if (eu != 0.f) {
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
       }
+    }
+  } else {
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int sw = s0 + lane;
+      float e = 0.f;
+      if (sw < n) {
+        const f32x2 t = s0 == 0 ? ml0 : piece_ml(sw);
+        if (t[1] > 0.f) e = exp2f(t[0] - M) * t[1];
+      }
+      den += e;
+      const int m = min(64, n - s0);
+      for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
+        if (s0 + u0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kPieceChunk; ++u) {
-        const float eu = __shfl(e, u0 + u, 64);
-        if (u0 + u < m) {
+          for (int u = 0; u < kPieceChunk; ++u)
+            if (u0 + u < m) v[u] = piece_o(s0 + u0 + u);
+        }
 #pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
+        for (int u = 0; u < kPieceChunk; ++u) {
+          const float eu = lane_value(e, u0 + u);
+          if (u0 + u < m && eu != 0.f) {
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
+          }
         }
       }
     }
@@ -695,7 +789,7 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
     return;
   }
   *(lds_bf16x8*)(uintptr_t)(ob + o_off(wave, lane)) = o;
-  wait_vmcnt<0>();
+  store_w_uv(wr, wb, ob);
   __syncthreads();
 
   // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows (8 used) x Dv, K = 512,
@@ -730,12 +824,13 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
 template <int HEADS>
 __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
-    const int* __restrict__ block_table, int max_blocks, int shift,
+    const int* __restrict__ block_table, int max_blocks, int shift, int num_blocks,
     const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
     int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   decode_attention_wg<HEADS>(smem, blockIdx.x, q_full, pool, block_table, max_blocks, shift,
-                             seq_lens, batch, H, n_wg, guess_tiles, prefix_out, part_ml, part_o);
+                             num_blocks, seq_lens, batch, H, n_wg, guess_tiles, prefix_out,
+                             part_ml, part_o);
 }
 
 // Combine of the partials (the staged call): grid (H, ceil(batch / 8)).
@@ -772,7 +867,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
   const int len = start_pos[b] + t + 1;
   (void)tid;
   SegArgs a{q_full + ((long)n * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
-            max_blocks, shift, len, 0, (len + kTok - 1) / kTok, nullptr};
+            max_blocks, shift, len, 0, (len + kTok - 1) / kTok, nullptr, false};
   float m, tot;
   attend_segment<HEADS>(a, lds, o_lat + ((long)n * H + hg * HEADS) * kR, wave, lane, m, tot);
 }
@@ -798,20 +893,21 @@ int decode_num_wg(int head_groups, int num_cus) {
   return n < 8 ? 8 : n;
 }
 
-void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
-                                    int max_blocks, int block_shift, const int* seq_lens,
+void launch_attention_partials_bf16(const void* q_full, const void* pool, int num_blocks,
+                                    const int* block_table, int max_blocks, int block_shift,
+                                    const int* seq_lens,
                                     int batch, int max_seq_len, int H, int heads_per_wg, int n_wg,
                                     int* prefix, float* part_ml, void* part_o, hipStream_t st) {
   const int hgc = H / heads_per_wg;
   const int guess_tiles = (max_seq_len + kTok - 1) / kTok;
   if (heads_per_wg == 64)
     attn_decode_partials_kernel<64><<<n_wg * hgc, kThreads, 0, st>>>(
-        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, seq_lens,
-        batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
+        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, num_blocks,
+        seq_lens, batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
   else
     attn_decode_partials_kernel<32><<<n_wg * hgc, kThreads, 0, st>>>(
-        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, seq_lens,
-        batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
+        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, num_blocks,
+        seq_lens, batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
 }
 
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,

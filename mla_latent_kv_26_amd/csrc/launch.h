@@ -78,8 +78,9 @@ size_t decode_partial_slots(int batch, int n_wg);
 int decode_heads_per_wg(int H, int batch, int max_seq_len, int num_cus);
 int decode_num_wg(int head_groups, int num_cus);
 
-void launch_attention_partials_bf16(const void* q_full, const void* pool, const int* block_table,
-                                    int max_blocks, int block_shift, const int* seq_lens,
+void launch_attention_partials_bf16(const void* q_full, const void* pool, int num_blocks,
+                                    const int* block_table, int max_blocks, int block_shift,
+                                    const int* seq_lens,
                                     int batch, int max_seq_len, int H, int heads_per_wg, int n_wg,
                                     int* prefix, float* part_ml, void* part_o, hipStream_t st);
 

@@ -353,18 +353,23 @@ static mla_status check_decode_common(const Dims& d, const void* pool, int32_t n
     return fail(MLA_ERR_INVALID_ARG,
                 "max_seq_len %d exceeds the page table capacity %ld (max_blocks_per_seq %d x block_size %d)",
                 max_seq_len, (long)max_blocks * d.bs, max_blocks, d.bs);
+  // the split-KV partition counts 32-token tiles of the whole batch in 32 bits
+  if ((long)batch * ((max_seq_len + 31) / 32) > 0x7fffffffL)
+    return fail(MLA_ERR_UNSUPPORTED, "batch x max_seq_len / 32 must stay below 2^31 (got %d x %d)",
+                batch, max_seq_len);
   return check_decode_kernels(d, batch);
 }
 
 static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* pool,
-                                 const int32_t* table, int32_t max_blocks, const int32_t* seq_lens,
+                                 int32_t num_blocks, const int32_t* table, int32_t max_blocks, const int32_t* seq_lens,
                                  int32_t batch, int32_t max_seq_len, const void* w_uv, void* dst,
                                  void* ws, hipStream_t st) {
   const DecodeWs w = decode_ws(d, batch, max_seq_len);
   if (d.dt == MLA_DTYPE_BF16) {
-    mla::launch_attention_partials_bf16(q_full, pool, table, max_blocks, d.shift, seq_lens, batch,
-                                        max_seq_len, d.H, w.heads, w.n_wg, (int*)at(ws, w.prefix),
-                                        (float*)at(ws, w.part_ml), at(ws, w.part_o), st);
+    mla::launch_attention_partials_bf16(q_full, pool, num_blocks, table, max_blocks, d.shift,
+                                        seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
+                                        (int*)at(ws, w.prefix), (float*)at(ws, w.part_ml),
+                                        at(ws, w.part_o), st);
     mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
                         at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, w_uv, d.Dv, dst, st);
   } else {
@@ -400,7 +405,7 @@ mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_r
   hipStream_t st = (hipStream_t)stream;
   void* q_full = at(workspace, w.q_full);
   enqueue_absorb(d, q_nope, q_rope, w_uk, batch, q_full, st);
-  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+  enqueue_latent(d, q_full, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
                  w_uv, out, workspace, st);
   return launched("mla_decode");
 }
@@ -440,7 +445,7 @@ mla_status mla_latent_attention(const mla_config* cfg, const void* q_full, const
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
                 workspace ? "" : ", NULL");
   if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  enqueue_latent(d, q_full, kv_pool, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+  enqueue_latent(d, q_full, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
                  nullptr, o_lat, workspace, (hipStream_t)stream);
   return launched("mla_latent_attention");
 }
@@ -472,8 +477,8 @@ mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, con
   const DecodeWs w = decode_ws(d, batch, max_seq_len);
   s = check_ws(w, workspace, workspace_bytes);
   if (s != MLA_OK) return s;
-  mla::launch_attention_partials_bf16(q_full, kv_pool, block_table, max_blocks_per_seq, d.shift,
-                                      seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
+  mla::launch_attention_partials_bf16(q_full, kv_pool, num_blocks, block_table, max_blocks_per_seq,
+                                      d.shift, seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
                                       (int*)at(workspace, w.prefix),
                                       (float*)at(workspace, w.part_ml), at(workspace, w.part_o),
                                       (hipStream_t)stream);
