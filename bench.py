@@ -7,10 +7,12 @@ by its time (TB/s); `ms_per_step` gives the step time.  Inputs are synthetic
 timed steps rotate over several independently drawn input sets whose total
 size exceeds the 256 MB Infinity Cache, so repeats are served from HBM.
 
-Timing: the step's kernels are captured in a HIP graph (one replay launches
-every step of one rotation), and HIP events on the launching stream bracket
-the replays.  The split-KV attention kernel is timed the same way on its own
-for the roofline entry.  The oracle is timed on the host cores on a bounded
+Timing: the step's kernels are captured in a HIP graph whose one replay
+launches --passes rotations (every input set several times, as a model's
+layers follow one another in one graph), and HIP events on the launching
+stream bracket the replays; the launch gap between replays is then spread
+over many steps, as in a multi-layer graph.  The split-KV attention kernel
+is timed the same way on its own for the roofline entry.  The oracle is timed on the host cores on a bounded
 sample of the same workload.
 """
 import argparse
@@ -198,6 +200,8 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE,
                     choices=[k for k, v in workloads.WORKLOADS.items() if v["dtype"] == "bf16"])
     ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--passes", type=int, default=10,
+                    help="rotations over the input sets captured in one graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -265,12 +269,13 @@ def main():
     b.synchronize()
     eager_ms = a.elapsed_time(b) / args.steps
 
-    # graph: one replay = one step on each input set
+    # graph: one replay = `passes` rotations over the input sets
     side = torch.cuda.Stream()
-    reps = max(1, args.steps // R)
-    step_ms = graph_time(torch, lambda: [step(i) for i in range(R)], reps, side) / R
-    attn_ms = graph_time(torch, lambda: [attn(i) for i in range(R)], reps, side) / R
-    steps_timed = reps * R
+    per = R * max(1, args.passes)
+    reps = max(1, args.steps // per)
+    step_ms = graph_time(torch, lambda: [step(i % R) for i in range(per)], reps, side) / per
+    attn_ms = graph_time(torch, lambda: [attn(i % R) for i in range(per)], reps, side) / per
+    steps_timed = reps * per
 
     value = alg["step_bytes"] / (step_ms * 1e-3) / 1e12
     achieved = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
@@ -296,7 +301,7 @@ def main():
                    "kv_lora_rank": cfg["kv_lora_rank"], "rope_dim": cfg["rope_dim"],
                    "qk_nope_dim": cfg["qk_nope_dim"], "v_dim": cfg["v_dim"],
                    "block_size": cfg["block_size"], "input_sets_rotated": R,
-                   "timing": "hip graph replay, events on the launching stream"},
+                   "timing": f"hip graph replay ({per} steps per replay), events on the launching stream"},
         "roofline": {
             "kernel": "attn_decode_partials_kernel",
             "bound": "hbm",

@@ -297,10 +297,13 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
   l_out = l;
 }
 
-// P*C wave `pw` (columns 128 pw .. 128 pw + 127 of O, all HEADS heads).
+// P*C wave `pw` (columns 128 pw .. 128 pw + 127 of O, all HEADS heads),
+// accumulated transposed: register v of o[hb][cb] holds column
+// 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 of head 32 hb + lane%32, so a
+// lane owns one head per hb (one rescale factor) and runs of 4 columns.
 template <int HEADS>
 struct OAcc {
-  f32x16 o[Geo<HEADS>::HB][4];  // O[32 hb + ..][128 pw + 32 cb + ..]
+  f32x16 o[Geo<HEADS>::HB][4];
 };
 
 template <int HEADS>
@@ -337,9 +340,9 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
       tr_off[cb][hi] = (row * kCh + 8u * (2u * pw + (cb >> 1)) + (cc ^ swz(row))) * 16u +
                        8u * (li & 1);
     }
-  // P fragments (A operand of 32x32x16): row 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
+  // P fragments (B operand of 32x32x16): head 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
   const uint32_t pa_base = lds + kOffP + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
-  const uint32_t al_base = lds + kOffAlpha + 16 * (lane >> 5);
+  const uint32_t al_base = lds + kOffAlpha + (lane & 31) * 4;
 
   for (int k = 0; k <= n; ++k) {
     step_sync<kPLoads>(a, pc, lds, j0, k, n, lane);
@@ -352,15 +355,13 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
     if (G::SW > 2) fs += f[2] + f[3];
     if (fs != 0.0f) {
 #pragma unroll
-      for (int hb = 0; hb < G::HB; ++hb)
+      for (int hb = 0; hb < G::HB; ++hb) {
+        const float al = lds_ld(al_base + (par * kMaxHG + 32 * hb) * 4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 a4 = lds_ld4(al_base + (par * kMaxHG + 32 * hb + 8 * q) * 4);
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc.o[hb][cb][4 * q + r] *= a4[r];
-        }
+          for (int v = 0; v < 16; ++v) acc.o[hb][cb][v] *= al;
+      }
     }
     const uint32_t pbase = pa_base + par * (kMaxHG * kPStride * 2);
     uint32_t ta[8];
@@ -383,7 +384,7 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
       for (int cb = 0; cb < 4; ++cb) {
         const bf16x8 bv = cat(t[2 * cb], t[2 * cb + 1]);
 #pragma unroll
-        for (int hb = 0; hb < G::HB; ++hb) acc.o[hb][cb] = mfma32(pa[hb], bv, acc.o[hb][cb]);
+        for (int hb = 0; hb < G::HB; ++hb) acc.o[hb][cb] = mfma32(bv, pa[hb], acc.o[hb][cb]);
       }
     }
   }
@@ -398,7 +399,6 @@ template <int HEADS>
 __device__ __forceinline__ void attend_segment(const SegArgs& a, uint32_t lds, bf16* dst,
                                                int wave, int lane, float& m_out, float& l_out) {
   using G = Geo<HEADS>;
-  typedef __attribute__((address_space(3))) bf16 lds_bf16;
   if (wave < 4) {
     score_role<HEADS>(a, lds, wave, lane, m_out, l_out);
     if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
@@ -409,22 +409,23 @@ __device__ __forceinline__ void attend_segment(const SegArgs& a, uint32_t lds, b
     OAcc<HEADS> acc;
     pv_role<HEADS>(a, lds, pw, lane, acc);
     lds_barrier();
-    // register v of o[hb][cb] <-> head 32 hb + 8 (v/4) + 4 (lane/32) + v%4,
-    // column 128 pw + 32 cb + lane%32
-    const uint32_t st_base = lds + ((4 * (lane >> 5)) * kOStride + 128 * pw + (lane & 31)) * 2;
-    const uint32_t inv_base = lds + kOffInv + 16 * (lane >> 5);
+    // lane: head 32 hb + lane%32; register v of o[hb][cb]: column
+    // 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 (runs of 4 -> 8-byte stores)
 #pragma unroll
-    for (int hb = 0; hb < G::HB; ++hb)
+    for (int hb = 0; hb < G::HB; ++hb) {
+      const int head = 32 * hb + (lane & 31);
+      const float inv = lds_ld(lds + kOffInv + head * 4);
+      const uint32_t row = lds + (head * kOStride + 128 * pw + 4 * (lane >> 5)) * 2;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 inv = lds_ld4(inv_base + (32 * hb + 8 * q) * 4);
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 w4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            *(lds_bf16*)(uintptr_t)(st_base + ((32 * hb + 8 * q + r) * kOStride + 32 * cb) * 2) =
-                (bf16)(acc.o[hb][cb][4 * q + r] * inv[r]);
-      }
+          for (int r = 0; r < 4; ++r) w4[r] = (bf16)(acc.o[hb][cb][4 * q + r] * inv);
+          lds_st(row + (32 * cb + 8 * q) * 2, w4);
+        }
+    }
     lds_barrier();
     m_out = 0.f;
     l_out = 0.f;
