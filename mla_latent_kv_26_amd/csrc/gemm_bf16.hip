@@ -237,6 +237,10 @@ void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K
                       int c_f32, hipStream_t st, const void* side_src, long side_ld,
                       long side_sb, void* side_dst, int side_cols) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
+  if (!side_src && gemm_tile256_fits(M, N, K, lda, ldb, ldc)) {
+    launch_gemm_tile256(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, false, st);
+    return;
+  }
   const Side side{(const bf16*)side_src, side_ld, side_sb, (bf16*)side_dst, side_cols};
   if (K <= 128)
     launch_bk<128, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
@@ -250,6 +254,10 @@ void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, i
                          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
                          int c_f32, hipStream_t st) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
+  if (gemm_tile256_fits(M, N, K, lda, ldb, ldc)) {
+    launch_gemm_tile256(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, true, st);
+    return;
+  }
   const Side side{nullptr, 0, 0, nullptr, 0};
   if (K <= 128)
     launch_bk<128, true>(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,

@@ -59,6 +59,17 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 // bases and batch strides.  When side_src is set (bf16 C only), also
 // C_b[r, c] = alpha * side_src[b * side_sb + r * side_ld + c] into
 // side_dst (same ldc / sC as C) for c < side_cols.
+// 256 x (256|128) x 32 tiles, direct-to-LDS staging (gemm_tile256.hip): taken
+// by launch_gemm_bf16(_bt) when the shape fits (M >= 256, N >= 128, K a
+// multiple of 32, rows and leading dimensions in whole 16-byte chunks).
+bool gemm_tile256_fits(int M, int N, int K, long lda, long ldb, long ldc);
+// nb > 0 (row-major B only): B's columns come in blocks of nb, block j at
+// B + j * sBn, i.e. element (k, n) at B[(n / nb) * sBn + k * ldb + n % nb]
+// (nb a multiple of 8); nb <= 0 means one plain [K, N] matrix.
+void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, int K, long lda,
+                         long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
+                         int c_f32, bool b_transposed, hipStream_t st, int nb = 0, long sBn = 0);
+
 // As launch_gemm_bf16 with B given transposed: Bt[b] is [N, K] row-major
 // (row stride ldb), C[b] = alpha * A[b] * Bt[b]^T.
 void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, int K, long lda,

@@ -661,15 +661,30 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
     void* cg = at(workspace, w.cg);
     mla::launch_gather_rows(kv_pool, block_table, max_blocks_per_seq, d.shift, start_pos, batch,
                             q_len, w.ctx_pad, cg, st);
-    for (int b = 0; b < batch; ++b) {
-      const long r0 = (long)b * w.ctx_pad;
-      const uint16_t* a = (const uint16_t*)cg + r0 * d.W;
-      mla::launch_gemm_bf16_bt(a, w_uk, (uint16_t*)at(workspace, w.kn) + r0 * d.H * d.Dn, w.ctx_pad,
-                               d.Dn, d.R, d.W, d.R, (long)d.H * d.Dn, 0, (long)d.Dn * d.R, d.Dn,
-                               d.H, 1.0f, 0, st);
-      mla::launch_gemm_bf16(a, w_uv, (uint16_t*)at(workspace, w.vv) + r0 * d.H * d.Dv, w.ctx_pad,
-                            d.Dv, d.R, d.W, d.Dv, (long)d.H * d.Dv, 0, (long)d.R * d.Dv, d.Dv,
-                            d.H, 1.0f, 0, st);
+    // K_nope[t, h*Dn + d] = c_t . W_UK[h, d, :] (W_UK as one [H*Dn, R] matrix, given
+    // transposed) and V[t, h*Dv + e] = c_t . W_UV[h, :, e] (W_UV as column blocks of Dv),
+    // every sequence of the batch in one launch each
+    const long sa = (long)w.ctx_pad * d.W;
+    if (mla::gemm_tile256_fits(w.ctx_pad, d.H * d.Dn, d.R, d.W, d.R, (long)d.H * d.Dn) &&
+        mla::gemm_tile256_fits(w.ctx_pad, d.H * d.Dv, d.R, d.W, d.Dv, (long)d.H * d.Dv) &&
+        d.Dv % 8 == 0) {
+      mla::launch_gemm_tile256(cg, w_uk, at(workspace, w.kn), w.ctx_pad, d.H * d.Dn, d.R, d.W,
+                               d.R, (long)d.H * d.Dn, sa, 0, (long)w.ctx_pad * d.H * d.Dn, batch,
+                               1.0f, 0, true, st);
+      mla::launch_gemm_tile256(cg, w_uv, at(workspace, w.vv), w.ctx_pad, d.H * d.Dv, d.R, d.W,
+                               d.Dv, (long)d.H * d.Dv, sa, 0, (long)w.ctx_pad * d.H * d.Dv, batch,
+                               1.0f, 0, false, st, d.Dv, (long)d.R * d.Dv);
+    } else {
+      for (int b = 0; b < batch; ++b) {
+        const long r0 = (long)b * w.ctx_pad;
+        const uint16_t* a = (const uint16_t*)cg + r0 * d.W;
+        mla::launch_gemm_bf16_bt(a, w_uk, (uint16_t*)at(workspace, w.kn) + r0 * d.H * d.Dn,
+                                 w.ctx_pad, d.H * d.Dn, d.R, d.W, d.R, (long)d.H * d.Dn, 0, 0, 0,
+                                 1, 1.0f, 0, st);
+        mla::launch_gemm_bf16(a, w_uv, (uint16_t*)at(workspace, w.vv) + r0 * d.H * d.Dv,
+                              w.ctx_pad, d.Dv, d.R, d.W, d.Dv, (long)d.H * d.Dv, 0,
+                              (long)d.R * d.Dv, d.Dv, d.H, 1.0f, 0, st);
+      }
     }
     mla::launch_flash_prefill(q, rope_table, alpha, at(workspace, w.kn), cg, at(workspace, w.vv),
                               start_pos, batch, q_len, d.H, w.ctx_pad, out, st);

@@ -12,14 +12,17 @@
 // as it loads them and whose output is the layer's per-head output.
 //
 // Attention kernel: workgroup = (sequence, head, 256 query rows), 8 waves of
-// 32 queries.  Per 64-key tile in LDS (K 64 x 192, V 64 x 128; three
-// buffers, two tiles in flight):
+// 32 queries.  Per 64-key tile in LDS (K 64 x 192, V 64 x 128; four
+// buffers, three tiles in flight):
 //   S^T [64 keys x 32 q] = K_tile [64 x 192] Q^T          (32x32x16 MFMAs)
 //   O^T [128 x 32 q]    += V_tile^T [128 x 64] P^T [64 x 32 q]
 // Computing the transposes puts one query in each lane, so row maxima,
-// sums and rescales are per-lane values.  P goes through a per-wave LDS
-// buffer to change its layout for the second product.  Scores are in base 2
-// (the queries carry scale * log2 e).
+// sums and rescales are per-lane values.  P stays in registers: in a 16-key
+// step the S^T accumulator gives lane l (h = l/32) keys 4h .. 4h+3 and
+// 8+4h .. 8+4h+3, which is the second product's k order once the V^T
+// fragments are read from those same key rows (a permutation of the 16 keys
+// of the step, applied to both operands).  Scores are in base 2 (the
+// queries carry scale * log2 e).
 #include "device_common.h"
 #include "launch.h"
 
@@ -36,14 +39,11 @@ constexpr int kVCh = kNDv * 2 / 16;           // 16 chunks per V row (256 B)
 constexpr int kKBytes = kFK * kNDk * 2;       // 24576
 constexpr int kVBytes = kFK * kNDv * 2;       // 16384
 constexpr int kTBytes = kKBytes + kVBytes;    // 40960
-constexpr int kFBuf = 3;
+constexpr int kFBuf = 4;                      // tile buffers; three tiles in flight
 constexpr int kTLoads = kTBytes / 1024;       // 40 one-KB load instructions per tile
 constexpr int kWLoads = kTLoads / kFW;        // 5 per wave
 static_assert(kWLoads * kFW == kTLoads, "tile loads split evenly");
-constexpr int kFPStride = kFK + 8;            // bf16 per P row
-constexpr int kFPWave = 32 * kFPStride * 2;   // 4608 B of P per wave
-constexpr int kFOffP = kFBuf * kTBytes;
-constexpr int kFLds = kFOffP + kFW * kFPWave;
+constexpr int kFLds = kFBuf * kTBytes;
 static_assert(kFLds <= 163840, "LDS budget");
 constexpr int kFSStride = kNDv + 8;           // bf16 per staged output row
 static_assert(kFW * 32 * kFSStride * 2 <= kFBuf * kTBytes, "output staging fits the tile buffers");
@@ -101,6 +101,17 @@ struct KvSource {
     }
   }
 };
+
+// Wait for this wave's tile loads except those of its c most recent tiles.
+__device__ __forceinline__ void wait_tiles(int c) {
+  static_assert(kFBuf <= 4, "up to two later tiles in flight");
+  if (c >= 2)
+    wait_vmcnt<2 * kWLoads>();
+  else if (c == 1)
+    wait_vmcnt<kWLoads>();
+  else
+    wait_vmcnt<0>();
+}
 
 __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
     const bf16* __restrict__ q, const float* __restrict__ rope, float alpha,
@@ -161,11 +172,8 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
       *(f32x4*)(c + 8 * e + 4) = *(const f32x4*)(rr + 16 * e + 4);
     }
   }
-  if (n > 1) src.issue(lds + kTBytes, wave);
-  if (n > 1)
-    wait_vmcnt<kWLoads>();
-  else
-    wait_vmcnt<0>();
+  for (int t = 1; t < min(n, kFBuf - 1); ++t) src.issue(lds + (uint32_t)t * kTBytes, wave);
+  wait_tiles(min(n, kFBuf - 1) - 1);  // tile 0 and the queries have landed
   {
     const float* c = (const float*)cs;
     const float* sv = (const float*)sn;
@@ -194,21 +202,19 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) k_off[q] = ((lane & 31) * kKCh + ((2u * q + hi) ^ fk)) * 16u;
   // V^T fragment (transposing reads): group g, lane li = 4a + bb reads key
-  // row 8 (g/2) + 4 hi + a (+ 16 ks), dv chunk 4 db + 2 (g%2) + bb/2 at
-  // position chunk ^ 4a, plus 8 bytes for odd bb.
+  // row 4 (g/2) + 8 hh + a (+ 16 ks; hh: first or second 4 keys of the
+  // lane's k order), dv chunk 4 db + 2 (g%2) + bb/2 at position chunk ^ 4a,
+  // plus 8 bytes for odd bb.
   const uint32_t g = lane >> 4, li = lane & 15, a4 = li >> 2, bb = li & 3;
   uint32_t v_off[8];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const uint32_t row = 8u * (g >> 1) + 4u * hh + a4;
+      const uint32_t row = 4u * (g >> 1) + 8u * hh + a4;
       const uint32_t ch = 4u * db + 2u * (g & 1) + (bb >> 1);
       v_off[2 * db + hh] = kKBytes + (row * kVCh + (ch ^ (a4 << 2))) * 16u + 8u * (bb & 1);
     }
-  const uint32_t pw = lds + kFOffP + wave * kFPWave;
-  const uint32_t p_wr = pw + ((lane & 31) * kFPStride + 4 * hi) * 2;
-  const uint32_t p_rd = pw + ((lane & 31) * kFPStride + 8 * hi) * 2;
 
   f32x16 o[4];
 #pragma unroll
@@ -216,12 +222,10 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
   float m = -INFINITY, l = 0.f;
 
   for (int k = 0; k < n; ++k) {
-    if (k + 1 < n)
-      wait_vmcnt<kWLoads>();
-    else
-      wait_vmcnt<0>();
+    wait_tiles(min(n - 1 - k, kFBuf - 2));
     lds_barrier();  // tile k visible; tile k-1 fully consumed
-    if (k + 2 < n) src.issue(lds + (uint32_t)((k + 2) % kFBuf) * kTBytes, wave);
+    if (k + kFBuf - 1 < n)
+      src.issue(lds + (uint32_t)((k + kFBuf - 1) % kFBuf) * kTBytes, wave);
     const int key0 = k * kFK;
     if (!wave_live || key0 > wave_last) continue;  // every key of the tile is masked for the wave
     const uint32_t buf = lds + (uint32_t)(k % kFBuf) * kTBytes;
@@ -269,19 +273,16 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
     const bool grow = hmax > m + kFSlack;
     const float m_new = grow ? hmax : m;
     const float alpha = grow ? exp2f(m - m_new) : 1.0f;
+    // P^T fragment of 16-key step ks: registers 8 (ks%2) .. + 7 of block ks/2
     float psum = 0.f;
+    bf16x8 pr[kFK / 16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 pk;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bf16 p = (bf16)exp2f(s[kb][4 * q4 + r] - m_new);
-          pk[r] = p;
-          psum += (float)p;
-        }
-        lds_st(p_wr + (uint32_t)((32 * kb + 8 * q4) * 2), pk);
+      for (int v = 0; v < 16; ++v) {
+        const bf16 p = (bf16)exp2f(s[kb][v] - m_new);
+        pr[2 * kb + (v >> 3)][v & 7] = p;
+        psum += (float)p;
       }
     l = l * alpha + psum;
     m = m_new;
@@ -298,14 +299,13 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
     for (int i = 0; i < 8; ++i) ta[i] = buf + v_off[i];
 #pragma unroll
     for (int ks = 0; ks < kFK / 16; ++ks) {
-      const bf16x8 pf = lds_read_b128(p_rd + ks * 32);
       bf16x4 t[8];
       if (ks == 0) lds_read_tr_x8<0>(ta, t);
       else if (ks == 1) lds_read_tr_x8<16 * kVCh * 16>(ta, t);
       else if (ks == 2) lds_read_tr_x8<32 * kVCh * 16>(ta, t);
       else lds_read_tr_x8<48 * kVCh * 16>(ta, t);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma32(cat(t[2 * db], t[2 * db + 1]), pf, o[db]);
+      for (int db = 0; db < 4; ++db) o[db] = mfma32(cat(t[2 * db], t[2 * db + 1]), pr[ks], o[db]);
     }
   }
 

@@ -267,6 +267,22 @@ def test_staged_calls_match_decode_and_oracle_latent(m):
     assert_bf16(to_host_f64(qf), want, "q_full")
 
 
+def test_output_projection_many_rows(m):
+    """From 256 rows on, the projection takes the 256-row tile GEMM
+    (direct-to-LDS stages, transposed accumulators): 700 and 300 rows (a
+    ragged last row tile), 64 heads of 512 x 128, against the oracle."""
+    cfg = bf16_decode_cfg()
+    mc = m.MLAConfig.from_dict(cfg)
+    H, R, Dv = cfg["num_heads"], cfg["kv_lora_rank"], cfg["v_dim"]
+    w_uv = workloads.normal_tensor((H, R, Dv), seed=53, std=1.0 / np.sqrt(R))
+    for n, seed in ((700, 51), (300, 52)):
+        o_lat = workloads.normal_tensor((n, H, R), seed=seed)
+        got = m.mla_output_projection(mc, to_dev(o_lat), to_dev(w_uv))
+        sync()
+        ref = oracle.project_output(to_f64(o_lat), to_f64(w_uv))
+        assert_bf16(to_host_f64(got), ref, f"projection n={n}", per_row_axis=0)
+
+
 def test_page_permutation_invariance_and_determinism(m):
     """Same logical rows in two physical page orders give bitwise-equal
     outputs, and a repeated call is bitwise identical."""

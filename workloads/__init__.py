@@ -97,6 +97,11 @@ def _normal(rng, shape, std=1.0) -> np.ndarray:
     return out.reshape(shape)
 
 
+def normal_tensor(shape, seed: int, dtype: str = "bf16", std: float = 1.0) -> np.ndarray:
+    """A seeded N(0, std^2) draw of the given shape in the storage dtype."""
+    return _store(_normal(_rng(seed), tuple(shape), std), dtype)
+
+
 def _gain(rng, n, gain_jitter):
     if gain_jitter == 0.0:
         return np.ones(n, dtype=np.float32)
