@@ -271,7 +271,7 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
     hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
     const bool grow = hmax > m + kRescaleSlack;
     const float m_new = grow ? hmax : m;
-    const float alpha = grow ? exp2f(m - m_new) : 1.0f;
+    const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
     const bool any = __ballot(grow) != 0ull;
     const uint32_t pb = pw_base + (uint32_t)(k & 1) * (kMaxHG * kPStride * 2);
     float psum = 0.f;
@@ -280,7 +280,7 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
       bf16x4 pk;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const bf16 p = (bf16)exp2f(sacc[tb][v] - m_new);
+        const bf16 p = (bf16)fast_exp2(sacc[tb][v] - m_new);
         pk[v] = p;
         psum += (float)p;
       }

@@ -107,6 +107,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// 2^x by the hardware instruction (no denormal range fix-up): results below
+// 2^-126 come out as zero, which only drops softmax weights far below
+// anything a bf16 probability or a float32 sum can register.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Lane permutations within rows of 16 lanes (DPP, no LDS traffic; an LDS
 // permute would also make the compiler wait for in-flight direct-to-LDS
 // loads).  Controls: quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror,

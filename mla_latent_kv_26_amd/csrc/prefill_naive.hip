@@ -260,19 +260,25 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
       }
     }
     // register v of block kb <-> key key0 + 32 kb + 8 (v/4) + 4 hi + v%4, query lane%32
+    // causal mask, only where the tile reaches past the wave's first query
+    if (key0 + kFK - 1 > sp + qw0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * (int)hi + (v & 3);
+          if (key > pos) s[kb][v] = -INFINITY;
+        }
+    }
     float hmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * (int)hi + (v & 3);
-        if (key > pos) s[kb][v] = -INFINITY;
-        hmax = fmaxf(hmax, s[kb][v]);
-      }
+      for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, s[kb][v]);
     hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
     const bool grow = hmax > m + kFSlack;
     const float m_new = grow ? hmax : m;
-    const float alpha = grow ? exp2f(m - m_new) : 1.0f;
+    const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
     // P^T fragment of 16-key step ks: registers 8 (ks%2) .. + 7 of block ks/2
     float psum = 0.f;
     bf16x8 pr[kFK / 16];
@@ -280,7 +286,7 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const bf16 p = (bf16)exp2f(s[kb][v] - m_new);
+        const bf16 p = (bf16)fast_exp2(s[kb][v] - m_new);
         pr[2 * kb + (v >> 3)][v & 7] = p;
         psum += (float)p;
       }
