@@ -121,6 +121,44 @@ def prefill_main(args, torch, m):
     print(json.dumps(line), flush=True)
 
 
+def output_gate_main(args, torch, m):
+    """Time mla_output_gate_projection (gate GEMM with the sigmoid and the
+    head outputs fused into its epilogue, then W_O; MFMA-bound)."""
+    dev = torch.device("cuda", 0)
+    cfg = workloads.WORKLOADS[args.workload]
+    mc = m.MLAConfig.from_dict(cfg)
+    inp = workloads.output_gate_inputs_torch(cfg, cfg["seed"], dev)
+    n, M, HV = cfg["rows"], cfg["d_model"], cfg["num_heads"] * cfg["v_dim"]
+    ws = torch.zeros(m.mla_output_gate_workspace_size(mc, n), dtype=torch.uint8, device=dev)
+    out = torch.empty((n, M), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        m.mla_output_gate_projection(mc, inp["x"], inp["head_out"], inp["w_o"],
+                                     w_g=inp["w_g"] if cfg["gated"] else None, out=out,
+                                     workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = graph_time(torch, call, args.steps, torch.cuda.Stream())
+    flops = 2 * n * M * HV * (2 if cfg["gated"] else 1)
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "MLA output gate + W_O: TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": n, "d_model": M, "heads": cfg["num_heads"],
+                   "v_dim": cfg["v_dim"], "gated": cfg["gated"], "flops": flops,
+                   "timing": "hip graph replay, events on the launching stream"},
+        "roofline": {"kernel": "mla_output_gate_projection (gate GEMM + W_O GEMM)",
+                     "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_call": flops},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(cfg, seconds):
     """Time the oracle's decode (float64 numpy, as it stands) on whole steps of
     the same workload until about `seconds` of work; report TB/s of
@@ -228,6 +266,8 @@ def main():
     import mla_latent_kv_26_amd as m
     if "q_len" in workloads.WORKLOADS[args.workload]:
         return prefill_main(args, torch, m)
+    if "rows" in workloads.WORKLOADS[args.workload]:
+        return output_gate_main(args, torch, m)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

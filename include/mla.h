@@ -249,6 +249,28 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
                        int32_t q_len, void* out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ---- after the heads: optional output gate, then W_O ---------------------- */
+
+/* Workspace bytes for mla_output_gate_projection with n_rows rows (the gated
+ * head outputs, n_rows x H x Dv values of the storage dtype; 0 is enough
+ * without a gate).  Scratch only. */
+mla_status mla_output_gate_workspace_size(const mla_config* cfg, int32_t n_rows,
+                                          size_t* bytes /* host out */);
+
+/* The layer's attention contribution from its head outputs ("GatedMLA" docs,
+ * "Output projection and optional gate"): the heads' outputs, one row of
+ * H x Dv values per token, are multiplied elementwise by sigmoid(x W_G) when
+ * a gate is given (the gate reads the layer input x, not the attention
+ * result), then projected by W_O back to the model width.  No residual.
+ *   x [n_rows, M] (M = d_model > 0); head_out [n_rows, H, Dv] (as written by
+ *   mla_decode / mla_prefill); w_g [M, H Dv] or NULL (no gate);
+ *   w_o [H Dv, M]; out [n_rows, M] (written).
+ * bf16 needs M and H Dv multiples of 8.  The gated values are rounded to the
+ * storage dtype before W_O (they are staged in the workspace). */
+mla_status mla_output_gate_projection(const mla_config* cfg, const void* x, const void* head_out,
+                                      const void* w_g, const void* w_o, int32_t n_rows, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

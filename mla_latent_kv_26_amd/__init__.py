@@ -11,5 +11,6 @@ from .api import (  # noqa: F401
     mla_absorb_query, mla_latent_attention, mla_attention_partials, mla_combine_output,
     mla_output_projection,
     mla_cache_append_workspace_size, mla_cache_append, mla_prefill_workspace_size, mla_prefill,
+    mla_output_gate_workspace_size, mla_output_gate_projection,
 )
 from .pool import LatentKVPool  # noqa: F401

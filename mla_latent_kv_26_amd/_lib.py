@@ -85,6 +85,8 @@ SIGNATURES = {
     "mla_cache_append_workspace_size": (_I, [_CFG, _I, ctypes.POINTER(_SZ)]),
     "mla_cache_append": (_I, [_CFG, _P, _P, _FP, _FP, _I, _IP, _IP, _I, _P, _I, _P, _SZ, _P]),
     "mla_prefill_workspace_size": (_I, [_CFG, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "mla_output_gate_workspace_size": (_I, [_CFG, _I, ctypes.POINTER(_SZ)]),
+    "mla_output_gate_projection": (_I, [_CFG, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "mla_prefill": (_I, [_CFG, _P, _P, _P, _FP, _P, _P, _FP, _P, _P, _FP, _I, _P, _I, _IP, _I,
                          _IP, _I, _I, _I, _P, _P, _SZ, _P]),
 }

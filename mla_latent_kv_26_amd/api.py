@@ -144,6 +144,13 @@ def mla_cache_append_workspace_size(cfg: MLAConfig, n_tokens: int) -> int:
     return n.value
 
 
+def mla_output_gate_workspace_size(cfg: MLAConfig, n_rows: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib.mla_output_gate_workspace_size(_ref(cfg), n_rows, ctypes.byref(n)),
+          "mla_output_gate_workspace_size")
+    return n.value
+
+
 def mla_prefill_workspace_size(cfg: MLAConfig, batch: int, q_len: int, max_context: int = 0) -> int:
     n = ctypes.c_size_t()
     check(lib.mla_prefill_workspace_size(_ref(cfg), batch, q_len, max_context, ctypes.byref(n)),
@@ -341,4 +348,37 @@ def mla_prefill(cfg: MLAConfig, x, weights: dict, kv_pool, block_table, start_po
                           nb, block_table.data_ptr(), mb, start_pos.data_ptr(),
                           int(max_start_pos), B, T, out.data_ptr(), ws.data_ptr(), ws.numel(),
                           _stream(stream)), "mla_prefill")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# after the heads
+# ---------------------------------------------------------------------------
+def mla_output_gate_projection(cfg: MLAConfig, x, head_out, w_o, w_g=None, out=None,
+                               workspace=None, stream=None) -> torch.Tensor:
+    """out [n, M] = (head_out * sigmoid(x W_G)) W_O, or head_out W_O without a
+    gate (see mla_output_gate_projection in include/mla.h).  x [n, M];
+    head_out [n, H, Dv] (or [n, H*Dv]); w_g [M, H*Dv] or None; w_o [H*Dv, M]."""
+    dt = cfg.torch_dtype
+    n, M, HV = x.shape[0], cfg.d_model, cfg.num_heads * cfg.v_dim
+    _dev(x, "x", dt, (n, M))
+    _dev(head_out, "head_out", dt)
+    if head_out.numel() != n * HV:
+        raise ValueError(f"head_out must hold {n} x {HV} values")
+    _dev(w_o, "w_o", dt, (HV, M))
+    if w_g is not None:
+        _dev(w_g, "w_g", dt, (M, HV))
+    if out is None:
+        out = torch.empty((n, M), dtype=dt, device=x.device)
+    _dev(out, "out", dt, (n, M))
+    ws_ptr, ws_len = 0, 0
+    if w_g is not None:
+        need = mla_output_gate_workspace_size(cfg, n)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib.mla_output_gate_projection(_ref(cfg), x.data_ptr(), head_out.data_ptr(),
+                                         0 if w_g is None else w_g.data_ptr(), w_o.data_ptr(), n,
+                                         out.data_ptr(), ws_ptr, ws_len, _stream(stream)),
+          "mla_output_gate_projection")
     return out

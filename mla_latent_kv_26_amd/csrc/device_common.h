@@ -111,6 +111,10 @@ __device__ __forceinline__ void lds_barrier() {
 // 2^-126 come out as zero, which only drops softmax weights far below
 // anything a bf16 probability or a float32 sum can register.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// 1 / (1 + e^-x), saturating to 0 and 1 (2^x is +inf or 0 at the ends)
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return 1.0f / (1.0f + fast_exp2(-1.4426950408889634f * x));
+}
 
 // Lane permutations within rows of 16 lanes (DPP, no LDS traffic; an LDS
 // permute would also make the compiler wait for in-flight direct-to-LDS

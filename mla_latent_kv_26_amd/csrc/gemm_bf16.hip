@@ -32,6 +32,7 @@ struct Side {
   long ld, sb;
   bf16* dst;
   int cols;
+  const bf16* gmul;  // bf16 C only: C = gmul * sigmoid(alpha A B), gmul laid out as C
 };
 
 template <int BM, int kBK>
@@ -190,11 +191,14 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const bf16* __restrict__
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + (wm * C_::FM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < M) {
-          const float x = alpha * acc[i][j][v];
-          if constexpr (kOutF32)
-            ((float*)Cv)[blockIdx.z * sC + (long)row * ldc + col] = x;
-          else
-            ((bf16*)Cv)[blockIdx.z * sC + (long)row * ldc + col] = (bf16)x;
+          const long ci = blockIdx.z * sC + (long)row * ldc + col;
+          float x = alpha * acc[i][j][v];
+          if constexpr (kOutF32) {
+            ((float*)Cv)[ci] = x;
+          } else {
+            if (side.gmul) x = (float)side.gmul[ci] * sigmoid_f(x);
+            ((bf16*)Cv)[ci] = (bf16)x;
+          }
         }
       }
     }
@@ -241,7 +245,7 @@ void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K
     launch_gemm_tile256(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, false, st);
     return;
   }
-  const Side side{(const bf16*)side_src, side_ld, side_sb, (bf16*)side_dst, side_cols};
+  const Side side{(const bf16*)side_src, side_ld, side_sb, (bf16*)side_dst, side_cols, nullptr};
   if (K <= 128)
     launch_bk<128, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
                           st);
@@ -258,13 +262,28 @@ void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, i
     launch_gemm_tile256(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, true, st);
     return;
   }
-  const Side side{nullptr, 0, 0, nullptr, 0};
+  const Side side{nullptr, 0, 0, nullptr, 0, nullptr};
   if (K <= 128)
     launch_bk<128, true>(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
                          st);
   else
     launch_bk<32, true>(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, side,
                         st);
+}
+
+void launch_gemm_bf16_gated(const void* A, const void* B, void* C, int M, int N, int K, long lda,
+                            long ldb, long ldc, float alpha, const void* gmul, hipStream_t st) {
+  if (M <= 0 || N <= 0) return;
+  if (gemm_tile256_fits(M, N, K, lda, ldb, ldc)) {
+    launch_gemm_tile256(A, B, C, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, 0, false, st, 0, 0,
+                        gmul);
+    return;
+  }
+  const Side side{nullptr, 0, 0, nullptr, 0, (const bf16*)gmul};
+  if (K <= 128)
+    launch_bk<128, false>(A, B, C, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, 0, side, st);
+  else
+    launch_bk<32, false>(A, B, C, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, 0, side, st);
 }
 
 }  // namespace mla

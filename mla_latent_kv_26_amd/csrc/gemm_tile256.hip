@@ -78,7 +78,7 @@ template <int BN, bool kBT, bool kOutF32>
 __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* __restrict__ Cv, int M, int N,
     int K, long lda, long ldb, long ldc, long sA, long sB, long sC, int batch, int m_per,
-    float alpha, int nb, long sBn) {
+    float alpha, int nb, long sBn, const bf16* __restrict__ gmul) {
   using Cf = TileCfg<BN>;
   __shared__ __attribute__((aligned(16))) char smem[kTStages * Cf::STAGE];
   const uint32_t lds = lds_addr(smem);
@@ -287,10 +287,18 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
                            alpha * acc[i][jb][4 * q + 2], alpha * acc[i][jb][4 * q + 3]};
           *(f32x4*)((float*)Cv + z * sC + (long)m * ldc + n) = v;
         } else {
+          const long ci = z * sC + (long)m * ldc + n;
           bf16x4 v;
+          if (gmul) {  // gate: C = gmul * sigmoid(alpha A B)
+            const bf16x4 gv = *(const bf16x4*)(gmul + ci);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = (bf16)(alpha * acc[i][jb][4 * q + r]);
-          *(bf16x4*)((bf16*)Cv + z * sC + (long)m * ldc + n) = v;
+            for (int r = 0; r < 4; ++r)
+              v[r] = (bf16)((float)gv[r] * sigmoid_f(alpha * acc[i][jb][4 * q + r]));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (bf16)(alpha * acc[i][jb][4 * q + r]);
+          }
+          *(bf16x4*)((bf16*)Cv + ci) = v;
         }
       }
   }
@@ -299,7 +307,7 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
 template <int BN, bool kBT>
 void launch_tile(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
                  long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, int nb,
-                 long sBn, hipStream_t st) {
+                 long sBn, const void* gmul, hipStream_t st) {
   const int n_mt = (M + kTM - 1) / kTM, n_nt = (N + BN - 1) / BN;
   const int rows_total = n_mt * batch;
   const int m_per = (rows_total + 7) / 8;
@@ -307,11 +315,11 @@ void launch_tile(const void* A, const void* B, void* C, int M, int N, int K, lon
   if (c_f32)
     gemm_tile256_kernel<BN, kBT, true><<<grid, kTThreads, 0, st>>>(
         (const bf16*)A, (const bf16*)B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, m_per, alpha,
-        nb, sBn);
+        nb, sBn, (const bf16*)gmul);
   else
     gemm_tile256_kernel<BN, kBT, false><<<grid, kTThreads, 0, st>>>(
         (const bf16*)A, (const bf16*)B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, m_per, alpha,
-        nb, sBn);
+        nb, sBn, (const bf16*)gmul);
 }
 
 }  // namespace
@@ -324,7 +332,8 @@ bool gemm_tile256_fits(int M, int N, int K, long lda, long ldb, long ldc) {
 
 void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, int K, long lda,
                          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
-                         int c_f32, bool b_transposed, hipStream_t st, int nb, long sBn) {
+                         int c_f32, bool b_transposed, hipStream_t st, int nb, long sBn,
+                         const void* gmul) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
   if (nb <= 0) {
     nb = N;
@@ -334,17 +343,17 @@ void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, in
   if (b_transposed) {
     if (wide)
       launch_tile<256, true>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, nb,
-                             sBn, st);
+                             sBn, gmul, st);
     else
       launch_tile<128, true>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, nb,
-                             sBn, st);
+                             sBn, gmul, st);
   } else {
     if (wide)
       launch_tile<256, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, nb,
-                              sBn, st);
+                              sBn, gmul, st);
     else
       launch_tile<128, false>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, nb,
-                              sBn, st);
+                              sBn, gmul, st);
   }
 }
 

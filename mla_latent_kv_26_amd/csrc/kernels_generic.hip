@@ -40,6 +40,18 @@ void launch_gemm_f32(const float* A, const float* B, float* C, int M, int N, int
   gemm_f32_kernel<<<grid, 256, 0, st>>>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, alpha);
 }
 
+// g[i] = h[i] * sigmoid(g[i]) (the output gate, float32 storage).
+__global__ void __launch_bounds__(256) gate_mul_f32_kernel(float* __restrict__ g,
+                                                           const float* __restrict__ h, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) g[i] = h[i] * (1.0f / (1.0f + expf(-g[i])));
+}
+
+void launch_gate_mul_f32(float* g, const float* h, long n, hipStream_t st) {
+  if (n <= 0) return;
+  gate_mul_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, h, n);
+}
+
 // ---------------------------------------------------------------------------
 // Block-wide sum over 256 threads.
 // ---------------------------------------------------------------------------

@@ -52,6 +52,9 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
                           const int* start_pos, int T, float* o_lat, int n, int H, int R, int Dr,
                           hipStream_t st);
 
+// g[i] = h[i] * sigmoid(g[i]) for i < n (float32 output gate).
+void launch_gate_mul_f32(float* g, const float* h, long n, hipStream_t st);
+
 // ---- bf16 MFMA kernels (gfx950) ----
 
 // C[b] = alpha * A[b] * B[b]; A, B bf16 row-major; C bf16 (c_f32 == 0) or
@@ -68,7 +71,12 @@ bool gemm_tile256_fits(int M, int N, int K, long lda, long ldb, long ldc);
 // (nb a multiple of 8); nb <= 0 means one plain [K, N] matrix.
 void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, int K, long lda,
                          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
-                         int c_f32, bool b_transposed, hipStream_t st, int nb = 0, long sBn = 0);
+                         int c_f32, bool b_transposed, hipStream_t st, int nb = 0, long sBn = 0,
+                         const void* gmul = nullptr);
+// Gated GEMM (bf16 out, batch 1): C = gmul * sigmoid(alpha A B), gmul [M, N]
+// laid out as C (row stride ldc).
+void launch_gemm_bf16_gated(const void* A, const void* B, void* C, int M, int N, int K, long lda,
+                            long ldb, long ldc, float alpha, const void* gmul, hipStream_t st);
 
 // As launch_gemm_bf16 with B given transposed: Bt[b] is [N, K] row-major
 // (row stride ldb), C[b] = alpha * A[b] * Bt[b]^T.

@@ -526,6 +526,56 @@ mla_status mla_output_projection(const mla_config* cfg, const void* o_lat, const
 }
 
 // ---------------------------------------------------------------------------
+mla_status mla_output_gate_workspace_size(const mla_config* cfg, int32_t n_rows, size_t* bytes) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (n_rows <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be positive (got %d)", n_rows);
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = up256((size_t)n_rows * d.H * d.Dv * d.esz);
+  return MLA_OK;
+}
+
+mla_status mla_output_gate_projection(const mla_config* cfg, const void* x, const void* head_out,
+                                      const void* w_g, const void* w_o, int32_t n_rows, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (d.M <= 0) return fail(MLA_ERR_INVALID_ARG, "the output projection needs d_model > 0");
+  if (n_rows <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be positive (got %d)", n_rows);
+  s = check_ptrs16(d, {x, head_out, w_o, out}, "x, head_out, w_o, out");
+  if (s != MLA_OK) return s;
+  const int HV = d.H * d.Dv;
+  if (d.dt == MLA_DTYPE_BF16 && (d.M % 8 || HV % 8))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 output projection needs d_model and H*v_dim multiples of 8");
+  hipStream_t st = (hipStream_t)stream;
+  const void* src = head_out;
+  if (w_g) {
+    s = check_ptrs16(d, {w_g}, "w_g");
+    if (s != MLA_OK) return s;
+    const size_t need = up256((size_t)n_rows * HV * d.esz);
+    if (!workspace || workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                  workspace ? "" : ", NULL");
+    if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (d.dt == MLA_DTYPE_BF16) {
+      mla::launch_gemm_bf16_gated(x, w_g, workspace, n_rows, HV, d.M, d.M, HV, HV, 1.0f, head_out,
+                                  st);
+    } else {
+      mla::launch_gemm_f32((const float*)x, (const float*)w_g, (float*)workspace, n_rows, HV, d.M,
+                           d.M, HV, HV, 0, 0, 0, 1, 1.0f, st);
+      mla::launch_gate_mul_f32((float*)workspace, (const float*)head_out, (long)n_rows * HV, st);
+    }
+    src = workspace;
+  }
+  gemm(d, src, w_o, out, n_rows, d.M, HV, HV, d.M, d.M, 0, 0, 0, 1, 1.0f, false, st);
+  return launched("mla_output_gate_projection");
+}
+
+// ---------------------------------------------------------------------------
 mla_status mla_cache_append_workspace_size(const mla_config* cfg, int32_t n_tokens, size_t* bytes) {
   Dims d;
   g_err.clear();

@@ -22,7 +22,7 @@ Sources (cited in each function by page title and section):
   * "GatedMLA" docs: projection geometry, per-head Q/K/V with the shared key
     broadcast, causal SDPA scaled over the full Q/K width (Projection
     geometry and stored weights; Build per-head Q, K and V; Observe logits,
-    then compute causal attention).
+    then compute causal attention; Output projection and optional gate).
 
 Readings where the pages are silent (each one is also listed in the design doc):
   RoPE pairs element i with i + Dr/2 (half split), frequency theta^(-2i/Dr),

@@ -16,7 +16,7 @@ __all__ = [
     "latent_attention", "project_output", "absorbed_attention",
     "chunk_partials", "merge_partials", "gather_sequence", "decode",
     "append_rows", "attend_tokens", "layer_forward", "incremental_decode",
-    "softmax_scale", "DEFAULT_EPS", "DEFAULT_THETA",
+    "softmax_scale", "DEFAULT_EPS", "DEFAULT_THETA", "sigmoid", "output_gate_projection",
 ]
 
 DEFAULT_EPS = 1e-6
@@ -407,3 +407,24 @@ def incremental_decode(x, weights, cfg, storage: str = "f64", path: str = "absor
         rows = np.concatenate([rows, new], axis=0)
         outs.append(o)
     return np.concatenate(outs, axis=0)
+
+
+def sigmoid(z, wd=np.float64):
+    """The logistic function 1 / (1 + e^-z), the output gate's squashing."""
+    z = np.asarray(z, dtype=wd)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def output_gate_projection(head_out, x, w_o, w_g=None, wd=np.float64):
+    """The layer's attention contribution from its head outputs ("GatedMLA"
+    docs, "Output projection and optional gate"): the head outputs are laid
+    side by side as one row of H*Dv values per token; with a gate they are
+    multiplied elementwise by sigmoid(x W_G), where x is the layer input (not
+    the attention result); then W_O maps them back to the model width.  No
+    residual is added.  head_out [n, H, Dv] or [n, H*Dv]; x [n, M];
+    w_g [M, H*Dv] or None; w_o [H*Dv, M].  Returns [n, M]."""
+    h = np.asarray(head_out, dtype=wd)
+    h = h.reshape(h.shape[0], -1)
+    if w_g is not None:
+        h = h * sigmoid(np.asarray(x, dtype=wd) @ np.asarray(w_g, dtype=wd), wd)
+    return h @ np.asarray(w_o, dtype=wd)

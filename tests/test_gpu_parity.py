@@ -421,3 +421,54 @@ def test_prefill_d7168_b2_t4096_full(m):
         got = to_host_f64(out[b, sample])
         e = assert_bf16(got, ref, f"prefill b={b}", per_row_axis=0)
         print("prefill_d7168_b2_t4096", b, e)
+
+
+# ---------------------------------------------------------------------------
+# output gate and W_O ("GatedMLA" docs, "Output projection and optional gate")
+# ---------------------------------------------------------------------------
+def gate_inputs(cfg, n, seed):
+    M, HV = cfg["d_model"], cfg["num_heads"] * cfg["v_dim"]
+    dt = cfg["dtype"]
+    return (workloads.normal_tensor((n, M), seed, dt),
+            workloads.normal_tensor((n, cfg["num_heads"], cfg["v_dim"]), seed + 1, dt),
+            workloads.normal_tensor((M, HV), seed + 2, dt, std=1.0 / np.sqrt(M)),
+            workloads.normal_tensor((HV, M), seed + 3, dt, std=1.0 / np.sqrt(HV)))
+
+
+def run_gate(m, cfg, n, seed, gated):
+    mc = m.MLAConfig.from_dict(cfg)
+    x, h, w_g, w_o = gate_inputs(cfg, n, seed)
+    got = m.mla_output_gate_projection(mc, to_dev(x), to_dev(h), to_dev(w_o),
+                                       w_g=to_dev(w_g) if gated else None)
+    sync()
+    ref = oracle.output_gate_projection(to_f64(h), to_f64(x), to_f64(w_o),
+                                        to_f64(w_g) if gated else None)
+    return to_host_f64(got), ref
+
+
+def test_output_gate_tiny_fp32(m):
+    """float32, d_model 64, 4 heads of 16: with and without the gate."""
+    cfg = workloads.WORKLOADS["tiny_fp32"]
+    for gated in (True, False):
+        got, ref = run_gate(m, cfg, 65, 71, gated)
+        assert_f32(got, ref, f"gate={gated}")
+
+
+def test_output_gate_bf16_decode_rows(m):
+    """bf16, d_model 7168, 64 heads of 128 (the prefill workload's widths), 32
+    rows as in a decode step: the small-row GEMM with the gate fused into its
+    epilogue, then W_O."""
+    cfg = workloads.WORKLOADS["prefill_d7168_b2_t4096"]
+    for gated in (True, False):
+        got, ref = run_gate(m, cfg, 32, 81, gated)
+        assert_bf16(got, ref, f"gate={gated}", per_row_axis=0)
+
+
+def test_output_gate_bf16_many_rows(m):
+    """bf16, 600 rows (the 256-row tile GEMM, ragged last row tile), d_model
+    1024, 16 heads of 128."""
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=1024, q_lora_rank=0,
+               num_heads=16)
+    for gated in (True, False):
+        got, ref = run_gate(m, cfg, 600, 91, gated)
+        assert_bf16(got, ref, f"gate={gated}", per_row_axis=0)

@@ -425,6 +425,64 @@ def test_decode_of_token_64_uses_stored_rows():
 
 
 # ===========================================================================
+# 4b. Output gate and W_O ("GatedMLA" docs, "Output projection and optional
+#     gate"): sigmoid closed forms, brute-force loops, invariants
+# ===========================================================================
+def test_sigmoid_closed_forms():
+    assert oracle.sigmoid(0.0) == 0.5
+    assert abs(oracle.sigmoid(math.log(3.0)) - 0.75) < 1e-15          # 1 / (1 + 1/3)
+    z = rng(60).standard_normal(50) * 4
+    assert np.max(np.abs(oracle.sigmoid(z) + oracle.sigmoid(-z) - 1.0)) < 1e-15
+
+
+def brute_gate_projection(h, x, w_o, w_g):
+    """out[i][m] = sum_j h[i][j] * gate[i][j] * w_o[j][m], gate = 1 / (1 + e^-(x w_g)),
+    with plain loops (gate 1 without w_g)."""
+    n, HV, M = len(h), len(w_o), len(w_o[0])
+    out = [[0.0] * M for _ in range(n)]
+    for i in range(n):
+        for j in range(HV):
+            g = 1.0
+            if w_g is not None:
+                z = sum(x[i][k] * w_g[k][j] for k in range(len(x[i])))
+                g = 1.0 / (1.0 + math.exp(-z))
+            for m in range(M):
+                out[i][m] += h[i][j] * g * w_o[j][m]
+    return np.array(out)
+
+
+def gate_case(seed, n=3, H=2, Dv=3, M=5):
+    r = rng(seed)
+    return (r.standard_normal((n, H, Dv)), r.standard_normal((n, M)),
+            r.standard_normal((H * Dv, M)), r.standard_normal((M, H * Dv)))
+
+
+def test_output_gate_projection_brute_force():
+    h, x, w_o, w_g = gate_case(61)
+    hf = h.reshape(h.shape[0], -1)
+    for g in (w_g, None):
+        got = oracle.output_gate_projection(h, x, w_o, g)
+        ref = brute_gate_projection(hf.tolist(), x.tolist(), w_o.tolist(),
+                                    None if g is None else g.tolist())
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_output_gate_invariants():
+    h, x, w_o, w_g = gate_case(62)
+    plain = oracle.output_gate_projection(h, x, w_o)
+    # W_G = 0: sigmoid(0) = 1/2 on every value
+    half = oracle.output_gate_projection(h, x, w_o, np.zeros_like(w_g))
+    assert np.max(np.abs(half - 0.5 * plain)) < 1e-12
+    # the gate reads x only: linear in the head outputs for a fixed x
+    a = oracle.output_gate_projection(h, x, w_o, w_g)
+    b = oracle.output_gate_projection(2.0 * h, x, w_o, w_g)
+    assert np.max(np.abs(b - 2.0 * a)) < 1e-12
+    # ... and it does depend on x
+    c = oracle.output_gate_projection(h, x + 1.0, w_o, w_g)
+    assert np.max(np.abs(c - a)) > 1e-3
+
+
+# ===========================================================================
 # 5. Planted mistakes: a wrong oracle fails the pins above
 # ===========================================================================
 def test_planted_wrong_scale_is_caught():
@@ -492,3 +550,34 @@ def test_planted_norm_over_whole_row_is_caught(monkeypatch):
     _, brows = brute_layer(x.tolist(), w, cfg, 0, [], False)
     assert np.max(np.abs(rows - brows)) > 1e-3
     monkeypatch.setattr(oracle.mla_oracle, "kv_latent_rows", real)
+
+
+def test_planted_gate_from_attention_result_is_caught():
+    h, x, w_o, w_g = gate_case(63, M=6)   # M = H*Dv so h W_G type-checks
+
+    def wrong(h, x, w_o, w_g):
+        hf = h.reshape(h.shape[0], -1)
+        return (hf * oracle.sigmoid(hf @ w_g)) @ w_o
+    ref = brute_gate_projection(h.reshape(3, -1).tolist(), x.tolist(), w_o.tolist(), w_g.tolist())
+    assert np.max(np.abs(wrong(h, x, w_o, w_g) - ref)) > 1e-3
+    a, b = wrong(h, x, w_o, w_g), wrong(2.0 * h, x, w_o, w_g)
+    assert np.max(np.abs(b - 2.0 * a)) > 1e-3           # breaks the linearity pin
+
+
+def test_planted_gate_after_projection_is_caught():
+    h, x, w_o, w_g = gate_case(64, M=6)
+
+    def wrong(h, x, w_o, w_g):
+        return (h.reshape(h.shape[0], -1) @ w_o) * oracle.sigmoid(x @ w_g)
+    ref = brute_gate_projection(h.reshape(3, -1).tolist(), x.tolist(), w_o.tolist(), w_g.tolist())
+    assert np.max(np.abs(wrong(h, x, w_o, w_g) - ref)) > 1e-3
+
+
+def test_planted_missing_sigmoid_is_caught():
+    h, x, w_o, w_g = gate_case(65)
+
+    def wrong(h, x, w_o, w_g):
+        return (h.reshape(h.shape[0], -1) * (x @ w_g)) @ w_o
+    plain = oracle.output_gate_projection(h, x, w_o)
+    half = wrong(h, x, w_o, np.zeros_like(w_g))
+    assert np.max(np.abs(half - 0.5 * plain)) > 1e-3    # the W_G = 0 pin fails

@@ -52,6 +52,12 @@ WORKLOADS: Dict[str, dict] = {
         d_model=7168, q_lora_rank=1536, kv_lora_rank=512, rope_dim=64,
         num_heads=64, qk_nope_dim=128, v_dim=128, batch=2, q_len=4096,
         block_size=64, dtype="bf16", rope_theta=10000.0, seed=5),
+    # The output gate and W_O after the heads, at the prefill workload's widths
+    # and token count (2 x 4096 rows).
+    "output_gate_d7168_t8192": dict(
+        d_model=7168, q_lora_rank=0, kv_lora_rank=512, rope_dim=64, num_heads=64,
+        qk_nope_dim=128, v_dim=128, rows=8192, gated=True, block_size=64, dtype="bf16",
+        seed=6),
 }
 
 HEADLINE = "decode_h64_b32_l4096"
@@ -317,3 +323,22 @@ def prefill_inputs_torch(cfg: dict, seed: int, device):
                 pool=torch.zeros((nblocks, bs, R + Dr), dtype=dt, device=device),
                 block_table=torch.from_numpy(table).to(device),
                 start_pos=torch.zeros(B, dtype=torch.int32, device=device))
+
+
+def output_gate_inputs_torch(cfg: dict, seed: int, device):
+    """x [rows, M], head outputs [rows, H, Dv] ~ N(0,1); W_G [M, H Dv] ~
+    N(0, 1/M), W_O [H Dv, M] ~ N(0, 1/(H Dv)); drawn on the device."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    n, M, H, Dv = cfg["rows"], cfg["d_model"], cfg["num_heads"], cfg["v_dim"]
+
+    def draw(shape, std=1.0):
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return t.to(torch.bfloat16)
+
+    return dict(x=draw((n, M)), head_out=draw((n, H, Dv)),
+                w_g=draw((M, H * Dv), 1.0 / math.sqrt(M)),
+                w_o=draw((H * Dv, M), 1.0 / math.sqrt(H * Dv)))
