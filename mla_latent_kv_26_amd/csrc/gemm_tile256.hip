@@ -1,12 +1,28 @@
 // Large bf16 GEMM on MFMA (gfx950): C[z] = alpha * A[z] * B[z] (or A Bt^T),
-// float32 accumulate, bf16 or float32 output.  For the prefill projections
-// and the per-head key/value reconstruction (M in the thousands, N >= 128,
-// K a multiple of 32).
+// float32 accumulate, bf16 or float32 output.  For the prefill projections,
+// the per-head key/value reconstruction and the output projections (M in the
+// thousands, N >= 128, K a multiple of 32).
 //
-// Tile 256 x BN x 32 (BN = 256 or 128) per 512-thread workgroup, 8 waves as
-// 2 (M) x 4 (N), each wave 128 x BN/4 with 32x32x16 MFMAs.  Tiles move
-// HBM/L2 -> LDS with direct-to-LDS loads into four stages, three in flight
-// while one is multiplied; one LDS-only barrier per stage.
+// Tile 256 x BN x 32 (BN = 256 or 128) per 256-thread workgroup: 4 waves as
+// 2 (M) x 2 (N), one per SIMD, each wave 128 x BN/2 with 32x32x16 MFMAs
+// (the accumulators, 128 or 256 registers, live in AGPRs).  Operand tiles
+// move HBM/L2 -> LDS with direct-to-LDS loads into four stages.
+//
+// One wave per SIMD means nothing hides a stall of the MFMA pipe but the
+// wave's own instruction order, so each half step (16 of the stage's 32 k,
+// 16 or 8 MFMAs per wave) carries, between its MFMAs, the LDS fragment
+// reads of the next half step and, after the stage barrier, the
+// direct-to-LDS loads of the stage four ahead.  The reads sit in MFMA slots
+// 4..9 (they end several MFMAs before the wait for them, and the first
+// MFMAs of a half step never queue behind them), the loads in slots from a
+// quarter of the way on.  Measured on MI355X at 8192 x 8192 x 7168: 0.37
+// of the bf16 peak with each half step's reads issued as one block ahead
+// of its MFMAs (8 waves, two per SIMD), 0.49 interleaved like this.
+//
+// Stage lifetime: stage s is read during iteration s - 1 (its first half
+// step) and iteration s (its second); the barrier after the second read has
+// completed in every wave frees its buffer, which then receives stage s + 4.
+// So all four buffers hold loads in flight or landed data at once.
 //
 // LDS layouts (16-byte chunks, chosen by which global chunk each lane
 // loads, so the direct-to-LDS write pattern stays linear):
@@ -16,6 +32,9 @@
 //            the 4 rows x 64 bytes of a transposing read fall on 4 distinct
 //            quarters of a bank window.
 //   Bt stage [BN n][32 k] (B given transposed): as A.
+// Fragment reads are issued from inline assembly and completed by a
+// separate wait that names their registers: reads the compiler issues
+// itself make it wait for every direct-to-LDS load in flight first.
 // The accumulators hold C transposed (the MFMA takes the B fragment as its
 // first operand): a lane owns one row of C and runs of 4 columns, so the
 // epilogue writes 16-byte (float32) or 8-byte (bf16) vectors.
@@ -25,32 +44,37 @@
 // all column tiles with the row tile fastest, so the workgroups resident on
 // one XCD share their B column tiles in its L2 and each A row tile stays in
 // L2 while the columns pass.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
 namespace {
 
-constexpr int kTM = 256, kTK = 32, kTStages = 4;
-constexpr int kTWavesN = 4;                    // waves along N (2 along M)
-constexpr int kTThreads = 128 * kTWavesN;
+constexpr int kTM = 256, kTK = 32, kTStages = 4, kTThreads = 256;
 constexpr int kTABytes = kTM * kTK * 2;  // 16 KB
 
 template <int BN>
 struct TileCfg {
-  static constexpr int WN = BN / kTWavesN;             // columns per wave
+  static constexpr int WN = BN / 2;                    // columns per wave
   static constexpr int FN = WN / 32;                   // 32-column blocks per wave
   static constexpr int B_BYTES = BN * kTK * 2;
   static constexpr int STAGE = kTABytes + B_BYTES;
   static constexpr int A_LOADS = kTM * kTK / 8 / kTThreads;  // 16-byte loads per thread
   static constexpr int B_LOADS = BN * kTK / 8 / kTThreads;
   static constexpr int LOADS = A_LOADS + B_LOADS;
+  static constexpr int T = 4 * FN;                     // MFMAs per wave per half step
+  // MFMA slots of a half step that carry the fragment reads: RO .. RO + RS - 1
+  static constexpr int RO = T >= 16 ? 4 : 2, RS = 6;
   static_assert(kTStages * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(RO + RS <= T, "read slots inside the half step");
 };
 
+// waits until at most `pending` later stages of this thread's loads are in flight
 template <int N>
 __device__ __forceinline__ void wait_stages(int pending) {
-  static_assert(kTStages <= 5, "up to three later stages in flight");
+  static_assert(kTStages <= 4 && 3 * N < 64, "vmcnt range");
   if (pending >= 3)
     wait_vmcnt<3 * N>();
   else if (pending == 2)
@@ -61,17 +85,65 @@ __device__ __forceinline__ void wait_stages(int pending) {
     wait_vmcnt<0>();
 }
 
-// Four transposing LDS reads, finished inside the asm block (see
-// lds_read_tr_x8).
-__device__ __forceinline__ void lds_read_tr_x4(const uint32_t (&a)[4], bf16x4 (&o)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+// Fragment reads without a wait: the data is valid after settle() below.
+template <int OFF>
+__device__ __forceinline__ void ds_b128_nowait(bf16x8& o, uint32_t a) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr_nowait(bf16x4& o, uint32_t a) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+// r selects the 32-row block (2048 bytes apart); a constant after unrolling
+__device__ __forceinline__ void read_blk(bf16x8& o, uint32_t a, int r) {
+  switch (r) {
+    case 0: ds_b128_nowait<0>(o, a); break;
+    case 1: ds_b128_nowait<2048>(o, a); break;
+    case 2: ds_b128_nowait<4096>(o, a); break;
+    default: ds_b128_nowait<6144>(o, a); break;
+  }
+}
+// sh = 2 s + h2: k moves by 16 s + 4 h2 rows of RB bytes
+template <int RB>
+__device__ __forceinline__ void read_tr(bf16x4& o, uint32_t a, int sh) {
+  switch (sh) {
+    case 0: ds_tr_nowait<0>(o, a); break;
+    case 1: ds_tr_nowait<4 * RB>(o, a); break;
+    case 2: ds_tr_nowait<16 * RB>(o, a); break;
+    default: ds_tr_nowait<20 * RB>(o, a); break;
+  }
+}
+
+// One half step's fragments: A blocks, and B blocks either as plain rows
+// (transposed B) or as two transposing halves (row-major B).
+template <int FN, bool BT>
+struct Frag {
+  bf16x8 a[4];
+  bf16x8 b[FN];
+  bf16x4 t[FN][2];
+};
+
+// Waits for this wave's LDS reads and hands their registers on as written
+// here, so no use of them is scheduled before the wait.
+template <int FN, bool BT>
+__device__ __forceinline__ void settle(Frag<FN, BT>& f) {
+  if constexpr (BT && FN == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
+                   "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
+  else if constexpr (BT)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
+                   "+v"(f.b[1]));
+  else if constexpr (FN == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.t[0][0]),
+                   "+v"(f.t[0][1]), "+v"(f.t[1][0]), "+v"(f.t[1][1]), "+v"(f.t[2][0]),
+                   "+v"(f.t[2][1]), "+v"(f.t[3][0]), "+v"(f.t[3][1]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.t[0][0]),
+                   "+v"(f.t[0][1]), "+v"(f.t[1][0]), "+v"(f.t[1][1]));
 }
 
 template <int BN, bool kBT, bool kOutF32>
@@ -80,6 +152,11 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
     int K, long lda, long ldb, long ldc, long sA, long sB, long sC, int batch, int m_per,
     float alpha, int nb, long sBn, const bf16* __restrict__ gmul) {
   using Cf = TileCfg<BN>;
+  constexpr int FN = Cf::FN, T = Cf::T, L = Cf::LOADS;
+  constexpr int NR = kBT ? 4 + FN : 4 + 2 * FN;  // fragment reads per half step
+  constexpr int RB = BN * 2;                     // bytes per k row of a row-major B stage
+  constexpr int kDOff = T / 4;                   // first MFMA slot carrying loads
+  constexpr int kROff = Cf::RO, kRSpan = Cf::RS;
   __shared__ __attribute__((aligned(16))) char smem[kTStages * Cf::STAGE];
   const uint32_t lds = lds_addr(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -119,165 +196,149 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
       b_src[i] = B + (long)(n / nb) * sBn + (long)k * ldb + n % nb;
     }
   }
-  auto issue = [&](int kt) {
+  // load q (0 .. L-1) of stage kt
+  auto issue_one = [&](int kt, int q) {
     const uint32_t st = lds + (uint32_t)(kt % kTStages) * Cf::STAGE;
-#pragma unroll
-    for (int i = 0; i < Cf::A_LOADS; ++i)
-      g2lds16(a_src[i] + (long)kt * kTK, st + (uint32_t)(wave * Cf::A_LOADS + i) * 1024u);
-#pragma unroll
-    for (int i = 0; i < Cf::B_LOADS; ++i) {
+    if (q < Cf::A_LOADS) {
+      g2lds16(a_src[q] + (long)kt * kTK, st + (uint32_t)(wave * Cf::A_LOADS + q) * 1024u);
+    } else {
+      const int i = q - Cf::A_LOADS;
       const long off = kBT ? (long)kt * kTK : (long)kt * kTK * ldb;
       g2lds16(b_src[i] + off, st + kTABytes + (uint32_t)(wave * Cf::B_LOADS + i) * 1024u);
     }
   };
 
-  const int wm = wave / kTWavesN, wn = wave % kTWavesN;
+  const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
-  // A fragment (m-block i, k-step s): row 128 wm + 32 i + l32, chunk 2 s + hi
-  uint32_t a_off[4][2];
+  // A fragment (block i, k step s): row 128 wm + 32 i + l32, chunk (2 s + hi)
+  // swizzled; blocks are 2048 bytes apart (the swizzle sees row bits 2..3 only)
+  uint32_t a_off[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int m = 128 * wm + 32 * i + l32;
-      a_off[i][s] = (uint32_t)(m * 64 + (((2 * s + hi) ^ ((m >> 2) & 3)) * 16));
-    }
-  // B fragment (n-block jb, k-step s): 32 columns at BN/4 wn + 32 jb
-  uint32_t b_off[Cf::FN][2][2];  // [jb][s][lo/hi] (transposing reads) or [jb][s][0] (rows)
+  for (int s = 0; s < 2; ++s) {
+    const int m = 128 * wm + l32;
+    a_off[s] = (uint32_t)(m * 64 + (((2 * s + hi) ^ ((m >> 2) & 3)) * 16));
+  }
+  // B fragment offsets.  Transposed B: as A, per k step.  Row-major B: one
+  // address per 32-column block jb (in a 16-lane group g, lane 4a + b reads
+  // row k0 + a, columns c0 + 4b .. +3); the k step s and the half h2 move k
+  // by 16 s + 4 h2, which keeps k & 3 and so the swizzle.
+  uint32_t b_off[kBT ? 2 : FN];
   {
     const int g = lane >> 4, li = lane & 15;
-#pragma unroll
-    for (int jb = 0; jb < Cf::FN; ++jb)
+    if constexpr (kBT) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        if constexpr (kBT) {
-          const int n = Cf::WN * wn + 32 * jb + l32;
-          b_off[jb][s][0] = (uint32_t)(n * 64 + (((2 * s + hi) ^ ((n >> 2) & 3)) * 16));
-          b_off[jb][s][1] = 0;
-        } else {
-          constexpr int RB = BN * 2;  // bytes per k row
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int k = 16 * s + 8 * (g >> 1) + (li >> 2) + 4 * h2;
-            const int col = Cf::WN * wn + 32 * jb + 16 * (g & 1) + 4 * (li & 3);
-            b_off[jb][s][h2] =
-                (uint32_t)(k * RB + (((col >> 3) ^ (4 * (k & 3))) * 16) + ((col >> 2) & 1) * 8);
-          }
-        }
+        const int n = Cf::WN * wn + l32;
+        b_off[s] = (uint32_t)(kTABytes + n * 64 + (((2 * s + hi) ^ ((n >> 2) & 3)) * 16));
       }
+    } else {
+#pragma unroll
+      for (int jb = 0; jb < FN; ++jb) {
+        const int k = 8 * (g >> 1) + (li >> 2);
+        const int col = Cf::WN * wn + 32 * jb + 16 * (g & 1) + 4 * (li & 3);
+        b_off[jb] = (uint32_t)(kTABytes + k * RB + (((col >> 3) ^ (4 * (k & 3))) * 16) +
+                               ((col >> 2) & 1) * 8);
+      }
+    }
   }
 
-  f32x16 acc[4][Cf::FN];
+  // read r (0 .. NR-1) of half step s of the stage at LDS address st
+  auto read_one = [&](uint32_t st, int s, int r, Frag<FN, kBT>& f) {
+    if (r < 4) {
+      read_blk(f.a[r], st + a_off[s], r);
+    } else if constexpr (kBT) {
+      read_blk(f.b[r - 4], st + b_off[s], r - 4);
+    } else {
+      const int jb = (r - 4) >> 1, h2 = (r - 4) & 1;
+      read_tr<RB>(f.t[jb][h2], st + b_off[jb], 2 * s + h2);
+    }
+  };
+
+  f32x16 acc[4][FN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jb = 0; jb < Cf::FN; ++jb) acc[i][jb] = f32x16{};
+    for (int jb = 0; jb < FN; ++jb) acc[i][jb] = f32x16{};
+
+  auto mfma_one = [&](const Frag<FN, kBT>& f, int e) {
+    const int i = e / FN, jb = e % FN;
+    if constexpr (kBT)
+      acc[i][jb] = mfma32(f.b[jb], f.a[i], acc[i][jb]);
+    else
+      acc[i][jb] = mfma32(cat(f.t[jb][0], f.t[jb][1]), f.a[i], acc[i][jb]);
+  };
 
   const int nk = K / kTK;
-  for (int kt = 0; kt < min(nk, kTStages - 1); ++kt) issue(kt);
-  if constexpr (kBT) {
-    // Both operands are read as rows (plain 16-byte LDS reads), so the
-    // fragments of each k-step are read during the previous k-step's MFMAs
-    // (two half-stage fragment sets, H0 for k 0..15 and H1 for 16..31 of a
-    // stage).  A fragment base is the same for every 32-row block (the row
-    // swizzle only looks at bits 2..3), so blocks differ by a constant.
-    struct Half {
-      bf16x8 a[4];
-      bf16x8 b[Cf::FN];
-    };
-    auto read_half = [&](int kt, int s, Half& h) {
-      const uint32_t st = lds + (uint32_t)(kt % kTStages) * Cf::STAGE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h.a[i] = lds_read_b128(st + a_off[0][s] + 2048u * i);
-#pragma unroll
-      for (int jb = 0; jb < Cf::FN; ++jb)
-        h.b[jb] = lds_read_b128(st + kTABytes + b_off[0][s][0] + 2048u * jb);
-    };
-    // hand fragments whose reads are known to be done on as plain values
-    auto settle = [](Half& h) {
-      asm volatile("" : "+v"(h.a[0]), "+v"(h.a[1]), "+v"(h.a[2]), "+v"(h.a[3]));
-#pragma unroll
-      for (int jb = 0; jb < Cf::FN; ++jb) asm volatile("" : "+v"(h.b[jb]));
-    };
-    auto mfma_half = [&](const Half& h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jb = 0; jb < Cf::FN; ++jb) acc[i][jb] = mfma32(h.b[jb], h.a[i], acc[i][jb]);
-    };
-    Half h0, h1;
-    wait_stages<Cf::LOADS>(min(nk - 1, kTStages - 2));
-    lds_barrier();
-    if (kTStages - 1 < nk) issue(kTStages - 1);
-    read_half(0, 0, h0);
-    for (int kt = 0; kt < nk; ++kt) {
-      settle(h0);
-      read_half(kt, 1, h1);
-      mfma_half(h0);
-      if (kt + 1 < nk) {
-        wait_stages<Cf::LOADS>(min(nk - 2 - kt, kTStages - 2));
-        lds_barrier();  // also retires h1's reads
-        settle(h1);
-        if (kt + kTStages < nk) issue(kt + kTStages);
-        read_half(kt + 1, 0, h0);
-      } else {
-        settle(h1);
-      }
-      mfma_half(h1);
-    }
-  } else
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stages<Cf::LOADS>(min(nk - 1 - kt, kTStages - 2));
-    lds_barrier();
-    if (kt + kTStages - 1 < nk) issue(kt + kTStages - 1);
+  Frag<FN, kBT> f0, f1;
+  // Iteration kt: half step (kt, 0) on f0 while f1 = (kt, 1) is read; the
+  // barrier that publishes stage kt + 1 (and frees stage kt's buffer); half
+  // step (kt, 1) on f1 while f0 = (kt + 1, 0) is read and stage kt + 4 is
+  // loaded into kt's buffer.
+  auto body = [&](int kt, auto load_c, auto next_c) {
+    constexpr bool LOAD = decltype(load_c)::value;  // stage kt + 4 exists
+    constexpr bool NEXT = decltype(next_c)::value;  // stage kt + 1 exists
     const uint32_t st = lds + (uint32_t)(kt % kTStages) * Cf::STAGE;
-    // every fragment of the stage in flight at once (the transposing reads
-    // end with a wait that also covers the A reads issued before them)
-    bf16x8 af[2][4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int e = 0; e < T; ++e) {
+      mfma_one(f0, e);
+      __builtin_amdgcn_sched_barrier(0);
+      if (e >= kROff && e < kROff + kRSpan) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[s][i] = lds_read_b128(st + a_off[i][s]);
-    bf16x8 bf[Cf::FN][2];
-    if constexpr (Cf::FN % 2 == 0) {
-      // reads q = 8 g + r: block 2 g + r / 4, k-step (r / 2) % 2, half r % 2
-#pragma unroll
-      for (int g8 = 0; g8 < Cf::FN / 2; ++g8) {
-        uint32_t ta[8];
-        bf16x4 t[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          ta[r] = st + kTABytes + b_off[2 * g8 + (r >> 2)][(r >> 1) & 1][r & 1];
-        lds_read_tr_x8<0>(ta, t);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bf[2 * g8 + (r >> 1)][r & 1] = cat(t[2 * r], t[2 * r + 1]);
+        for (int r = (e - kROff) * NR / kRSpan; r < (e - kROff + 1) * NR / kRSpan; ++r)
+          read_one(st, 1, r, f1);
       }
-    } else {
-      uint32_t ta[4];
-      bf16x4 t[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ta[q] = st + kTABytes + b_off[0][q >> 1][q & 1];
-      lds_read_tr_x4(ta, t);
-      bf[0][0] = cat(t[0], t[1]);
-      bf[0][1] = cat(t[2], t[3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    settle(f1);
+    if constexpr (NEXT) {
+      wait_stages<L>(min(nk - 2 - kt, kTStages - 2));
+      lds_barrier();
+    }
+    const uint32_t sn = lds + (uint32_t)((kt + 1) % kTStages) * Cf::STAGE;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int e = 0; e < T; ++e) {
+      mfma_one(f1, e);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NEXT) {
+        if (e >= kROff && e < kROff + kRSpan) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int r = (e - kROff) * NR / kRSpan; r < (e - kROff + 1) * NR / kRSpan; ++r)
+            read_one(sn, 0, r, f0);
+        }
+      }
+      if constexpr (LOAD) {
+        if (e >= kDOff) {
 #pragma unroll
-        for (int jb = 0; jb < Cf::FN; ++jb) acc[i][jb] = mfma32(bf[jb][s], af[s][i], acc[i][jb]);
-  }
+          for (int q = (e - kDOff) * L / (T - kDOff); q < (e - kDOff + 1) * L / (T - kDOff); ++q)
+            issue_one(kt + kTStages, q);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) settle(f0);
+  };
 
-  // register v of acc[i][jb]: column (BN/4) wn + 32 jb + 8 (v/4) + 4 (lane/32) + v%4,
+  for (int kt = 0; kt < min(nk, kTStages); ++kt)
+#pragma unroll
+    for (int q = 0; q < L; ++q) issue_one(kt, q);
+  wait_stages<L>(min(nk - 1, kTStages - 1));
+  lds_barrier();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read_one(lds, 0, r, f0);
+  settle(f0);
+  int kt = 0;
+  for (; kt + kTStages < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
+  for (; kt + 1 < nk; ++kt) body(kt, std::false_type{}, std::true_type{});
+  body(kt, std::false_type{}, std::false_type{});
+
+  // register v of acc[i][jb]: column (BN/2) wn + 32 jb + 8 (v/4) + 4 (lane/32) + v%4,
   // row 128 wm + 32 i + lane%32
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 128 * wm + 32 * i + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int jb = 0; jb < Cf::FN; ++jb)
+    for (int jb = 0; jb < FN; ++jb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + Cf::WN * wn + 32 * jb + 8 * q + 4 * hi;
