@@ -65,6 +65,32 @@ __device__ __forceinline__ void lds_read_tr_x8(const uint32_t (&a)[8], bf16x4 (&
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
         "i"(OFF));
 }
+// LDS reads without a wait, for reads kept in flight across other work: the
+// result registers are valid only after an lds_settle that names them (the
+// compiler treats an asm output as written when the asm ends, so nothing
+// may read or copy them before that wait).  The compiler's own LDS reads
+// would make it wait for every direct-to-LDS load in flight first.
+template <int OFF>
+__device__ __forceinline__ void ds_b128_nowait(bf16x8& o, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr_nowait(bf16x4& o, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+// Waits until at most N LDS operations of this wave are outstanding (they
+// complete in issue order) and hands the named registers on as written here.
+template <int N, typename T>
+__device__ __forceinline__ void lds_settle(T& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void lds_settle(T& x, T& y) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
+}
+
 __device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -127,6 +153,20 @@ __device__ __forceinline__ float dpp_f32(float v) {
 }
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// max / sum of v over lanes l and l ^ 32 (both lanes get the same bits):
+// one permlane32 swap, no LDS traffic.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  // the two registers hold x[l] and x[l ^ 32] in either order; a sum of two
+  // is the same bits in either order
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 // Reductions over the 64 lanes; every lane gets the same value (each step
 // combines a pair of lanes with a commutative operation, so both members of

@@ -85,15 +85,7 @@ __device__ __forceinline__ void wait_stages(int pending) {
     wait_vmcnt<0>();
 }
 
-// Fragment reads without a wait: the data is valid after settle() below.
-template <int OFF>
-__device__ __forceinline__ void ds_b128_nowait(bf16x8& o, uint32_t a) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
-}
-template <int OFF>
-__device__ __forceinline__ void ds_tr_nowait(bf16x4& o, uint32_t a) {
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
-}
+// Fragment reads (ds_*_nowait) are valid after settle() below.
 // r selects the 32-row block (2048 bytes apart); a constant after unrolling
 __device__ __forceinline__ void read_blk(bf16x8& o, uint32_t a, int r) {
   switch (r) {

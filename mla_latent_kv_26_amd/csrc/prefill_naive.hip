@@ -29,24 +29,27 @@
 namespace mla {
 namespace {
 
-constexpr int kFW = 8;                        // waves per workgroup
+constexpr int kQH = 1;                        // 32-query halves per wave
+constexpr int kQW = 32 * kQH;                 // queries per wave
+constexpr int kFW = 8 / kQH;                  // waves per workgroup
 constexpr int kFThreads = 64 * kFW;
-constexpr int kFQ = 32 * kFW;                 // queries per workgroup
+constexpr int kFQ = kQW * kFW;                // queries per workgroup
 constexpr int kFK = 64;                       // keys per tile
 constexpr int kNDn = 128, kNDr = 64, kNDk = kNDn + kNDr, kNDv = 128;
+constexpr int kKS = kNDk / 16;                // 12 k steps of S^T
 constexpr int kKCh = kNDk * 2 / 16;           // 24 chunks per K row (384 B)
 constexpr int kVCh = kNDv * 2 / 16;           // 16 chunks per V row (256 B)
 constexpr int kKBytes = kFK * kNDk * 2;       // 24576
 constexpr int kVBytes = kFK * kNDv * 2;       // 16384
 constexpr int kTBytes = kKBytes + kVBytes;    // 40960
-constexpr int kFBuf = 4;                      // tile buffers; three tiles in flight
+constexpr int kFBuf = 4;                      // tile buffers
 constexpr int kTLoads = kTBytes / 1024;       // 40 one-KB load instructions per tile
-constexpr int kWLoads = kTLoads / kFW;        // 5 per wave
+constexpr int kWLoads = kTLoads / kFW;        // 10 per wave
 static_assert(kWLoads * kFW == kTLoads, "tile loads split evenly");
 constexpr int kFLds = kFBuf * kTBytes;
 static_assert(kFLds <= 163840, "LDS budget");
 constexpr int kFSStride = kNDv + 8;           // bf16 per staged output row
-static_assert(kFW * 32 * kFSStride * 2 <= kFBuf * kTBytes, "output staging fits the tile buffers");
+static_assert(kFW * kQW * kFSStride * 2 <= kFLds, "output staging fits the tile buffers");
 constexpr float kFSlack = 8.0f;               // lazy rescale threshold (log2 units)
 
 // The LDS serves a 16-byte read 16 lanes (256 bytes) at a time and an
@@ -61,15 +64,17 @@ __device__ __forceinline__ uint32_t v_pos(uint32_t t, uint32_t k) { return k ^ (
 
 // This wave's share of one tile's loads: instruction j fills slots
 // [64 j, 64 j + 64); slots [0, 1536) are K (row t = s / 24), the rest V.
-// Each lane's source pointer for the first tile and its row stride are set
-// up once; issuing a tile advances them by 64 rows.  Keys past a sequence's
-// length are zero rows of the buffers, so every address is in bounds.
+// Each lane's source pointer for the first tile is set up once; issuing a
+// tile advances it by 64 rows, of the latent rows (rope chunks, bit i of
+// `rope`) or of the per-head rows.  Keys past a sequence's length are zero
+// rows of the buffers, so every address is in bounds.
 struct KvSource {
   const bf16* p[kWLoads];
-  uint32_t stride[kWLoads];  // elements per key row
+  uint32_t rope;  // bit i: load i reads the rope key from the latent rows
 
   __device__ __forceinline__ void setup(const bf16* kn, const bf16* cg, const bf16* vv, long row0,
                                         int H, int h, int wave, int lane) {
+    rope = 0;
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i) {
       const uint32_t j = (uint32_t)(wave * kWLoads + i);
@@ -79,25 +84,24 @@ struct KvSource {
         const long r = row0 + t;
         if (k < 16) {
           p[i] = kn + (r * H + h) * kNDn + k * 8;
-          stride[i] = (uint32_t)H * kNDn;
         } else {
           p[i] = cg + r * 576 + 512 + (k - 16) * 8;
-          stride[i] = 576;
+          rope |= 1u << i;
         }
       } else {
         const uint32_t sv = s - kFK * kKCh;
         const uint32_t t = sv / kVCh, k = v_pos(t, sv % kVCh);
         p[i] = vv + ((row0 + t) * H + h) * kNDv + k * 8;
-        stride[i] = (uint32_t)H * kNDv;
       }
     }
   }
-  // issue the next tile into `buf`
-  __device__ __forceinline__ void issue(uint32_t buf, int wave) {
+  // issue the next tile into `buf` (per-head rows: H * 128 elements, the
+  // same for K_nope and V)
+  __device__ __forceinline__ void issue(uint32_t buf, int wave, int H) {
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i) {
       g2lds16(p[i], buf + (uint32_t)(wave * kWLoads + i) * 1024u);
-      p[i] += (size_t)kFK * stride[i];
+      p[i] += ((rope >> i) & 1u) ? (size_t)kFK * 576 : (size_t)kFK * H * kNDn;
     }
   }
 };
@@ -113,6 +117,46 @@ __device__ __forceinline__ void wait_tiles(int c) {
     wait_vmcnt<0>();
 }
 
+// K fragment (S^T A operand) of k step ks, 32-key block kb: the lane's base
+// address for ks % 4 plus 128 bytes per 4 steps and 32 rows per block.
+__device__ __forceinline__ void read_k(bf16x8& o, uint32_t a, int ks, int kb) {
+  switch (2 * (ks >> 2) + kb) {
+    case 0: ds_b128_nowait<0>(o, a); break;
+    case 1: ds_b128_nowait<32 * kKCh * 16>(o, a); break;
+    case 2: ds_b128_nowait<128>(o, a); break;
+    case 3: ds_b128_nowait<128 + 32 * kKCh * 16>(o, a); break;
+    case 4: ds_b128_nowait<256>(o, a); break;
+    default: ds_b128_nowait<256 + 32 * kKCh * 16>(o, a); break;
+  }
+}
+// V^T fragment half of 16-key step ks: 16 rows of V per step
+__device__ __forceinline__ void read_v(bf16x4& o, uint32_t a, int ks) {
+  switch (ks) {
+    case 0: ds_tr_nowait<0>(o, a); break;
+    case 1: ds_tr_nowait<16 * kVCh * 16>(o, a); break;
+    case 2: ds_tr_nowait<32 * kVCh * 16>(o, a); break;
+    default: ds_tr_nowait<48 * kVCh * 16>(o, a); break;
+  }
+}
+
+// Workgroup = (sequence, head, 256 query rows), 8 waves of 32 queries (a
+// lane owns query lane%32), two waves per SIMD.  Per 64-key tile:
+//   S^T = K Q^T                 24 MFMAs per wave, K fragments read one step ahead
+//   causal mask, row maxima, lazy rescale (VALU)
+//   O^T += V^T P^T              4 steps of 16 keys, 4 MFMAs each
+// The weights P of 16-key step ks + 1 (8 exponentials per lane) are
+// computed while the MFMAs of step ks run, and the V^T fragments of step
+// ks + 1 are read as soon as step ks's MFMAs have taken theirs.  LDS reads
+// are issued without a wait and completed by waits that name their
+// registers (the compiler's own reads would wait for the tile loads in
+// flight).  Tiles go through four buffers, three in flight; the barrier at
+// the top of tile k frees tile k - 1's buffer for tile k + 3.
+// Measured on MI355X (the 2 x 4096 prefill at 64 heads): the LDS serves
+// 16-byte reads at about 190 bytes per clock per CU and transposing 8-byte
+// reads at about 100, so the K and V^T fragment reads of the 8 waves
+// (192 + 128 KB per tile) occupy the LDS for about as long as the MFMAs
+// take; 64 queries per wave would halve them, but then the registers of
+// one wave (queries, O and S for 64 rows) no longer fit without spills.
 __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
     const bf16* __restrict__ q, const float* __restrict__ rope, float alpha,
     const bf16* __restrict__ kn, const bf16* __restrict__ cg, const bf16* __restrict__ vv,
@@ -132,75 +176,70 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
   const int n = (sp + last) / kFK + 1;                  // key tiles the block needs
   const long row0 = (long)b * ctx_pad;
 
-  // this lane's query row (rows past T repeat the last one; not stored)
-  const int qw0 = q0 + 32 * wave;
-  const int tq = min(qw0 + (lane & 31), T - 1);
-  const int pos = sp + tq;                              // its absolute position
-  const int wave_last = sp + min(qw0 + 31, T - 1);      // largest position in the wave
+  // this wave's queries (rows past T repeat the last one; not stored)
+  const int qw0 = q0 + kQW * wave;
   const bool wave_live = qw0 < T;
+  const int wave_last = sp + min(qw0 + kQW - 1, T - 1);  // largest position in the wave
+  const int kw = wave_live ? min(wave_last / kFK, n - 1) : -1;  // its last tile with a live key
+  int pos[kQH];
+  int tq[kQH];
+#pragma unroll
+  for (int qh = 0; qh < kQH; ++qh) {
+    tq[qh] = min(qw0 + 32 * qh + (lane & 31), T - 1);
+    pos[qh] = sp + tq[qh];
+  }
 
   KvSource src;
   src.setup(kn, cg, vv, row0, H, h, wave, lane);
-  src.issue(lds, wave);
+  src.issue(lds, wave, H);
   // This lane's query fragments (B operand of S^T): dims 16 ks + 8 (lane/32)
   // .. + 7 of head h, straight from the query projection; the rope dims
   // (ks >= 8) are rotated here (dim i of the rope part pairs with i + 32,
   // two steps further in the same lane) and all are scaled by alpha.
-  bf16x8 qf[kNDk / 16];
-  f32x4 cs[4];  // cos (ks 8, 9) and sin (ks 8, 9) of the lane's 16 rope angles, 4 at a time
-  {
-    const bf16* qr = q + (((long)b * T + tq) * H + h) * kNDk + 8 * (lane >> 5);
+  bf16x8 qf[kQH][kKS];
+  f32x4 cs[kQH][4], sn[kQH][4];  // cos, sin of the lane's 16 rope angles per half
 #pragma unroll
-    for (int ks = 0; ks < kNDk / 16; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
-  }
-  {
-    const float* rr = rope + (long)pos * kNDr + 8 * (lane >> 5);
-    float* c = (float*)cs;
+  for (int qh = 0; qh < kQH; ++qh) {
+    const bf16* qr = q + (((long)b * T + tq[qh]) * H + h) * kNDk + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qf[qh][ks] = *(const bf16x8*)(qr + 16 * ks);
+    const float* rc = rope + (long)pos[qh] * kNDr + 8 * (lane >> 5);
+    const float* rs = rc + kNDr / 2;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {  // ks = 8 + e: angles 16 e + 8 (lane/32) + j
-      *(f32x4*)(c + 8 * e) = *(const f32x4*)(rr + 16 * e);
-      *(f32x4*)(c + 8 * e + 4) = *(const f32x4*)(rr + 16 * e + 4);
+      cs[qh][2 * e] = *(const f32x4*)(rc + 16 * e);
+      cs[qh][2 * e + 1] = *(const f32x4*)(rc + 16 * e + 4);
+      sn[qh][2 * e] = *(const f32x4*)(rs + 16 * e);
+      sn[qh][2 * e + 1] = *(const f32x4*)(rs + 16 * e + 4);
     }
   }
-  f32x4 sn[4];
-  {
-    const float* rr = rope + (long)pos * kNDr + kNDr / 2 + 8 * (lane >> 5);
-    float* c = (float*)sn;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      *(f32x4*)(c + 8 * e) = *(const f32x4*)(rr + 16 * e);
-      *(f32x4*)(c + 8 * e + 4) = *(const f32x4*)(rr + 16 * e + 4);
-    }
-  }
-  for (int t = 1; t < min(n, kFBuf - 1); ++t) src.issue(lds + (uint32_t)t * kTBytes, wave);
+  for (int t = 1; t < min(n, kFBuf - 1); ++t) src.issue(lds + (uint32_t)t * kTBytes, wave, H);
   wait_tiles(min(n, kFBuf - 1) - 1);  // tile 0 and the queries have landed
-  {
-    const float* c = (const float*)cs;
-    const float* sv = (const float*)sn;
+#pragma unroll
+  for (int qh = 0; qh < kQH; ++qh) {
+    const float* c = (const float*)cs[qh];
+    const float* sv = (const float*)sn[qh];
 #pragma unroll
     for (int ks = 0; ks < kNDn / 16; ++ks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qf[ks][j] = (bf16)(alpha * (float)qf[ks][j]);
+      for (int j = 0; j < 8; ++j) qf[qh][ks][j] = (bf16)(alpha * (float)qf[qh][ks][j]);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = (float)qf[8 + e][j], y = (float)qf[10 + e][j];
+        const float x = (float)qf[qh][8 + e][j], y = (float)qf[qh][10 + e][j];
         const float co = c[8 * e + j], si = sv[8 * e + j];
-        qf[8 + e][j] = (bf16)(alpha * (x * co - y * si));
-        qf[10 + e][j] = (bf16)(alpha * (y * co + x * si));
+        qf[qh][8 + e][j] = (bf16)(alpha * (x * co - y * si));
+        qf[qh][10 + e][j] = (bf16)(alpha * (y * co + x * si));
       }
   }
-  // the queries are plain register values from here on
-#pragma unroll
-  for (int ks = 0; ks < kNDk / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
 
-  // per-lane LDS offsets.  K fragment (S^T A operand): row 32 kb + lane%32,
-  // chunk 2 ks + lane/32 -> position 8 (ks/4) + ((2 (ks%4) + lane/32) ^ f(row)).
+  // per-lane LDS offsets.  K fragment: row 32 kb + lane%32, chunk
+  // 2 ks + lane/32 -> position 8 (ks/4) + ((2 (ks%4) + lane/32) ^ f(row)).
   const uint32_t hi = lane >> 5, fk = k_swz(lane & 31);
   uint32_t k_off[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) k_off[q] = ((lane & 31) * kKCh + ((2u * q + hi) ^ fk)) * 16u;
+  for (int q4 = 0; q4 < 4; ++q4) k_off[q4] = ((lane & 31) * kKCh + ((2u * q4 + hi) ^ fk)) * 16u;
   // V^T fragment (transposing reads): group g, lane li = 4a + bb reads key
   // row 4 (g/2) + 8 hh + a (+ 16 ks; hh: first or second 4 keys of the
   // lane's k order), dv chunk 4 db + 2 (g%2) + bb/2 at position chunk ^ 4a,
@@ -216,123 +255,171 @@ __global__ void __launch_bounds__(kFThreads, 1) flash_prefill_kernel(
       v_off[2 * db + hh] = kKBytes + (row * kVCh + (ch ^ (a4 << 2))) * 16u + 8u * (bb & 1);
     }
 
-  f32x16 o[4];
+  f32x16 o[kQH][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  for (int qh = 0; qh < kQH; ++qh)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[qh][db] = f32x16{};
+  float m[kQH], l[kQH];
+#pragma unroll
+  for (int qh = 0; qh < kQH; ++qh) {
+    m[qh] = -INFINITY;
+    l[qh] = 0.f;
+  }
+  f32x16 sacc[kQH][2];
+
+  // S^T = K Q^T for the tile in kbuf, the K fragments read two steps ahead
+  auto scores = [&](uint32_t kbuf) {
+    uint32_t ka[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) ka[q4] = kbuf + k_off[q4];
+    bf16x8 fr[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) read_k(fr[0][kb], ka[0], 0, kb);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      if (ks + 1 < kKS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) read_k(fr[(ks + 1) & 1][kb], ka[(ks + 1) & 3], ks + 1, kb);
+        lds_settle<2>(fr[ks & 1][0], fr[ks & 1][1]);
+      } else {
+        lds_settle<0>(fr[ks & 1][0], fr[ks & 1][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qh = 0; qh < kQH; ++qh)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[qh][kb] = mfma32(fr[ks & 1][kb], qf[qh][ks], ks == 0 ? f32x16{} : sacc[qh][kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
   for (int k = 0; k < n; ++k) {
     wait_tiles(min(n - 1 - k, kFBuf - 2));
-    lds_barrier();  // tile k visible; tile k-1 fully consumed
+    lds_barrier();  // tile k visible; tile k - 1 consumed by every wave
     if (k + kFBuf - 1 < n)
-      src.issue(lds + (uint32_t)((k + kFBuf - 1) % kFBuf) * kTBytes, wave);
-    const int key0 = k * kFK;
-    if (!wave_live || key0 > wave_last) continue;  // every key of the tile is masked for the wave
+      src.issue(lds + (uint32_t)((k + kFBuf - 1) % kFBuf) * kTBytes, wave, H);
+    if (k > kw) continue;  // every key of the tile is masked for the wave
     const uint32_t buf = lds + (uint32_t)(k % kFBuf) * kTBytes;
+    scores(buf);
 
-    // ---- S^T = K Q^T: two 32-key blocks, K = 192 (12 steps of 16)
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    {
-      // fragments read two steps ahead of the MFMAs that use them
-      auto frag = [&](int ks, int kb) {
-        return lds_read_b128(buf + k_off[ks & 3] + (uint32_t)((ks >> 2) * 128) +
-                             (uint32_t)(kb * 32 * kKCh * 16));
-      };
-      constexpr int D = 2;
-      bf16x8 fr[D + 1][2];
+    // the first V^T fragments go out before the softmax needs the scores
+    uint32_t va[8];
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        fr[d][0] = frag(d, 0);
-        fr[d][1] = frag(d, 1);
-      }
-      // (the scheduling barriers keep the compiler from folding the reads
-      // back next to their MFMAs, which would expose every LDS latency)
+    for (int i = 0; i < 8; ++i) va[i] = buf + v_off[i];
+    bf16x4 vt[8];
 #pragma unroll
-      for (int ks = 0; ks < kNDk / 16; ++ks) {
-        if (ks + D < kNDk / 16) {
-          fr[(ks + D) % (D + 1)][0] = frag(ks + D, 0);
-          fr[(ks + D) % (D + 1)][1] = frag(ks + D, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        s[0] = mfma32(fr[ks % (D + 1)][0], qf[ks], s[0]);
-        s[1] = mfma32(fr[ks % (D + 1)][1], qf[ks], s[1]);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 8; ++i) read_v(vt[i], va[i], 0);
+
+    // causal mask, only where the tile reaches past the wave's first query;
+    // register v of block kb <-> key key0 + 32 kb + 8 (v/4) + 4 hi + v%4
+    const int key0 = k * kFK;
+    if (key0 + kFK - 1 > sp + qw0) {
+#pragma unroll
+      for (int qh = 0; qh < kQH; ++qh) {
+        const int lim = pos[qh] - key0 - 4 * (int)hi;  // mask where 32 kb + 8 (v/4) + v%4 > lim
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * kb + 8 * (v >> 2) + (v & 3) > lim) sacc[qh][kb][v] = -INFINITY;
       }
     }
-    // register v of block kb <-> key key0 + 32 kb + 8 (v/4) + 4 hi + v%4, query lane%32
-    // causal mask, only where the tile reaches past the wave's first query
-    if (key0 + kFK - 1 > sp + qw0) {
+    // row maxima over the tile's 64 keys (32 in this lane, 32 in lane ^ 32)
+    float m_new[kQH], al[kQH];
+    bool grow_any = false;
+#pragma unroll
+    for (int qh = 0; qh < kQH; ++qh) {
+      float hm = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * (int)hi + (v & 3);
-          if (key > pos) s[kb][v] = -INFINITY;
+        for (int v = 0; v < 16; ++v) hm = fmaxf(hm, sacc[qh][kb][v]);
+      hm = max_xor32(hm);
+      const bool grow = hm > m[qh] + kFSlack;
+      m_new[qh] = grow ? hm : m[qh];
+      al[qh] = grow ? fast_exp2(m[qh] - m_new[qh]) : 1.0f;
+      grow_any = grow_any || grow;
+    }
+    if (__ballot(grow_any) != 0ull) {
+#pragma unroll
+      for (int qh = 0; qh < kQH; ++qh)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[qh][db][v] *= al[qh];
+    }
+    // P^T of 16-key step ks for half qh: registers 8 (ks%2) .. + 7 of block ks/2
+    float psum[kQH];
+#pragma unroll
+    for (int qh = 0; qh < kQH; ++qh) psum[qh] = 0.f;
+    bf16x8 pr[2][kQH];  // [step parity][half]
+    auto weights = [&](int ks, bf16x8 (&dst)[kQH]) {
+#pragma unroll
+      for (int qh = 0; qh < kQH; ++qh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pv = fast_exp2(sacc[qh][ks >> 1][8 * (ks & 1) + j] - m_new[qh]);
+          psum[qh] += pv;
+          dst[qh][j] = (bf16)pv;
         }
-    }
-    float hmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, s[kb][v]);
-    hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-    const bool grow = hmax > m + kFSlack;
-    const float m_new = grow ? hmax : m;
-    const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
-    // P^T fragment of 16-key step ks: registers 8 (ks%2) .. + 7 of block ks/2
-    float psum = 0.f;
-    bf16x8 pr[kFK / 16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const bf16 p = (bf16)fast_exp2(s[kb][v] - m_new);
-        pr[2 * kb + (v >> 3)][v & 7] = p;
-        psum += (float)p;
-      }
-    l = l * alpha + psum;
-    m = m_new;
-    if (__ballot(grow) != 0ull) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-    }
-
-    // ---- O^T += V^T P^T: 4 steps of 16 keys
-    uint32_t ta[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ta[i] = buf + v_off[i];
+    };
+    weights(0, pr[0]);
 #pragma unroll
     for (int ks = 0; ks < kFK / 16; ++ks) {
-      bf16x4 t[8];
-      if (ks == 0) lds_read_tr_x8<0>(ta, t);
-      else if (ks == 1) lds_read_tr_x8<16 * kVCh * 16>(ta, t);
-      else if (ks == 2) lds_read_tr_x8<32 * kVCh * 16>(ta, t);
-      else lds_read_tr_x8<48 * kVCh * 16>(ta, t);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma32(cat(t[2 * db], t[2 * db + 1]), pr[ks], o[db]);
+      for (int i = 0; i < 8; i += 2) lds_settle<0>(vt[i], vt[i + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // step ks's MFMAs; the next step's fragments are read as soon as the
+      // MFMAs have taken these (the reads land long after the MFMAs read
+      // their operands), and its weights are computed beside them
+#pragma unroll
+      for (int qh = 0; qh < kQH; ++qh)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[qh][db] = mfma32(cat(vt[2 * db], vt[2 * db + 1]), pr[ks & 1][qh], o[qh][db]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < kFK / 16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) read_v(vt[i], va[i], ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        weights(ks + 1, pr[(ks + 1) & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qh = 0; qh < kQH; ++qh) {
+      l[qh] = l[qh] * al[qh] + psum[qh];
+      m[qh] = m_new[qh];
     }
   }
 
   // ---- out[b, t, h, :] = O / l, staged per wave in the (idle) tile buffers
-  l += __shfl_xor(l, 32, 64);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  float inv[kQH];
+#pragma unroll
+  for (int qh = 0; qh < kQH; ++qh) {
+    const float lt = sum_xor32(l[qh]);
+    inv[qh] = lt > 0.f ? 1.0f / lt : 0.f;
+  }
   lds_barrier();  // every wave is done with the tile buffers
   typedef __attribute__((address_space(3))) bf16x4 lds_b4;
-  const uint32_t st = lds + wave * 32 * kFSStride * 2;
+  const uint32_t st = lds + wave * kQW * kFSStride * 2;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qh = 0; qh < kQH; ++qh)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 w4;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w4[r] = (bf16)(o[db][4 * q4 + r] * inv);
-      *(lds_b4*)(uintptr_t)(st + ((lane & 31) * kFSStride + 32 * db + 8 * q4 + 4 * hi) * 2) = w4;
-    }
-  // each wave writes its 32 rows (256 B each) with 16-byte stores
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w4;
 #pragma unroll
-  for (int i = 0; i < 32 * kVCh / 64; ++i) {
+        for (int r = 0; r < 4; ++r) w4[r] = (bf16)(o[qh][db][4 * q4 + r] * inv[qh]);
+        const int row = 32 * qh + (lane & 31);
+        *(lds_b4*)(uintptr_t)(st + (row * kFSStride + 32 * db + 8 * q4 + 4 * hi) * 2) = w4;
+      }
+  // each wave writes its 64 rows (256 B each) with 16-byte stores
+#pragma unroll
+  for (int i = 0; i < kQW * kVCh / 64; ++i) {
     const int c = i * 64 + lane;
     const int r = c / kVCh, ch = c % kVCh;
     const int t = qw0 + r;
