@@ -138,65 +138,66 @@ __device__ __forceinline__ void settle(Frag<FN, BT>& f) {
                    "+v"(f.t[0][1]), "+v"(f.t[1][0]), "+v"(f.t[1][1]));
 }
 
-template <int BN, bool kBT, bool kOutF32>
-__global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ B, void* __restrict__ Cv, int M, int N,
-    int K, long lda, long ldb, long ldc, long sA, long sB, long sC, int batch, int m_per,
-    float alpha, int nb, long sBn, const bf16* __restrict__ gmul) {
+// This thread's direct-to-LDS sources for one tile (the global chunk for
+// each of its LDS slots) and B's row stride.
+template <int BN, bool kBT>
+struct TileSrc {
+  const bf16* a[TileCfg<BN>::A_LOADS];
+  const bf16* b[TileCfg<BN>::B_LOADS];
+  long ldb;
+};
+
+// Sources of tile (m0, n0).  Row-major B may come as column blocks of nb
+// (block j at B + j * sBn); nb = N for one plain matrix.
+template <int BN, bool kBT>
+__device__ __forceinline__ void tile_sources(TileSrc<BN, kBT>& t, const bf16* A, int M, long lda,
+                                             int m0, const bf16* B, int N, long ldb, int n0,
+                                             int nb, long sBn, int wave, int lane) {
+  using Cf = TileCfg<BN>;
+#pragma unroll
+  for (int i = 0; i < Cf::A_LOADS; ++i) {
+    const int p = (wave * Cf::A_LOADS + i) * 64 + lane;  // LDS chunk slot
+    const int m = p >> 2, c = (p & 3) ^ ((m >> 2) & 3);
+    t.a[i] = A + (long)min(m0 + m, M - 1) * lda + 8 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < Cf::B_LOADS; ++i) {
+    const int p = (wave * Cf::B_LOADS + i) * 64 + lane;
+    if constexpr (kBT) {
+      const int n = p >> 2, c = (p & 3) ^ ((n >> 2) & 3);
+      t.b[i] = B + (long)min(n0 + n, N - 1) * ldb + 8 * c;
+    } else {
+      constexpr int CPR = BN / 8;  // chunks per k row
+      const int k = p / CPR, c = (p % CPR) ^ (4 * (k & 3));
+      const int n = min(n0 + 8 * c, N - 8);  // column blocks of nb (a chunk never straddles one)
+      t.b[i] = B + (long)(n / nb) * sBn + (long)k * ldb + n % nb;
+    }
+  }
+  t.ldb = ldb;
+}
+
+// acc += the product over k stages [kt0, kt1) of the tile whose sources are
+// `src` (kt1 > kt0).  The LDS buffers are free on entry and on return.
+template <int BN, bool kBT>
+__device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kBT>& src, int kt0,
+                                              int kt1, f32x16 (&acc)[4][TileCfg<BN>::FN]) {
   using Cf = TileCfg<BN>;
   constexpr int FN = Cf::FN, T = Cf::T, L = Cf::LOADS;
   constexpr int NR = kBT ? 4 + FN : 4 + 2 * FN;  // fragment reads per half step
   constexpr int RB = BN * 2;                     // bytes per k row of a row-major B stage
   constexpr int kDOff = T / 4;                   // first MFMA slot carrying loads
   constexpr int kROff = Cf::RO, kRSpan = Cf::RS;
-  __shared__ __attribute__((aligned(16))) char smem[kTStages * Cf::STAGE];
-  const uint32_t lds = lds_addr(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // tile of this block
-  const int n_mt = (M + kTM - 1) / kTM, n_nt = (N + BN - 1) / BN;
-  const int rows_total = n_mt * batch;
-  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int r_first = x * m_per;
-  if (r_first >= rows_total) return;
-  const int rows_here = min(m_per, rows_total - r_first);
-  if (j >= rows_here * n_nt) return;
-  const int row_tile = r_first + j % rows_here, nt = j / rows_here;
-  const int z = row_tile / n_mt, m0 = (row_tile % n_mt) * kTM, n0 = nt * BN;
-  A += z * sA;
-  B += z * sB;
-
-  // this thread's direct-to-LDS sources (global chunk for each LDS slot)
-  const bf16* a_src[Cf::A_LOADS];
-#pragma unroll
-  for (int i = 0; i < Cf::A_LOADS; ++i) {
-    const int p = (wave * Cf::A_LOADS + i) * 64 + lane;  // LDS chunk slot
-    const int m = p >> 2, c = (p & 3) ^ ((m >> 2) & 3);
-    a_src[i] = A + (long)min(m0 + m, M - 1) * lda + 8 * c;
-  }
-  const bf16* b_src[Cf::B_LOADS];
-#pragma unroll
-  for (int i = 0; i < Cf::B_LOADS; ++i) {
-    const int p = (wave * Cf::B_LOADS + i) * 64 + lane;
-    if constexpr (kBT) {
-      const int n = p >> 2, c = (p & 3) ^ ((n >> 2) & 3);
-      b_src[i] = B + (long)min(n0 + n, N - 1) * ldb + 8 * c;
-    } else {
-      constexpr int CPR = BN / 8;  // chunks per k row
-      const int k = p / CPR, c = (p % CPR) ^ (4 * (k & 3));
-      const int n = min(n0 + 8 * c, N - 8);  // column blocks of nb (a chunk never straddles one)
-      b_src[i] = B + (long)(n / nb) * sBn + (long)k * ldb + n % nb;
-    }
-  }
   // load q (0 .. L-1) of stage kt
   auto issue_one = [&](int kt, int q) {
     const uint32_t st = lds + (uint32_t)(kt % kTStages) * Cf::STAGE;
     if (q < Cf::A_LOADS) {
-      g2lds16(a_src[q] + (long)kt * kTK, st + (uint32_t)(wave * Cf::A_LOADS + q) * 1024u);
+      g2lds16(src.a[q] + (long)kt * kTK, st + (uint32_t)(wave * Cf::A_LOADS + q) * 1024u);
     } else {
       const int i = q - Cf::A_LOADS;
-      const long off = kBT ? (long)kt * kTK : (long)kt * kTK * ldb;
-      g2lds16(b_src[i] + off, st + kTABytes + (uint32_t)(wave * Cf::B_LOADS + i) * 1024u);
+      const long off = kBT ? (long)kt * kTK : (long)kt * kTK * src.ldb;
+      g2lds16(src.b[i] + off, st + kTABytes + (uint32_t)(wave * Cf::B_LOADS + i) * 1024u);
     }
   };
 
@@ -245,13 +246,6 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
       read_tr<RB>(f.t[jb][h2], st + b_off[jb], 2 * s + h2);
     }
   };
-
-  f32x16 acc[4][FN];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jb = 0; jb < FN; ++jb) acc[i][jb] = f32x16{};
-
   auto mfma_one = [&](const Frag<FN, kBT>& f, int e) {
     const int i = e / FN, jb = e % FN;
     if constexpr (kBT)
@@ -260,7 +254,6 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
       acc[i][jb] = mfma32(cat(f.t[jb][0], f.t[jb][1]), f.a[i], acc[i][jb]);
   };
 
-  const int nk = K / kTK;
   Frag<FN, kBT> f0, f1;
   // Iteration kt: half step (kt, 0) on f0 while f1 = (kt, 1) is read; the
   // barrier that publishes stage kt + 1 (and frees stage kt's buffer); half
@@ -283,7 +276,7 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
     }
     settle(f1);
     if constexpr (NEXT) {
-      wait_stages<L>(min(nk - 2 - kt, kTStages - 2));
+      wait_stages<L>(min(kt1 - 2 - kt, kTStages - 2));
       lds_barrier();
     }
     const uint32_t sn = lds + (uint32_t)((kt + 1) % kTStages) * Cf::STAGE;
@@ -310,37 +303,56 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
     if constexpr (NEXT) settle(f0);
   };
 
-  for (int kt = 0; kt < min(nk, kTStages); ++kt)
+  for (int kt = kt0; kt < min(kt1, kt0 + kTStages); ++kt)
 #pragma unroll
     for (int q = 0; q < L; ++q) issue_one(kt, q);
-  wait_stages<L>(min(nk - 1, kTStages - 1));
+  wait_stages<L>(min(kt1 - kt0 - 1, kTStages - 1));
   lds_barrier();
+  {
+    const uint32_t st = lds + (uint32_t)(kt0 % kTStages) * Cf::STAGE;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) read_one(lds, 0, r, f0);
+    for (int r = 0; r < NR; ++r) read_one(st, 0, r, f0);
+  }
   settle(f0);
-  int kt = 0;
-  for (; kt + kTStages < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
-  for (; kt + 1 < nk; ++kt) body(kt, std::false_type{}, std::true_type{});
+  int kt = kt0;
+  for (; kt + kTStages < kt1; ++kt) body(kt, std::true_type{}, std::true_type{});
+  for (; kt + 1 < kt1; ++kt) body(kt, std::false_type{}, std::true_type{});
   body(kt, std::false_type{}, std::false_type{});
+  lds_barrier();  // every wave is done with the buffers
+}
 
-  // register v of acc[i][jb]: column (BN/2) wn + 32 jb + 8 (v/4) + 4 (lane/32) + v%4,
-  // row 128 wm + 32 i + lane%32
+// C[m0.., n0..] = alpha * acc (kAdd: += by float32 atomics), optionally gated.
+// Register v of acc[i][jb]: column (BN/2) wn + 32 jb + 8 (v/4) + 4 (lane/32)
+// + v%4, row 128 wm + 32 i + lane%32.
+template <int BN, bool kOutF32, bool kAdd>
+__device__ __forceinline__ void tile_epilogue(const f32x16 (&acc)[4][TileCfg<BN>::FN], void* Cv,
+                                              int M, int N, long ldc, int m0, int n0,
+                                              float alpha, const bf16* gmul) {
+  using Cf = TileCfg<BN>;
+  static_assert(!kAdd || kOutF32, "accumulating epilogue is float32");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 128 * wm + 32 * i + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int jb = 0; jb < FN; ++jb)
+    for (int jb = 0; jb < Cf::FN; ++jb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + Cf::WN * wn + 32 * jb + 8 * q + 4 * hi;
         if (n >= N) continue;
-        if constexpr (kOutF32) {
+        const long ci = (long)m * ldc + n;
+        if constexpr (kAdd) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            unsafeAtomicAdd((float*)Cv + ci + r, alpha * acc[i][jb][4 * q + r]);
+        } else if constexpr (kOutF32) {
           const f32x4 v = {alpha * acc[i][jb][4 * q], alpha * acc[i][jb][4 * q + 1],
                            alpha * acc[i][jb][4 * q + 2], alpha * acc[i][jb][4 * q + 3]};
-          *(f32x4*)((float*)Cv + z * sC + (long)m * ldc + n) = v;
+          *(f32x4*)((float*)Cv + ci) = v;
         } else {
-          const long ci = z * sC + (long)m * ldc + n;
           bf16x4 v;
           if (gmul) {  // gate: C = gmul * sigmoid(alpha A B)
             const bf16x4 gv = *(const bf16x4*)(gmul + ci);
@@ -355,6 +367,137 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
         }
       }
   }
+}
+
+template <int BN, bool kBT, bool kOutF32>
+__global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ B, void* __restrict__ Cv, int M, int N,
+    int K, long lda, long ldb, long ldc, long sA, long sB, long sC, int batch, int m_per,
+    float alpha, int nb, long sBn, const bf16* __restrict__ gmul) {
+  using Cf = TileCfg<BN>;
+  __shared__ __attribute__((aligned(16))) char smem[kTStages * Cf::STAGE];
+  const uint32_t lds = lds_addr(smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // tile of this block
+  const int n_mt = (M + kTM - 1) / kTM, n_nt = (N + BN - 1) / BN;
+  const int rows_total = n_mt * batch;
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int r_first = x * m_per;
+  if (r_first >= rows_total) return;
+  const int rows_here = min(m_per, rows_total - r_first);
+  if (j >= rows_here * n_nt) return;
+  const int row_tile = r_first + j % rows_here, nt = j / rows_here;
+  const int z = row_tile / n_mt, m0 = (row_tile % n_mt) * kTM, n0 = nt * BN;
+
+  TileSrc<BN, kBT> src;
+  tile_sources<BN, kBT>(src, A + z * sA, M, lda, m0, B + z * sB, N, ldb, n0, nb, sBn, wave,
+                        lane);
+  f32x16 acc[4][Cf::FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jb = 0; jb < Cf::FN; ++jb) acc[i][jb] = f32x16{};
+  tile_mainloop<BN, kBT>(lds, src, 0, K / kTK, acc);
+  if constexpr (kOutF32)
+    tile_epilogue<BN, true, false>(acc, (float*)Cv + z * sC, M, N, ldc, m0, n0, alpha, nullptr);
+  else
+    tile_epilogue<BN, false, false>(acc, (bf16*)Cv + z * sC, M, N, ldc, m0, n0, alpha,
+                                    gmul ? gmul + z * sC : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Two float32 GEMMs that share A as one launch: C1 = alpha A B1 ([M, N1],
+// N1 a multiple of 256) and C2 = alpha A B2 ([M, N2]), B row-major.  Their
+// column tiles side by side (C1's first) give n_nt tiles per 256-row tile.
+// All but the last column are whole tiles, one per workgroup, with the
+// row-group-per-XCD mapping above; the last column tile of each row tile is
+// split along k into S = n_nt - 1 parts, one per workgroup, whose float32
+// partial tiles a second kernel adds in a fixed order (deterministic).  The
+// split parts are as long as a whole tile's k loop divided by S, so when the
+// whole tiles take exactly one round of all CUs, the parts take one short
+// round more instead of a second full one.  (The prefill's x [W_DQ | W_DKV]
+// at 8192 rows: 256 whole tiles and 32 last-column tiles, split 8 ways.)
+// ---------------------------------------------------------------------------
+struct PairGemm {
+  const bf16* A;
+  const bf16* B1;
+  const bf16* B2;
+  float* C1;
+  float* C2;
+  float* part;  // S x n_mt partial tiles of 256 x 256 floats
+  int M, N1, N2, K;
+  long lda, ldb1, ldb2, ldc1, ldc2;
+  float alpha;
+  int n_nt1, n_nt, n_mt, m_per, S, nk;
+};
+
+// column tile ct of the pair: its matrix and column offset
+struct PairCol {
+  const bf16* B;
+  float* C;
+  long ldb, ldc;
+  int N, n0;
+};
+__device__ __forceinline__ PairCol pair_col(const PairGemm& g, int ct) {
+  if (ct < g.n_nt1) return PairCol{g.B1, g.C1, g.ldb1, g.ldc1, g.N1, ct * 256};
+  return PairCol{g.B2, g.C2, g.ldb2, g.ldc2, g.N2, (ct - g.n_nt1) * 256};
+}
+
+__global__ void __launch_bounds__(kTThreads, 1) gemm_pair_kernel(PairGemm g) {
+  using Cf = TileCfg<256>;
+  __shared__ __attribute__((aligned(16))) char smem[kTStages * Cf::STAGE];
+  const uint32_t lds = lds_addr(smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int r_first = x * g.m_per;
+  const int n_whole = g.m_per * (g.n_nt - 1);
+  int rt, ct, kt0, kt1, s = -1;
+  if (j < n_whole) {
+    rt = r_first + j % g.m_per;
+    ct = j / g.m_per;
+    kt0 = 0;
+    kt1 = g.nk;
+  } else {
+    const int jj = j - n_whole;
+    s = jj / g.m_per;
+    rt = r_first + jj % g.m_per;
+    ct = g.n_nt - 1;
+    kt0 = s * g.nk / g.S;
+    kt1 = (s + 1) * g.nk / g.S;
+  }
+  const PairCol c = pair_col(g, ct);
+  const int m0 = rt * kTM;
+  TileSrc<256, false> src;
+  tile_sources<256, false>(src, g.A, g.M, g.lda, m0, c.B, c.N, c.ldb, c.n0, c.N, 0, wave, lane);
+  f32x16 acc[4][Cf::FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jb = 0; jb < Cf::FN; ++jb) acc[i][jb] = f32x16{};
+  tile_mainloop<256, false>(lds, src, kt0, kt1, acc);
+  // a split part writes its whole 256 x 256 partial tile, unscaled
+  const bool whole = s < 0;
+  float* C = whole ? c.C : g.part + ((long)s * g.n_mt + rt) * kTM * 256;
+  tile_epilogue<256, true, false>(acc, C, whole ? g.M : kTM, whole ? c.N : 256,
+                                  whole ? c.ldc : 256, whole ? m0 : 0, whole ? c.n0 : 0,
+                                  whole ? g.alpha : 1.0f, nullptr);
+}
+
+// last column tiles: C = alpha * sum over s of the partial tiles, s in order
+__global__ void __launch_bounds__(256) gemm_pair_reduce_kernel(PairGemm g) {
+  const PairCol c = pair_col(g, g.n_nt - 1);
+  const long per_tile = (long)kTM * 64;  // 16-byte chunks of a 256 x 256 float tile
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_tile * g.n_mt) return;
+  const int rt = (int)(i / per_tile);
+  const int e = (int)(i % per_tile), r = e >> 6, col = (e & 63) * 4;
+  const int m = rt * kTM + r, n = c.n0 + col;
+  if (m >= g.M || n >= c.N) return;
+  f32x4 sum = f32x4{};
+  for (int s = 0; s < g.S; ++s)
+    sum += *(const f32x4*)(g.part + ((long)s * g.n_mt + rt) * kTM * 256 + (long)r * 256 + col);
+  *(f32x4*)(c.C + (long)m * c.ldc + n) = g.alpha * sum;
 }
 
 template <int BN, bool kBT>
@@ -381,6 +524,52 @@ bool gemm_tile256_fits(int M, int N, int K, long lda, long ldb, long ldc) {
   // 16-byte aligned rows and chunks, whole 32-wide k steps, vector stores of 4
   return M >= kTM && N >= 128 && K >= kTK && K % kTK == 0 && N % 8 == 0 && lda % 8 == 0 &&
          ldb % 8 == 0 && ldc % 4 == 0;
+}
+
+size_t gemm_pair_scratch_bytes(int M, int N1, int N2) {
+  const int n_mt = (M + kTM - 1) / kTM, n_nt = N1 / 256 + (N2 + 255) / 256;
+  return (size_t)(n_nt - 1) * n_mt * kTM * 256 * sizeof(float);
+}
+
+bool launch_gemm_pair_f32(const void* A, int M, int K, long lda, const void* B1, int N1,
+                          long ldb1, float* C1, long ldc1, const void* B2, int N2, long ldb2,
+                          float* C2, long ldc2, float alpha, int num_cus, void* scratch,
+                          size_t scratch_bytes, hipStream_t st) {
+  if (M < kTM || K % kTK != 0 || N1 % 256 != 0 || N1 <= 0 || N2 < 8 || N2 % 8 != 0 ||
+      lda % 8 != 0 || ldb1 % 8 != 0 || ldb2 % 8 != 0 || ldc1 % 4 != 0 || ldc2 % 4 != 0)
+    return false;
+  PairGemm g;
+  g.A = (const bf16*)A;
+  g.B1 = (const bf16*)B1;
+  g.B2 = (const bf16*)B2;
+  g.C1 = C1;
+  g.C2 = C2;
+  g.part = (float*)scratch;
+  g.M = M;
+  g.N1 = N1;
+  g.N2 = N2;
+  g.K = K;
+  g.lda = lda;
+  g.ldb1 = ldb1;
+  g.ldb2 = ldb2;
+  g.ldc1 = ldc1;
+  g.ldc2 = ldc2;
+  g.alpha = alpha;
+  g.n_nt1 = N1 / 256;
+  g.n_nt = g.n_nt1 + (N2 + 255) / 256;
+  g.n_mt = (M + kTM - 1) / kTM;
+  g.m_per = g.n_mt / 8;
+  g.S = g.n_nt - 1;
+  g.nk = K / kTK;
+  // the whole tiles must take exactly one round of the CUs (8 row groups of
+  // m_per row tiles, one per XCD), the split parts at least two k stages each
+  if (g.n_mt % 8 != 0 || g.S < 2 || 8 * g.m_per * g.S != num_cus || g.nk < 2 * g.S ||
+      scratch_bytes < gemm_pair_scratch_bytes(M, N1, N2))
+    return false;
+  gemm_pair_kernel<<<8 * g.m_per * 2 * g.S, kTThreads, 0, st>>>(g);
+  const long chunks = (long)g.n_mt * kTM * 64;
+  gemm_pair_reduce_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(g);
+  return true;
 }
 
 void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, int K, long lda,

@@ -73,6 +73,18 @@ void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, in
                          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
                          int c_f32, bool b_transposed, hipStream_t st, int nb = 0, long sBn = 0,
                          const void* gmul = nullptr);
+// Two float32 GEMMs that share A, C1 = alpha A B1 ([M, N1]) and C2 = alpha
+// A B2 ([M, N2]), B row-major, as one launch that fills the CUs when their
+// whole tiles make exactly one round (the last column tile split along k
+// into partial tiles in `scratch`, gemm_pair_scratch_bytes of it, added in a
+// fixed order by a second launch).  Returns false, having launched nothing,
+// for other shapes (N1 a multiple of 256, M a multiple of 2048, K of 32,
+// 16-byte rows) or a smaller scratch.
+size_t gemm_pair_scratch_bytes(int M, int N1, int N2);
+bool launch_gemm_pair_f32(const void* A, int M, int K, long lda, const void* B1, int N1,
+                          long ldb1, float* C1, long ldc1, const void* B2, int N2, long ldb2,
+                          float* C2, long ldc2, float alpha, int num_cus, void* scratch,
+                          size_t scratch_bytes, hipStream_t st);
 // Gated GEMM (bf16 out, batch 1): C = gmul * sigmoid(alpha A B), gmul [M, N]
 // laid out as C (row stride ldc).
 void launch_gemm_bf16_gated(const void* A, const void* B, void* C, int M, int N, int K, long lda,

@@ -688,19 +688,31 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   hipStream_t st = (hipStream_t)stream;
   const int QW = d.H * (d.Dn + d.Dr);
   const float alpha = d.scale * 1.4426950408889634f;
-  // 1. cache rows
+  // 1. cache rows (with a q rank, x W_DQ goes in the same launch as x W_DKV:
+  //    both read x, and together they fill the CUs)
   float* z = (float*)at(workspace, w.z);
-  gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
+  float* cq32 = d.Rq > 0 ? (float*)at(workspace, w.cq32) : nullptr;
+  // (the query buffer, not yet written, holds the split partial tiles)
+  const bool paired =
+      d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
+      mla::launch_gemm_pair_f32(x, (int)n, d.M, d.M, w_dq, d.Rq, d.Rq, cq32, d.Rq, w_dkv, d.W,
+                                d.W, z, d.W, 1.0f, num_cus(), at(workspace, w.q),
+                                (size_t)n * d.H * (d.Dn + d.Dr) * d.esz, st);
+  void* cq = d.Rq > 0 ? at(workspace, w.cq) : nullptr;
+  if (paired)  // normalise c_q while it is still in the cache
+    mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
+  else
+    gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
   mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
                                 max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
                                 d.dt, st);
   // 2. queries
   void* q = at(workspace, w.q);
   if (d.Rq > 0) {
-    float* cq32 = (float*)at(workspace, w.cq32);
-    void* cq = at(workspace, w.cq);
-    gemm(d, x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 0, 0, 0, 1, 1.0f, true, st);
-    mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
+    if (!paired) {
+      gemm(d, x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 0, 0, 0, 1, 1.0f, true, st);
+      mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
+    }
     gemm(d, cq, w_uq, q, (int)n, QW, d.Rq, d.Rq, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
   } else {
     gemm(d, x, w_q, q, (int)n, QW, d.M, d.M, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
