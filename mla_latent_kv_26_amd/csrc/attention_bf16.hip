@@ -97,12 +97,18 @@ struct PageCursor {
     cur = fetch(base, lane);
     nxt = fetch(base + 64, lane);
   }
-  // page id of page index p (p >= base, p < base + 128, non-decreasing)
+  // page id of page index p (p >= base, p < base + 128, non-decreasing).
+  // A new chunk (once per 64 pages) is waited for at once and handed on as
+  // a plain value: a load still in flight in a register carried around the
+  // tile loop makes the compiler wait for every load, tile loads included,
+  // wherever the register is copied.
   __device__ __forceinline__ int page(int p, int lane) {
     if (p - base >= 64) {
       cur = nxt;
       base += 64;
       nxt = fetch(base + 64, lane);
+      wait_vmcnt<0>();
+      asm volatile("" : "+v"(nxt));
     }
     return __builtin_amdgcn_readlane(cur, p - base);
   }
@@ -172,6 +178,11 @@ __device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint
     else
       wait_vmcnt<0>();
   }
+  // The page-id loads went out before the tile loads just waited for, so
+  // they have landed: hand their registers on as plain values (the compiler
+  // would otherwise wait for every load in flight, tile k+1 included, before
+  // it reads a page id).
+  asm volatile("" : "+v"(pc.cur), "+v"(pc.nxt));
   lds_barrier();
   if (k + 2 < n) {
     const int tile = a.tile0 + k + 2;
@@ -267,8 +278,7 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
         if (16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
         hmax = fmaxf(hmax, sacc[tb][v]);
       }
-    hmax = fmaxf(hmax, __shfl_xor(hmax, 16, 64));
-    hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+    hmax = max_xor32(max_xor16(hmax));
     const bool grow = hmax > m + kRescaleSlack;
     const float m_new = grow ? hmax : m;
     const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
@@ -291,8 +301,7 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
     if (lane < 16) lds_st(lds + kOffAlpha + ((k & 1) * kMaxHG + h) * 4, alpha);
     if (lane == 0) lds_st(lds + kOffFlag + ((k & 1) * 4 + sw) * 4, any ? 1.0f : 0.0f);
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_xor32(sum_xor16(l));
   m_out = m;
   l_out = l;
 }

@@ -154,6 +154,18 @@ __device__ __forceinline__ float dpp_f32(float v) {
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
+// max / sum of v over lanes l and l ^ 16 (rows of 16 lanes swapped in pairs
+// by one permlane16 swap; no LDS traffic).  Both lanes get the same bits.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 // max / sum of v over lanes l and l ^ 32 (both lanes get the same bits):
 // one permlane32 swap, no LDS traffic.
 __device__ __forceinline__ float max_xor32(float v) {
