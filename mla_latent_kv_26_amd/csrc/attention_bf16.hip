@@ -32,6 +32,8 @@
 // fragment read 16 distinct 16-byte bank slots, and the 4 rows x 4 chunks
 // of a transposing read (rows 4-aligned, chunks 4-aligned) 16 distinct
 // slots too: neither access pattern has bank conflicts.
+#include <algorithm>
+#include <climits>
 #include "device_common.h"
 #include "launch.h"
 
@@ -698,16 +700,34 @@ __device__ __forceinline__ void store_w_uv(const bf16x8 (&wr)[kWChunks], uint32_
 
 __device__ __forceinline__ void combine_rows(const int* prefix, const float* __restrict__ part_ml,
                                              const bf16* __restrict__ part_o, int batch, int H,
-                                             int hg_heads, int n_wg, const bf16* __restrict__ w_uv,
-                                             int Dv, bf16* __restrict__ out, int h, int b0,
-                                             uint32_t wb, uint32_t ob) {
+                                             int hg_heads, int n_wg, int guess_tiles,
+                                             const bf16* __restrict__ w_uv, int Dv,
+                                             bf16* __restrict__ out, int h, int b0, uint32_t wb,
+                                             uint32_t ob) {
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = h / hg_heads, hl = h % hg_heads;
   const long n_slots = (long)n_wg + batch;
   const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
-
   const int b = b0 + wave;
+
+  // Where this sequence's pieces are if every sequence has guess_tiles
+  // tiles (the common equal-length batch): their statistics and first
+  // values go in flight at once, in parallel with the prefix sums they
+  // would otherwise wait for, and are kept if the real layout matches.
+  int fg = 0, ng = 1;
+  if (b < batch) {
+    const StreamSplit gsplit(batch * guess_tiles, n_wg);
+    fg = gsplit.owner(b * guess_tiles);
+    ng = gsplit.owner((b + 1) * guess_tiles - 1) - fg + 1;
+  }
+  const long slotg = (long)hg * n_slots + fg + min(b, batch - 1);
+  f32x2 ml_raw = *(const f32x2*)(part_ml + ((slotg + min(lane, ng - 1)) * hg_heads + hl) * 2);
+  bf16x8 v[kPieceChunk];
+#pragma unroll
+  for (int u = 0; u < kPieceChunk; ++u)
+    v[u] = *(const bf16x8*)(part_o + ((slotg + min(u, ng - 1)) * hg_heads + hl) * kR + 8 * lane);
+
   const StreamSplit split(prefix[batch], n_wg);
   const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
   int f = 0, n = 0;
@@ -727,16 +747,17 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
     return has_piece(s) ? *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2)
                         : f32x2{-INFINITY, 0.f};
   };
-  // Statistics and the first pieces' values, all in flight, then W_UV.  The
-  // loads are unconditional (piece index clamped to the last piece; what is
-  // not a piece is masked afterwards), so the compiler can wait for each in
-  // turn instead of for everything, W_UV included.
-  const int last = max(n, 1) - 1;
-  const f32x2 ml_raw = *(const f32x2*)(part_ml + ((slot0 + min(lane, last)) * hg_heads + hl) * 2);
-  bf16x8 v[kPieceChunk];
+  // A wrong guess: the statistics and the first pieces' values from the real
+  // slots.  The loads are unconditional (piece index clamped to the last
+  // piece; what is not a piece is masked afterwards), so the compiler can
+  // wait for each in turn instead of for everything, W_UV included.
+  if (f != fg || max(n, 1) != ng) {
+    const int last = max(n, 1) - 1;
+    ml_raw = *(const f32x2*)(part_ml + ((slot0 + min(lane, last)) * hg_heads + hl) * 2);
 #pragma unroll
-  for (int u = 0; u < kPieceChunk; ++u)
-    v[u] = *(const bf16x8*)(part_o + ((slot0 + min(u, last)) * hg_heads + hl) * kR + 8 * lane);
+    for (int u = 0; u < kPieceChunk; ++u)
+      v[u] = *(const bf16x8*)(part_o + ((slot0 + min(u, last)) * hg_heads + hl) * kR + 8 * lane);
+  }
   bf16x8 wr[kWChunks];
   if (W) load_w_uv(W, Dv, wr);
   const f32x2 ml0 = lane < n && has_piece(lane) ? ml_raw : f32x2{-INFINITY, 0.f};
@@ -846,11 +867,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
 // Combine of the partials (the staged call): grid (H, ceil(batch / 8)).
 __global__ void __launch_bounds__(kCThreads) combine_kernel(
     const int* __restrict__ prefix, const float* __restrict__ part_ml,
-    const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg,
+    const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg, int guess_tiles,
     const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char smem[kCWBytes + kCOBytes];
   const uint32_t wb = lds_addr(smem), ob = wb + kCWBytes;
-  combine_rows(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, w_uv, Dv, out, blockIdx.x,
+  combine_rows(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, guess_tiles, w_uv, Dv, out,
+               blockIdx.x,
                blockIdx.y * kCRows, wb, ob);
 }
 
@@ -921,12 +943,14 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
 }
 
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
-                    int heads_per_wg, int n_wg, const void* w_uv, int Dv, void* out,
-                    hipStream_t st) {
+                    int heads_per_wg, int n_wg, int max_seq_len, const void* w_uv, int Dv,
+                    void* out, hipStream_t st) {
   dim3 grid(H, (batch + kCRows - 1) / kCRows);
+  const int guess_tiles =
+      (int)std::clamp(((long)max_seq_len + kTok - 1) / kTok, 1L, (long)INT_MAX / max(batch, 1));
   combine_kernel<<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
-                                           heads_per_wg, n_wg, (const bf16*)w_uv, Dv,
-                                           (bf16*)out);
+                                           heads_per_wg, n_wg, guess_tiles, (const bf16*)w_uv,
+                                           Dv, (bf16*)out);
 }
 
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
