@@ -197,9 +197,21 @@ __device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint
 // returns (in lanes 0..15) the reference max and full row sum of head
 // 16 sw + lane.  Inactive score waves (sw >= SW) only take part in loads and
 // barriers.
+// Queries of head 16 sw + lane%16, chunks 4 ks + lane/16 (the B operand of
+// the score MFMAs), from the segment's query rows.
+__device__ __forceinline__ void load_queries(const bf16* q_rows, int sw, int lane,
+                                             bf16x8 (&qf)[kW / 32]) {
+  const bf16* q = q_rows + (16 * sw + (lane & 15)) * kW + 8 * (lane >> 4);
+#pragma unroll
+  for (int ks = 0; ks < kW / 32; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
+}
+
+// qf: the segment's queries when q_ready (loaded before the segment's
+// tiles), else loaded here.
 template <int HEADS>
 __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int sw, int lane,
-                                           float& m_out, float& l_out) {
+                                           bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,
+                                           float& l_out) {
   using G = Geo<HEADS>;
   const bool active = sw < G::SW;
   const int n = a.tile1 - a.tile0;
@@ -209,12 +221,8 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
 
   const int h = 16 * sw + (lane & 15);
   const uint32_t kq = lane >> 4;
-  bf16x8 qf[kW / 32];
-  if (active) {
-    const bf16* q = a.q_rows + h * kW + 8 * kq;
-#pragma unroll
-    for (int ks = 0; ks < kW / 32; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
-  }
+  if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
+  // tile 0 and the queries (issued before tile 1) land; tile 1 may stay in flight
   if (n > 1) {
     const int tile = a.tile0 + 1;
     issue_part<kSLoads>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
@@ -401,46 +409,14 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
   }
 }
 
-// A whole segment plus its normalised output: score waves publish 1/l per
-// head, P*C waves stage O/l in LDS (the tile buffers, idle by then), all
-// waves copy it out with 16-byte stores.  m and the sum come back in lanes
+// A whole segment plus its normalised output, in two halves by wave role
+// (with the same barriers): score waves publish 1/l per head, P*C waves
+// stage O/l in LDS (the tile buffers, idle by then), then all waves copy it
+// out with 16-byte stores (copy_out).  m and the sum come back in lanes
 // 0..15 of the active score waves (for the split statistics).  Ends with a
 // barrier, so the next segment may refill the buffers.
 template <int HEADS>
-__device__ __forceinline__ void attend_segment(const SegArgs& a, uint32_t lds, bf16* dst,
-                                               int wave, int lane, float& m_out, float& l_out) {
-  using G = Geo<HEADS>;
-  if (wave < 4) {
-    score_role<HEADS>(a, lds, wave, lane, m_out, l_out);
-    if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
-    lds_barrier();
-    lds_barrier();
-  } else {
-    const int pw = wave - 4;
-    OAcc<HEADS> acc;
-    pv_role<HEADS>(a, lds, pw, lane, acc);
-    lds_barrier();
-    // lane: head 32 hb + lane%32; register v of o[hb][cb]: column
-    // 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 (runs of 4 -> 8-byte stores)
-#pragma unroll
-    for (int hb = 0; hb < G::HB; ++hb) {
-      const int head = 32 * hb + (lane & 31);
-      const float inv = lds_ld(lds + kOffInv + head * 4);
-      const uint32_t row = lds + (head * kOStride + 128 * pw + 4 * (lane >> 5)) * 2;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 w4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) w4[r] = (bf16)(acc.o[hb][cb][4 * q + r] * inv);
-          lds_st(row + (32 * cb + 8 * q) * 2, w4);
-        }
-    }
-    lds_barrier();
-    m_out = 0.f;
-    l_out = 0.f;
-  }
+__device__ __forceinline__ void copy_out(uint32_t lds, bf16* dst) {
 #pragma unroll
   for (int i0 = 0; i0 < HEADS * kR / 8; i0 += kThreads) {
     const int i = i0 + (int)threadIdx.x;
@@ -449,6 +425,47 @@ __device__ __forceinline__ void attend_segment(const SegArgs& a, uint32_t lds, b
                                 (bf16x8*)(dst + hh * kR + c8));
   }
   lds_barrier();
+}
+
+template <int HEADS>
+__device__ __forceinline__ void score_segment(const SegArgs& a, uint32_t lds, bf16* dst, int wave,
+                                              int lane, bf16x8 (&qf)[kW / 32], bool q_ready,
+                                              float& m_out, float& l_out) {
+  using G = Geo<HEADS>;
+  score_role<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
+  if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
+  lds_barrier();
+  lds_barrier();
+  copy_out<HEADS>(lds, dst);
+}
+
+template <int HEADS>
+__device__ __forceinline__ void pv_segment(const SegArgs& a, uint32_t lds, bf16* dst, int wave,
+                                           int lane) {
+  using G = Geo<HEADS>;
+  const int pw = wave - 4;
+  OAcc<HEADS> acc;
+  pv_role<HEADS>(a, lds, pw, lane, acc);
+  lds_barrier();
+  // lane: head 32 hb + lane%32; register v of o[hb][cb]: column
+  // 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 (runs of 4 -> 8-byte stores)
+#pragma unroll
+  for (int hb = 0; hb < G::HB; ++hb) {
+    const int head = 32 * hb + (lane & 31);
+    const float inv = lds_ld(lds + kOffInv + head * 4);
+    const uint32_t row = lds + (head * kOStride + 128 * pw + 4 * (lane >> 5)) * 2;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 w4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w4[r] = (bf16)(acc.o[hb][cb][4 * q + r] * inv);
+        lds_st(row + (32 * cb + 8 * q) * 2, w4);
+      }
+  }
+  lds_barrier();
+  copy_out<HEADS>(lds, dst);
 }
 
 // Workgroup -> (head group, stream index).  Blocks go round-robin over the
@@ -555,26 +572,36 @@ __device__ __forceinline__ bool decode_attention_wg(
   // Where this workgroup's range would start if every sequence had
   // guess_tiles tiles (the common equal-length batch): load that page-id
   // chunk now, in parallel with the lengths, and keep it if the guess holds.
-  // As soon as the ids land, the guessed first tile (as a full tile) goes
-  // in flight into buffer 0, overlapping the prefix sums and the range
-  // search; a page id outside the pool is never dereferenced.
-  const int xg = StreamSplit(batch * guess_tiles, n_wg).start(w);
+  // As soon as the ids land, the guessed first tile (as a full tile) goes in
+  // flight into buffer 0, then the guessed sequence's queries (score waves),
+  // overlapping the prefix sums and the range search; a page id outside the
+  // pool is never dereferenced.  (Issuing three tiles there measured slower:
+  // the opening burst delays every workgroup's first tile.)
+  const StreamSplit gsplit(batch * guess_tiles, n_wg);
+  const int xg = gsplit.start(w);
   const int bg = min(xg / guess_tiles, batch - 1);
   const int tg0 = xg - bg * guess_tiles;
   const int pg0 = (tg0 * kTok) >> shift;
   PageCursor spec;
   spec.start(block_table + (long)bg * max_blocks, max_blocks, pg0, lane);
+  bf16x8 qf[kW / 32];  // score waves: the queries of sequence qb
+  int qb = -1;
   bool spec_issued = false;
   auto early = [&]() {
     const int page = spec.page(pg0, lane);
-    if (page < 0 || page >= num_blocks) return;
-    const int tok = tg0 * kTok;
-    const bf16* rows = pool + ((long)page * (1 << shift) + (tok & ((1 << shift) - 1))) * kW;
-    if (wave < 4)
-      issue_part<kSLoads>(rows, kTok, lds, (uint32_t)wave * kSLoads, lane);
-    else
-      issue_part<kPLoads>(rows, kTok, lds, 4u * kSLoads + (uint32_t)(wave - 4) * kPLoads, lane);
-    spec_issued = true;
+    if (page >= 0 && page < num_blocks) {
+      const int tok = tg0 * kTok;
+      const bf16* rows = pool + ((long)page * (1 << shift) + (tok & ((1 << shift) - 1))) * kW;
+      if (wave < 4)
+        issue_part<kSLoads>(rows, kTok, lds, (uint32_t)wave * kSLoads, lane);
+      else
+        issue_part<kPLoads>(rows, kTok, lds, 4u * kSLoads + (uint32_t)(wave - 4) * kPLoads, lane);
+      spec_issued = true;
+    }
+    if (wave < Geo<HEADS>::SW) {
+      load_queries(q_full + ((long)bg * H + hg * HEADS) * kW, wave, lane, qf);
+      qb = bg;
+    }
   };
 
   tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo, early);
@@ -583,50 +610,68 @@ __device__ __forceinline__ bool decode_attention_wg(
     for (int b = tid; b <= batch; b += kThreads) prefix_out[b] = prefix[b];
 
   const StreamSplit split(T, n_wg);
-  int x0 = split.start(w);
+  const int x0 = split.start(w);
   const int x1 = split.start(w + 1);
   if (x0 >= x1) {
-    if (spec_issued) wait_vmcnt<0>();  // no load may land in LDS after the exit
+    wait_vmcnt<0>();  // no load may land in LDS after the exit
     return false;
   }
   // first sequence touching x0
-  int b = 0;
+  int b0 = 0;
   {
     int lo = 0, hi = batch - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (prefix[mid] <= x0) lo = mid; else hi = mid - 1;
     }
-    b = lo;
+    b0 = lo;
   }
   const long n_slots = (long)n_wg + batch;
-  while (x0 < x1) {
-    const int p0 = prefix[b], p1 = prefix[b + 1];
-    const int seg_end = min(x1, p1);
-    const int tile0 = x0 - p0, tile1 = seg_end - p0;
-    if (tile1 <= tile0) {  // a sequence without rows (invalid input): nothing to attend
+  // The segments of [x0, x1), one per sequence, in order; both wave roles
+  // walk them with the same barriers (the roles are split at the top, so
+  // the score waves' queries and the P*C waves' accumulators never share
+  // registers).
+  auto walk = [&](auto&& segment) {
+    int x = x0, b = b0;
+    while (x < x1) {
+      const int p0 = prefix[b], p1 = prefix[b + 1];
+      const int seg_end = min(x1, p1);
+      const int tile0 = x - p0, tile1 = seg_end - p0;
+      if (tile1 <= tile0) {  // a sequence without rows (invalid input): nothing to attend
+        ++b;
+        continue;
+      }
+      const int len = (p1 - p0 - 1) * kTok + lenlo[b] + 1;
+      const long slot = (long)hg * n_slots + w + b;
+      const bool guessed = b == bg && ((tile0 * kTok) >> shift) == pg0;
+      // the speculative tile is this segment's tile 0 only if it is the same
+      // tile and a full one (a partial tile repeats its last row instead)
+      const bool reuse = spec_issued && guessed && tile0 == tg0 && (tile0 + 1) * kTok <= len;
+      if (spec_issued && !reuse) wait_vmcnt<0>();  // its loads land before buffer 0 is refilled
+      const SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool,
+                      block_table + (long)b * max_blocks, max_blocks, shift, len, tile0, tile1,
+                      guessed ? &spec : nullptr, reuse};
+      spec_issued = false;
+      segment(a, b, slot);
+      x = seg_end;
       ++b;
-      continue;
     }
-    const int len = (p1 - p0 - 1) * kTok + lenlo[b] + 1;
-    const long slot = (long)hg * n_slots + w + b;
-    const bool guessed = b == bg && ((tile0 * kTok) >> shift) == pg0;
-    // the speculative tile is this segment's tile 0 only if it is the same
-    // tile and a full one (a partial tile repeats its last row instead)
-    const bool reuse = spec_issued && guessed && tile0 == tg0 && (tile0 + 1) * kTok <= len;
-    if (spec_issued && !reuse) wait_vmcnt<0>();  // its loads land before buffer 0 is refilled
-    spec_issued = false;
-    SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
-              max_blocks, shift, len, tile0, tile1, guessed ? &spec : nullptr, reuse};
-    float m, tot;
-    attend_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane, m, tot);
-    if (wave < Geo<HEADS>::SW && lane < 16) {
-      const int h = 16 * wave + lane;
-      const f32x2 ml = {m, tot};
-      __builtin_nontemporal_store(ml, (f32x2*)(part_ml + (slot * HEADS + h) * 2));
-    }
-    x0 = seg_end;
-    ++b;
+  };
+  if (wave < 4) {
+    walk([&](const SegArgs& a, int b, long slot) {
+      float m, tot;
+      score_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane, qf, qb == b, m, tot);
+      qb = b;
+      if (wave < Geo<HEADS>::SW && lane < 16) {
+        const int h = 16 * wave + lane;
+        const f32x2 ml = {m, tot};
+        __builtin_nontemporal_store(ml, (f32x2*)(part_ml + (slot * HEADS + h) * 2));
+      }
+    });
+  } else {
+    walk([&](const SegArgs& a, int, long slot) {
+      pv_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane);
+    });
   }
   if (spec_issued) wait_vmcnt<0>();
   return true;
@@ -698,6 +743,8 @@ __device__ __forceinline__ void store_w_uv(const bf16x8 (&wr)[kWChunks], uint32_
   *(lds_bf16x8*)(uintptr_t)(ob + o_off(kCRows + wave, lane)) = bf16x8{};
 }
 
+// kProject: w_uv is given (non-NULL) and out receives o_lat W_UV.
+template <bool kProject>
 __device__ __forceinline__ void combine_rows(const int* prefix, const float* __restrict__ part_ml,
                                              const bf16* __restrict__ part_o, int batch, int H,
                                              int hg_heads, int n_wg, int guess_tiles,
@@ -705,16 +752,21 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
                                              bf16* __restrict__ out, int h, int b0, uint32_t wb,
                                              uint32_t ob) {
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index as a wave-uniform value: the prefix sums below then come
+  // through scalar loads, whose waits do not hold up the vector loads
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = h / hg_heads, hl = h % hg_heads;
   const long n_slots = (long)n_wg + batch;
-  const bf16* W = w_uv ? w_uv + (long)h * kR * Dv : nullptr;
+  const bf16* W = kProject ? w_uv + (long)h * kR * Dv : nullptr;
   const int b = b0 + wave;
+  const int total = prefix[batch];
+  const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
 
   // Where this sequence's pieces are if every sequence has guess_tiles
   // tiles (the common equal-length batch): their statistics and first
-  // values go in flight at once, in parallel with the prefix sums they
-  // would otherwise wait for, and are kept if the real layout matches.
+  // values go in flight at once, with W_UV behind them, in parallel with
+  // the prefix sums, and are kept if the real layout matches.
   int fg = 0, ng = 1;
   if (b < batch) {
     const StreamSplit gsplit(batch * guess_tiles, n_wg);
@@ -727,9 +779,10 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
 #pragma unroll
   for (int u = 0; u < kPieceChunk; ++u)
     v[u] = *(const bf16x8*)(part_o + ((slotg + min(u, ng - 1)) * hg_heads + hl) * kR + 8 * lane);
+  bf16x8 wr[kWChunks];
+  if constexpr (kProject) load_w_uv(W, Dv, wr);
 
-  const StreamSplit split(prefix[batch], n_wg);
-  const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
+  const StreamSplit split(total, n_wg);
   int f = 0, n = 0;
   if (p1 > p0) {
     f = split.owner(p0);
@@ -747,19 +800,21 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
     return has_piece(s) ? *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2)
                         : f32x2{-INFINITY, 0.f};
   };
-  // A wrong guess: the statistics and the first pieces' values from the real
-  // slots.  The loads are unconditional (piece index clamped to the last
-  // piece; what is not a piece is masked afterwards), so the compiler can
-  // wait for each in turn instead of for everything, W_UV included.
+  // A wrong guess: the statistics and the first pieces' values again from
+  // the real slots (piece index clamped to the last piece; what is not a
+  // piece is masked afterwards), waited for here, so that on the common path
+  // the compiler still waits for each piece in turn and not for W_UV.
   if (f != fg || max(n, 1) != ng) {
     const int last = max(n, 1) - 1;
     ml_raw = *(const f32x2*)(part_ml + ((slot0 + min(lane, last)) * hg_heads + hl) * 2);
 #pragma unroll
     for (int u = 0; u < kPieceChunk; ++u)
       v[u] = *(const bf16x8*)(part_o + ((slot0 + min(u, last)) * hg_heads + hl) * kR + 8 * lane);
+    wait_vmcnt<0>();
+    asm volatile("" : "+v"(ml_raw));
+#pragma unroll
+    for (int u = 0; u < kPieceChunk; ++u) asm volatile("" : "+v"(v[u]));
   }
-  bf16x8 wr[kWChunks];
-  if (W) load_w_uv(W, Dv, wr);
   const f32x2 ml0 = lane < n && has_piece(lane) ? ml_raw : f32x2{-INFINITY, 0.f};
 
   float M = ml0[0];
@@ -815,7 +870,7 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
   bf16x8 o;
 #pragma unroll
   for (int e8 = 0; e8 < 8; ++e8) o[e8] = (bf16)(acc[e8] * inv);
-  if (!W) {
+  if constexpr (!kProject) {
     if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
     return;
   }
@@ -826,24 +881,35 @@ __device__ __forceinline__ void combine_rows(const int* prefix, const float* __r
   // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows (8 used) x Dv, K = 512,
   // 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
   if (16 * wave >= Dv) return;
-  f32x4 pacc = {};
+  // Eight k-steps at a time: all their LDS reads first, then the MFMAs,
+  // alternating between two accumulators (shorter dependency chains).
+  f32x4 pacc[2] = {};
   const int g = lane >> 4, li = lane & 15;
-#pragma unroll 4
-  for (int ks = 0; ks < kR / 32; ++ks) {
-    // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
-    const uint32_t row = 32 * ks + 8 * g + (li >> 2);
-    const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
-    const bf16x4 lo = lds_read_tr(wb + w_off(row, c) + sub);
-    const bf16x4 hi = lds_read_tr(wb + w_off(row + 4, c) + sub);
-    const bf16x8 a = lds_read_b128(ob + o_off(lane & 15, 4 * ks + (lane >> 4)));
-    pacc = mfma16(a, cat(lo, hi), pacc);
+#pragma unroll
+  for (int k8 = 0; k8 < kR / 32; k8 += 8) {
+    bf16x8 a[8], bw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      a[u] = lds_read_b128(ob + o_off(lane & 15, 4 * (k8 + u) + (lane >> 4)));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
+      const uint32_t row = 32 * (k8 + u) + 8 * g + (li >> 2);
+      const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
+      bw[u] = cat(lds_read_tr(wb + w_off(row, c) + sub), lds_read_tr(wb + w_off(row + 4, c) + sub));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pacc[u & 1] = mfma16(a[u], bw[u], pacc[u & 1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // the 24 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
   }
   // register v of lane l: row 4(l/16) + v, column l%16
 #pragma unroll
   for (int v4 = 0; v4 < 4; ++v4) {
     const int r = 4 * (lane >> 4) + v4;
     if (r < kCRows && b0 + r < batch)
-      out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] = (bf16)pacc[v4];
+      out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] =
+          (bf16)(pacc[0][v4] + pacc[1][v4]);
   }
 }
 
@@ -865,15 +931,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
 }
 
 // Combine of the partials (the staged call): grid (H, ceil(batch / 8)).
+template <bool kProject>
 __global__ void __launch_bounds__(kCThreads) combine_kernel(
     const int* __restrict__ prefix, const float* __restrict__ part_ml,
     const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg, int guess_tiles,
     const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char smem[kCWBytes + kCOBytes];
   const uint32_t wb = lds_addr(smem), ob = wb + kCWBytes;
-  combine_rows(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, guess_tiles, w_uv, Dv, out,
-               blockIdx.x,
-               blockIdx.y * kCRows, wb, ob);
+  combine_rows<kProject>(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, guess_tiles, w_uv,
+                         Dv, out, blockIdx.x, blockIdx.y * kCRows, wb, ob);
 }
 
 // ---------------------------------------------------------------------------
@@ -900,8 +966,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
   (void)tid;
   SegArgs a{q_full + ((long)n * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
             max_blocks, shift, len, 0, (len + kTok - 1) / kTok, nullptr, false};
-  float m, tot;
-  attend_segment<HEADS>(a, lds, o_lat + ((long)n * H + hg * HEADS) * kR, wave, lane, m, tot);
+  bf16* dst = o_lat + ((long)n * H + hg * HEADS) * kR;
+  if (wave < 4) {
+    bf16x8 qf[kW / 32];
+    float m, tot;
+    score_segment<HEADS>(a, lds, dst, wave, lane, qf, false, m, tot);
+  } else {
+    pv_segment<HEADS>(a, lds, dst, wave, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -948,9 +1020,14 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
   dim3 grid(H, (batch + kCRows - 1) / kCRows);
   const int guess_tiles =
       (int)std::clamp(((long)max_seq_len + kTok - 1) / kTok, 1L, (long)INT_MAX / max(batch, 1));
-  combine_kernel<<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
-                                           heads_per_wg, n_wg, guess_tiles, (const bf16*)w_uv,
-                                           Dv, (bf16*)out);
+  if (w_uv)
+    combine_kernel<true><<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch,
+                                                     H, heads_per_wg, n_wg, guess_tiles,
+                                                     (const bf16*)w_uv, Dv, (bf16*)out);
+  else
+    combine_kernel<false><<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch,
+                                                      H, heads_per_wg, n_wg, guess_tiles, nullptr,
+                                                      Dv, (bf16*)out);
 }
 
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
