@@ -24,7 +24,7 @@ def command(out=LIB, extra=()):
     return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            "-x", "hip", *sources(), "-o", out, *extra]
+            "-x", "hip", *sources(), "-o", out, "-lhipblaslt", *extra]
 
 
 def build(verbose: bool = False) -> str:

@@ -54,6 +54,17 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 
 // g[i] = h[i] * sigmoid(g[i]) for i < n (float32 output gate).
 void launch_gate_mul_f32(float* g, const float* h, long n, hipStream_t st);
+// The same in bf16 (float32 math), n a multiple of 8, 16-byte aligned arrays.
+void launch_gate_mul_bf16(void* g, const void* h, long n, hipStream_t st);
+
+// Row-major C [M, N] = alpha A [M, K] B through hipBLASLt (blas_lt.cpp): A
+// bf16 (row stride lda), B bf16 row-major [K, N] or, when b_transposed,
+// [N, K] (row stride ldb), C bf16 or float32 (row stride ldc), float32
+// accumulation.  Returns false, having launched nothing, when the library is
+// unavailable or switched off (MLA_GEMM=tile), the shape is small (M < 256,
+// N < 128 or K < 32) or it has no algorithm for it.
+bool blas_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
+                    long ldc, float alpha, bool c_f32, bool b_transposed, hipStream_t st);
 
 // ---- bf16 MFMA kernels (gfx950) ----
 

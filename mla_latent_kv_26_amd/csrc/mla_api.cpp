@@ -693,16 +693,22 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   //    both read x, and together they fill the CUs)
   float* z = (float*)at(workspace, w.z);
   float* cq32 = d.Rq > 0 ? (float*)at(workspace, w.cq32) : nullptr;
-  // (the query buffer, not yet written, holds the split partial tiles)
+  // x W_DQ by the library GEMM when it takes the shape; otherwise, when the
+  // shapes allow, x W_DQ and x W_DKV as one launch of the tile kernel (the
+  // query buffer, not yet written, holds its split partial tiles)
+  const bool lib_q = d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
+                     mla::blas_gemm_bf16(x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 1.0f,
+                                         true, false, st);
   const bool paired =
-      d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
+      !lib_q && d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
       mla::launch_gemm_pair_f32(x, (int)n, d.M, d.M, w_dq, d.Rq, d.Rq, cq32, d.Rq, w_dkv, d.W,
                                 d.W, z, d.W, 1.0f, num_cus(), at(workspace, w.q),
                                 (size_t)n * d.H * (d.Dn + d.Dr) * d.esz, st);
   void* cq = d.Rq > 0 ? at(workspace, w.cq) : nullptr;
-  if (paired)  // normalise c_q while it is still in the cache
+  const bool have_cq = lib_q || paired;
+  if (have_cq)  // normalise c_q while it is still in the cache
     mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
-  else
+  if (!paired)
     gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
   mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
                                 max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
@@ -710,7 +716,7 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   // 2. queries
   void* q = at(workspace, w.q);
   if (d.Rq > 0) {
-    if (!paired) {
+    if (!have_cq) {
       gemm(d, x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 0, 0, 0, 1, 1.0f, true, st);
       mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
     }
@@ -731,9 +737,9 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
     if (mla::gemm_tile256_fits(w.ctx_pad, d.H * d.Dn, d.R, d.W, d.R, (long)d.H * d.Dn) &&
         mla::gemm_tile256_fits(w.ctx_pad, d.H * d.Dv, d.R, d.W, d.Dv, (long)d.H * d.Dv) &&
         d.Dv % 8 == 0) {
-      mla::launch_gemm_tile256(cg, w_uk, at(workspace, w.kn), w.ctx_pad, d.H * d.Dn, d.R, d.W,
+      mla::launch_gemm_bf16_bt(cg, w_uk, at(workspace, w.kn), w.ctx_pad, d.H * d.Dn, d.R, d.W,
                                d.R, (long)d.H * d.Dn, sa, 0, (long)w.ctx_pad * d.H * d.Dn, batch,
-                               1.0f, 0, true, st);
+                               1.0f, 0, st);
       mla::launch_gemm_tile256(cg, w_uv, at(workspace, w.vv), w.ctx_pad, d.H * d.Dv, d.R, d.W,
                                d.Dv, (long)d.H * d.Dv, sa, 0, (long)w.ctx_pad * d.H * d.Dv, batch,
                                1.0f, 0, false, st, d.Dv, (long)d.R * d.Dv);
