@@ -234,12 +234,15 @@ void launch_bk(const void* A, const void* B, void* C, int M, int N, int K, long 
                            st);
 }
 
-// Each batch item through hipBLASLt.  False, with nothing launched, when the
-// library does not take the first item; an item after that which it refuses
-// (not expected: same shape) goes to the tile kernel on its own.
+// Each batch item through hipBLASLt, for a few items (sequences of a
+// prefill); many small ones (one per head) stay one batched tile launch.
+// False, with nothing launched, when the library does not take the first
+// item; an item after that which it refuses (not expected: same shape) goes
+// to the tile kernel on its own.
 bool blas_batched(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
                   long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, bool bt,
                   hipStream_t st) {
+  if (batch > 4) return false;
   const size_t ec = c_f32 ? 4 : 2;
   for (int b = 0; b < batch; ++b) {
     const void* a = (const char*)A + (size_t)b * sA * 2;

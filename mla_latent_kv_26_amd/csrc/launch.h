@@ -112,6 +112,13 @@ void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K
                       long side_ld = 0, long side_sb = 0, void* side_dst = nullptr,
                       int side_cols = 0);
 
+// Query absorption for the bf16 decode: q_full[b, h] = alpha [q_nope[b, h]
+// W_UK[h] | q_rope[b, h]] (absorb_bf16.hip).  Returns false, having launched
+// nothing, unless Dn = 128, R = 512 and Dr = 64.
+bool launch_absorb_query_bf16(const void* q_nope, const void* q_rope, const void* w_uk,
+                              void* q_full, int B, int H, int Dn, int R, int Dr, float alpha,
+                              hipStream_t st);
+
 // Decode attention over a paged bf16 pool, R = 512, Dr = 64, 32 or 64 heads
 // per workgroup, block_size a power of two >= 64.  Writes split partials
 // (bf16 O normalised by its own sum, float32 (m, l) in log2 units) and the

@@ -239,6 +239,9 @@ void enqueue_absorb(const Dims& d, const void* q_nope, const void* q_rope, const
                     int n_rows, void* q_full, hipStream_t st) {
   const float alpha = d.scale * 1.4426950408889634f;
   if (d.dt == MLA_DTYPE_BF16) {
+    if (mla::launch_absorb_query_bf16(q_nope, q_rope, w_uk, q_full, n_rows, d.H, d.Dn, d.R, d.Dr,
+                                      alpha, st))
+      return;
     // one launch: q_lat = alpha * q_nope W_UK, plus the scaled copy of q_rope
     mla::launch_gemm_bf16(q_nope, w_uk, q_full, n_rows, d.R, d.Dn, (long)d.H * d.Dn, d.R,
                           (long)d.H * d.W, d.Dn, (long)d.Dn * d.R, d.W, d.H, alpha, 0, st, q_rope,

@@ -7,6 +7,7 @@ bf16 storage relative L2 <= 5e-3 and max abs <= 2e-2 (plus the cosine floor
 printed by the tutorial's bf16 run).
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -267,6 +268,19 @@ def test_staged_calls_match_decode_and_oracle_latent(m):
     assert_bf16(to_host_f64(qf), want, "q_full")
 
 
+@pytest.fixture(params=["library", "tile"])
+def gemm_backend(request):
+    """Plain GEMMs through hipBLASLt (the default) or forced onto the
+    hand-written tile kernel (MLA_GEMM=tile), so both stay covered."""
+    old = os.environ.pop("MLA_GEMM", None)
+    if request.param == "tile":
+        os.environ["MLA_GEMM"] = "tile"
+    yield request.param
+    os.environ.pop("MLA_GEMM", None)
+    if old is not None:
+        os.environ["MLA_GEMM"] = old
+
+
 def test_output_projection_many_rows(m):
     """From 256 rows on, the projection takes the 256-row tile GEMM
     (direct-to-LDS stages, transposed accumulators): 700 and 300 rows (a
@@ -368,7 +382,7 @@ def test_prefill_small_bf16_with_query_rank_and_continuation(m):
         assert_bf16(got[b], ref, f"small prefill b={b}", per_row_axis=0)
 
 
-def test_prefill_per_head_path_with_continuation(m):
+def test_prefill_per_head_path_with_continuation(m, gemm_backend):
     """Spans long enough for the per-head key/value path (600 new tokens,
     then 300 more at position 600): partial query blocks, keys from earlier
     calls through permuted pages, jittered gains; outputs and cache rows
@@ -464,7 +478,7 @@ def test_output_gate_bf16_decode_rows(m):
         assert_bf16(got, ref, f"gate={gated}", per_row_axis=0)
 
 
-def test_output_gate_bf16_many_rows(m):
+def test_output_gate_bf16_many_rows(m, gemm_backend):
     """bf16, 600 rows (the 256-row tile GEMM, ragged last row tile), d_model
     1024, 16 heads of 128."""
     cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=1024, q_lora_rank=0,
