@@ -678,32 +678,42 @@ __device__ __forceinline__ bool decode_attention_wg(
 }
 
 // ---------------------------------------------------------------------------
-// Combine (+ optional W_UV projection) of 8 sequences for one head: 8 waves,
-// one sequence each; lane l holds columns 8 l .. 8 l + 7 of o_lat.
+// Combine (+ optional W_UV projection): one workgroup per (head, S
+// consecutive sequences), 8 waves; lane l holds columns 8 l .. 8 l + 7 of a
+// row of o_lat.
 //   o_lat[b, h] = sum_s e_s O_s / sum_s e_s,  e_s = 2^(m_s - M) l_s.
-// Global round trips after the prefix sums: every piece's statistics and
-// the first pieces' values at once.  A wave's loads complete in issue order,
-// so W_UV (streamed into LDS with direct-to-LDS loads) is issued after them,
-// A piece is read only if its workgroup's range is non-empty (with fewer
-// tiles than workgroups some write nothing), so stale workspace contents
-// never enter the merge.
-// Measured: the combine is bound by per-CU bandwidth, so more workgroups of
-// fewer sequences beat fewer larger ones (4 sequences per wave on a quarter
-// of the workgroups ran the step 8 us slower at 32 sequences).
+// S is picked on the host so that the grid fills the CUs once (8 at 32
+// sequences x 64 heads, 1 at 4 long sequences, 32 at 64 sequences x 128
+// heads): with S < 8, 8/S waves share a sequence, each taking every
+// (8/S)-th piece, and their partial sums meet in LDS; with S > 8 a wave
+// merges S/8 sequences in turn.  Every wave computes all of its sequence's
+// weights (one statistics load per 64 pieces), so partial sums share one
+// reference max and add without rescaling, in a fixed order.
+// The first pieces of a wave's first sequence are fetched at the slots they
+// have in the equal-length layout (guessed from max_seq_len) before the
+// prefix sums (scalar loads) arrive, and reloaded only when the real layout
+// differs.  W_UV[h] (128 KB) streams into LDS with direct-to-LDS loads
+// issued after them, so it takes no registers and does not delay them; the
+// merge touches no LDS until its row is written, so nothing waits for W_UV
+// before that.  A piece is read only if its workgroup's range is non-empty
+// (with fewer tiles than workgroups some write nothing), so stale workspace
+// contents never enter the merge.
 // ---------------------------------------------------------------------------
 constexpr int kCWaves = 8;
 constexpr int kCThreads = 64 * kCWaves;
-constexpr int kCRows = kCWaves;           // sequences per workgroup
-constexpr int kPieceChunk = 8;            // pieces whose values are in flight together
-constexpr int kCOBytes = 16 * kR * 2;     // o_lat rows (16: the MFMA height; 8..15 zero)
-constexpr int kCWBytes = kR * 128 * 2;    // W_UV[h] (Dv <= 128)
+constexpr int kCMaxRows = 32;                  // sequences per workgroup, at most
+constexpr int kCOBytes = kCMaxRows * kR * 2;   // o_lat rows (partial sums at +16 KB when S < 8)
+constexpr int kCWBytes = kR * 128 * 2;         // W_UV[h] (Dv <= 128)
+constexpr int kCWLoads = kCWBytes / (kCThreads * 16);
+static_assert(kCWBytes + kCOBytes <= 163840, "LDS budget");
 
 // W_UV[h] in LDS: rows of 16 chunks (256 B, Dv <= 128), chunk c of row r at
 // position c ^ 2((r % 4) + 4 ((r / 8) % 2)), so the 8 rows (r0 .. r0+3 and
 // r0+8 .. r0+11) x 2 chunks that 32 lanes of a transposing read touch fall
 // on 16 distinct bank slots.
+__device__ __forceinline__ uint32_t w_swz(uint32_t r) { return ((r & 3u) | ((r >> 1) & 4u)) << 1; }
 __device__ __forceinline__ uint32_t w_off(uint32_t r, uint32_t c) {
-  return (r * 16u + (c ^ (((r & 3u) | ((r >> 1) & 4u)) << 1))) * 16u;
+  return (r * 16u + (c ^ w_swz(r))) * 16u;
 }
 // o_lat rows in LDS: 1 KB each, 16-byte chunk c of row r at position
 // c ^ (r % 16), so the 16 rows of a fragment read hit distinct bank groups.
@@ -711,205 +721,233 @@ __device__ __forceinline__ uint32_t o_off(uint32_t r, uint32_t c) {
   return (r * (kR / 8) + (c ^ (r & 15u))) * 16u;
 }
 
-// W_UV[h] goes through registers (16 chunks of 16 bytes per thread): plain
-// loads keep the compiler's per-load waits exact, where direct-to-LDS loads
-// in flight make it wait for everything before the first piece is used.
-constexpr int kWChunks = kR * 16 / 64 / kCWaves;
-
-__device__ __forceinline__ void load_w_uv(const bf16* W, int Dv, bf16x8 (&wr)[kWChunks]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // slot s = 64 j + lane holds row s/16, the chunk w_off puts at s%16; chunks
-  // past Dv/8 load the row's chunk 0 (unused)
+// Direct-to-LDS loads of W_UV[h]: instruction j of the workgroup fills slots
+// 64 j .. 64 j + 63, slot s holding row s/16, the chunk w_off puts at s%16;
+// chunks past Dv/8 load the row's chunk 0 (never read).
+__device__ __forceinline__ void issue_w_uv(const bf16* W, int Dv, uint32_t wb, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < kWChunks; ++i) {
-    const uint32_t j = (uint32_t)wave * kWChunks + i;
-    const uint32_t s = 64u * j + lane, r = s >> 4;
-    uint32_t c = (s & 15u) ^ (((r & 3u) | ((r >> 1) & 4u)) << 1);
+  for (int i = 0; i < kCWLoads; ++i) {
+    const uint32_t j = (uint32_t)wave * kCWLoads + i;
+    const uint32_t s = 64u * j + (uint32_t)lane, r = s >> 4;
+    uint32_t c = (s & 15u) ^ w_swz(r);
     if ((int)c >= Dv / 8) c = 0;
-    wr[i] = *(const bf16x8*)(W + (long)r * Dv + c * 8);
+    g2lds16(W + (long)r * Dv + c * 8, wb + j * 1024u);
   }
 }
 
-__device__ __forceinline__ void store_w_uv(const bf16x8 (&wr)[kWChunks], uint32_t wb,
+// The pieces of one sequence: workgroups f .. f+n-1 of the stream, slot
+// slot0 + s for piece s.
+struct SeqPieces {
+  long slot0;
+  int f, n;
+};
+
+// kChunk (8 or 16): piece values a wave has in flight at once; 16 also
+// brings the statistics of pieces 64..127 with the first chunk.
+template <bool kProject, int kChunk>
+__device__ __forceinline__ void combine_wg(const int* prefix, const float* __restrict__ part_ml,
+                                           const bf16* __restrict__ part_o, int batch, int H,
+                                           int hg_heads, int n_wg, int guess_tiles, int S,
+                                           const bf16* __restrict__ w_uv, int Dv,
+                                           bf16* __restrict__ out, int h, int b0, uint32_t wb,
                                            uint32_t ob) {
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < kWChunks; ++i) {
-    const uint32_t j = (uint32_t)wave * kWChunks + i;
-    *(lds_bf16x8*)(uintptr_t)(wb + (64u * j + lane) * 16u) = wr[i];
-  }
-  // zero rows kCRows .. 15 of o_lat (one 16-byte chunk per thread)
-  *(lds_bf16x8*)(uintptr_t)(ob + o_off(kCRows + wave, lane)) = bf16x8{};
-}
-
-// kProject: w_uv is given (non-NULL) and out receives o_lat W_UV.
-template <bool kProject>
-__device__ __forceinline__ void combine_rows(const int* prefix, const float* __restrict__ part_ml,
-                                             const bf16* __restrict__ part_o, int batch, int H,
-                                             int hg_heads, int n_wg, int guess_tiles,
-                                             const bf16* __restrict__ w_uv, int Dv,
-                                             bf16* __restrict__ out, int h, int b0, uint32_t wb,
-                                             uint32_t ob) {
-  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4v;
   const int tid = threadIdx.x, lane = tid & 63;
-  // the wave index as a wave-uniform value: the prefix sums below then come
+  // the wave index as a wave-uniform value: the prefix sums then come
   // through scalar loads, whose waits do not hold up the vector loads
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = h / hg_heads, hl = h % hg_heads;
   const long n_slots = (long)n_wg + batch;
-  const bf16* W = kProject ? w_uv + (long)h * kR * Dv : nullptr;
-  const int b = b0 + wave;
-  const int total = prefix[batch];
-  const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
+  const int wps = S < kCWaves ? kCWaves / S : 1;  // waves per sequence
+  const int spw = S > kCWaves ? S / kCWaves : 1;  // sequences per wave
+  const int part = wave % wps;                    // this wave's pieces: part + wps i
+  const int row0 = S < kCWaves ? wave / wps : wave;
 
-  // Where this sequence's pieces are if every sequence has guess_tiles
-  // tiles (the common equal-length batch): their statistics and first
-  // values go in flight at once, with W_UV behind them, in parallel with
-  // the prefix sums, and are kept if the real layout matches.
-  int fg = 0, ng = 1;
-  if (b < batch) {
-    const StreamSplit gsplit(batch * guess_tiles, n_wg);
-    fg = gsplit.owner(b * guess_tiles);
-    ng = gsplit.owner((b + 1) * guess_tiles - 1) - fg + 1;
-  }
-  const long slotg = (long)hg * n_slots + fg + min(b, batch - 1);
-  f32x2 ml_raw = *(const f32x2*)(part_ml + ((slotg + min(lane, ng - 1)) * hg_heads + hl) * 2);
-  bf16x8 v[kPieceChunk];
-#pragma unroll
-  for (int u = 0; u < kPieceChunk; ++u)
-    v[u] = *(const bf16x8*)(part_o + ((slotg + min(u, ng - 1)) * hg_heads + hl) * kR + 8 * lane);
-  bf16x8 wr[kWChunks];
-  if constexpr (kProject) load_w_uv(W, Dv, wr);
-
-  const StreamSplit split(total, n_wg);
-  int f = 0, n = 0;
-  if (p1 > p0) {
-    f = split.owner(p0);
-    n = split.owner(p1 - 1) - f + 1;
-  }
-  // Pieces f .. f+n-1 come from workgroups f .. f+n-1 of the stream; one
-  // whose range is empty (fewer tiles than workgroups) wrote nothing.
-  auto has_piece = [&](int s) { return split.nonempty(f + s); };
-  const long slot0 = (long)hg * n_slots + f + min(b, batch - 1);
-  auto piece_o = [&](int s) {
-    return has_piece(s) ? *(const bf16x8*)(part_o + ((slot0 + s) * hg_heads + hl) * kR + 8 * lane)
-                        : bf16x8{};
+  auto ld_ml = [&](long slot0, int s) {
+    return *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2);
   };
-  auto piece_ml = [&](int s) {
-    return has_piece(s) ? *(const f32x2*)(part_ml + ((slot0 + s) * hg_heads + hl) * 2)
-                        : f32x2{-INFINITY, 0.f};
+  auto ld_o = [&](long slot0, int s) {
+    return *(const bf16x8*)(part_o + ((slot0 + s) * hg_heads + hl) * kR + 8 * lane);
   };
-  // A wrong guess: the statistics and the first pieces' values again from
-  // the real slots (piece index clamped to the last piece; what is not a
-  // piece is masked afterwards), waited for here, so that on the common path
-  // the compiler still waits for each piece in turn and not for W_UV.
-  if (f != fg || max(n, 1) != ng) {
-    const int last = max(n, 1) - 1;
-    ml_raw = *(const f32x2*)(part_ml + ((slot0 + min(lane, last)) * hg_heads + hl) * 2);
+  // this wave's first chunk of a sequence: the statistics of pieces 0 ..
+  // 64 kStats - 1 (kStats per lane) and the values of pieces part + wps u,
+  // u < kChunk (below 64 kStats, as wps <= 8), indices clamped to the last
+  // piece (what is not a piece is masked afterwards)
+  constexpr int kStats = kChunk > 8 ? 2 : 1;
+  constexpr int kStatPieces = 64 * kStats;
+  bf16x8 v[kChunk];
+  f32x2 ml_raw[kStats];
+  auto first_chunk = [&](const SeqPieces& q) {
+    const int last = max(q.n, 1) - 1;
 #pragma unroll
-    for (int u = 0; u < kPieceChunk; ++u)
-      v[u] = *(const bf16x8*)(part_o + ((slot0 + min(u, last)) * hg_heads + hl) * kR + 8 * lane);
+    for (int i = 0; i < kStats; ++i) ml_raw[i] = ld_ml(q.slot0, min(64 * i + lane, last));
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) v[u] = ld_o(q.slot0, min(part + wps * u, last));
+  };
+  auto settle_first_chunk = [&]() {
     wait_vmcnt<0>();
-    asm volatile("" : "+v"(ml_raw));
 #pragma unroll
-    for (int u = 0; u < kPieceChunk; ++u) asm volatile("" : "+v"(v[u]));
-  }
-  const f32x2 ml0 = lane < n && has_piece(lane) ? ml_raw : f32x2{-INFINITY, 0.f};
+    for (int i = 0; i < kStats; ++i) asm volatile("" : "+v"(ml_raw[i]));
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) asm volatile("" : "+v"(v[u]));
+  };
 
-  float M = ml0[0];
-  for (int s = 64 + lane; s < n; s += 64) M = fmaxf(M, piece_ml(s)[0]);
-  M = wave_max(M);
-  float acc[8];
+  const int bw0 = b0 + row0;  // the wave's first sequence
+  SeqPieces g{0, 0, 1};
+  if (bw0 < batch) {
+    const StreamSplit gsplit(batch * guess_tiles, n_wg);
+    g.f = gsplit.owner(bw0 * guess_tiles);
+    g.n = gsplit.owner((bw0 + 1) * guess_tiles - 1) - g.f + 1;
+  }
+  g.slot0 = (long)hg * n_slots + g.f + min(bw0, batch - 1);
+  first_chunk(g);
+  if constexpr (kProject) issue_w_uv(w_uv + (long)h * kR * Dv, Dv, wb, wave, lane);
+
+  const StreamSplit split(prefix[batch], n_wg);
+  auto pieces = [&](int b) {
+    SeqPieces q{0, 0, 0};
+    const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
+    if (p1 > p0) {
+      q.f = split.owner(p0);
+      q.n = split.owner(p1 - 1) - q.f + 1;
+    }
+    q.slot0 = (long)hg * n_slots + q.f + min(b, batch - 1);
+    return q;
+  };
+  auto stat = [&](const SeqPieces& q, int s, f32x2 raw) {
+    return s < q.n && split.nonempty(q.f + s) ? raw : f32x2{-INFINITY, 0.f};
+  };
+
+  for (int j = 0; j < spw; ++j) {
+    const int row = row0 + kCWaves * j;
+    const int b = b0 + row;
+    const SeqPieces q = pieces(b);
+    // A wrong guess (first sequence) or a later sequence: the first chunk
+    // from the real slots, waited for here, so that on the common path the
+    // compiler waits for each piece in turn, not for W_UV behind them.
+    if (j > 0 || q.f != g.f || max(q.n, 1) != g.n) {
+      first_chunk(q);
+      settle_first_chunk();
+    }
+    const int n = q.n;
+    f32x2 st[kStats];
+    float M = -INFINITY;
 #pragma unroll
-  for (int e8 = 0; e8 < 8; ++e8) acc[e8] = 0.f;
-  float den = 0.f;
-  if (n <= kPieceChunk) {
-    // the common case: every piece is already in registers.  A piece with
-    // zero weight (missing, or a clamped duplicate) is skipped, so its
-    // values never meet the sum.
-    const float e = ml0[1] > 0.f ? exp2f(ml0[0] - M) * ml0[1] : 0.f;
-    den = e;
+    for (int i = 0; i < kStats; ++i) {
+      st[i] = stat(q, 64 * i + lane, ml_raw[i]);
+      M = fmaxf(M, st[i][0]);
+    }
+    for (int s = kStatPieces + lane; s < n; s += 64)  // long sequences only
+      M = fmaxf(M, stat(q, s, ld_ml(q.slot0, s))[0]);
+    M = wave_max(M);
+    auto weight = [&](f32x2 t) { return t[1] > 0.f ? exp2f(t[0] - M) * t[1] : 0.f; };
+    float e[kStats], den = 0.f;
 #pragma unroll
-    for (int u = 0; u < kPieceChunk; ++u) {
-      const float eu = lane_value(e, u);
+    for (int i = 0; i < kStats; ++i) den += (e[i] = weight(st[i]));
+    for (int s = kStatPieces + lane; s < n; s += 64) den += weight(stat(q, s, ld_ml(q.slot0, s)));
+    // weight of piece p (wave-uniform p < n)
+    auto weight_of = [&](int p) {
+      if (p < 64) return lane_value(e[0], p);
+      if (kStats > 1 && p < 128) return lane_value(e[kStats - 1], p - 64);
+      return weight(stat(q, p, ld_ml(q.slot0, p)));
+    };
+    float acc[8];
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) acc[e8] = 0.f;
+    // A piece with zero weight (missing, or a clamped duplicate) is
+    // skipped, so its values never meet the sum.
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int p = part + wps * u;
+      const float eu = p < n ? lane_value(e[p < 64 ? 0 : kStats - 1], p & 63) : 0.f;
       if (eu != 0.f) {
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
       }
     }
-  } else {
-    for (int s0 = 0; s0 < n; s0 += 64) {
-      const int sw = s0 + lane;
-      float e = 0.f;
-      if (sw < n) {
-        const f32x2 t = s0 == 0 ? ml0 : piece_ml(sw);
-        if (t[1] > 0.f) e = exp2f(t[0] - M) * t[1];
-      }
-      den += e;
-      const int m = min(64, n - s0);
-      for (int u0 = 0; u0 < m; u0 += kPieceChunk) {
-        if (s0 + u0 > 0) {
+    // the rest of this wave's pieces (more than kChunk per wave)
+    for (int u0 = kChunk; part + wps * u0 < n; u0 += kChunk) {
+      const int cnt = min(kChunk, (n - 1 - part) / wps + 1 - u0);
 #pragma unroll
-          for (int u = 0; u < kPieceChunk; ++u)
-            if (u0 + u < m) v[u] = piece_o(s0 + u0 + u);
+      for (int u = 0; u < kChunk; ++u) v[u] = ld_o(q.slot0, part + wps * (u0 + min(u, cnt - 1)));
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const float eu = u < cnt ? weight_of(part + wps * (u0 + u)) : 0.f;
+        if (eu != 0.f) {
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
         }
+      }
+    }
+    den = wave_sum(den);
+    if (wps > 1) {
+      // the sequence's waves add their partial sums in LDS, in wave order
+      const uint32_t ps = ob + 16 * 1024 + ((uint32_t)wave * 64 + lane) * 32;
+      *(lds_f32x4v*)(uintptr_t)ps = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(lds_f32x4v*)(uintptr_t)(ps + 16) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      __syncthreads();
+      if (part == 0) {
+        for (int w2 = 1; w2 < wps; ++w2) {
+          const uint32_t p2 = ps + (uint32_t)w2 * 64 * 32;
+          const f32x4 x0 = *(lds_f32x4v*)(uintptr_t)p2, x1 = *(lds_f32x4v*)(uintptr_t)(p2 + 16);
 #pragma unroll
-        for (int u = 0; u < kPieceChunk; ++u) {
-          const float eu = lane_value(e, u0 + u);
-          if (u0 + u < m && eu != 0.f) {
-#pragma unroll
-            for (int e8 = 0; e8 < 8; ++e8) acc[e8] += eu * (float)v[u][e8];
+          for (int e4 = 0; e4 < 4; ++e4) {
+            acc[e4] += x0[e4];
+            acc[4 + e4] += x1[e4];
           }
         }
       }
     }
-  }
-  den = wave_sum(den);
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  bf16x8 o;
+    if (part == 0) {
+      const float inv = den > 0.f ? 1.0f / den : 0.f;
+      bf16x8 o;
 #pragma unroll
-  for (int e8 = 0; e8 < 8; ++e8) o[e8] = (bf16)(acc[e8] * inv);
-  if constexpr (!kProject) {
-    if (b < batch) *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
-    return;
-  }
-  *(lds_bf16x8*)(uintptr_t)(ob + o_off(wave, lane)) = o;
-  store_w_uv(wr, wb, ob);
-  __syncthreads();
-
-  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: 16 rows (8 used) x Dv, K = 512,
-  // 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
-  if (16 * wave >= Dv) return;
-  // Eight k-steps at a time: all their LDS reads first, then the MFMAs,
-  // alternating between two accumulators (shorter dependency chains).
-  f32x4 pacc[2] = {};
-  const int g = lane >> 4, li = lane & 15;
-#pragma unroll
-  for (int k8 = 0; k8 < kR / 32; k8 += 8) {
-    bf16x8 a[8], bw[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      a[u] = lds_read_b128(ob + o_off(lane & 15, 4 * (k8 + u) + (lane >> 4)));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      // 16x16x32 B operand: lane (16g + li) needs column li of rows 8g .. 8g+7
-      const uint32_t row = 32 * (k8 + u) + 8 * g + (li >> 2);
-      const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
-      bw[u] = cat(lds_read_tr(wb + w_off(row, c) + sub), lds_read_tr(wb + w_off(row + 4, c) + sub));
+      for (int e8 = 0; e8 < 8; ++e8) o[e8] = (bf16)(acc[e8] * inv);
+      if constexpr (kProject)
+        *(lds_bf16x8*)(uintptr_t)(ob + o_off(row, lane)) = o;
+      else if (b < batch)
+        *(bf16x8*)(out + ((long)b * H + h) * kR + 8 * lane) = o;
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) pacc[u & 1] = mfma16(a[u], bw[u], pacc[u & 1]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // the 24 LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
   }
-  // register v of lane l: row 4(l/16) + v, column l%16
+  if constexpr (!kProject) return;
+
+  // out[b, h, :] = o_lat[b, h, :] W_UV[h]: rows in blocks of 16 x Dv, K =
+  // 512, 16x16x32 MFMAs; wave w owns the 16-column block w (Dv <= 128).
+  // Rows past S in a block hold stale LDS; they only reach output rows that
+  // are not stored.
+  __syncthreads();
+  if (16 * wave >= Dv) return;
+  const int g4 = lane >> 4, li = lane & 15;
+  for (int rb = 0; 16 * rb < S; ++rb) {
+    // eight k-steps at a time: their LDS reads first, then the MFMAs over
+    // two accumulators (shorter dependency chains)
+    f32x4 pacc[2] = {};
 #pragma unroll
-  for (int v4 = 0; v4 < 4; ++v4) {
-    const int r = 4 * (lane >> 4) + v4;
-    if (r < kCRows && b0 + r < batch)
-      out[((long)(b0 + r) * H + h) * Dv + 16 * wave + (lane & 15)] =
-          (bf16)(pacc[0][v4] + pacc[1][v4]);
+    for (int k8 = 0; k8 < kR / 32; k8 += 8) {
+      bf16x8 a[8], bwf[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        a[u] = lds_read_b128(ob + o_off(16 * rb + li, 4 * (k8 + u) + g4));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // 16x16x32 B operand: lane (16 g + li) needs column li of rows 8 g .. 8 g + 7
+        const uint32_t r = 32 * (k8 + u) + 8 * g4 + (li >> 2);
+        const uint32_t c = 2 * wave + ((li & 3) >> 1), sub = 8 * (li & 1);
+        bwf[u] = cat(lds_read_tr(wb + w_off(r, c) + sub), lds_read_tr(wb + w_off(r + 4, c) + sub));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pacc[u & 1] = mfma16(a[u], bwf[u], pacc[u & 1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // the 24 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then the 8 MFMAs
+    }
+    // register v of lane l: row 4 (l/16) + v of the block, column l%16
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int r = 16 * rb + 4 * g4 + v4;
+      if (r < S && b0 + r < batch)
+        out[((long)(b0 + r) * H + h) * Dv + 16 * wave + li] = (bf16)(pacc[0][v4] + pacc[1][v4]);
+    }
   }
 }
 
@@ -930,16 +968,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
                              part_ml, part_o);
 }
 
-// Combine of the partials (the staged call): grid (H, ceil(batch / 8)).
-template <bool kProject>
+// Combine of the partials (the staged call): grid (H, ceil(batch / S)).
+template <bool kProject, int kChunk>
 __global__ void __launch_bounds__(kCThreads) combine_kernel(
     const int* __restrict__ prefix, const float* __restrict__ part_ml,
     const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg, int guess_tiles,
-    const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
+    int S, const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char smem[kCWBytes + kCOBytes];
   const uint32_t wb = lds_addr(smem), ob = wb + kCWBytes;
-  combine_rows<kProject>(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, guess_tiles, w_uv,
-                         Dv, out, blockIdx.x, blockIdx.y * kCRows, wb, ob);
+  combine_wg<kProject, kChunk>(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, guess_tiles, S,
+                               w_uv, Dv, out, blockIdx.x, blockIdx.y * S, wb, ob);
 }
 
 // ---------------------------------------------------------------------------
@@ -1014,20 +1052,46 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
         seq_lens, batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
 }
 
+int combine_rows_per_wg(int H, int batch, int num_cus) {
+  // the largest power of two (at most 32) whose grid still fills the CUs once
+  int S = kCMaxRows;
+  while (S > 1 && (long)H * ((batch + S - 1) / S) < num_cus) S >>= 1;
+  return S;
+}
+
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
                     int heads_per_wg, int n_wg, int max_seq_len, const void* w_uv, int Dv,
-                    void* out, hipStream_t st) {
-  dim3 grid(H, (batch + kCRows - 1) / kCRows);
+                    void* out, int num_cus, hipStream_t st) {
+  const int S = combine_rows_per_wg(H, batch, num_cus);
+  dim3 grid(H, (batch + S - 1) / S);
   const int guess_tiles =
       (int)std::clamp(((long)max_seq_len + kTok - 1) / kTok, 1L, (long)INT_MAX / max(batch, 1));
+  // pieces of a sequence in the equal-length layout, at most: the first
+  // chunk holds 8 of a wave's pieces, or 16 when a wave has more
+  const long T = (long)batch * guess_tiles, q = T / n_wg, r = T % n_wg;
+  auto start = [&](long w) { return w * q + (w * r) / n_wg; };
+  auto owner = [&](long x) {  // the workgroup whose range holds tile x
+    long lo = 0, hi = n_wg - 1;
+    while (lo < hi) {
+      const long mid = (lo + hi + 1) / 2;
+      if (start(mid) <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  long n_max = 1;
+  for (long b = 0; b < batch; ++b)
+    n_max = std::max(n_max, owner((b + 1) * guess_tiles - 1) - owner(b * guess_tiles) + 1);
+  const int wps = S < kCWaves ? kCWaves / S : 1;
+  const bool wide = (n_max + wps - 1) / wps > 8;
+  auto go = [&](auto kernel, const void* w) {
+    kernel<<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
+                                       heads_per_wg, n_wg, guess_tiles, S, (const bf16*)w, Dv,
+                                       (bf16*)out);
+  };
   if (w_uv)
-    combine_kernel<true><<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch,
-                                                     H, heads_per_wg, n_wg, guess_tiles,
-                                                     (const bf16*)w_uv, Dv, (bf16*)out);
+    wide ? go(combine_kernel<true, 16>, w_uv) : go(combine_kernel<true, 8>, w_uv);
   else
-    combine_kernel<false><<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch,
-                                                      H, heads_per_wg, n_wg, guess_tiles, nullptr,
-                                                      Dv, (bf16*)out);
+    wide ? go(combine_kernel<false, 16>, nullptr) : go(combine_kernel<false, 8>, nullptr);
 }
 
 void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,

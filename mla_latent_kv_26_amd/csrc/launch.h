@@ -137,9 +137,11 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
 // or, when w_uv != NULL, project directly: out[b, h] = o_lat[b, h] W_UV[h].
 // max_seq_len only steers which partials are fetched before the prefix sums
 // arrive (right when all sequences have that length; any value is correct).
+// num_cus sets how many sequences share a workgroup (combine_rows_per_wg).
+int combine_rows_per_wg(int H, int batch, int num_cus);
 void launch_combine(const int* prefix, const float* part_ml, const void* part_o, int batch, int H,
                     int heads_per_wg, int n_wg, int max_seq_len, const void* w_uv, int Dv,
-                    void* out, hipStream_t st);
+                    void* out, int num_cus, hipStream_t st);
 
 // Prefill attention: query row n = b * T + t at position start_pos[b] + t
 // attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].

@@ -375,7 +375,7 @@ static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* 
                                         at(ws, w.part_o), st);
     mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
                         at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, max_seq_len, w_uv, d.Dv, dst,
-                        st);
+                        num_cus(), st);
   } else {
     float* o_lat = w_uv ? (float*)at(ws, w.o_lat) : (float*)dst;
     mla::launch_attention_f32((const float*)q_full, (const float*)pool, table, max_blocks, d.bs,
@@ -509,7 +509,7 @@ mla_status mla_combine_output(const mla_config* cfg, const void* w_uv, int32_t b
   if (s != MLA_OK) return s;
   mla::launch_combine((const int*)at(workspace, w.prefix), (const float*)at(workspace, w.part_ml),
                       at(workspace, w.part_o), batch, d.H, w.heads, w.n_wg, max_seq_len, w_uv, d.Dv,
-                      out, (hipStream_t)stream);
+                      out, num_cus(), (hipStream_t)stream);
   return launched("mla_combine_output");
 }
 
