@@ -19,6 +19,9 @@ Sources (cited in each function by page title and section):
   * modeldna "MLA" module: latent c of width kv_lora_rank plus a shared rope
     key, absorption of the up-projections (Under the hood); the Kimi-scale
     cache table.
+  * softved article "Multi-Head Latent Attention": quantize the latent cache
+    on top of MLA ("Practical Implementation Tips for MLA in LLM Serving");
+    the FP8 row format is a reading (``fp8_cache``).
   * "GatedMLA" docs: projection geometry, per-head Q/K/V with the shared key
     broadcast, causal SDPA scaled over the full Q/K width (Projection
     geometry and stored weights; Build per-head Q, K and V; Observe logits,
@@ -39,4 +42,5 @@ outputs of the five workloads have no printed values on the pages; they are
 pinned only through those identities.
 """
 from .mla_oracle import *  # noqa: F401,F403
+from .fp8_cache import *  # noqa: F401,F403
 from . import ledger  # noqa: F401

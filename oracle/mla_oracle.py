@@ -343,7 +343,11 @@ def append_rows(x, positions, weights, cfg, storage: str = "f64", wd=np.float64)
     c, kr = kv_latent_rows(x, _w(weights, "w_dkv"), _w(weights, "kv_norm_w"), positions,
                            _cfg(cfg, "kv_lora_rank"), _cfg(cfg, "rms_eps", DEFAULT_EPS),
                            _cfg(cfg, "rope_theta", DEFAULT_THETA), wd)
-    return store_round(np.concatenate([c, kr], axis=-1), storage).astype(wd)
+    rows = np.concatenate([c, kr], axis=-1)
+    if storage == "fp8":  # FP8 latent, bf16 rope key (fp8_cache)
+        from .fp8_cache import fp8_store_rows
+        return fp8_store_rows(rows, _cfg(cfg, "kv_lora_rank")).astype(wd)
+    return store_round(rows, storage).astype(wd)
 
 
 def attend_tokens(x, positions, weights, cfg, rows, path: str = "absorbed",

@@ -581,3 +581,107 @@ def test_planted_missing_sigmoid_is_caught():
     plain = oracle.output_gate_projection(h, x, w_o)
     half = wrong(h, x, w_o, np.zeros_like(w_g))
     assert np.max(np.abs(half - 0.5 * plain)) > 1e-3    # the W_G = 0 pin fails
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache rows (softved article, "Practical Implementation Tips for
+# MLA in LLM Serving": quantize the cache; the E4M3 format, the per-row
+# power-of-two scale and the row layout are readings, pinned here against the
+# format's definition and against torch's float8_e4m3fn)
+# ---------------------------------------------------------------------------
+def _torch_e4m3(values):
+    import torch
+    return torch.from_numpy(np.asarray(values, np.float64)).to(torch.float8_e4m3fn)
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_value(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    assert np.isnan(got).sum() == 2                      # S.1111.111 only: no infinities
+
+
+def test_e4m3_closed_forms():
+    v = oracle.e4m3_value
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0        # largest finite
+    assert v(0x01) == 2.0 ** -9                          # smallest subnormal
+    assert v(0x08) == 2.0 ** -6 and v(0x07) == 7 * 2.0 ** -9   # normal / subnormal edge
+    assert v(0x38) == 1.0 and v(0x39) == 1.125
+    r = oracle.e4m3_round
+    assert r(1.0625) == 0x38 and r(1.1875) == 0x3A      # ties go to the even code
+    assert r(448.0) == 0x7E and r(1e9) == 0x7E and r(-1e9) == 0xFE   # saturation
+    assert r(0.75 * 2.0 ** -9) == 0x01 and r(0.25 * 2.0 ** -9) == 0x00
+
+
+def test_e4m3_rounding_matches_torch_in_range():
+    rng = np.random.default_rng(71)
+    x = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(5000) * 1e-3,
+                        oracle.e4m3_value(np.arange(126)) * 1.0625])   # many exact ties
+    x = np.clip(x, -448, 448)
+    got = oracle.e4m3_value(oracle.e4m3_round(x))
+    want = _torch_e4m3(x).to(dtype=__import__("torch").float64).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_round_is_nearest():
+    rng = np.random.default_rng(72)
+    x = rng.uniform(-448, 448, 5000)
+    got = oracle.e4m3_value(oracle.e4m3_round(x))
+    grid = oracle.e4m3_value(np.arange(256))
+    grid = grid[~np.isnan(grid)]
+    best = np.min(np.abs(x[:, None] - grid[None, :]), axis=1)   # brute force
+    assert np.array_equal(np.abs(x - got), best)
+
+
+def test_fp8_row_scale_rule():
+    rng = np.random.default_rng(73)
+    c = rng.standard_normal((200, 512)) * np.exp2(rng.integers(-12, 12, (200, 1)))
+    s = oracle.fp8_row_scale(c)
+    assert np.all(np.exp2(np.round(np.log2(s))) == s)          # powers of two
+    ratio = np.max(np.abs(c), axis=1) / s
+    assert np.all(ratio <= 448.0) and np.all(ratio > 224.0)
+    assert oracle.fp8_row_scale(np.zeros((1, 8)))[0] == 1.0
+
+
+def test_fp8_rows_error_bound_and_layout():
+    rng = np.random.default_rng(74)
+    rows = rng.standard_normal((64, 576))
+    codes, s, rope = oracle.quantize_rows_fp8(rows, 512)
+    deq = oracle.dequantize_rows_fp8(codes, s, rope)
+    c, cq = rows[:, :512], deq[:, :512]
+    normal = np.abs(c) / s[:, None] >= 2.0 ** -6
+    # half a step of a 3-bit mantissa (relative), half a subnormal step below
+    assert np.all(np.abs(cq - c)[normal] <= 2.0 ** -4 * np.abs(c)[normal])
+    assert np.all(np.abs(cq - c)[~normal] <= (2.0 ** -10 * s[:, None] * np.ones_like(c))[~normal])
+    assert np.all(np.abs(deq[:, 512:] - rows[:, 512:]) <= 2.0 ** -8 * np.abs(rows[:, 512:]))
+    raw = oracle.pack_rows_fp8(codes, s, rope)
+    assert raw.shape == (64, 656) and oracle.fp8_row_bytes(512, 64) == 656
+    assert np.array_equal(raw[:, :512], codes) and np.all(raw[:, 644:] == 0)
+    assert np.array_equal(raw[:, 640:644].copy().view("<f4")[:, 0], s.astype(np.float32))
+    back = oracle.unpack_rows_fp8(raw, 512, 64)
+    assert all(np.array_equal(a, b) for a, b in zip(back, (codes, s, rope)))
+
+
+def test_fp8_append_rows_store_the_quantized_values():
+    cfg = dict(workloads.WORKLOADS["tiny_fp32"], kv_lora_rank=16, rope_dim=8)
+    rng = np.random.default_rng(75)
+    M = cfg["d_model"]
+    w = {"w_dkv": rng.standard_normal((M, 24)) / 8, "kv_norm_w": 1 + 0.1 * rng.standard_normal(16)}
+    x = rng.standard_normal((5, M))
+    f64 = oracle.append_rows(x, np.arange(5), w, cfg, storage="f64")
+    q = oracle.append_rows(x, np.arange(5), w, cfg, storage="fp8")
+    assert np.array_equal(q, oracle.fp8_store_rows(f64, 16))
+    assert not np.array_equal(q[:, :16], f64[:, :16])
+
+
+def test_planted_fnuz_bias_is_caught():
+    """The other common 8-bit E4M3 (exponent bias 8, as on earlier AMD
+    matrix cores) halves every value: the torch pin fails."""
+    import torch
+    codes = np.arange(0x7F, dtype=np.uint8)
+    wrong = oracle.e4m3_value(codes) / 2
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert not np.array_equal(wrong, want)
