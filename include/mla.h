@@ -38,6 +38,17 @@
  *     offset j % block_size (the ticket "MLA + KV cache (Tier 3 #5)",
  *     "Description": a PagedKVCache pool with a block allocator).  A
  *     contiguous cache is the same pool with an identity page table.
+ *   - FP8 cache (cache_dtype MLA_CACHE_FP8_E4M3, bf16 configs): the softved
+ *     article "Multi-Head Latent Attention" advises quantizing the cache on
+ *     top of MLA ("Practical Implementation Tips for MLA in LLM Serving")
+ *     without naming a format; here a row is R + 2 Dr + 16 bytes (656 at
+ *     R=512, Dr=64): R codes of c / s in OCP FP8 E4M3 (bias 7, largest
+ *     finite 448, round to nearest even), the Dr rope values in bf16, the
+ *     row's scale s as float32, 12 zero bytes.  s is the smallest power of
+ *     two with max|c| <= 448 s (1 for an all-zero c), so s * code is exact
+ *     in bf16.  The pool is then [num_blocks, block_size, R + 2 Dr + 16]
+ *     bytes.  Decode reads and mla_cache_append writes such pools (R=512,
+ *     Dr=64); mla_prefill returns MLA_ERR_UNSUPPORTED for them.
  */
 #ifndef MLA_LATENT_KV_H
 #define MLA_LATENT_KV_H
@@ -49,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -60,6 +71,9 @@ typedef enum mla_status {
 } mla_status;
 
 typedef enum mla_dtype { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+/* How cache rows are stored: in the config's dtype, or FP8 (see above). */
+typedef enum mla_cache_dtype { MLA_CACHE_SAME = 0, MLA_CACHE_FP8_E4M3 = 1 } mla_cache_dtype;
 
 /* One MLA layer's geometry ("GatedMLA" docs, "Projection geometry and stored
  * weights": W_DQ M->Rq, W_DKV M->R+Dr, W_UQ Rq->H(Dn+Dr), the KV
@@ -78,6 +92,7 @@ typedef struct mla_config {
   float rms_eps;        /* >= 0, RMSNorm epsilon                               */
   float rope_theta;     /* > 0, RoPE base                                      */
   int32_t dtype;        /* mla_dtype of every tensor (storage); fp32 accumulate */
+  int32_t cache_dtype;  /* mla_cache_dtype of the cache rows; FP8 needs bf16   */
 } mla_config;
 
 /* ---- library information ------------------------------------------------ */
@@ -94,7 +109,8 @@ mla_status mla_validate_config(const mla_config* cfg);
  * "MLA" module, cache-size table).  -1 if *cfg is invalid.  Host only. */
 int64_t mla_cache_row_elems(const mla_config* cfg);
 /* Bytes per cached token per layer, (R + Dr) * sizeof(dtype): 1152 for
- * bf16 at R=512, Dr=64 (same table).  -1 if *cfg is invalid.  Host only. */
+ * bf16 at R=512, Dr=64 (same table); R + 2 Dr + 16 for an FP8 cache (656).
+ * -1 if *cfg is invalid.  Host only. */
 int64_t mla_cache_bytes_per_token(const mla_config* cfg);
 
 /* RoPE table for positions 0..num_positions-1, written to HOST memory

@@ -18,6 +18,8 @@ MLA_ERR_WORKSPACE = 3
 MLA_ERR_HIP = 4
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+CACHE_SAME = 0
+CACHE_FP8_E4M3 = 1
 
 
 class MLAConfigC(ctypes.Structure):
@@ -34,6 +36,7 @@ class MLAConfigC(ctypes.Structure):
         ("rms_eps", ctypes.c_float),
         ("rope_theta", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32),
     ]
 
 

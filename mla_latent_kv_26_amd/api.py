@@ -18,6 +18,7 @@ from ._lib import lib, check, MLAConfigC
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _C_DTYPE = {"f32": _lib.DTYPE_F32, "bf16": _lib.DTYPE_BF16}
+_C_CACHE = {"same": _lib.CACHE_SAME, "fp8": _lib.CACHE_FP8_E4M3}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -35,6 +36,7 @@ class MLAConfig:
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
     dtype: str = "bf16"
+    cache_dtype: str = "same"   # "same" (rows in dtype) or "fp8" (E4M3 latent, see mla.h)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -45,6 +47,19 @@ class MLAConfig:
         return self.kv_lora_rank + self.rope_dim
 
     @property
+    def pool_dtype(self) -> torch.dtype:
+        """Element type of a cache pool tensor (bytes for FP8 rows)."""
+        return torch.uint8 if self.cache_dtype == "fp8" else self.torch_dtype
+
+    @property
+    def pool_row(self) -> int:
+        """Elements per cached row in a pool tensor: R + Dr values, or the
+        R + 2 Dr + 16 bytes of an FP8 row."""
+        if self.cache_dtype == "fp8":
+            return self.kv_lora_rank + 2 * self.rope_dim + 16
+        return self.row
+
+    @property
     def scale(self) -> float:
         return self.softmax_scale or 1.0 / math.sqrt(self.qk_nope_dim + self.rope_dim)
 
@@ -52,7 +67,7 @@ class MLAConfig:
         return MLAConfigC(self.num_heads, self.kv_lora_rank, self.rope_dim, self.qk_nope_dim,
                           self.v_dim, self.d_model, self.q_lora_rank, self.block_size,
                           self.softmax_scale, self.rms_eps, self.rope_theta,
-                          _C_DTYPE[self.dtype])
+                          _C_DTYPE[self.dtype], _C_CACHE[self.cache_dtype])
 
     @classmethod
     def from_dict(cls, d: dict, **over) -> "MLAConfig":
@@ -163,7 +178,7 @@ def mla_prefill_workspace_size(cfg: MLAConfig, batch: int, q_len: int, max_conte
 # ---------------------------------------------------------------------------
 def _pool_args(cfg, kv_pool, block_table, batch):
     nb = kv_pool.shape[0]
-    _dev(kv_pool, "kv_pool", cfg.torch_dtype, (nb, cfg.block_size, cfg.row))
+    _dev(kv_pool, "kv_pool", cfg.pool_dtype, (nb, cfg.block_size, cfg.pool_row))
     if block_table.dim() != 2 or block_table.shape[0] != batch:
         raise ValueError(f"block_table must be [batch={batch}, max_blocks]")
     _dev(block_table, "block_table", torch.int32)
@@ -298,7 +313,7 @@ def mla_cache_append(cfg: MLAConfig, x, w_dkv, kv_norm_w, positions, slot_mappin
     _dev(positions, "positions", torch.int32, (n,))
     _dev(slot_mapping, "slot_mapping", torch.int32, (n,))
     nb = kv_pool.shape[0]
-    _dev(kv_pool, "kv_pool", dt, (nb, cfg.block_size, cfg.row))
+    _dev(kv_pool, "kv_pool", cfg.pool_dtype, (nb, cfg.block_size, cfg.pool_row))
     if rope_table is None:
         rope_table = _rope_dev(cfg, None, int(positions.max().item()) + 1, x.device)
     rope_table = _rope_dev(cfg, rope_table, 0, x.device)

@@ -135,6 +135,80 @@ __device__ __forceinline__ void issue_part(const bf16* rows, int valid, uint32_t
   }
 }
 
+// FP8 cache rows (R E4M3 codes | Dr bf16 rope values | float32 scale | 12
+// zero bytes, 656 bytes = 41 chunks; the softved article's advice to
+// quantize the cache, in a format it leaves open).  The tile loop is the same
+// as for bf16 rows: the P*C waves turn each staged tile into the bf16 tile
+// layout one step before the score waves use it, so the fragment reads and
+// MFMAs are unchanged, and HBM moves 656 instead of 1152 bytes per token.
+// LDS: two bf16 tile buffers (ping-pong) and three staging slots of 24 KB.
+// A staged tile comes by 24 direct-to-LDS instructions of 1 KB, 3 per wave:
+// slot s < 1280 holds chunk s % 40 of row s / 40 (codes, rope key), slots
+// 1280 .. 1535 the scale chunk of row (s - 1280) % 32 (eight copies).  Rows
+// past `valid` repeat the last valid row.
+constexpr int kF8Row = kR + 2 * kDr + 16;               // 656 bytes
+constexpr int kF8Data = (kR + 2 * kDr) / 16;            // 40 data chunks per row
+constexpr int kF8Loads = 3;                             // per wave and tile
+constexpr int kF8StageBytes = 8 * kF8Loads * 1024;      // 24 KB
+static_assert(kTok * kF8Data + kTok <= kF8StageBytes / 16, "staging slots");
+static_assert(2 * kTileBytes + 3 * kF8StageBytes <= kOffP, "FP8 LDS layout");
+
+__device__ __forceinline__ void issue_part_fp8(const unsigned char* rows, int valid, uint32_t stg,
+                                               uint32_t j0, int lane) {
+#pragma unroll
+  for (int i = 0; i < kF8Loads; ++i) {
+    const uint32_t j = j0 + i;
+    const uint32_t s = 64u * j + (uint32_t)lane;
+    uint32_t t, c;
+    if (s < (uint32_t)(kTok * kF8Data)) {
+      t = s / kF8Data;
+      c = s - t * kF8Data;
+    } else {
+      t = (s - kTok * kF8Data) & (kTok - 1);
+      c = kF8Data;
+    }
+    const uint32_t tt = min(t, (uint32_t)(valid - 1));
+    g2lds16(rows + tt * kF8Row + c * 16, stg + j * 1024u);
+  }
+}
+
+// P*C wave pw turns a staged tile into the bf16 tile layout for its own
+// columns 128 pw .. 128 pw + 127 (the only ones it reads there, so it may
+// overwrite them right after its own P*C reads of the previous tile) and for
+// rows 8 pw .. 8 pw + 7 of the rope key (read by the score waves only, one
+// step later).  value = scale * code is exact in bf16 (a power-of-two scale,
+// 3 mantissa bits).  Staging reads: lanes 8 apart are consecutive rows, 640
+// bytes apart, so 16 lanes cover a 256-byte window once.
+__device__ __forceinline__ void convert_tile_fp8(uint32_t stg, uint32_t buf, int pw, int lane) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8v;
+  typedef __attribute__((address_space(3))) float lds_f32v;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t t = 8u * p + (uint32_t)(lane >> 3), i = 8u * pw + (uint32_t)(lane & 7);
+    const u32x4 raw = *(const lds_u32x4*)(uintptr_t)(stg + (t * kF8Data + i) * 16u);
+    const float sc = *(const lds_f32v*)(uintptr_t)(stg + (kTok * kF8Data + t) * 16u);
+    bf16x8 half[2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // dword d holds the codes of columns 16 i + 4 d .. 16 i + 4 d + 3
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[d], sc, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[d], sc, true);
+      half[d >> 1][4 * (d & 1) + 0] = lo[0];
+      half[d >> 1][4 * (d & 1) + 1] = lo[1];
+      half[d >> 1][4 * (d & 1) + 2] = hi[0];
+      half[d >> 1][4 * (d & 1) + 3] = hi[1];
+    }
+    const uint32_t sw = swz(t);
+    *(lds_bf16x8v*)(uintptr_t)(buf + (t * kCh + ((2 * i) ^ sw)) * 16u) = half[0];
+    *(lds_bf16x8v*)(uintptr_t)(buf + (t * kCh + ((2 * i + 1) ^ sw)) * 16u) = half[1];
+  }
+  const uint32_t t = 8u * pw + (uint32_t)(lane >> 3), r = (uint32_t)(lane & 7);
+  const bf16x8 kr = *(const lds_bf16x8v*)(uintptr_t)(stg + (t * kF8Data + kR / 16 + r) * 16u);
+  *(lds_bf16x8v*)(uintptr_t)(buf + (t * kCh + ((kR / 8 + r) ^ swz(t))) * 16u) = kr;
+}
+
 // One segment: a query row (HEADS heads at q_rows, row stride kW) against
 // tiles [tile0, tile1) of one sequence of `len` rows (page table `table`).
 struct SegArgs {
@@ -146,36 +220,72 @@ struct SegArgs {
   bool tile0_issued;      // tile0's loads already in flight into buffer 0
 };
 
-__device__ __forceinline__ const bf16* tile_rows(const SegArgs& a, PageCursor& pc, int tile,
-                                                 int lane) {
+// Where the loads of local tile x go, and where the score and P*C waves read
+// it: the same buffer for bf16 rows (four, round robin); a staging slot
+// (three) and then one of two bf16 buffers for FP8 rows.
+template <bool kFp8>
+__device__ __forceinline__ uint32_t load_slot(uint32_t lds, int x) {
+  if constexpr (kFp8)
+    return lds + 2u * kTileBytes + (uint32_t)(x % 3) * kF8StageBytes;
+  else
+    return lds + (uint32_t)(x % kNBuf) * kTileBytes;
+}
+template <bool kFp8>
+__device__ __forceinline__ uint32_t tile_buf(uint32_t lds, int x) {
+  if constexpr (kFp8)
+    return lds + (uint32_t)(x & 1) * kTileBytes;
+  else
+    return lds + (uint32_t)(x % kNBuf) * kTileBytes;
+}
+// Loads per wave and tile, and the first load index of wave `wave`.
+template <bool kFp8>
+__device__ __forceinline__ constexpr int tile_loads(bool score) {
+  return kFp8 ? kF8Loads : score ? kSLoads : kPLoads;
+}
+template <bool kFp8>
+__device__ __forceinline__ uint32_t first_load(int wave) {
+  if constexpr (kFp8) return (uint32_t)wave * kF8Loads;
+  return wave < 4 ? (uint32_t)wave * kSLoads : 4u * kSLoads + (uint32_t)(wave - 4) * kPLoads;
+}
+
+// This wave's share of the loads of segment tile `tile` into `dst`.
+template <bool kFp8, int NL>
+__device__ __forceinline__ void issue_tile(const SegArgs& a, PageCursor& pc, int tile,
+                                           uint32_t dst, uint32_t j0, int lane) {
   const int tok = tile * kTok;
   const int page = pc.page(tok >> a.shift, lane);
   const int mask = (1 << a.shift) - 1;
-  return a.pool + ((long)page * (mask + 1) + (tok & mask)) * kW;
+  const long row = (long)page * (mask + 1) + (tok & mask);
+  const int valid = min(kTok, a.len - tok);
+  if constexpr (kFp8)
+    issue_part_fp8((const unsigned char*)a.pool + row * kF8Row, valid, dst, j0, lane);
+  else
+    issue_part<NL>(a.pool + row * kW, valid, dst, j0, lane);
 }
 
 // Segment prologue shared by both wave roles: the page ids, then this
 // wave's share of tile 0 (the caller issues its queries, then tile 1).
-template <int NL>
+template <bool kFp8, int NL>
 __device__ __forceinline__ void seg_start(const SegArgs& a, PageCursor& pc, uint32_t lds,
                                           uint32_t j0, int lane) {
   if (a.pre)
     pc = *a.pre;
   else
     pc.start(a.table, a.max_blocks, (a.tile0 * kTok) >> a.shift, lane);
-  if (!a.tile0_issued)
-    issue_part<NL>(tile_rows(a, pc, a.tile0, lane), min(kTok, a.len - a.tile0 * kTok), lds, j0,
-                   lane);
+  if (!a.tile0_issued) issue_tile<kFp8, NL>(a, pc, a.tile0, load_slot<kFp8>(lds, 0), j0, lane);
 }
 
 // Step-top synchronisation shared by both wave roles: wait for this wave's
 // loads of tile k (tile k+1 may stay in flight), barrier, then issue tile
-// k+2 into the buffer tile k-2 used.
-template <int NL>
+// k+2 into the buffer tile k-2 used.  FP8 rows run one step ahead (steps
+// from -1): the loads of tile k+1 land for the P*C waves to convert during
+// step k, and tile k+3 goes into the staging slot tile k left.
+template <bool kFp8, int NL>
 __device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint32_t lds,
                                           uint32_t j0, int k, int n, int lane) {
-  if (k < n) {
-    if (k + 1 < n)
+  constexpr int A = kFp8 ? 1 : 0;
+  if (k + A < n) {
+    if (k + A + 1 < n)
       wait_vmcnt<NL>();
     else
       wait_vmcnt<0>();
@@ -186,17 +296,10 @@ __device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint
   // it reads a page id).
   asm volatile("" : "+v"(pc.cur), "+v"(pc.nxt));
   lds_barrier();
-  if (k + 2 < n) {
-    const int tile = a.tile0 + k + 2;
-    issue_part<NL>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
-                   lds + (uint32_t)((k + 2) % kNBuf) * kTileBytes, j0, lane);
-  }
+  if (k + 2 + A < n)
+    issue_tile<kFp8, NL>(a, pc, a.tile0 + k + 2 + A, load_slot<kFp8>(lds, k + 2 + A), j0, lane);
 }
 
-// Score wave `sw` (heads 16 sw .. 16 sw + 15): runs the segment's steps and
-// returns (in lanes 0..15) the reference max and full row sum of head
-// 16 sw + lane.  Inactive score waves (sw >= SW) only take part in loads and
-// barriers.
 // Queries of head 16 sw + lane%16, chunks 4 ks + lane/16 (the B operand of
 // the score MFMAs), from the segment's query rows.
 __device__ __forceinline__ void load_queries(const bf16* q_rows, int sw, int lane,
@@ -206,28 +309,30 @@ __device__ __forceinline__ void load_queries(const bf16* q_rows, int sw, int lan
   for (int ks = 0; ks < kW / 32; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
 }
 
-// qf: the segment's queries when q_ready (loaded before the segment's
-// tiles), else loaded here.
-template <int HEADS>
+// Score wave `sw` (heads 16 sw .. 16 sw + 15): runs the segment's steps and
+// returns (in lanes 0..15) the reference max and full row sum of head
+// 16 sw + lane.  Inactive score waves (sw >= SW) only take part in loads and
+// barriers.  qf: the segment's queries when q_ready (loaded before the
+// segment's tiles), else loaded here.
+template <int HEADS, bool kFp8>
 __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int sw, int lane,
                                            bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,
                                            float& l_out) {
   using G = Geo<HEADS>;
   const bool active = sw < G::SW;
   const int n = a.tile1 - a.tile0;
-  const uint32_t j0 = (uint32_t)sw * kSLoads;
+  constexpr int NL = tile_loads<kFp8>(true);
+  const uint32_t j0 = first_load<kFp8>(sw);
   PageCursor pc;
-  seg_start<kSLoads>(a, pc, lds, j0, lane);
+  seg_start<kFp8, NL>(a, pc, lds, j0, lane);
 
   const int h = 16 * sw + (lane & 15);
   const uint32_t kq = lane >> 4;
   if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
   // tile 0 and the queries (issued before tile 1) land; tile 1 may stay in flight
   if (n > 1) {
-    const int tile = a.tile0 + 1;
-    issue_part<kSLoads>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
-                        lds + kTileBytes, j0, lane);
-    wait_vmcnt<kSLoads>();
+    issue_tile<kFp8, NL>(a, pc, a.tile0 + 1, load_slot<kFp8>(lds, 1), j0, lane);
+    wait_vmcnt<NL>();
   } else {
     wait_vmcnt<0>();
   }
@@ -245,10 +350,10 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
   const uint32_t pw_base = lds + kOffP + (h * kPStride + 4 * kq) * 2;
 
   float m = -INFINITY, l = 0.f;
-  for (int k = 0; k <= n; ++k) {
-    step_sync<kSLoads>(a, pc, lds, j0, k, n, lane);
-    if (k == n || !active) continue;
-    const uint32_t buf = lds + (uint32_t)(k % kNBuf) * kTileBytes;
+  for (int k = kFp8 ? -1 : 0; k <= n; ++k) {
+    step_sync<kFp8, NL>(a, pc, lds, j0, k, n, lane);
+    if (k < 0 || k == n || !active) continue;
+    const uint32_t buf = tile_buf<kFp8>(lds, k);
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
       auto frag = [&](int ks, int tb) {
@@ -325,19 +430,16 @@ struct OAcc {
   f32x16 o[Geo<HEADS>::HB][4];
 };
 
-template <int HEADS>
+template <int HEADS, bool kFp8>
 __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, int lane,
                                         OAcc<HEADS>& acc) {
   using G = Geo<HEADS>;
   const int n = a.tile1 - a.tile0;
-  const uint32_t j0 = 4u * kSLoads + (uint32_t)pw * kPLoads;
+  constexpr int NL = tile_loads<kFp8>(false);
+  const uint32_t j0 = first_load<kFp8>(4 + pw);
   PageCursor pc;
-  seg_start<kPLoads>(a, pc, lds, j0, lane);
-  if (n > 1) {
-    const int tile = a.tile0 + 1;
-    issue_part<kPLoads>(tile_rows(a, pc, tile, lane), min(kTok, a.len - tile * kTok),
-                        lds + kTileBytes, j0, lane);
-  }
+  seg_start<kFp8, NL>(a, pc, lds, j0, lane);
+  if (n > 1) issue_tile<kFp8, NL>(a, pc, a.tile0 + 1, load_slot<kFp8>(lds, 1), j0, lane);
 #pragma unroll
   for (int hb = 0; hb < G::HB; ++hb)
 #pragma unroll
@@ -363,11 +465,21 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
   const uint32_t pa_base = lds + kOffP + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
   const uint32_t al_base = lds + kOffAlpha + (lane & 31) * 4;
 
-  for (int k = 0; k <= n; ++k) {
-    step_sync<kPLoads>(a, pc, lds, j0, k, n, lane);
-    if (k == 0) continue;
+  for (int k = kFp8 ? -1 : 0; k <= n; ++k) {
+    step_sync<kFp8, NL>(a, pc, lds, j0, k, n, lane);
+    if constexpr (kFp8) {
+      // the FP8 tile the score waves take next, once this step's P*C reads
+      // of the buffer it replaces are done (in this wave's program order)
+      if (k < 1) {
+        if (k + 1 < n)
+          convert_tile_fp8(load_slot<true>(lds, k + 1), tile_buf<true>(lds, k + 1), pw, lane);
+        continue;
+      }
+    } else {
+      if (k == 0) continue;
+    }
     const int kp = k - 1;  // tile whose P is ready
-    const uint32_t buf = lds + (uint32_t)(kp % kNBuf) * kTileBytes;
+    const uint32_t buf = tile_buf<kFp8>(lds, kp);
     const uint32_t par = (uint32_t)(kp & 1);
     const f32x4 f = lds_ld4(lds + kOffFlag + par * 16);
     float fs = f[0] + f[1];
@@ -406,6 +518,10 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
         for (int hb = 0; hb < G::HB; ++hb) acc.o[hb][cb] = mfma32(bv, pa[hb], acc.o[hb][cb]);
       }
     }
+    if constexpr (kFp8) {
+      if (k + 1 < n)
+        convert_tile_fp8(load_slot<true>(lds, k + 1), tile_buf<true>(lds, k + 1), pw, lane);
+    }
   }
 }
 
@@ -427,25 +543,25 @@ __device__ __forceinline__ void copy_out(uint32_t lds, bf16* dst) {
   lds_barrier();
 }
 
-template <int HEADS>
+template <int HEADS, bool kFp8>
 __device__ __forceinline__ void score_segment(const SegArgs& a, uint32_t lds, bf16* dst, int wave,
                                               int lane, bf16x8 (&qf)[kW / 32], bool q_ready,
                                               float& m_out, float& l_out) {
   using G = Geo<HEADS>;
-  score_role<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
+  score_role<HEADS, kFp8>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
   if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
   lds_barrier();
   lds_barrier();
   copy_out<HEADS>(lds, dst);
 }
 
-template <int HEADS>
+template <int HEADS, bool kFp8>
 __device__ __forceinline__ void pv_segment(const SegArgs& a, uint32_t lds, bf16* dst, int wave,
                                            int lane) {
   using G = Geo<HEADS>;
   const int pw = wave - 4;
   OAcc<HEADS> acc;
-  pv_role<HEADS>(a, lds, pw, lane, acc);
+  pv_role<HEADS, kFp8>(a, lds, pw, lane, acc);
   lds_barrier();
   // lane: head 32 hb + lane%32; register v of o[hb][cb]: column
   // 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 (runs of 4 -> 8-byte stores)
@@ -555,7 +671,7 @@ __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, in
 // One decode workgroup of the tile stream (block `blk`): every (workgroup,
 // sequence) piece writes one partial into slot w + b (unique: w + b grows
 // along the stream).  Returns whether this workgroup wrote any piece.
-template <int HEADS>
+template <int HEADS, bool kFp8>
 __device__ __forceinline__ bool decode_attention_wg(
     char* smem, int blk, const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int shift, int num_blocks,
@@ -591,11 +707,14 @@ __device__ __forceinline__ bool decode_attention_wg(
     const int page = spec.page(pg0, lane);
     if (page >= 0 && page < num_blocks) {
       const int tok = tg0 * kTok;
-      const bf16* rows = pool + ((long)page * (1 << shift) + (tok & ((1 << shift) - 1))) * kW;
-      if (wave < 4)
-        issue_part<kSLoads>(rows, kTok, lds, (uint32_t)wave * kSLoads, lane);
+      const long row = (long)page * (1 << shift) + (tok & ((1 << shift) - 1));
+      if constexpr (kFp8)
+        issue_part_fp8((const unsigned char*)pool + row * kF8Row, kTok, load_slot<true>(lds, 0),
+                       first_load<true>(wave), lane);
+      else if (wave < 4)
+        issue_part<kSLoads>(pool + row * kW, kTok, lds, first_load<false>(wave), lane);
       else
-        issue_part<kPLoads>(rows, kTok, lds, 4u * kSLoads + (uint32_t)(wave - 4) * kPLoads, lane);
+        issue_part<kPLoads>(pool + row * kW, kTok, lds, first_load<false>(wave), lane);
       spec_issued = true;
     }
     if (wave < Geo<HEADS>::SW) {
@@ -660,7 +779,8 @@ __device__ __forceinline__ bool decode_attention_wg(
   if (wave < 4) {
     walk([&](const SegArgs& a, int b, long slot) {
       float m, tot;
-      score_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane, qf, qb == b, m, tot);
+      score_segment<HEADS, kFp8>(a, lds, part_o + slot * HEADS * kR, wave, lane, qf, qb == b, m,
+                                 tot);
       qb = b;
       if (wave < Geo<HEADS>::SW && lane < 16) {
         const int h = 16 * wave + lane;
@@ -670,7 +790,7 @@ __device__ __forceinline__ bool decode_attention_wg(
     });
   } else {
     walk([&](const SegArgs& a, int, long slot) {
-      pv_segment<HEADS>(a, lds, part_o + slot * HEADS * kR, wave, lane);
+      pv_segment<HEADS, kFp8>(a, lds, part_o + slot * HEADS * kR, wave, lane);
     });
   }
   if (spec_issued) wait_vmcnt<0>();
@@ -956,16 +1076,16 @@ __device__ __forceinline__ void combine_wg(const int* prefix, const float* __res
 // ---------------------------------------------------------------------------
 // Split-KV attention partials only (the staged call).
 // ---------------------------------------------------------------------------
-template <int HEADS>
+template <int HEADS, bool kFp8>
 __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int shift, int num_blocks,
     const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
     int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  decode_attention_wg<HEADS>(smem, blockIdx.x, q_full, pool, block_table, max_blocks, shift,
-                             num_blocks, seq_lens, batch, H, n_wg, guess_tiles, prefix_out,
-                             part_ml, part_o);
+  decode_attention_wg<HEADS, kFp8>(smem, blockIdx.x, q_full, pool, block_table, max_blocks,
+                                   shift, num_blocks, seq_lens, batch, H, n_wg, guess_tiles,
+                                   prefix_out, part_ml, part_o);
 }
 
 // Combine of the partials (the staged call): grid (H, ceil(batch / S)).
@@ -1008,9 +1128,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
   if (wave < 4) {
     bf16x8 qf[kW / 32];
     float m, tot;
-    score_segment<HEADS>(a, lds, dst, wave, lane, qf, false, m, tot);
+    score_segment<HEADS, false>(a, lds, dst, wave, lane, qf, false, m, tot);
   } else {
-    pv_segment<HEADS>(a, lds, dst, wave, lane);
+    pv_segment<HEADS, false>(a, lds, dst, wave, lane);
   }
 }
 
@@ -1039,17 +1159,19 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
                                     const int* block_table, int max_blocks, int block_shift,
                                     const int* seq_lens,
                                     int batch, int max_seq_len, int H, int heads_per_wg, int n_wg,
-                                    int* prefix, float* part_ml, void* part_o, hipStream_t st) {
+                                    int* prefix, float* part_ml, void* part_o, hipStream_t st,
+                                    bool fp8) {
   const int hgc = H / heads_per_wg;
   const int guess_tiles = (max_seq_len + kTok - 1) / kTok;
+  auto go = [&](auto kernel) {
+    kernel<<<n_wg * hgc, kThreads, 0, st>>>((const bf16*)q_full, (const bf16*)pool, block_table,
+                                            max_blocks, block_shift, num_blocks, seq_lens, batch,
+                                            H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
+  };
   if (heads_per_wg == 64)
-    attn_decode_partials_kernel<64><<<n_wg * hgc, kThreads, 0, st>>>(
-        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, num_blocks,
-        seq_lens, batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
+    fp8 ? go(attn_decode_partials_kernel<64, true>) : go(attn_decode_partials_kernel<64, false>);
   else
-    attn_decode_partials_kernel<32><<<n_wg * hgc, kThreads, 0, st>>>(
-        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, num_blocks,
-        seq_lens, batch, H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
+    fp8 ? go(attn_decode_partials_kernel<32, true>) : go(attn_decode_partials_kernel<32, false>);
 }
 
 int combine_rows_per_wg(int H, int batch, int num_cus) {

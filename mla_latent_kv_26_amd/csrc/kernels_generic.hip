@@ -85,6 +85,17 @@ __device__ __forceinline__ float block_sum_256(float v, float* red /* [4] */) {
   return s;
 }
 
+// Block-wide max over 256 threads.
+__device__ __forceinline__ float block_max_256(float v, float* red /* [4] */) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return m;
+}
+
 // RMSNorm of float32 rows into dtype T.  One block per row.
 template <typename T>
 __global__ void __launch_bounds__(256) rms_norm_rows_kernel(const float* __restrict__ in, long ld_in,
@@ -162,11 +173,69 @@ __global__ void __launch_bounds__(256) append_rows_paged_kernel(
   store_row<T>(z + (long)n * ld_z, gain, rope + (long)p * Dr, pool + s * (R + Dr), R, Dr, eps, red);
 }
 
+// FP8 cache rows (R + 2 Dr + 16 bytes): the latent c = RMSNorm(z[:R]) g in
+// FP8 E4M3 with one power-of-two scale per row, s = 2^e for the smallest e
+// with max|c| <= 448 2^e (1 for an all-zero c), code = RNE(c / s); then the
+// rotated rope key in bf16, then s as float32 and 12 zero bytes.  The
+// exponent comes from frexp (max|c| = m 2^E, m in [0.5, 1): e = E - 9 when
+// m <= 0.875, else E - 8), so no rounding enters the choice of s, and c / s
+// is exact before the hardware's round-to-nearest-even conversion.
+__device__ __forceinline__ void store_row_fp8(const float* z, const float* gain,
+                                              const float* rope_row, unsigned char* dst, int R,
+                                              int Dr, float eps, float* red) {
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < R; k += 256) ss = fmaf(z[k], z[k], ss);
+  ss = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)R + eps);
+  float amax = 0.f;
+  for (int k = threadIdx.x; k < R; k += 256) amax = fmaxf(amax, fabsf(z[k] * inv * gain[k]));
+  amax = block_max_256(amax, red);
+  float scale = 1.0f;
+  if (amax > 0.f) {
+    int E;
+    const float m = frexpf(amax, &E);
+    scale = ldexpf(1.0f, m <= 0.875f ? E - 9 : E - 8);
+  }
+  typedef short __attribute__((ext_vector_type(2))) short2v;
+  for (int k2 = threadIdx.x; 2 * k2 < R; k2 += 256) {
+    const float a = z[2 * k2] * inv * gain[2 * k2], b = z[2 * k2 + 1] * inv * gain[2 * k2 + 1];
+    const short2v pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2v{0, 0}, a, b, scale, false);
+    *(unsigned short*)(dst + 2 * k2) = (unsigned short)pk[0];
+  }
+  bf16* rope_dst = (bf16*)(dst + R);
+  const int half = Dr >> 1;
+  for (int i = threadIdx.x; i < half; i += 256) {
+    const float c = rope_row[i], s = rope_row[half + i];
+    const float a = z[R + i], b = z[R + half + i];
+    rope_dst[i] = (bf16)(a * c - b * s);
+    rope_dst[half + i] = (bf16)(b * c + a * s);
+  }
+  if (threadIdx.x < 4) {
+    float* tail = (float*)(dst + R + 2 * Dr);
+    tail[threadIdx.x] = threadIdx.x == 0 ? scale : 0.f;
+  }
+}
+
+__global__ void __launch_bounds__(256) append_rows_fp8_kernel(
+    const float* __restrict__ z, long ld_z, const float* __restrict__ gain,
+    const float* __restrict__ rope, const int* __restrict__ pos, const int* __restrict__ slot,
+    unsigned char* __restrict__ pool, int R, int Dr, float eps) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int s = slot[t];
+  if (s < 0) return;  // uniform across the block
+  store_row_fp8(z + (long)t * ld_z, gain, rope + (long)pos[t] * Dr,
+                pool + (long)s * (R + 2 * Dr + 16), R, Dr, eps, red);
+}
+
 void launch_append_rows(const float* z, long ld_z, const float* gain, const float* rope,
                         const int* pos, const int* slot, void* pool, int n, int R, int Dr,
                         float eps, int dtype, hipStream_t st) {
   if (n <= 0) return;
-  if (dtype == 1)
+  if (dtype == 2)
+    append_rows_fp8_kernel<<<n, 256, 0, st>>>(z, ld_z, gain, rope, pos, slot, (unsigned char*)pool,
+                                              R, Dr, eps);
+  else if (dtype == 1)
     append_rows_kernel<bf16><<<n, 256, 0, st>>>(z, ld_z, gain, rope, pos, slot, (bf16*)pool, R, Dr, eps);
   else
     append_rows_kernel<float><<<n, 256, 0, st>>>(z, ld_z, gain, rope, pos, slot, (float*)pool, R, Dr, eps);

@@ -22,7 +22,8 @@ void launch_rms_norm_rows(const float* in, long ld_in, const float* gain, void* 
 
 // Cache rows from z = x W_DKV (float32 [n, R + Dr], row stride ld_z):
 // pool[slot[t]] = [RMSNorm(z[t, :R]) * gain | RoPE(z[t, R:], pos[t])].
-// Tokens with slot < 0 are skipped.  dtype: 0 f32, 1 bf16 pool.
+// Tokens with slot < 0 are skipped.  dtype: 0 f32, 1 bf16 pool, 2 FP8 rows
+// (R E4M3 codes | Dr bf16 | float32 power-of-two scale | 12 zero bytes).
 void launch_append_rows(const float* z, long ld_z, const float* gain, const float* rope,
                         const int* pos, const int* slot, void* pool, int n, int R, int Dr,
                         float eps, int dtype, hipStream_t st);
@@ -119,8 +120,9 @@ bool launch_absorb_query_bf16(const void* q_nope, const void* q_rope, const void
                               void* q_full, int B, int H, int Dn, int R, int Dr, float alpha,
                               hipStream_t st);
 
-// Decode attention over a paged bf16 pool, R = 512, Dr = 64, 32 or 64 heads
-// per workgroup, block_size a power of two >= 64.  Writes split partials
+// Decode attention over a paged bf16 pool (or, with fp8, FP8 cache rows of
+// 656 bytes), R = 512, Dr = 64, 32 or 64 heads per workgroup, block_size a
+// power of two >= 64.  Writes split partials
 // (bf16 O normalised by its own sum, float32 (m, l) in log2 units) and the
 // tile prefix sums, for launch_combine.
 size_t decode_partial_slots(int batch, int n_wg);
@@ -131,7 +133,8 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
                                     const int* block_table, int max_blocks, int block_shift,
                                     const int* seq_lens,
                                     int batch, int max_seq_len, int H, int heads_per_wg, int n_wg,
-                                    int* prefix, float* part_ml, void* part_o, hipStream_t st);
+                                    int* prefix, float* part_ml, void* part_o, hipStream_t st,
+                                    bool fp8 = false);
 
 // Merge the partials of each (sequence, head) into o_lat (bf16 [batch, H, R])
 // or, when w_uv != NULL, project directly: out[b, h] = o_lat[b, h] W_UV[h].

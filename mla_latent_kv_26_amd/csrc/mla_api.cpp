@@ -30,6 +30,8 @@ struct Dims {
   int H, R, Dr, Dn, Dv, M, Rq, bs, dt, W, shift;
   float scale, eps, theta;
   size_t esz;
+  bool fp8;          // FP8 cache rows
+  size_t row_bytes;  // bytes per cache row
 };
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -67,6 +69,10 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
     return fail(MLA_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
   if (c->dtype != MLA_DTYPE_F32 && c->dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (c->cache_dtype != MLA_CACHE_SAME && c->cache_dtype != MLA_CACHE_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARG, "unknown cache_dtype %d", c->cache_dtype);
+  if (c->cache_dtype == MLA_CACHE_FP8_E4M3 && c->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "an FP8 cache needs dtype bf16");
   if (d) {
     d->H = c->num_heads;
     d->R = c->kv_lora_rank;
@@ -84,6 +90,8 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
     d->eps = c->rms_eps;
     d->theta = c->rope_theta;
     d->esz = d->dt == MLA_DTYPE_BF16 ? 2 : 4;
+    d->fp8 = c->cache_dtype == MLA_CACHE_FP8_E4M3;
+    d->row_bytes = d->fp8 ? (size_t)d->R + 2 * (size_t)d->Dr + 16 : (size_t)d->W * d->esz;
   }
   return MLA_OK;
 }
@@ -308,7 +316,7 @@ int64_t mla_cache_bytes_per_token(const mla_config* cfg) {
   Dims d;
   g_err.clear();
   if (check_cfg(cfg, &d) != MLA_OK) return -1;
-  return (int64_t)d.W * (int64_t)d.esz;
+  return (int64_t)d.row_bytes;
 }
 
 mla_status mla_rope_table(const mla_config* cfg, int32_t num_positions, float* host_table) {
@@ -372,7 +380,7 @@ static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* 
     mla::launch_attention_partials_bf16(q_full, pool, num_blocks, table, max_blocks, d.shift,
                                         seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
                                         (int*)at(ws, w.prefix), (float*)at(ws, w.part_ml),
-                                        at(ws, w.part_o), st);
+                                        at(ws, w.part_o), st, d.fp8);
     mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
                         at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, max_seq_len, w_uv, d.Dv, dst,
                         num_cus(), st);
@@ -485,7 +493,7 @@ mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, con
                                       d.shift, seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
                                       (int*)at(workspace, w.prefix),
                                       (float*)at(workspace, w.part_ml), at(workspace, w.part_o),
-                                      (hipStream_t)stream);
+                                      (hipStream_t)stream, d.fp8);
   return launched("mla_attention_partials");
 }
 
@@ -610,6 +618,8 @@ mla_status mla_cache_append(const mla_config* cfg, const void* x, const void* w_
   if (s != MLA_OK) return s;
   if (d.dt == MLA_DTYPE_BF16 && (d.M % 8 || d.W % 8))
     return fail(MLA_ERR_UNSUPPORTED, "bf16 append needs d_model and kv_lora_rank + rope_dim multiples of 8");
+  if (d.fp8 && (d.R % 16 || d.Dr % 8))
+    return fail(MLA_ERR_UNSUPPORTED, "FP8 cache rows need kv_lora_rank % 16 == 0 and rope_dim % 8 == 0");
   size_t need = 0;
   mla_cache_append_workspace_size(cfg, n_tokens, &need);
   if (!workspace || workspace_bytes < need)
@@ -619,7 +629,7 @@ mla_status mla_cache_append(const mla_config* cfg, const void* x, const void* w_
   float* z = (float*)at(workspace, 256);
   gemm(d, x, w_dkv, z, n_tokens, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
   mla::launch_append_rows(z, d.W, kv_norm_w, rope_table, positions, slot_mapping, kv_pool, n_tokens,
-                          d.R, d.Dr, d.eps, d.dt, st);
+                          d.R, d.Dr, d.eps, d.fp8 ? 2 : d.dt, st);
   return launched("mla_cache_append");
 }
 
@@ -651,6 +661,10 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
   if (d.M <= 0) return fail(MLA_ERR_INVALID_ARG, "prefill needs d_model > 0");
+  if (d.fp8)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "prefill over an FP8 cache is not built; append with mla_cache_append and attend "
+                "with the decode calls");
   if (batch <= 0 || q_len <= 0)
     return fail(MLA_ERR_INVALID_ARG, "batch and q_len must be positive (got %d, %d)", batch, q_len);
   if (max_start_pos < 0) return fail(MLA_ERR_INVALID_ARG, "max_start_pos must be >= 0");

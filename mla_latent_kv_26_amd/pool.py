@@ -22,9 +22,9 @@ class LatentKVPool:
             raise ValueError("num_blocks must be positive")
         self.cfg = cfg
         self.num_blocks = num_blocks
-        shape = (num_blocks, cfg.block_size, cfg.row)
+        shape = (num_blocks, cfg.block_size, cfg.pool_row)
         alloc = torch.zeros if zero else torch.empty
-        self.data = alloc(shape, dtype=cfg.torch_dtype, device=device)
+        self.data = alloc(shape, dtype=cfg.pool_dtype, device=device)
         self._free: List[int] = list(range(num_blocks - 1, -1, -1))
         self._blocks: Dict[int, List[int]] = {}
         self._len: Dict[int, int] = {}

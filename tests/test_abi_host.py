@@ -36,7 +36,7 @@ def test_every_header_symbol_is_exported_and_bound():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     for s, name in _lib.STATUS_NAMES.items():
         assert lib.mla_status_string(s).decode() == name
 
