@@ -44,7 +44,8 @@ def algorithmic(cfg, lens):
                                          "qk_nope_dim", "v_dim"))
     B = len(lens)
     tokens = int(np.sum(lens))
-    row_bytes = (R + Dr) * 2
+    # bf16 rows, or FP8 rows: R codes, Dr bf16 rope values, scale and padding
+    row_bytes = R + 2 * Dr + 16 if cfg.get("cache_dtype") == "fp8" else (R + Dr) * 2
     cache = tokens * row_bytes
     weights = 2 * H * R * (Dn + Dv)
     io = 2 * B * H * (Dn + Dr + Dv)
@@ -341,6 +342,8 @@ def main():
                    "kv_lora_rank": cfg["kv_lora_rank"], "rope_dim": cfg["rope_dim"],
                    "qk_nope_dim": cfg["qk_nope_dim"], "v_dim": cfg["v_dim"],
                    "block_size": cfg["block_size"], "input_sets_rotated": R,
+                   "cache": "fp8 e4m3 rows, 656 B/token" if cfg.get("cache_dtype") == "fp8"
+                   else "bf16 rows, 1152 B/token",
                    "timing": f"hip graph replay ({per} steps per replay), events on the launching stream"},
         "roofline": {
             "kernel": "attn_decode_partials_kernel",

@@ -59,6 +59,13 @@ WORKLOADS: Dict[str, dict] = {
         qk_nope_dim=128, v_dim=128, rows=8192, gated=True, block_size=64, dtype="bf16",
         seed=6),
 }
+# The same decode shapes over an FP8 latent cache (E4M3 codes with a per-row
+# power-of-two scale, bf16 rope key: 656 bytes per token instead of 1152).
+WORKLOADS["decode_h64_b32_l4096_fp8"] = dict(WORKLOADS["decode_h64_b32_l4096"],
+                                             cache_dtype="fp8")
+WORKLOADS["longctx_h64_b4_l131072_fp8"] = dict(WORKLOADS["longctx_h64_b4_l131072"],
+                                               cache_dtype="fp8")
+
 
 HEADLINE = "decode_h64_b32_l4096"
 
@@ -278,11 +285,29 @@ def decode_inputs_torch(cfg: dict, seed: int, device, lengths=None):
             t.mul_(std)
         return t.to(dt)
 
+    if cfg.get("cache_dtype") == "fp8":
+        # FP8 rows drawn directly (no values are quantized here): codes
+        # uniform over the finite non-negative E4M3 codes with a random sign,
+        # one power-of-two scale per row (2^-9 .. 2^-7), a N(0,1) bf16 rope
+        # key, zero padding: R codes | Dr bf16 | float32 scale | 12 bytes
+        pool = torch.zeros((nblocks, bs, R + 2 * Dr + 16), dtype=torch.uint8, device=device)
+        codes = torch.randint(0, 0x7F, (nblocks, bs, R), generator=g, device=device,
+                              dtype=torch.uint8)
+        sign = torch.randint(0, 2, (nblocks, bs, R), generator=g, device=device,
+                             dtype=torch.uint8)
+        pool[..., :R] = codes | (sign << 7)
+        pool[..., R:R + 2 * Dr] = torch.randn((nblocks, bs, Dr), generator=g, device=device,
+                                              dtype=torch.float32).to(torch.bfloat16).view(
+                                                  torch.uint8)
+        expo = torch.randint(-9, -6, (nblocks, bs, 1), generator=g, device=device)
+        pool[..., R + 2 * Dr:R + 2 * Dr + 4] = torch.exp2(expo.float()).view(torch.uint8)
+    else:
+        pool = n((nblocks, bs, R + Dr))
     return dict(
         seq_lens=torch.from_numpy(lens).to(device),
         block_table=torch.from_numpy(table).to(device),
         max_seq_len=int(lens.max()),
-        pool=n((nblocks, bs, R + Dr)),
+        pool=pool,
         q_nope=n((B, H, Dn)), q_rope=n((B, H, Dr)),
         w_uk=n((H, Dn, R), 1.0 / math.sqrt(R)), w_uv=n((H, R, Dv), 1.0 / math.sqrt(R)),
     )
