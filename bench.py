@@ -113,6 +113,8 @@ def prefill_main(args, torch, m):
                    "q_lora_rank": cfg.get("q_lora_rank", 0), "heads": cfg["num_heads"],
                    "algorithmic_flops": alg["flops"], "attention_flops": alg["attn_flops"],
                    "executed_flops_per_head_path": alg["per_head_flops"],
+                   "cache": "fp8 e4m3 rows, 656 B/token" if cfg.get("cache_dtype") == "fp8"
+                            else "bf16 rows, 1152 B/token",
                    "timing": "hip graph replay, events on the launching stream"},
         "roofline": {"kernel": "mla_prefill (whole call, per-head key/value path)",
                      "bound": "mfma", "achieved": round(executed, 2), "peak": BF16_PEAK_TFLOPS,

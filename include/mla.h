@@ -48,7 +48,8 @@
  *     two with max|c| <= 448 s (1 for an all-zero c), so s * code is exact
  *     in bf16.  The pool is then [num_blocks, block_size, R + 2 Dr + 16]
  *     bytes.  Decode reads and mla_cache_append writes such pools (R=512,
- *     Dr=64); mla_prefill returns MLA_ERR_UNSUPPORTED for them.
+ *     Dr=64); mla_prefill takes them when Dn = Dv = 128 as well (else
+ *     MLA_ERR_UNSUPPORTED).
  */
 #ifndef MLA_LATENT_KV_H
 #define MLA_LATENT_KV_H
@@ -255,7 +256,10 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int3
  * Q, K and V").  bf16 with R = 512, Dr = 64, Dn = Dv = 128 takes the second
  * when it needs fewer FLOPs: 2H(Dn + Dr + Dv) per (query, key) pair plus
  * 2H R (Dn + Dv) per context token, against 2H(2R + Dr) per pair (long new
- * spans; continuations of a few tokens stay on the latent rows). */
+ * spans; continuations of a few tokens stay on the latent rows).  Over an
+ * FP8 cache the second form is always taken: the new rows are stored in FP8
+ * first, and every key and value, the new tokens' own included, comes from
+ * the stored rows. */
 mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, const void* w_dq,
                        const float* q_norm_w, const void* w_uq, const void* w_dkv,
                        const float* kv_norm_w, const void* w_uk, const void* w_uv,

@@ -228,6 +228,22 @@ __global__ void __launch_bounds__(256) append_rows_fp8_kernel(
                 pool + (long)s * (R + 2 * Dr + 16), R, Dr, eps, red);
 }
 
+// FP8 rows of a prefill: token t of sequence b goes to position start_pos[b] + t
+// through the page table, in the format of store_row_fp8.
+__global__ void __launch_bounds__(256) append_rows_paged_fp8_kernel(
+    const float* __restrict__ z, long ld_z, const float* __restrict__ gain,
+    const float* __restrict__ rope, const int* __restrict__ start_pos,
+    const int* __restrict__ block_table, int max_blocks, int block_size,
+    unsigned char* __restrict__ pool, int T_len, int R, int Dr, float eps) {
+  __shared__ float red[4];
+  const int n = blockIdx.x;
+  const int b = n / T_len, t = n - b * T_len;
+  const int p = start_pos[b] + t;
+  const long s = (long)block_table[(long)b * max_blocks + p / block_size] * block_size + p % block_size;
+  store_row_fp8(z + (long)n * ld_z, gain, rope + (long)p * Dr, pool + s * (R + 2 * Dr + 16), R, Dr,
+                eps, red);
+}
+
 void launch_append_rows(const float* z, long ld_z, const float* gain, const float* rope,
                         const int* pos, const int* slot, void* pool, int n, int R, int Dr,
                         float eps, int dtype, hipStream_t st) {
@@ -247,7 +263,11 @@ void launch_append_rows_paged(const float* z, long ld_z, const float* gain, cons
                               float eps, int dtype, hipStream_t st) {
   const int n = batch * T;
   if (n <= 0) return;
-  if (dtype == 1)
+  if (dtype == 2)
+    append_rows_paged_fp8_kernel<<<n, 256, 0, st>>>(z, ld_z, gain, rope, start_pos, block_table,
+                                                    max_blocks, block_size, (unsigned char*)pool,
+                                                    T, R, Dr, eps);
+  else if (dtype == 1)
     append_rows_paged_kernel<bf16><<<n, 256, 0, st>>>(z, ld_z, gain, rope, start_pos, block_table,
                                                       max_blocks, block_size, (bf16*)pool, T, R,
                                                       Dr, eps);

@@ -150,13 +150,14 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
 // attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].
 // Prefill through per-head keys and values (bf16, R = 512, Dn = Dv = 128,
 // Dr = 64).  gather: dst [batch, ctx_pad, R + Dr] = each sequence's cache
-// rows 0 .. start_pos[b] + T - 1, zero after.  flash: out [batch, T, H, Dv] =
+// rows 0 .. start_pos[b] + T - 1, zero after (fp8: from 656-byte FP8 rows,
+// widened to bf16).  flash: out [batch, T, H, Dv] =
 // causal softmax(Q K^T) V with Q = alpha [q_nope | RoPE(q_pe, position)] from
 // q [batch * T, H (Dn + Dr)], K = [kn | rope part of cg] (kn, v: [batch,
 // ctx_pad, H, 128]).
 void launch_gather_rows(const void* pool, const int* block_table, int max_blocks, int shift,
                         const int* start_pos, int batch, int T, int ctx_pad, void* dst,
-                        hipStream_t st);
+                        bool fp8, hipStream_t st);
 void launch_flash_prefill(const void* q, const float* rope, float alpha, const void* kn,
                           const void* cg, const void* v, const int* start_pos, int batch, int T,
                           int H, int ctx_pad, void* out, hipStream_t st);

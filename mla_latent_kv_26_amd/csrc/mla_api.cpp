@@ -176,9 +176,14 @@ DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
 // attending on the latent rows: per (query, key) pair 2H(Dn + Dr + Dv)
 // against 2H(2R + Dr), plus 2H R (Dn + Dv) per context token to build K and V
 // (context = max_start_pos + q_len).  bf16 with the shapes of its kernels.
+bool prefill_naive_shapes(const Dims& d) {
+  return d.dt == MLA_DTYPE_BF16 && d.R == 512 && d.Dr == 64 && d.Dn == 128 && d.Dv == 128;
+}
+// An FP8 cache always takes the naive path: its gather widens the stored
+// rows to bf16, and everything after it is the bf16 path.
 bool prefill_naive(const Dims& d, int q_len, int max_start_pos) {
-  if (d.dt != MLA_DTYPE_BF16 || d.R != 512 || d.Dr != 64 || d.Dn != 128 || d.Dv != 128)
-    return false;
+  if (!prefill_naive_shapes(d)) return false;
+  if (d.fp8) return true;
   const double T = q_len, S = max_start_pos;
   const double pairs = T * (S + (T + 1) / 2);
   const double latent = (2.0 * d.R + d.Dr) * pairs;
@@ -661,10 +666,10 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
   if (d.M <= 0) return fail(MLA_ERR_INVALID_ARG, "prefill needs d_model > 0");
-  if (d.fp8)
+  if (d.fp8 && !prefill_naive_shapes(d))
     return fail(MLA_ERR_UNSUPPORTED,
-                "prefill over an FP8 cache is not built; append with mla_cache_append and attend "
-                "with the decode calls");
+                "prefill over an FP8 cache needs bf16 with kv_lora_rank 512, rope_dim 64 and "
+                "qk_nope_dim = v_dim = 128");
   if (batch <= 0 || q_len <= 0)
     return fail(MLA_ERR_INVALID_ARG, "batch and q_len must be positive (got %d, %d)", batch, q_len);
   if (max_start_pos < 0) return fail(MLA_ERR_INVALID_ARG, "max_start_pos must be >= 0");
@@ -729,7 +734,7 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
     gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
   mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
                                 max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
-                                d.dt, st);
+                                d.fp8 ? 2 : d.dt, st);
   // 2. queries
   void* q = at(workspace, w.q);
   if (d.Rq > 0) {
@@ -746,7 +751,7 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
     //     attention straight to the output
     void* cg = at(workspace, w.cg);
     mla::launch_gather_rows(kv_pool, block_table, max_blocks_per_seq, d.shift, start_pos, batch,
-                            q_len, w.ctx_pad, cg, st);
+                            q_len, w.ctx_pad, cg, d.fp8, st);
     // K_nope[t, h*Dn + d] = c_t . W_UK[h, d, :] (W_UK as one [H*Dn, R] matrix, given
     // transposed) and V[t, h*Dv + e] = c_t . W_UV[h, :, e] (W_UV as column blocks of Dv),
     // every sequence of the batch in one launch each

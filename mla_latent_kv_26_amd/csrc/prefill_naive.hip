@@ -448,12 +448,56 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(
   *(bf16x8*)(dst + row * 576 + c * 8) = v;
 }
 
+// The same rows from an FP8 cache (656-byte rows: 512 E4M3 codes, 64 bf16
+// rope values, the float32 power-of-two scale), widened to bf16 rows.  scale
+// times a code is exact in bf16 (3 mantissa bits, a power-of-two factor), so
+// the rows match what the decode path reads.  One thread per 8 values.
+__global__ void __launch_bounds__(256) gather_rows_fp8_kernel(
+    const unsigned char* __restrict__ pool, const int* __restrict__ block_table, int max_blocks,
+    int shift, const int* __restrict__ start_pos, int T, int ctx_pad, long total,
+    bf16* __restrict__ dst) {
+  constexpr int kChunks = 576 / 8, kRow = 656;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long row = i / kChunks;
+  const int c = (int)(i - row * kChunks);
+  const int b = (int)(row / ctx_pad), j = (int)(row - (long)b * ctx_pad);
+  bf16x8 v = {};
+  if (j < start_pos[b] + T) {
+    const int page = block_table[(long)b * max_blocks + (j >> shift)];
+    const unsigned char* src = pool + (((long)page << shift) + (j & ((1 << shift) - 1))) * kRow;
+    if (c < 64) {
+      const float sc = *(const float*)(src + 640);
+      const uint2 raw = *(const uint2*)(src + c * 8);
+      const uint32_t w[2] = {raw.x, raw.y};
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], sc, false);
+        const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], sc, true);
+        v[4 * d + 0] = lo[0];
+        v[4 * d + 1] = lo[1];
+        v[4 * d + 2] = hi[0];
+        v[4 * d + 3] = hi[1];
+      }
+    } else {
+      v = *(const bf16x8*)(src + 512 + (c - 64) * 16);
+    }
+  }
+  *(bf16x8*)(dst + row * 576 + c * 8) = v;
+}
+
 }  // namespace
 
 void launch_gather_rows(const void* pool, const int* block_table, int max_blocks, int shift,
                         const int* start_pos, int batch, int T, int ctx_pad, void* dst,
-                        hipStream_t st) {
+                        bool fp8, hipStream_t st) {
   const long chunks = (long)batch * ctx_pad * (576 / 8);
+  if (fp8) {
+    gather_rows_fp8_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(
+        (const unsigned char*)pool, block_table, max_blocks, shift, start_pos, T, ctx_pad, chunks,
+        (bf16*)dst);
+    return;
+  }
   gather_rows_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(
       (const bf16*)pool, block_table, max_blocks, shift, start_pos, T, ctx_pad, chunks,
       (bf16*)dst);

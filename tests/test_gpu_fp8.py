@@ -96,6 +96,26 @@ def bf16(a):
     return bits, workloads.to_f64(bits)
 
 
+def check_fp8_rows(got_raw, rows, R, Dr):
+    """Stored FP8 rows against the oracle's unrounded rows (float64): scales
+    equal unless max|c| sits on a power-of-two boundary, codes within one
+    E4M3 step (the two sides round different float32/float64 sums), the rope
+    key within a bf16 step, pad bytes zero."""
+    codes, s, rope = oracle.unpack_rows_fp8(got_raw, R, Dr)
+    q_codes, q_s, _ = oracle.quantize_rows_fp8(rows, R)
+    same = s == q_s
+    assert same.mean() >= 0.98, same.mean()
+    assert np.all((s == 2 * q_s) | (2 * s == q_s) | same)
+    got_c = oracle.e4m3_value(codes) * s[:, None]
+    ref_c = rows[:, :R]
+    # one E4M3 step of |c| / s (3 mantissa bits), at least a subnormal step
+    step = np.maximum(np.abs(ref_c) / 8.0, 2.0 ** -9 * q_s[:, None])
+    assert np.all(np.abs(got_c - ref_c) <= step + 1e-12)
+    assert np.mean(codes[same] == q_codes[same]) >= 0.999
+    assert np.all(np.abs(rope - rows[:, R:]) <= 2.0 ** -7 * np.abs(rows[:, R:]) + 1e-6)
+    assert np.all(got_raw[:, R + 2 * Dr + 4:] == 0)
+
+
 def _append_case(n=300, seed=41):
     rng = np.random.default_rng(seed)
     cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=0,
@@ -127,22 +147,9 @@ def test_fp8_cache_append_rows(m):
     sync()
     raw = pool.cpu().numpy().reshape(nb * bs, -1)
     keep = slots >= 0
-    got_raw = raw[slots[keep]]
-    codes, s, rope = oracle.unpack_rows_fp8(got_raw, R, Dr)
     w64 = {"w_dkv": w_dkv, "kv_norm_w": gain.astype(np.float64)}
     rows = oracle.append_rows(x[keep], pos[keep], w64, cfg, storage="f64")
-    q_codes, q_s, q_rope = oracle.quantize_rows_fp8(rows, R)
-    same = s == q_s
-    assert same.mean() >= 0.98, same.mean()
-    assert np.all((s == 2 * q_s) | (2 * s == q_s) | same)
-    got_c = oracle.e4m3_value(codes) * s[:, None]
-    ref_c = rows[:, :R]
-    # one E4M3 step of |c| / s (3 mantissa bits), at least a subnormal step
-    step = np.maximum(np.abs(ref_c) / 8.0, 2.0 ** -9 * q_s[:, None])
-    assert np.all(np.abs(got_c - ref_c) <= step + 1e-12)
-    assert np.mean(codes[same] == q_codes[same]) >= 0.999
-    assert np.all(np.abs(rope - rows[:, R:]) <= 2.0 ** -7 * np.abs(rows[:, R:]) + 1e-6)
-    assert np.all(got_raw[:, R + 2 * Dr + 4:] == 0)
+    check_fp8_rows(raw[slots[keep]], rows, R, Dr)
     untouched = np.setdiff1d(np.arange(nb * bs), slots[keep])
     assert np.all(raw[untouched] == 0xAB)
 
@@ -179,10 +186,74 @@ def test_fp8_append_then_decode(m):
     assert_bf16(to_host_f64(out), ref, "fp8 append then decode", per_row_axis=0)
 
 
-def test_fp8_prefill_is_rejected(m):
+def _pool_raw(pool, table, L):
+    raw = pool.cpu().numpy()
+    j = np.arange(L)
+    return raw[table[j // raw.shape[1]], j % raw.shape[1]]
+
+
+def test_fp8_prefill_with_continuation(m):
+    """Prefill into an FP8 cache (600 new tokens, then 300 more at position
+    600, permuted pages, jittered gains): the stored rows against the
+    oracle's quantization, the outputs against the oracle's forward over an
+    FP8 cache (new rows stored first, every key and value read back from
+    the stored rows)."""
     import torch
     cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=128,
-               cache_dtype="fp8", seed=46)
+               cache_dtype="fp8", seed=47)
+    mc = m.MLAConfig.from_dict(cfg)
+    R, Dr = cfg["kv_lora_rank"], cfg["rope_dim"]
+    inp = workloads.prefill_inputs(cfg, q_len=900, batch=2, gain_jitter=0.1)
+    w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+    w64 = {k: (None if v is None else workloads.to_f64(v)) for k, v in vars(inp.weights).items()}
+    pool = torch.zeros((inp.num_blocks, 64, mc.pool_row), dtype=torch.uint8, device="cuda")
+    table = to_dev(inp.block_table)
+    x = to_dev(inp.x)
+    out1 = m.mla_prefill(mc, x[:, :600].contiguous(), w, pool, table,
+                         torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+    out2 = m.mla_prefill(mc, x[:, 600:].contiguous(), w, pool, table,
+                         torch.full((2,), 600, dtype=torch.int32, device="cuda"), 600)
+    sync()
+    got = np.concatenate([to_host_f64(out1), to_host_f64(out2)], axis=1)
+    for b in range(2):
+        x64 = workloads.to_f64(inp.x[b])
+        rows = oracle.append_rows(x64, np.arange(900), w64, cfg, storage="f64")
+        check_fp8_rows(_pool_raw(pool, inp.block_table[b], 900), rows, R, Dr)
+        ref, _ = oracle.layer_forward(x64, w64, cfg, storage="fp8")
+        assert_bf16(got[b], ref, f"fp8 prefill b={b}", per_row_axis=0)
+
+
+def test_fp8_prefill_d7168_b2_t4096_sample(m):
+    """The full-size prefill over an FP8 cache: every stored row checked,
+    outputs on a sample of query rows of both sequences."""
+    import torch
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], cache_dtype="fp8")
+    mc = m.MLAConfig.from_dict(cfg)
+    R, Dr, T = cfg["kv_lora_rank"], cfg["rope_dim"], cfg["q_len"]
+    inp = workloads.prefill_inputs(cfg)
+    w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+    pool = torch.zeros((inp.num_blocks, 64, mc.pool_row), dtype=torch.uint8, device="cuda")
+    out = m.mla_prefill(mc, to_dev(inp.x), w, pool, to_dev(inp.block_table),
+                        torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+    sync()
+    w64 = {k: (None if v is None else workloads.to_f64(v)) for k, v in vars(inp.weights).items()}
+    sample = [0, 1, 63, 64, 65, 1000, 2047, 4095]
+    for b in range(2):
+        x64 = workloads.to_f64(inp.x[b])
+        rows = oracle.append_rows(x64, np.arange(T), w64, cfg, storage="f64")
+        check_fp8_rows(_pool_raw(pool, inp.block_table[b], T), rows, R, Dr)
+        stored = oracle.fp8_store_rows(rows, R)
+        ref = oracle.attend_tokens(x64[sample], np.array(sample), w64, cfg, stored, q_block=1)
+        e = assert_bf16(to_host_f64(out[b, sample]), ref, f"fp8 prefill b={b}", per_row_axis=0)
+        print("fp8 prefill_d7168_b2_t4096", b, e)
+
+
+def test_fp8_prefill_other_widths_rejected(m):
+    """FP8 prefill runs on the per-head key/value kernels only (Dn = Dv =
+    128); other head widths get MLA_ERR_UNSUPPORTED before any launch."""
+    import torch
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=128,
+               qk_nope_dim=64, v_dim=64, cache_dtype="fp8", seed=46)
     mc = m.MLAConfig.from_dict(cfg)
     inp = workloads.prefill_inputs(cfg, q_len=8, batch=1)
     w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}

@@ -65,6 +65,8 @@ WORKLOADS["decode_h64_b32_l4096_fp8"] = dict(WORKLOADS["decode_h64_b32_l4096"],
                                              cache_dtype="fp8")
 WORKLOADS["longctx_h64_b4_l131072_fp8"] = dict(WORKLOADS["longctx_h64_b4_l131072"],
                                                cache_dtype="fp8")
+WORKLOADS["prefill_d7168_b2_t4096_fp8"] = dict(WORKLOADS["prefill_d7168_b2_t4096"],
+                                               cache_dtype="fp8")
 
 
 HEADLINE = "decode_h64_b32_l4096"
@@ -344,8 +346,11 @@ def prefill_inputs_torch(cfg: dict, seed: int, device):
                  w_uq=n((Rq, qw), 1.0 / math.sqrt(Rq)))
     else:
         w.update(w_q=n((M, qw), 1.0 / math.sqrt(M)))
-    return dict(x=n((B, T, M)), weights=w,
-                pool=torch.zeros((nblocks, bs, R + Dr), dtype=dt, device=device),
+    if cfg.get("cache_dtype") == "fp8":   # rows of R + 2 Dr + 16 bytes
+        pool = torch.zeros((nblocks, bs, R + 2 * Dr + 16), dtype=torch.uint8, device=device)
+    else:
+        pool = torch.zeros((nblocks, bs, R + Dr), dtype=dt, device=device)
+    return dict(x=n((B, T, M)), weights=w, pool=pool,
                 block_table=torch.from_numpy(table).to(device),
                 start_pos=torch.zeros(B, dtype=torch.int32, device=device))
 
