@@ -47,7 +47,7 @@ def algorithmic(cfg, lens):
     # bf16 rows, or FP8 rows: R codes, Dr bf16 rope values, scale and padding
     row_bytes = R + 2 * Dr + 16 if cfg.get("cache_dtype") == "fp8" else (R + Dr) * 2
     cache = tokens * row_bytes
-    weights = 2 * H * R * (Dn + Dv)
+    weights = 2 * (cfg.get("kv_groups") or H) * R * (Dn + Dv)   # W_UK, W_UV (shared or per head)
     io = 2 * B * H * (Dn + Dr + Dv)
     flops_attn = 2 * H * (R + Dr + R) * tokens
     flops_proj = 2 * B * H * R * (Dn + Dv)
@@ -214,6 +214,23 @@ def traffic_entry(workload):
     return rec.get("bytes_per_launch")
 
 
+VALU_PEAK_TFLOPS = 157.3      # fp32 vector ALU, 256 CUs at 2.4 GHz
+
+
+def narrow_roofline(alg, attn_ms):
+    """Narrow latents run on vector-ALU kernels: 2 H (2R + Dr) flops per
+    token against (R + Dr) 2 bytes, beyond what the ALUs can do at the HBM
+    rate, so the bound is the ALU peak."""
+    tf = alg["attn_flops"] / (attn_ms * 1e-3) / 1e12
+    return {"kernel": "attention_generic_kernel + merge_generic_kernel", "bound": "alu",
+            "achieved": round(tf, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / VALU_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel_us": round(attn_ms * 1e3, 3),
+            "hbm_gbs": round(alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
+            "algorithmic_flops_per_launch": alg["attn_flops"],
+            "algorithmic_bytes_per_launch": alg["attn_bytes"]}
+
+
 def graph_time(torch, fn, reps, stream):
     """Capture fn() once in a graph, replay `reps` times between two events."""
     g = torch.cuda.CUDAGraph()
@@ -293,8 +310,14 @@ def main():
         m.mla_decode(mc, s["q_nope"], s["q_rope"], s["w_uk"], s["w_uv"], s["pool"],
                      s["block_table"], s["seq_lens"], max_len, out=out, workspace=ws[i])
 
+    narrow = cfg["kv_lora_rank"] != 512   # the narrow-latent kernels (attention + merge)
+
     def attn(i):
         s = sets[i]
+        if narrow:
+            m.mla_latent_attention(mc, qf[i], s["pool"], s["block_table"], s["seq_lens"], max_len,
+                                   workspace=ws[i])
+            return
         m.mla_attention_partials(mc, qf[i], s["pool"], s["block_table"], s["seq_lens"], max_len,
                                  ws[i])
 
@@ -344,10 +367,11 @@ def main():
                    "kv_lora_rank": cfg["kv_lora_rank"], "rope_dim": cfg["rope_dim"],
                    "qk_nope_dim": cfg["qk_nope_dim"], "v_dim": cfg["v_dim"],
                    "block_size": cfg["block_size"], "input_sets_rotated": R,
+                   "kv_groups": cfg.get("kv_groups", 0),
                    "cache": "fp8 e4m3 rows, 656 B/token" if cfg.get("cache_dtype") == "fp8"
-                   else "bf16 rows, 1152 B/token",
+                   else f"bf16 rows, {2 * (cfg['kv_lora_rank'] + cfg['rope_dim'])} B/token",
                    "timing": f"hip graph replay ({per} steps per replay), events on the launching stream"},
-        "roofline": {
+        "roofline": narrow_roofline(alg, attn_ms) if narrow else {
             "kernel": "attn_decode_partials_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1),

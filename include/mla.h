@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -94,6 +94,9 @@ typedef struct mla_config {
   float rope_theta;     /* > 0, RoPE base                                      */
   int32_t dtype;        /* mla_dtype of every tensor (storage); fp32 accumulate */
   int32_t cache_dtype;  /* mla_cache_dtype of the cache rows; FP8 needs bf16   */
+  int32_t kv_groups;    /* G >= 0: 0 = one W_UK and W_UV per head; else H % G
+                           == 0 and heads g H/G .. (g+1) H/G - 1 share
+                           W_UK[g], W_UV[g] (w_uk [G, Dn, R], w_uv [G, R, Dv])  */
 } mla_config;
 
 /* ---- library information ------------------------------------------------ */
@@ -136,7 +139,9 @@ mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32
  * hood": absorbed up-projections; the ticket's "Description": the new token's
  * row is already in the cache and the token attends over the cache).
  *   q_nope [batch, H, Dn]; q_rope [batch, H, Dr], already rotated;
- *   w_uk [H, Dn, R]; w_uv [H, R, Dv];
+ *   w_uk [H, Dn, R]; w_uv [H, R, Dv] ([G, Dn, R], [G, R, Dv] with kv_groups
+ *     G > 0: the tutorial "ARCH-MLA. Multihead Latent Attention", 5.1,
+ *     rebuilds 4 key/value heads for 16 query heads);
  *   kv_pool [num_blocks, block_size, R + Dr];
  *   block_table int32 [batch, max_blocks_per_seq];
  *   seq_lens int32 [batch]: tokens in each sequence's cache including the
@@ -144,7 +149,13 @@ mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32
  *   max_seq_len (host): bound on seq_lens, <= max_blocks_per_seq * block_size;
  *   out [batch, H, Dv] (written).
  * Runs mla_absorb_query, mla_latent_attention and mla_output_projection,
- * with q and o_lat staged in the workspace. */
+ * with q and o_lat staged in the workspace.  Shapes (bf16): the tuned
+ * kernels take R = 512, Dr = 64, H a multiple of 32, block_size a power of
+ * two >= 64, batch <= 1024; the narrow-latent kernels take R = 128 or 256,
+ * Dr = 64, H a multiple of 16, any block_size (bf16 rows, no FP8);
+ * anything else is MLA_ERR_UNSUPPORTED.  mla_attention_partials and
+ * mla_combine_output exist for the tuned kernels only, and
+ * mla_combine_output applies W_UV only without kv_groups. */
 mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_rope,
                       const void* w_uk, const void* w_uv, const void* kv_pool, int32_t num_blocks,
                       const int32_t* block_table, int32_t max_blocks_per_seq,

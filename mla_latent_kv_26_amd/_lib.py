@@ -37,6 +37,7 @@ class MLAConfigC(ctypes.Structure):
         ("rope_theta", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("cache_dtype", ctypes.c_int32),
+        ("kv_groups", ctypes.c_int32),
     ]
 
 

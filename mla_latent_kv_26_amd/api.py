@@ -37,6 +37,7 @@ class MLAConfig:
     rope_theta: float = 10000.0
     dtype: str = "bf16"
     cache_dtype: str = "same"   # "same" (rows in dtype) or "fp8" (E4M3 latent, see mla.h)
+    kv_groups: int = 0          # 0: W_UK, W_UV per head; G: heads share G matrices in order
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -60,6 +61,11 @@ class MLAConfig:
         return self.row
 
     @property
+    def uk_heads(self) -> int:
+        """Leading dimension of w_uk and w_uv: H, or kv_groups when set."""
+        return self.kv_groups or self.num_heads
+
+    @property
     def scale(self) -> float:
         return self.softmax_scale or 1.0 / math.sqrt(self.qk_nope_dim + self.rope_dim)
 
@@ -67,7 +73,7 @@ class MLAConfig:
         return MLAConfigC(self.num_heads, self.kv_lora_rank, self.rope_dim, self.qk_nope_dim,
                           self.v_dim, self.d_model, self.q_lora_rank, self.block_size,
                           self.softmax_scale, self.rms_eps, self.rope_theta,
-                          _C_DTYPE[self.dtype], _C_CACHE[self.cache_dtype])
+                          _C_DTYPE[self.dtype], _C_CACHE[self.cache_dtype], self.kv_groups)
 
     @classmethod
     def from_dict(cls, d: dict, **over) -> "MLAConfig":
@@ -192,8 +198,8 @@ def mla_decode(cfg: MLAConfig, q_nope, q_rope, w_uk, w_uv, kv_pool, block_table,
     B, H = q_nope.shape[0], cfg.num_heads
     _dev(q_nope, "q_nope", dt, (B, H, cfg.qk_nope_dim))
     _dev(q_rope, "q_rope", dt, (B, H, cfg.rope_dim))
-    _dev(w_uk, "w_uk", dt, (H, cfg.qk_nope_dim, cfg.kv_lora_rank))
-    _dev(w_uv, "w_uv", dt, (H, cfg.kv_lora_rank, cfg.v_dim))
+    _dev(w_uk, "w_uk", dt, (cfg.uk_heads, cfg.qk_nope_dim, cfg.kv_lora_rank))
+    _dev(w_uv, "w_uv", dt, (cfg.uk_heads, cfg.kv_lora_rank, cfg.v_dim))
     nb, mb = _pool_args(cfg, kv_pool, block_table, B)
     _dev(seq_lens, "seq_lens", torch.int32, (B,))
     if out is None:
@@ -214,7 +220,7 @@ def mla_absorb_query(cfg: MLAConfig, q_nope, q_rope, w_uk, q_full=None, stream=N
     n, H = q_nope.shape[0], cfg.num_heads
     _dev(q_nope, "q_nope", dt, (n, H, cfg.qk_nope_dim))
     _dev(q_rope, "q_rope", dt, (n, H, cfg.rope_dim))
-    _dev(w_uk, "w_uk", dt, (H, cfg.qk_nope_dim, cfg.kv_lora_rank))
+    _dev(w_uk, "w_uk", dt, (cfg.uk_heads, cfg.qk_nope_dim, cfg.kv_lora_rank))
     if q_full is None:
         q_full = torch.empty((n, H, cfg.row), dtype=dt, device=q_nope.device)
     _dev(q_full, "q_full", dt, (n, H, cfg.row))
@@ -266,7 +272,7 @@ def mla_combine_output(cfg: MLAConfig, batch: int, max_seq_len: int, workspace, 
     _dev(workspace, "workspace", torch.uint8)
     width = cfg.kv_lora_rank if w_uv is None else cfg.v_dim
     if w_uv is not None:
-        _dev(w_uv, "w_uv", dt, (H, cfg.kv_lora_rank, cfg.v_dim))
+        _dev(w_uv, "w_uv", dt, (cfg.uk_heads, cfg.kv_lora_rank, cfg.v_dim))
     if out is None:
         out = torch.empty((batch, H, width), dtype=dt, device=workspace.device)
     _dev(out, "out", dt, (batch, H, width))
@@ -281,7 +287,7 @@ def mla_output_projection(cfg: MLAConfig, o_lat, w_uv, out=None, stream=None):
     dt = cfg.torch_dtype
     n, H = o_lat.shape[0], cfg.num_heads
     _dev(o_lat, "o_lat", dt, (n, H, cfg.kv_lora_rank))
-    _dev(w_uv, "w_uv", dt, (H, cfg.kv_lora_rank, cfg.v_dim))
+    _dev(w_uv, "w_uv", dt, (cfg.uk_heads, cfg.kv_lora_rank, cfg.v_dim))
     if out is None:
         out = torch.empty((n, H, cfg.v_dim), dtype=dt, device=o_lat.device)
     _dev(out, "out", dt, (n, H, cfg.v_dim))
@@ -348,8 +354,8 @@ def mla_prefill(cfg: MLAConfig, x, weights: dict, kv_pool, block_table, start_po
         p_wdq = p_qn = p_wuq = null
     p_wdkv = _dev(w["w_dkv"], "w_dkv", dt, (cfg.d_model, cfg.row))
     p_kvn = _dev(w["kv_norm_w"], "kv_norm_w", torch.float32, (cfg.kv_lora_rank,))
-    p_wuk = _dev(w["w_uk"], "w_uk", dt, (H, cfg.qk_nope_dim, cfg.kv_lora_rank))
-    p_wuv = _dev(w["w_uv"], "w_uv", dt, (H, cfg.kv_lora_rank, cfg.v_dim))
+    p_wuk = _dev(w["w_uk"], "w_uk", dt, (cfg.uk_heads, cfg.qk_nope_dim, cfg.kv_lora_rank))
+    p_wuv = _dev(w["w_uv"], "w_uv", dt, (cfg.uk_heads, cfg.kv_lora_rank, cfg.v_dim))
     nb, mb = _pool_args(cfg, kv_pool, block_table, B)
     _dev(start_pos, "start_pos", torch.int32, (B,))
     rope_table = _rope_dev(cfg, rope_table, int(max_start_pos) + T, x.device)

@@ -388,3 +388,97 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 }
 
 }  // namespace mla
+
+// ---------------------------------------------------------------------------
+// Per-head projections for a few rows (decode of small batches), with G
+// matrices shared by H / G consecutive heads: one block per (row, head), the
+// head's input vector in LDS, threads over the output columns.  Used where a
+// tiled GEMM would run one row tile per launch.
+// ---------------------------------------------------------------------------
+namespace mla {
+namespace {
+
+// q_full[n, h] = alpha [q_nope[n, h] W_UK[h / gs] | q_rope[n, h]]
+template <typename T>
+__global__ void __launch_bounds__(256) absorb_small_kernel(const T* __restrict__ q_nope,
+                                                           const T* __restrict__ q_rope,
+                                                           const T* __restrict__ w_uk, int H,
+                                                           int gs, int Dn, int R, int Dr,
+                                                           float alpha, T* __restrict__ q_full) {
+  __shared__ float qv[1024];
+  const int n = blockIdx.x, h = blockIdx.y;
+  const T* q = q_nope + ((long)n * H + h) * Dn;
+  for (int d = threadIdx.x; d < Dn; d += 256) qv[d] = to_f32(q[d]);
+  __syncthreads();
+  const T* w = w_uk + (long)(h / gs) * Dn * R;
+  T* dst = q_full + ((long)n * H + h) * (R + Dr);
+  for (int r = threadIdx.x; r < R; r += 256) {
+    float acc = 0.f;
+    for (int d = 0; d < Dn; ++d) acc = fmaf(qv[d], to_f32(w[(long)d * R + r]), acc);
+    dst[r] = from_f32<T>(alpha * acc);
+  }
+  const T* qr = q_rope + ((long)n * H + h) * Dr;
+  for (int i = threadIdx.x; i < Dr; i += 256) dst[R + i] = from_f32<T>(alpha * to_f32(qr[i]));
+}
+
+// out[n, h] = o_lat[n, h] W_UV[h / gs]; thread t sums part t / Dv of the R
+// inputs for column t % Dv, the parts are added through LDS
+template <typename T>
+__global__ void __launch_bounds__(256) project_small_kernel(const T* __restrict__ o_lat,
+                                                            const T* __restrict__ w_uv, int H,
+                                                            int gs, int R, int Dv,
+                                                            T* __restrict__ out) {
+  __shared__ float ov[1024];
+  __shared__ float part[256];
+  const int n = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const T* o = o_lat + ((long)n * H + h) * R;
+  for (int r = t; r < R; r += 256) ov[r] = to_f32(o[r]);
+  __syncthreads();
+  const int parts = 256 / Dv, e = t % Dv, p = t / Dv;
+  const T* w = w_uv + (long)(h / gs) * R * Dv;
+  float acc = 0.f;
+  if (p < parts) {
+    const int r0 = (int)((long)R * p / parts), r1 = (int)((long)R * (p + 1) / parts);
+    for (int r = r0; r < r1; ++r) acc = fmaf(ov[r], to_f32(w[(long)r * Dv + e]), acc);
+  }
+  part[t] = acc;
+  __syncthreads();
+  if (t < Dv) {
+    float s = 0.f;
+    for (int q = 0; q < parts; ++q) s += part[q * Dv + t];
+    out[((long)n * H + h) * Dv + t] = from_f32<T>(s);
+  }
+}
+
+}  // namespace
+
+bool small_projection_fits(int rows, int Dn, int R, int Dv) {
+  return rows <= 32 && Dn <= 1024 && R <= 1024 && Dv <= 256;
+}
+
+void launch_absorb_small(const void* q_nope, const void* q_rope, const void* w_uk, int n, int H,
+                         int gs, int Dn, int R, int Dr, float alpha, int dtype, void* q_full,
+                         hipStream_t st) {
+  const dim3 grid(n, H);
+  if (dtype == 1)
+    absorb_small_kernel<bf16><<<grid, 256, 0, st>>>((const bf16*)q_nope, (const bf16*)q_rope,
+                                                    (const bf16*)w_uk, H, gs, Dn, R, Dr, alpha,
+                                                    (bf16*)q_full);
+  else
+    absorb_small_kernel<float><<<grid, 256, 0, st>>>((const float*)q_nope, (const float*)q_rope,
+                                                     (const float*)w_uk, H, gs, Dn, R, Dr, alpha,
+                                                     (float*)q_full);
+}
+
+void launch_project_small(const void* o_lat, const void* w_uv, int n, int H, int gs, int R, int Dv,
+                          int dtype, void* out, hipStream_t st) {
+  const dim3 grid(n, H);
+  if (dtype == 1)
+    project_small_kernel<bf16><<<grid, 256, 0, st>>>((const bf16*)o_lat, (const bf16*)w_uv, H, gs,
+                                                     R, Dv, (bf16*)out);
+  else
+    project_small_kernel<float><<<grid, 256, 0, st>>>((const float*)o_lat, (const float*)w_uv, H,
+                                                      gs, R, Dv, (float*)out);
+}
+
+}  // namespace mla

@@ -146,6 +146,29 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
                     int heads_per_wg, int n_wg, int max_seq_len, const void* w_uv, int Dv,
                     void* out, int num_cus, hipStream_t st);
 
+// Decode attention for narrower latents (attention_generic.hip): R = 128 or
+// 256, Dr = 64, H a multiple of 16, any block size.  q_full [batch, H, R +
+// Dr] bf16 (scaled by softmax_scale * log2 e), pool bf16 rows; chunk /
+// n_split from generic_split; part_ml float [batch, n_split, H, 2] and
+// part_o float [batch, n_split, H, R] scratch; o_lat [batch, H, R] in bf16 or
+// float32.
+bool attention_generic_fits(int H, int R, int Dr);
+void generic_split(int batch, int H, int max_seq_len, int num_cus, int* chunk, int* n_split);
+void launch_attention_generic(const void* q_full, const void* pool, const int* block_table,
+                              int max_blocks, int block_size, const int* seq_lens, int batch,
+                              int H, int R, int chunk, int n_split, float* part_ml, float* part_o,
+                              void* o_lat, bool o_f32, hipStream_t st);
+
+// Per-head projections of a few rows (rows <= 32, Dn, R <= 1024, Dv <= 256)
+// with W_UK / W_UV shared by gs consecutive heads: q_full [n, H, R + Dr] =
+// alpha [q_nope W_UK[h / gs] | q_rope]; out [n, H, Dv] = o_lat W_UV[h / gs].
+bool small_projection_fits(int rows, int Dn, int R, int Dv);
+void launch_absorb_small(const void* q_nope, const void* q_rope, const void* w_uk, int n, int H,
+                         int gs, int Dn, int R, int Dr, float alpha, int dtype, void* q_full,
+                         hipStream_t st);
+void launch_project_small(const void* o_lat, const void* w_uv, int n, int H, int gs, int R, int Dv,
+                          int dtype, void* out, hipStream_t st);
+
 // Prefill attention: query row n = b * T + t at position start_pos[b] + t
 // attends to its sequence's rows 0..position; writes o_lat bf16 [n, H, R].
 // Prefill through per-head keys and values (bf16, R = 512, Dn = Dv = 128,

@@ -32,6 +32,7 @@ struct Dims {
   size_t esz;
   bool fp8;          // FP8 cache rows
   size_t row_bytes;  // bytes per cache row
+  int G, gs;         // W_UK / W_UV matrices, heads per matrix
 };
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -73,6 +74,9 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
     return fail(MLA_ERR_INVALID_ARG, "unknown cache_dtype %d", c->cache_dtype);
   if (c->cache_dtype == MLA_CACHE_FP8_E4M3 && c->dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERR_INVALID_ARG, "an FP8 cache needs dtype bf16");
+  if (c->kv_groups < 0 || (c->kv_groups > 0 && c->num_heads % c->kv_groups))
+    return fail(MLA_ERR_INVALID_ARG, "kv_groups (%d) must be 0 or divide num_heads (%d)",
+                c->kv_groups, c->num_heads);
   if (d) {
     d->H = c->num_heads;
     d->R = c->kv_lora_rank;
@@ -92,6 +96,8 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
     d->esz = d->dt == MLA_DTYPE_BF16 ? 2 : 4;
     d->fp8 = c->cache_dtype == MLA_CACHE_FP8_E4M3;
     d->row_bytes = d->fp8 ? (size_t)d->R + 2 * (size_t)d->Dr + 16 : (size_t)d->W * d->esz;
+    d->G = c->kv_groups > 0 ? c->kv_groups : d->H;
+    d->gs = d->H / d->G;
   }
   return MLA_OK;
 }
@@ -103,18 +109,20 @@ mla_status check_decode_kernels(const Dims& d, int batch) {
       return fail(MLA_ERR_UNSUPPORTED, "float32 path supports kv_lora_rank <= 1024 (got %d)", d.R);
     return MLA_OK;
   }
+  if (d.Dn % 8 || d.Dv % 16 || d.Dv > 128)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "bf16 projections need qk_nope_dim % 8 == 0 and v_dim % 16 == 0, v_dim <= 128");
+  if (d.R != 512 && !d.fp8 && mla::attention_generic_fits(d.H, d.R, d.Dr)) return MLA_OK;
   if (d.R != 512 || d.Dr != 64)
     return fail(MLA_ERR_UNSUPPORTED,
-                "bf16 attention kernels are built for kv_lora_rank 512 and rope_dim 64 (got %d, %d)",
-                d.R, d.Dr);
+                "bf16 attention kernels are built for kv_lora_rank 512 (or 128, 256 with heads in "
+                "multiples of 16, bf16 rows) and rope_dim 64 (got %d, %d, %d heads)",
+                d.R, d.Dr, d.H);
   if (d.H % 32)
     return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs num_heads a multiple of 32 (got %d)", d.H);
   if (d.shift < 6)
     return fail(MLA_ERR_UNSUPPORTED, "bf16 attention needs block_size a power of two >= 64 (got %d)",
                 d.bs);
-  if (d.Dn % 8 || d.Dv % 16 || d.Dv > 128)
-    return fail(MLA_ERR_UNSUPPORTED,
-                "bf16 projections need qk_nope_dim % 8 == 0 and v_dim % 16 == 0, v_dim <= 128");
   if (batch > 1024)
     return fail(MLA_ERR_UNSUPPORTED, "bf16 decode handles at most 1024 sequences per call (got %d)",
                 batch);
@@ -144,11 +152,23 @@ mla_status launched(const char* what) {
 struct DecodeWs {
   size_t prefix, part_ml, part_o, q_full, o_lat, total;
   int n_wg, hgc, heads;
+  int chunk, n_split;  // narrow-latent kernels
 };
+// bf16 shapes that go to the narrow-latent kernels instead of the tuned ones
+bool generic_decode(const Dims& d) { return d.dt == MLA_DTYPE_BF16 && d.R != 512; }
+
 DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
   DecodeWs w{};
   size_t off = 256;  // reserved
-  if (d.dt == MLA_DTYPE_BF16) {
+  if (generic_decode(d)) {
+    mla::generic_split(batch, d.H, max_seq_len, num_cus(), &w.chunk, &w.n_split);
+    w.part_ml = off;
+    off = up256(off + (size_t)batch * w.n_split * d.H * 2 * 4);
+    w.part_o = off;
+    off = up256(off + (size_t)batch * w.n_split * d.H * d.R * 4);
+    w.o_lat = off;
+    off = up256(off + (size_t)batch * d.H * d.R * 2);
+  } else if (d.dt == MLA_DTYPE_BF16) {
     const int cus = num_cus();
     w.heads = mla::decode_heads_per_wg(d.H, batch, max_seq_len, cus);
     w.hgc = d.H / w.heads;
@@ -160,6 +180,10 @@ DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
     off = up256(off + (size_t)w.hgc * slots * w.heads * 2 * 4);
     w.part_o = off;
     off = up256(off + (size_t)w.hgc * slots * w.heads * 512 * 2);
+    if (d.gs > 1) {  // o_lat for the grouped W_UV product
+      w.o_lat = off;
+      off = up256(off + (size_t)batch * d.H * d.R * 2);
+    }
   }
   w.q_full = off;
   off = up256(off + (size_t)batch * d.H * d.W * d.esz);
@@ -248,9 +272,50 @@ void gemm(const Dims& d, const void* A, const void* B, void* C, int M, int N, in
 }
 
 // Stage 1 (shared by decode entry points).
+// C[., h, :] = alpha A[., h, :] Wm[h / gs] for every head h: one batched
+// GEMM over the heads when each has its own matrix (gs = 1), else one per
+// group of heads sharing a matrix (batch stride 0 on Wm).  a_head, w_head,
+// c_head: element strides between heads (A, C) and between matrices (Wm).
+void head_gemm(const Dims& d, const void* A, long lda, long a_head, const void* Wm, long ldb,
+               long w_head, void* C, long ldc, long c_head, int rows, int N, int K, float alpha,
+               bool out_f32, hipStream_t st) {
+  if (d.gs == 1) {
+    gemm(d, A, Wm, C, rows, N, K, lda, ldb, ldc, a_head, w_head, c_head, d.H, alpha, out_f32, st);
+    return;
+  }
+  const size_t ce = out_f32 ? 4 : d.esz;
+  for (int g = 0; g < d.G; ++g)
+    gemm(d, (const char*)A + (size_t)g * d.gs * a_head * d.esz,
+         (const char*)Wm + (size_t)g * w_head * d.esz, (char*)C + (size_t)g * d.gs * c_head * ce,
+         rows, N, K, lda, ldb, ldc, a_head, 0, c_head, d.gs, alpha, out_f32, st);
+}
+
+// out[., h, :] = o_lat[., h, :] W_UV[h / gs] for `rows` rows
+void project_out(const Dims& d, const void* o_lat, const void* w_uv, void* out, int rows,
+                 hipStream_t st) {
+  if ((d.gs > 1 || generic_decode(d)) && mla::small_projection_fits(rows, d.Dn, d.R, d.Dv)) {
+    mla::launch_project_small(o_lat, w_uv, rows, d.H, d.gs, d.R, d.Dv, d.dt, out, st);
+    return;
+  }
+  head_gemm(d, o_lat, (long)d.H * d.R, d.R, w_uv, d.Dv, (long)d.R * d.Dv, out, (long)d.H * d.Dv,
+            d.Dv, rows, d.Dv, d.R, 1.0f, false, st);
+}
+
 void enqueue_absorb(const Dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
                     int n_rows, void* q_full, hipStream_t st) {
   const float alpha = d.scale * 1.4426950408889634f;
+  if ((d.gs > 1 || generic_decode(d)) && mla::small_projection_fits(n_rows, d.Dn, d.R, d.Dv)) {
+    mla::launch_absorb_small(q_nope, q_rope, w_uk, n_rows, d.H, d.gs, d.Dn, d.R, d.Dr, alpha, d.dt,
+                             q_full, st);
+    return;
+  }
+  if (d.gs > 1) {  // heads sharing W_UK: one GEMM per group, then the scaled q_rope copy
+    head_gemm(d, q_nope, (long)d.H * d.Dn, d.Dn, w_uk, d.R, (long)d.Dn * d.R, q_full,
+              (long)d.H * d.W, d.W, n_rows, d.R, d.Dn, alpha, false, st);
+    mla::launch_q_rope(q_rope, (long)d.H * d.Dr, d.Dr, 0, nullptr, nullptr, 1, q_full, n_rows, d.H,
+                       d.R, d.Dr, alpha, d.dt, st);
+    return;
+  }
   if (d.dt == MLA_DTYPE_BF16) {
     if (mla::launch_absorb_query_bf16(q_nope, q_rope, w_uk, q_full, n_rows, d.H, d.Dn, d.R, d.Dr,
                                       alpha, st))
@@ -381,22 +446,30 @@ static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* 
                                  int32_t batch, int32_t max_seq_len, const void* w_uv, void* dst,
                                  void* ws, hipStream_t st) {
   const DecodeWs w = decode_ws(d, batch, max_seq_len);
-  if (d.dt == MLA_DTYPE_BF16) {
+  // o_lat in the workspace when W_UV follows as its own product
+  void* o_lat = dst;
+  if (generic_decode(d)) {
+    if (w_uv) o_lat = at(ws, w.o_lat);
+    mla::launch_attention_generic(q_full, pool, table, max_blocks, d.bs, seq_lens, batch, d.H,
+                                  d.R, w.chunk, w.n_split, (float*)at(ws, w.part_ml),
+                                  (float*)at(ws, w.part_o), o_lat, false, st);
+  } else if (d.dt == MLA_DTYPE_BF16) {
     mla::launch_attention_partials_bf16(q_full, pool, num_blocks, table, max_blocks, d.shift,
                                         seq_lens, batch, max_seq_len, d.H, w.heads, w.n_wg,
                                         (int*)at(ws, w.prefix), (float*)at(ws, w.part_ml),
                                         at(ws, w.part_o), st, d.fp8);
+    const bool fuse = w_uv && d.gs == 1;  // the merge applies per-head W_UV itself
+    if (w_uv && !fuse) o_lat = at(ws, w.o_lat);
     mla::launch_combine((const int*)at(ws, w.prefix), (const float*)at(ws, w.part_ml),
-                        at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, max_seq_len, w_uv, d.Dv, dst,
-                        num_cus(), st);
+                        at(ws, w.part_o), batch, d.H, w.heads, w.n_wg, max_seq_len,
+                        fuse ? w_uv : nullptr, d.Dv, fuse ? dst : o_lat, num_cus(), st);
+    if (fuse) return MLA_OK;
   } else {
-    float* o_lat = w_uv ? (float*)at(ws, w.o_lat) : (float*)dst;
+    if (w_uv) o_lat = at(ws, w.o_lat);
     mla::launch_attention_f32((const float*)q_full, (const float*)pool, table, max_blocks, d.bs,
-                              seq_lens, nullptr, 1, o_lat, batch, d.H, d.R, d.Dr, st);
-    if (w_uv)
-      gemm(d, o_lat, w_uv, dst, batch, d.Dv, d.R, (long)d.H * d.R, d.Dv, (long)d.H * d.Dv, d.R,
-           (long)d.R * d.Dv, d.Dv, d.H, 1.0f, false, st);
+                              seq_lens, nullptr, 1, (float*)o_lat, batch, d.H, d.R, d.Dr, st);
   }
+  if (w_uv) project_out(d, o_lat, w_uv, dst, batch, st);
   return MLA_OK;
 }
 
@@ -484,8 +557,10 @@ mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, con
   g_err.clear();
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
-  if (d.dt != MLA_DTYPE_BF16)
-    return fail(MLA_ERR_UNSUPPORTED, "split partials exist for bf16 only; use mla_latent_attention");
+  if (d.dt != MLA_DTYPE_BF16 || generic_decode(d))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "split partials exist for the bf16 kernels at kv_lora_rank 512 only; use "
+                "mla_latent_attention");
   s = check_decode_common(d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
                           max_seq_len);
   if (s != MLA_OK) return s;
@@ -509,8 +584,14 @@ mla_status mla_combine_output(const mla_config* cfg, const void* w_uv, int32_t b
   g_err.clear();
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
-  if (d.dt != MLA_DTYPE_BF16)
-    return fail(MLA_ERR_UNSUPPORTED, "split partials exist for bf16 only; use mla_latent_attention");
+  if (d.dt != MLA_DTYPE_BF16 || generic_decode(d))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "split partials exist for the bf16 kernels at kv_lora_rank 512 only; use "
+                "mla_latent_attention");
+  if (w_uv && d.gs > 1)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "the merge applies W_UV per head only; with kv_groups merge to o_lat and call "
+                "mla_output_projection");
   if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be positive (got %d)", batch);
   if (max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be positive");
   s = check_decode_kernels(d, batch);
@@ -537,8 +618,7 @@ mla_status mla_output_projection(const mla_config* cfg, const void* o_lat, const
   if (s != MLA_OK) return s;
   if (d.dt == MLA_DTYPE_BF16 && (d.R % 8 || d.Dv % 8))
     return fail(MLA_ERR_UNSUPPORTED, "bf16 projection needs kv_lora_rank and v_dim multiples of 8");
-  gemm(d, o_lat, w_uv, out, n_rows, d.Dv, d.R, (long)d.H * d.R, d.Dv, (long)d.H * d.Dv, d.R,
-       (long)d.R * d.Dv, d.Dv, d.H, 1.0f, false, (hipStream_t)stream);
+project_out(d, o_lat, w_uv, out, n_rows, (hipStream_t)stream);
   return launched("mla_output_projection");
 }
 
@@ -666,6 +746,10 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
   if (d.M <= 0) return fail(MLA_ERR_INVALID_ARG, "prefill needs d_model > 0");
+  if (d.gs > 1)
+    return fail(MLA_ERR_UNSUPPORTED, "prefill takes one W_UK and W_UV per head (kv_groups 0)");
+  if (d.dt == MLA_DTYPE_BF16 && d.R != 512)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill kernels are built for kv_lora_rank 512");
   if (d.fp8 && !prefill_naive_shapes(d))
     return fail(MLA_ERR_UNSUPPORTED,
                 "prefill over an FP8 cache needs bf16 with kv_lora_rank 512, rope_dim 64 and "

@@ -17,6 +17,7 @@ __all__ = [
     "chunk_partials", "merge_partials", "gather_sequence", "decode",
     "append_rows", "attend_tokens", "layer_forward", "incremental_decode",
     "softmax_scale", "DEFAULT_EPS", "DEFAULT_THETA", "sigmoid", "output_gate_projection",
+    "head_matrices",
 ]
 
 DEFAULT_EPS = 1e-6
@@ -304,6 +305,19 @@ def gather_sequence(pool, block_table_row, seq_len: int) -> np.ndarray:
     return np.asarray(pool)[np.asarray(block_table_row)[j // bs], j % bs]
 
 
+def head_matrices(w, H: int) -> np.ndarray:
+    """One matrix per query head from G shared ones ([G, ...] -> [H, ...]):
+    head h uses matrix h // (H / G), i.e. consecutive heads share, the way the
+    tutorial's experiment ("ARCH-MLA. Multihead Latent Attention", 5.1)
+    rebuilds 4 key/value heads for 16 query heads (reading: the grouping of
+    grouped-query attention).  G = H returns w unchanged."""
+    w = np.asarray(w)
+    G = w.shape[0]
+    if H % G:
+        raise ValueError(f"{G} matrices cannot be shared evenly by {H} heads")
+    return np.repeat(w, H // G, axis=0)
+
+
 def decode(q_nope, q_rope, w_uk, w_uv, pool, block_table, seq_lens, cfg,
            path: str = "absorbed", wd=np.float64, batch_ids=None):
     """One decode step for a batch of sequences over a paged latent cache.
@@ -311,8 +325,12 @@ def decode(q_nope, q_rope, w_uk, w_uv, pool, block_table, seq_lens, cfg,
     The current token's row is already in the cache, so sequence b attends
     to its rows 0..seq_lens[b]-1 (ticket, "Description": project the new
     token, concat with the cache, attend).  q_rope is already rotated.
+    w_uk / w_uv hold H matrices, or G < H shared by consecutive heads
+    (``head_matrices``).
     Returns (o [B, H, Dv], o_lat [B, H, R] or None for the naive path).
     """
+    H = np.asarray(q_nope).shape[1]
+    w_uk, w_uv = head_matrices(w_uk, H), head_matrices(w_uv, H)
     R = _cfg(cfg, "kv_lora_rank")
     scale = softmax_scale(cfg)
     ids = range(len(seq_lens)) if batch_ids is None else batch_ids

@@ -36,7 +36,7 @@ def test_every_header_symbol_is_exported_and_bound():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
     for s, name in _lib.STATUS_NAMES.items():
         assert lib.mla_status_string(s).decode() == name
 
@@ -110,10 +110,20 @@ def test_decode_rejects_invalid_calls(over, status):
 
 def test_decode_rejects_unsupported_shapes():
     import dataclasses
-    for over in (dict(kv_lora_rank=256), dict(rope_dim=32), dict(num_heads=48),
-                 dict(block_size=16), dict(block_size=96), dict(v_dim=136)):
+    for over in (dict(kv_lora_rank=384), dict(rope_dim=32), dict(num_heads=48),
+                 dict(block_size=16), dict(block_size=96), dict(v_dim=136),
+                 dict(kv_lora_rank=256, num_heads=24), dict(kv_lora_rank=256, rope_dim=32),
+                 dict(kv_lora_rank=256, cache_dtype="fp8")):
         cfg = dataclasses.replace(KIMI, **over)
         assert _decode(cfg, max_len=64) == _lib.MLA_ERR_UNSUPPORTED, over
+
+
+def test_kv_groups_must_divide_heads():
+    import dataclasses
+    for g, st in ((0, _lib.MLA_OK), (1, _lib.MLA_OK), (8, _lib.MLA_OK), (64, _lib.MLA_OK),
+                  (3, _lib.MLA_ERR_INVALID_ARG), (-1, _lib.MLA_ERR_INVALID_ARG)):
+        cfg = dataclasses.replace(KIMI, kv_groups=g)
+        assert lib.mla_validate_config(ctypes.byref(cfg.c())) == st, g
 
 
 def test_prefill_and_append_reject_invalid_calls():

@@ -685,3 +685,66 @@ def test_planted_fnuz_bias_is_caught():
     wrong = oracle.e4m3_value(codes) / 2
     want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     assert not np.array_equal(wrong, want)
+
+
+# ===========================================================================
+# Shared W_UK / W_UV: G matrices for H heads ("ARCH-MLA. Multihead Latent
+# Attention", 5.1: 4 key/value heads for 16 query heads)
+# ===========================================================================
+def _grouped_case(seed=61, H=8, G=2, L=37):
+    r = rng(seed)
+    R, Dr, Dn, Dv, bs = 24, 8, 12, 10, 16
+    cfg = dict(num_heads=H, kv_lora_rank=R, rope_dim=Dr, qk_nope_dim=Dn, v_dim=Dv,
+               block_size=bs)
+    nblk = -(-L // bs)
+    pool = r.standard_normal((nblk, bs, R + Dr))
+    qn, qr = r.standard_normal((1, H, Dn)), r.standard_normal((1, H, Dr))
+    w_uk, w_uv = r.standard_normal((G, Dn, R)), r.standard_normal((G, R, Dv))
+    return cfg, pool, qn, qr, w_uk, w_uv, L
+
+
+@pytest.mark.parametrize("path", ["absorbed", "naive"])
+def test_grouped_decode_matches_torch_gqa_sdpa(path):
+    """Library check of the grouping convention: keys and values rebuilt for
+    the G groups only, then torch's SDPA with grouped-query heads (query
+    head h reads key/value head h // (H / G)); the oracle expands the G
+    matrices to H heads and attends per head."""
+    torch = pytest.importorskip("torch")
+    cfg, pool, qn, qr, w_uk, w_uv, L = _grouped_case()
+    R = cfg["kv_lora_rank"]
+    rows = pool.reshape(-1, pool.shape[-1])[:L]
+    k, v = oracle.reconstruct_kv(rows[:, :R], rows[:, R:], w_uk, w_uv)     # [L, G, .]
+    q = np.concatenate([qn, qr], axis=-1)                                  # [1, H, Dn + Dr]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), scale=oracle.softmax_scale(cfg), enable_gqa=True)[0].numpy()
+    ref = ref.transpose(1, 0, 2)[0]                                        # [H, Dv]
+    table = np.arange(pool.shape[0])[None]
+    got, _ = oracle.decode(qn, qr, w_uk, w_uv, pool, table, np.array([L]), cfg, path=path)
+    assert np.max(np.abs(got[0] - ref)) < 1e-12
+
+
+def test_head_matrices_special_cases():
+    """G = H returns the per-head matrices unchanged; G = 1 gives every head
+    the one matrix; consecutive heads share (not round-robin); a G that does
+    not divide H is refused."""
+    w = rng(62).standard_normal((4, 3, 5))
+    assert np.array_equal(oracle.head_matrices(w, 4), w)
+    one = oracle.head_matrices(w[:1], 6)
+    assert all(np.array_equal(one[h], w[0]) for h in range(6))
+    two = oracle.head_matrices(w[:2], 4)
+    assert np.array_equal(two[1], w[0]) and np.array_equal(two[2], w[1])
+    with pytest.raises(ValueError):
+        oracle.head_matrices(w[:3], 4)
+
+
+def test_grouped_decode_planted_round_robin_is_caught():
+    """A round-robin grouping (head h reads matrix h % G) differs from the
+    consecutive grouping the torch check fixes."""
+    cfg, pool, qn, qr, w_uk, w_uv, L = _grouped_case(seed=63)
+    table = np.arange(pool.shape[0])[None]
+    got, _ = oracle.decode(qn, qr, w_uk, w_uv, pool, table, np.array([L]), cfg)
+    H, G = qn.shape[1], w_uk.shape[0]
+    rr = np.stack([w_uk[h % G] for h in range(H)]), np.stack([w_uv[h % G] for h in range(H)])
+    bad, _ = oracle.decode(qn, qr, rr[0], rr[1], pool, table, np.array([L]), cfg)
+    assert np.max(np.abs(got - bad)) > 1e-3

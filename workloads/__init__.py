@@ -67,6 +67,15 @@ WORKLOADS["longctx_h64_b4_l131072_fp8"] = dict(WORKLOADS["longctx_h64_b4_l131072
                                                cache_dtype="fp8")
 WORKLOADS["prefill_d7168_b2_t4096_fp8"] = dict(WORKLOADS["prefill_d7168_b2_t4096"],
                                                cache_dtype="fp8")
+# The tutorial's mechanism experiment widths ("ARCH-MLA. Multihead Latent
+# Attention", 5.1): 16 query heads sharing 4 W_UK / W_UV matrices, head
+# width 64, latent 256, rope 64, bf16; one sequence per history length
+# 512, 2048, 8192 (the batch is not stated: one sequence is the reading).
+for _L in (512, 2048, 8192):
+    WORKLOADS[f"mechanism_h16_g4_r256_l{_L}"] = dict(
+        num_heads=16, kv_groups=4, kv_lora_rank=256, rope_dim=64, qk_nope_dim=64, v_dim=64,
+        batch=1, lengths="fixed", context=_L, block_size=64, paged=False, dtype="bf16",
+        seed=60 + _L % 97)
 
 
 HEADLINE = "decode_h64_b32_l4096"
@@ -153,8 +162,8 @@ class DecodeInputs:
     pool: np.ndarray          # [num_blocks, block_size, R + Dr] storage dtype
     q_nope: np.ndarray        # [B, H, Dn]
     q_rope: np.ndarray        # [B, H, Dr] (already rotated)
-    w_uk: np.ndarray          # [H, Dn, R]
-    w_uv: np.ndarray          # [H, R, Dv]
+    w_uk: np.ndarray          # [H or kv_groups, Dn, R]
+    w_uv: np.ndarray          # [H or kv_groups, R, Dv]
 
 
 def decode_lengths(cfg: dict, rng) -> np.ndarray:
@@ -188,8 +197,9 @@ def decode_inputs(cfg: dict, seed: Optional[int] = None,
     B = len(lens)
     q_nope = _store(_normal(rng, (B, H, Dn)), dt)
     q_rope = _store(_normal(rng, (B, H, Dr)), dt)
-    w_uk = _store(_normal(rng, (H, Dn, R), 1.0 / math.sqrt(R)), dt)
-    w_uv = _store(_normal(rng, (H, R, Dv), 1.0 / math.sqrt(R)), dt)
+    G = cfg.get("kv_groups") or H          # matrices shared by H / G consecutive heads
+    w_uk = _store(_normal(rng, (G, Dn, R), 1.0 / math.sqrt(R)), dt)
+    w_uv = _store(_normal(rng, (G, R, Dv), 1.0 / math.sqrt(R)), dt)
     return DecodeInputs(cfg, lens, table, pool, q_nope, q_rope, w_uk, w_uv)
 
 
@@ -278,6 +288,7 @@ def decode_inputs_torch(cfg: dict, seed: int, device, lengths=None):
     g.manual_seed(seed)
     H, R, Dr = cfg["num_heads"], cfg["kv_lora_rank"], cfg["rope_dim"]
     Dn, Dv, bs = cfg["qk_nope_dim"], cfg["v_dim"], cfg["block_size"]
+    G = cfg.get("kv_groups") or H
     dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     B = len(lens)
 
@@ -311,7 +322,7 @@ def decode_inputs_torch(cfg: dict, seed: int, device, lengths=None):
         max_seq_len=int(lens.max()),
         pool=pool,
         q_nope=n((B, H, Dn)), q_rope=n((B, H, Dr)),
-        w_uk=n((H, Dn, R), 1.0 / math.sqrt(R)), w_uv=n((H, R, Dv), 1.0 / math.sqrt(R)),
+        w_uk=n((G, Dn, R), 1.0 / math.sqrt(R)), w_uv=n((G, R, Dv), 1.0 / math.sqrt(R)),
     )
 
 
