@@ -7,10 +7,10 @@
 // q_full already scaled by softmax_scale * log2(e), softmax over each
 // sequence's tokens, weights applied to c.
 //
-// One workgroup (4 waves) takes 16 heads of one sequence over one chunk of
+// One workgroup (8 waves) takes 16 heads of one sequence over one chunk of
 // its tokens, 64-token tiles staged in LDS (two buffers; the next tile's
 // global loads are in flight while the current one is used).  Wave w owns
-// heads 4w..4w+3: lane n scores token n of the tile (bf16 dot2 products,
+// heads 2w, 2w+1: lane n scores token n of the tile (bf16 dot2 products,
 // float32 sums), the wave keeps the running max and sum of its heads, and for
 // the weighted sum lane n owns R/64 latent columns of those heads.  Each
 // chunk writes an unnormalised partial (m, l, O) in float32; a second kernel
@@ -36,8 +36,8 @@ __device__ __forceinline__ float hi_bf16(uint32_t v) {
   return __builtin_bit_cast(float, v & 0xffff0000u);
 }
 
-template <int R>
-__global__ void __launch_bounds__(256) attention_generic_kernel(
+template <int R, int kWaves>
+__global__ void __launch_bounds__(64 * kWaves) attention_generic_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int block_size,
     const int* __restrict__ seq_lens, int H, int chunk, int n_split, float* __restrict__ part_ml,
@@ -45,9 +45,12 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
   constexpr int W = R + 64;           // row width (values)
   constexpr int kRow = W * 2 + 16;    // LDS row stride (bytes), padded
   constexpr int kChunks = W / 8;      // 16-byte pieces per row
-  constexpr int kLoads = kGT * kChunks / 256;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kHW = kGH / kWaves;   // heads per wave
+  constexpr int kLoads = kGT * kChunks / kThreads;
   constexpr int kC = R / 64;          // latent columns per lane
-  static_assert(kGT * kChunks % 256 == 0, "tile pieces must split evenly over the block");
+  static_assert(kGT * kChunks % kThreads == 0, "tile pieces must split evenly over the block");
+  static_assert(kHW == 2 || kHW == 4, "two or four heads per wave");
   __shared__ __align__(16) unsigned char tile[2][kGT * kRow];
   __shared__ __align__(16) unsigned char qs[kGH * W * 2];
   __shared__ __align__(16) float ps[kGT * kGH];
@@ -57,27 +60,27 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
   const int len = seq_lens[b];
   const int begin = split * chunk;
   const int end = min(len, begin + chunk);
-  const long slot = ((long)b * n_split + split) * H + hb * kGH + 4 * w;
+  const long slot = ((long)b * n_split + split) * H + hb * kGH + kHW * w;
   if (begin >= end) {  // nothing in this chunk: an empty partial (uniform per block)
-    if (lane < 4) {
+    if (lane < kHW) {
       part_ml[(slot + lane) * 2] = -INFINITY;
       part_ml[(slot + lane) * 2 + 1] = 0.f;
     }
     // zero O too, so the merge reads every chunk's O without a branch
-    for (int i = lane; i < 4 * R; i += 64) part_o[slot * R + i] = 0.f;
+    for (int i = lane; i < kHW * R; i += 64) part_o[slot * R + i] = 0.f;
     return;
   }
 
   // queries of the 16 heads
   const bf16* qsrc = q_full + ((long)b * H + hb * kGH) * W;
-  for (int i = tid; i < kGH * kChunks; i += 256)
+  for (int i = tid; i < kGH * kChunks; i += kThreads)
     *(uint4*)(qs + i * 16) = *(const uint4*)(qsrc + i * 8);
 
   uint4 pre[kLoads];
   auto load = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + 256 * i, r = c / kChunks, k = c - r * kChunks;
+      const int c = tid + kThreads * i, r = c / kChunks, k = c - r * kChunks;
       const int j = t0 + r;
       uint4 v = {0u, 0u, 0u, 0u};
       if (j < end) {
@@ -90,14 +93,14 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
   auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + 256 * i, r = c / kChunks, k = c - r * kChunks;
+      const int c = tid + kThreads * i, r = c / kChunks, k = c - r * kChunks;
       *(uint4*)(tile[buf] + r * kRow + k * 16) = pre[i];
     }
   };
 
-  float m[4], l[4], acc[4][kC];
+  float m[kHW], l[kHW], acc[kHW][kC];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kHW; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.f;
 #pragma unroll
@@ -114,15 +117,17 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
     if (more) load(t0 + kGT);
     const unsigned char* tb = tile[t & 1];
 
-    // scores of token `lane` for heads 4w..4w+3
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    // scores of token `lane` for heads kHW w .. kHW w + kHW - 1
+    float s[kHW];
+#pragma unroll
+    for (int j = 0; j < kHW; ++j) s[j] = 0.f;
     const unsigned char* rowp = tb + lane * kRow;
-    const unsigned char* qp = qs + (4 * w) * W * 2;
+    const unsigned char* qp = qs + (kHW * w) * W * 2;
 #pragma unroll 4
     for (int k = 0; k < kChunks; ++k) {
       const uint4 rv = *(const uint4*)(rowp + k * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kHW; ++j) {
         const uint4 qv = *(const uint4*)(qp + j * W * 2 + k * 16);
         s[j] = dot2(rv.x, qv.x, s[j]);
         s[j] = dot2(rv.y, qv.y, s[j]);
@@ -131,9 +136,9 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
       }
     }
     const bool valid = t0 + lane < end;
-    float p[4];
+    float p[kHW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kHW; ++j) {
       const float sj = valid ? s[j] : -INFINITY;
       const float mn = fmaxf(m[j], wave_max(sj));   // finite: the tile has a valid token
       const float corr = exp2f(m[j] - mn);          // 0 on the first tile
@@ -143,13 +148,23 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
 #pragma unroll
       for (int c = 0; c < kC; ++c) acc[j][c] *= corr;
     }
-    *(f32x4*)(ps + lane * kGH + 4 * w) = f32x4{p[0], p[1], p[2], p[3]};
+    if constexpr (kHW == 4)
+      *(f32x4*)(ps + lane * kGH + 4 * w) = f32x4{p[0], p[1], p[2], p[3]};
+    else
+      *(f32x2*)(ps + lane * kGH + 2 * w) = f32x2{p[0], p[1]};
     __syncthreads();
 
     // weighted sum: lane owns latent columns kC*lane .. kC*lane + kC - 1
 #pragma unroll 4
     for (int n = 0; n < kGT; ++n) {
-      const f32x4 pn = *(const f32x4*)(ps + n * kGH + 4 * w);
+      float pn[kHW];
+      if constexpr (kHW == 4) {
+        const f32x4 v = *(const f32x4*)(ps + n * kGH + 4 * w);
+        pn[0] = v[0], pn[1] = v[1], pn[2] = v[2], pn[3] = v[3];
+      } else {
+        const f32x2 v = *(const f32x2*)(ps + n * kGH + 2 * w);
+        pn[0] = v[0], pn[1] = v[1];
+      }
       float cv[kC];
       if constexpr (kC == 4) {
         const uint2 raw = *(const uint2*)(tb + n * kRow + lane * 8);
@@ -163,7 +178,7 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
         cv[1] = hi_bf16(raw);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kHW; ++j)
 #pragma unroll
         for (int c = 0; c < kC; ++c) acc[j][c] = fmaf(pn[j], cv[c], acc[j][c]);
     }
@@ -173,13 +188,13 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(
 
   if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kHW; ++j) {
       part_ml[(slot + j) * 2] = m[j];
       part_ml[(slot + j) * 2 + 1] = l[j];
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kHW; ++j) {
     float* dst = part_o + (slot + j) * R + kC * lane;
     if constexpr (kC == 4)
       *(f32x4*)dst = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
@@ -268,11 +283,11 @@ void launch_attention_generic(const void* q_full, const void* pool, const int* b
                               void* o_lat, bool o_f32, hipStream_t st) {
   const dim3 grid(n_split, H / kGH, batch);
   if (R == 256)
-    attention_generic_kernel<256><<<grid, 256, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
+    attention_generic_kernel<256, 8><<<grid, 512, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
                                                        block_table, max_blocks, block_size,
                                                        seq_lens, H, chunk, n_split, part_ml, part_o);
   else
-    attention_generic_kernel<128><<<grid, 256, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
+    attention_generic_kernel<128, 8><<<grid, 512, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
                                                        block_table, max_blocks, block_size,
                                                        seq_lens, H, chunk, n_split, part_ml, part_o);
   const dim3 mg(H, batch);

@@ -413,9 +413,15 @@ __global__ void __launch_bounds__(256) absorb_small_kernel(const T* __restrict__
   const T* w = w_uk + (long)(h / gs) * Dn * R;
   T* dst = q_full + ((long)n * H + h) * (R + Dr);
   for (int r = threadIdx.x; r < R; r += 256) {
-    float acc = 0.f;
-    for (int d = 0; d < Dn; ++d) acc = fmaf(qv[d], to_f32(w[(long)d * R + r]), acc);
-    dst[r] = from_f32<T>(alpha * acc);
+    // four partial sums and an unrolled loop keep several loads of W in flight
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int d = 0;
+#pragma unroll 4
+    for (; d + 4 <= Dn; d += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fmaf(qv[d + u], to_f32(w[(long)(d + u) * R + r]), acc[u]);
+    for (; d < Dn; ++d) acc[0] = fmaf(qv[d], to_f32(w[(long)d * R + r]), acc[0]);
+    dst[r] = from_f32<T>(alpha * ((acc[0] + acc[1]) + (acc[2] + acc[3])));
   }
   const T* qr = q_rope + ((long)n * H + h) * Dr;
   for (int i = threadIdx.x; i < Dr; i += 256) dst[R + i] = from_f32<T>(alpha * to_f32(qr[i]));
@@ -436,12 +442,17 @@ __global__ void __launch_bounds__(256) project_small_kernel(const T* __restrict_
   __syncthreads();
   const int parts = 256 / Dv, e = t % Dv, p = t / Dv;
   const T* w = w_uv + (long)(h / gs) * R * Dv;
-  float acc = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (p < parts) {
     const int r0 = (int)((long)R * p / parts), r1 = (int)((long)R * (p + 1) / parts);
-    for (int r = r0; r < r1; ++r) acc = fmaf(ov[r], to_f32(w[(long)r * Dv + e]), acc);
+    int r = r0;
+#pragma unroll 4
+    for (; r + 4 <= r1; r += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fmaf(ov[r + u], to_f32(w[(long)(r + u) * Dv + e]), acc[u]);
+    for (; r < r1; ++r) acc[0] = fmaf(ov[r], to_f32(w[(long)r * Dv + e]), acc[0]);
   }
-  part[t] = acc;
+  part[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (t < Dv) {
     float s = 0.f;
