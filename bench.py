@@ -343,6 +343,7 @@ def main():
     attn_ms = graph_time(torch, lambda: [attn(i % R) for i in range(per)], reps, side) / per
     steps_timed = reps * per
 
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
     value = alg["step_bytes"] / (step_ms * 1e-3) / 1e12
     achieved = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
     line = {
@@ -368,6 +369,11 @@ def main():
                    "qk_nope_dim": cfg["qk_nope_dim"], "v_dim": cfg["v_dim"],
                    "block_size": cfg["block_size"], "input_sets_rotated": R,
                    "kv_groups": cfg.get("kv_groups", 0),
+                   # the tutorial's state ledger (5.4): cached bytes per token against
+                   # multi-head K and V at the same head width
+                   "state_bytes_per_token": alg["attn_bytes"] // max(1, alg["tokens"]),
+                   "mha_state_bytes_per_token": 2 * H * cfg["qk_nope_dim"] * 2,
+                   "peak_allocated_bytes": peak_bytes,
                    "cache": "fp8 e4m3 rows, 656 B/token" if cfg.get("cache_dtype") == "fp8"
                    else f"bf16 rows, {2 * (cfg['kv_lora_rank'] + cfg['rope_dim'])} B/token",
                    "timing": f"hip graph replay ({per} steps per replay), events on the launching stream"},
