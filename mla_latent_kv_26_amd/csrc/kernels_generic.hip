@@ -398,49 +398,59 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 namespace mla {
 namespace {
 
-// q_full[n, h] = alpha [q_nope[n, h] W_UK[h / gs] | q_rope[n, h]]
+// q_full[n, h] = alpha [q_nope[n, h] W_UK[h / gs] | q_rope[n, h]]; thread t
+// sums part t / R of the Dn inputs for column t % R, the parts are added
+// through LDS
 template <typename T>
-__global__ void __launch_bounds__(256) absorb_small_kernel(const T* __restrict__ q_nope,
-                                                           const T* __restrict__ q_rope,
-                                                           const T* __restrict__ w_uk, int H,
-                                                           int gs, int Dn, int R, int Dr,
-                                                           float alpha, T* __restrict__ q_full) {
+__global__ void __launch_bounds__(1024) absorb_small_kernel(const T* __restrict__ q_nope,
+                                                            const T* __restrict__ q_rope,
+                                                            const T* __restrict__ w_uk, int H,
+                                                            int gs, int Dn, int R, int Dr,
+                                                            float alpha, T* __restrict__ q_full) {
   __shared__ float qv[1024];
-  const int n = blockIdx.x, h = blockIdx.y;
+  __shared__ float part[1024];
+  const int n = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const T* q = q_nope + ((long)n * H + h) * Dn;
-  for (int d = threadIdx.x; d < Dn; d += 256) qv[d] = to_f32(q[d]);
+  for (int d = t; d < Dn; d += 1024) qv[d] = to_f32(q[d]);
   __syncthreads();
+  const int parts = 1024 / R, r = t % R, p = t / R;
   const T* w = w_uk + (long)(h / gs) * Dn * R;
-  T* dst = q_full + ((long)n * H + h) * (R + Dr);
-  for (int r = threadIdx.x; r < R; r += 256) {
-    // four partial sums and an unrolled loop keep several loads of W in flight
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int d = 0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p < parts) {
+    const int d0 = (int)((long)Dn * p / parts), d1 = (int)((long)Dn * (p + 1) / parts);
+    int d = d0;
 #pragma unroll 4
-    for (; d + 4 <= Dn; d += 4)
+    for (; d + 4 <= d1; d += 4)
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc[u] = fmaf(qv[d + u], to_f32(w[(long)(d + u) * R + r]), acc[u]);
-    for (; d < Dn; ++d) acc[0] = fmaf(qv[d], to_f32(w[(long)d * R + r]), acc[0]);
-    dst[r] = from_f32<T>(alpha * ((acc[0] + acc[1]) + (acc[2] + acc[3])));
+    for (; d < d1; ++d) acc[0] = fmaf(qv[d], to_f32(w[(long)d * R + r]), acc[0]);
+  }
+  part[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  T* dst = q_full + ((long)n * H + h) * (R + Dr);
+  if (t < R) {
+    float s = 0.f;
+    for (int k = 0; k < parts; ++k) s += part[k * R + t];
+    dst[t] = from_f32<T>(alpha * s);
   }
   const T* qr = q_rope + ((long)n * H + h) * Dr;
-  for (int i = threadIdx.x; i < Dr; i += 256) dst[R + i] = from_f32<T>(alpha * to_f32(qr[i]));
+  for (int i = t; i < Dr; i += 1024) dst[R + i] = from_f32<T>(alpha * to_f32(qr[i]));
 }
 
 // out[n, h] = o_lat[n, h] W_UV[h / gs]; thread t sums part t / Dv of the R
 // inputs for column t % Dv, the parts are added through LDS
 template <typename T>
-__global__ void __launch_bounds__(256) project_small_kernel(const T* __restrict__ o_lat,
-                                                            const T* __restrict__ w_uv, int H,
-                                                            int gs, int R, int Dv,
-                                                            T* __restrict__ out) {
+__global__ void __launch_bounds__(1024) project_small_kernel(const T* __restrict__ o_lat,
+                                                             const T* __restrict__ w_uv, int H,
+                                                             int gs, int R, int Dv,
+                                                             T* __restrict__ out) {
   __shared__ float ov[1024];
-  __shared__ float part[256];
+  __shared__ float part[1024];
   const int n = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const T* o = o_lat + ((long)n * H + h) * R;
-  for (int r = t; r < R; r += 256) ov[r] = to_f32(o[r]);
+  for (int r = t; r < R; r += 1024) ov[r] = to_f32(o[r]);
   __syncthreads();
-  const int parts = 256 / Dv, e = t % Dv, p = t / Dv;
+  const int parts = 1024 / Dv, e = t % Dv, p = t / Dv;
   const T* w = w_uv + (long)(h / gs) * R * Dv;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (p < parts) {
@@ -456,7 +466,7 @@ __global__ void __launch_bounds__(256) project_small_kernel(const T* __restrict_
   __syncthreads();
   if (t < Dv) {
     float s = 0.f;
-    for (int q = 0; q < parts; ++q) s += part[q * Dv + t];
+    for (int k = 0; k < parts; ++k) s += part[k * Dv + t];
     out[((long)n * H + h) * Dv + t] = from_f32<T>(s);
   }
 }
@@ -464,7 +474,7 @@ __global__ void __launch_bounds__(256) project_small_kernel(const T* __restrict_
 }  // namespace
 
 bool small_projection_fits(int rows, int Dn, int R, int Dv) {
-  return rows <= 32 && Dn <= 1024 && R <= 1024 && Dv <= 256;
+  return rows <= 32 && Dn <= 1024 && R <= 1024 && Dv <= 1024;
 }
 
 void launch_absorb_small(const void* q_nope, const void* q_rope, const void* w_uk, int n, int H,
@@ -472,11 +482,11 @@ void launch_absorb_small(const void* q_nope, const void* q_rope, const void* w_u
                          hipStream_t st) {
   const dim3 grid(n, H);
   if (dtype == 1)
-    absorb_small_kernel<bf16><<<grid, 256, 0, st>>>((const bf16*)q_nope, (const bf16*)q_rope,
+    absorb_small_kernel<bf16><<<grid, 1024, 0, st>>>((const bf16*)q_nope, (const bf16*)q_rope,
                                                     (const bf16*)w_uk, H, gs, Dn, R, Dr, alpha,
                                                     (bf16*)q_full);
   else
-    absorb_small_kernel<float><<<grid, 256, 0, st>>>((const float*)q_nope, (const float*)q_rope,
+    absorb_small_kernel<float><<<grid, 1024, 0, st>>>((const float*)q_nope, (const float*)q_rope,
                                                      (const float*)w_uk, H, gs, Dn, R, Dr, alpha,
                                                      (float*)q_full);
 }
@@ -485,10 +495,10 @@ void launch_project_small(const void* o_lat, const void* w_uv, int n, int H, int
                           int dtype, void* out, hipStream_t st) {
   const dim3 grid(n, H);
   if (dtype == 1)
-    project_small_kernel<bf16><<<grid, 256, 0, st>>>((const bf16*)o_lat, (const bf16*)w_uv, H, gs,
+    project_small_kernel<bf16><<<grid, 1024, 0, st>>>((const bf16*)o_lat, (const bf16*)w_uv, H, gs,
                                                      R, Dv, (bf16*)out);
   else
-    project_small_kernel<float><<<grid, 256, 0, st>>>((const float*)o_lat, (const float*)w_uv, H,
+    project_small_kernel<float><<<grid, 1024, 0, st>>>((const float*)o_lat, (const float*)w_uv, H,
                                                       gs, R, Dv, (float*)out);
 }
 

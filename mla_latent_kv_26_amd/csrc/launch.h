@@ -159,7 +159,7 @@ void launch_attention_generic(const void* q_full, const void* pool, const int* b
                               int H, int R, int chunk, int n_split, float* part_ml, float* part_o,
                               void* o_lat, bool o_f32, hipStream_t st);
 
-// Per-head projections of a few rows (rows <= 32, Dn, R <= 1024, Dv <= 256)
+// Per-head projections of a few rows (rows <= 32, Dn, R, Dv <= 1024)
 // with W_UK / W_UV shared by gs consecutive heads: q_full [n, H, R + Dr] =
 // alpha [q_nope W_UK[h / gs] | q_rope]; out [n, H, Dv] = o_lat W_UV[h / gs].
 bool small_projection_fits(int rows, int Dn, int R, int Dv);
