@@ -7,18 +7,18 @@ by its time (TB/s); `ms_per_step` gives the step time.  Inputs are synthetic
 timed steps rotate over several independently drawn input sets whose total
 size exceeds the 256 MB Infinity Cache, so repeats are served from HBM.
 
-Timing: the step's kernels are captured in a HIP graph whose one replay
-launches --passes rotations (every input set several times, as a model's
-layers follow one another in one graph), and HIP events on the launching
-stream bracket the replays; the launch gap between replays is then spread
-over many steps, as in a multi-layer graph.  The split-KV attention kernel
-is timed the same way on its own for the roofline entry.  The oracle is timed on the host cores on a bounded
-sample of the same workload.
+Timing: after --warmup untimed steps, exactly --steps steps (rotating over
+the input sets) are captured in one HIP graph; the graph is replayed
+--repeats times, each replay bracketed by HIP events on the launching
+stream, and the median replay (with p10 and p90) divided by --steps is the
+step time.  The same steps issued eagerly from Python are timed the same
+way and reported beside it.  The split-KV attention kernel alone is timed
+the same way for the roofline entry.  The oracle is timed on the host cores
+on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -56,9 +56,9 @@ def algorithmic(cfg, lens):
 
 
 def prefill_algorithmic(cfg):
-    """FLOPs and bytes of one prefill call (T new tokens per sequence, causal,
-    absorbed path): projections, cache append, attention on the latent rows,
-    W_UV."""
+    """FLOPs of one prefill call (T new tokens per sequence, causal) in both
+    attention forms: on the latent rows (absorbed) and through per-head keys
+    and values rebuilt for the context (T tokens per sequence here)."""
     B, T, M, H = cfg["batch"], cfg["q_len"], cfg["d_model"], cfg["num_heads"]
     R, Dr, Dn, Dv = (cfg[k] for k in ("kv_lora_rank", "rope_dim", "qk_nope_dim", "v_dim"))
     Rq = cfg.get("q_lora_rank", 0)
@@ -69,15 +69,41 @@ def prefill_algorithmic(cfg):
     pairs = B * T * (T + 1) // 2                        # causal (query, key) pairs
     attn = 2 * H * (R + Dr + R) * pairs
     out = 2 * n * H * R * Dv
-    weights = 2 * (M * (R + Dr) + (M * Rq + Rq * qw if Rq else M * qw) + H * R * (Dn + Dv))
-    bytes_ = 2 * n * M + weights + 2 * n * (R + Dr) + 2 * n * H * Dv
-    # the same result through per-head keys and values (rebuilt for the
-    # context, T tokens per sequence here): what the library executes for
-    # long spans
     recon = 2 * n * H * R * (Dn + Dv)
     attn_heads = 2 * H * (Dn + Dr + Dv) * pairs
-    return dict(flops=proj + absorb + attn + out, attn_flops=attn, bytes=bytes_,
+    return dict(latent_flops=proj + absorb + attn + out, latent_attn_flops=attn,
                 per_head_flops=proj + recon + attn_heads, per_head_attn_flops=attn_heads)
+
+
+def stats(per_step_ms):
+    a = np.asarray(per_step_ms, np.float64)
+    return dict(median=float(np.median(a)), p10=float(np.percentile(a, 10)),
+                p90=float(np.percentile(a, 90)), mean=float(a.mean()))
+
+
+def capture(torch, fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    g.replay()                   # first replay uploads the graph
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, run, repeats):
+    """ms of each of `repeats` calls of run(), each bracketed by HIP events on
+    the current stream (the one graph replays and library calls launch on)."""
+    cur = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(repeats)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(cur)
+        run()
+        b.record(cur)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
 
 
 def prefill_main(args, torch, m):
@@ -90,6 +116,7 @@ def prefill_main(args, torch, m):
     rope = m.mla_rope_table(mc, T).to(dev)
     ws = torch.zeros(m.mla_prefill_workspace_size(mc, B, T, T), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, cfg["num_heads"], cfg["v_dim"]), dtype=torch.bfloat16, device=dev)
+    form = m.mla_prefill_attention_form(mc, T, 0)
 
     def call():
         m.mla_prefill(mc, inp["x"], inp["weights"], inp["pool"], inp["block_table"],
@@ -98,28 +125,33 @@ def prefill_main(args, torch, m):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    ms = graph_time(torch, call, args.steps, side)
+    g = capture(torch, call, torch.cuda.Stream())
+    st = stats(time_replays(torch, g.replay, args.steps))
+    ms = st["median"]
     alg = prefill_algorithmic(cfg)
-    tflops = alg["flops"] / (ms * 1e-3) / 1e12
-    executed = alg["per_head_flops"] / (ms * 1e-3) / 1e12
+    executed = alg["per_head_flops"] if form == "per_head" else alg["latent_flops"]
+    tflops = executed / (ms * 1e-3) / 1e12
     line = {
-        "metric": "MLA prefill with cache append: ms per call; effective TFLOP/s over the "
-                  "latent-path FLOP count",
+        "metric": "MLA prefill with cache append: ms per call; TFLOP/s of the FLOPs the "
+                  "call executes",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_p10": round(st["p10"], 4), "ms_p90": round(st["p90"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_len": T, "d_model": cfg["d_model"],
                    "q_lora_rank": cfg.get("q_lora_rank", 0), "heads": cfg["num_heads"],
-                   "algorithmic_flops": alg["flops"], "attention_flops": alg["attn_flops"],
-                   "executed_flops_per_head_path": alg["per_head_flops"],
+                   "attention_form": form, "executed_flops": executed,
+                   "latent_form_flops": alg["latent_flops"],
+                   "per_head_form_flops": alg["per_head_flops"],
                    "cache": "fp8 e4m3 rows, 656 B/token" if cfg.get("cache_dtype") == "fp8"
                             else "bf16 rows, 1152 B/token",
-                   "timing": "hip graph replay, events on the launching stream"},
-        "roofline": {"kernel": "mla_prefill (whole call, per-head key/value path)",
-                     "bound": "mfma", "achieved": round(executed, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(executed / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_call": alg["per_head_flops"]},
+                   "timing": f"one call per graph replay, {args.steps} replays, median "
+                             "(events on the launching stream)"},
+        "roofline": {"kernel": f"mla_prefill (whole call, {form} attention)",
+                     "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_call": executed},
     }
     print(json.dumps(line), flush=True)
 
@@ -143,17 +175,21 @@ def output_gate_main(args, torch, m):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    ms = graph_time(torch, call, args.steps, torch.cuda.Stream())
+    g = capture(torch, call, torch.cuda.Stream())
+    st = stats(time_replays(torch, g.replay, args.steps))
+    ms = st["median"]
     flops = 2 * n * M * HV * (2 if cfg["gated"] else 1)
     tflops = flops / (ms * 1e-3) / 1e12
     line = {
         "metric": "MLA output gate + W_O: TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_p10": round(st["p10"], 4), "ms_p90": round(st["p90"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "rows": n, "d_model": M, "heads": cfg["num_heads"],
                    "v_dim": cfg["v_dim"], "gated": cfg["gated"], "flops": flops,
-                   "timing": "hip graph replay, events on the launching stream"},
+                   "timing": f"one call per graph replay, {args.steps} replays, median "
+                             "(events on the launching stream)"},
         "roofline": {"kernel": "mla_output_gate_projection (gate GEMM + W_O GEMM)",
                      "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
@@ -163,33 +199,62 @@ def output_gate_main(args, torch, m):
 
 
 def cpu_baseline(cfg, seconds):
-    """Time the oracle's decode (float64 numpy, as it stands) on whole steps of
-    the same workload until about `seconds` of work; report TB/s of
-    algorithmic bytes like the GPU line."""
+    """Time the oracle's decode as it stands on whole steps of the same
+    workload: the absorbed path in float32 (the fastest faithful CPU form),
+    the absorbed path in float64 (the parity reference) and the naive
+    reconstruction path in float32 on a few sequences (scaled to a step).
+    BLAS threads = the cores this process may run on.  `value` is the float32
+    absorbed rate in the metric's unit (TB/s of algorithmic step bytes)."""
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
     inp = workloads.decode_inputs(cfg)
-    args = [workloads.to_f64(a) for a in (inp.q_nope, inp.q_rope, inp.w_uk, inp.w_uv, inp.pool)]
     alg = algorithmic(cfg, inp.seq_lens)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.decode(*args, inp.block_table, inp.seq_lens, cfg)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > seconds:
-            break
-    t = float(np.median(times))
-    pools = threadpool_info()
-    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    B = len(inp.seq_lens)
+
+    def timed(fn, budget, max_reps=50):
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < max_reps:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget:
+                break
+        return float(np.median(times)), len(times)
+
+    def inputs(wd):
+        return [workloads.to_f64(a).astype(wd)
+                for a in (inp.q_nope, inp.q_rope, inp.w_uk, inp.w_uv, inp.pool)]
+
+    paths = {}
+    with threadpool_limits(limits=cores):
+        for wd, name in ((np.float32, "absorbed_f32"), (np.float64, "absorbed_f64")):
+            args = inputs(wd)
+            t, n = timed(lambda: oracle.decode(*args, inp.block_table, inp.seq_lens, cfg,
+                                               wd=wd), seconds * 0.4)
+            paths[name] = {"ms_per_step": round(t * 1e3, 2), "steps_timed": n}
+            del args
+        args = inputs(np.float32)
+        ids = [0, B // 2, B - 1]
+        per_seq = [timed(lambda: oracle.decode(*args, inp.block_table, inp.seq_lens, cfg,
+                                               path="naive", wd=np.float32, batch_ids=[b]),
+                         0.0, max_reps=1)[0] for b in ids]
+        paths["naive_f32"] = {"ms_per_step": round(float(np.mean(per_seq)) * B * 1e3, 2),
+                              "sequences_timed": ids}
+        pools = threadpool_info()
     blas = ",".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
                             if p.get("user_api") == "blas"})) or "unknown"
-    return {"value": alg["step_bytes"] / t / 1e12, "unit": "TB/s", "cores": int(threads),
+    t = paths["absorbed_f32"]["ms_per_step"] * 1e-3
+    return {"value": alg["step_bytes"] / t / 1e12, "unit": "TB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{len(times)} full decode steps of {cfg['batch']}x{cfg['context']} tokens, "
-                      f"absorbed path in float64 numpy, median {t * 1e3:.1f} ms/step; "
-                      f"CPU {cpu_model()}, BLAS {blas}",
-            "ms_per_step": t * 1e3}
+            "sample": f"decode steps of {B}x{cfg['context']} tokens: absorbed path in "
+                      f"float32 numpy ({paths['absorbed_f32']['steps_timed']} whole steps, "
+                      f"median; this is value), in float64 "
+                      f"({paths['absorbed_f64']['steps_timed']} steps), naive "
+                      f"reconstruction path in float32 on sequences {ids} scaled to the "
+                      f"batch; CPU {cpu_model()}, BLAS {blas}, {cores} threads",
+            "ms_per_step": paths["absorbed_f32"]["ms_per_step"], "paths": paths}
 
 
 def cpu_model():
@@ -214,40 +279,24 @@ def traffic_entry(workload):
     return rec.get("bytes_per_launch")
 
 
-VALU_PEAK_TFLOPS = 157.3      # fp32 vector ALU, 256 CUs at 2.4 GHz
-
-
 def narrow_roofline(alg, attn_ms):
-    """Narrow latents run on vector-ALU kernels: 2 H (2R + Dr) flops per
-    token against (R + Dr) 2 bytes, beyond what the ALUs can do at the HBM
-    rate, so the bound is the ALU peak."""
+    """Narrow latents (kv_lora_rank 128 / 256): the attention and merge
+    kernels move (R + Dr) 2 bytes and do 2 H (2R + Dr) flops per token; both
+    rooflines are given, `bound` names the nearer one."""
     tf = alg["attn_flops"] / (attn_ms * 1e-3) / 1e12
-    return {"kernel": "attention_generic_kernel + merge_generic_kernel", "bound": "alu",
-            "achieved": round(tf, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / VALU_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel_us": round(attn_ms * 1e3, 3),
-            "hbm_gbs": round(alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
+    gbs = alg["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tf / BF16_PEAK_TFLOPS
+    if hbm_frac >= mfma_frac:
+        entry = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(hbm_frac, 4)}
+    else:
+        entry = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
+    return {"kernel": "narrow-latent attention + merge", **entry, "traffic": None,
+            "kernel_us": round(attn_ms * 1e3, 3), "hbm_frac": round(hbm_frac, 4),
+            "mfma_frac": round(mfma_frac, 4),
             "algorithmic_flops_per_launch": alg["attn_flops"],
             "algorithmic_bytes_per_launch": alg["attn_bytes"]}
-
-
-def graph_time(torch, fn, reps, stream):
-    """Capture fn() once in a graph, replay `reps` times between two events."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        fn()
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    cur = torch.cuda.current_stream()
-    a.record(cur)
-    for _ in range(reps):
-        g.replay()
-    b.record(cur)
-    b.synchronize()
-    return a.elapsed_time(b) / reps  # ms per replay
 
 
 def main():
@@ -255,11 +304,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--repeats", type=int, default=20,
+                    help="graph replays of --steps steps each; the median is reported")
     ap.add_argument("--workload", default=workloads.HEADLINE,
                     choices=[k for k, v in workloads.WORKLOADS.items() if v["dtype"] == "bf16"])
     ap.add_argument("--rotate", type=int, default=3)
-    ap.add_argument("--passes", type=int, default=10,
-                    help="rotations over the input sets captured in one graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -271,6 +320,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.repeats < 1:
+        print("--steps and --repeats must be positive", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -304,44 +356,40 @@ def main():
     out = torch.empty((B, H, cfg["v_dim"]), dtype=torch.bfloat16, device=dev)
     qf = [m.mla_absorb_query(mc, s["q_nope"], s["q_rope"], s["w_uk"]) for s in sets]
     torch.cuda.synchronize()
+    R = len(sets)
+    K = args.steps
 
     def step(i):
-        s = sets[i]
+        s = sets[i % R]
         m.mla_decode(mc, s["q_nope"], s["q_rope"], s["w_uk"], s["w_uv"], s["pool"],
-                     s["block_table"], s["seq_lens"], max_len, out=out, workspace=ws[i])
+                     s["block_table"], s["seq_lens"], max_len, out=out, workspace=ws[i % R])
 
     narrow = cfg["kv_lora_rank"] != 512   # the narrow-latent kernels (attention + merge)
 
     def attn(i):
-        s = sets[i]
+        s = sets[i % R]
         if narrow:
-            m.mla_latent_attention(mc, qf[i], s["pool"], s["block_table"], s["seq_lens"], max_len,
-                                   workspace=ws[i])
+            m.mla_latent_attention(mc, qf[i % R], s["pool"], s["block_table"], s["seq_lens"],
+                                   max_len, workspace=ws[i % R])
             return
-        m.mla_attention_partials(mc, qf[i], s["pool"], s["block_table"], s["seq_lens"], max_len,
-                                 ws[i])
+        m.mla_attention_partials(mc, qf[i % R], s["pool"], s["block_table"], s["seq_lens"],
+                                 max_len, ws[i % R])
 
-    R = len(sets)
     for i in range(args.warmup):
-        step(i % R)
+        step(i)
     torch.cuda.synchronize()
 
-    # eager: python issues every call
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(args.steps):
-        step(i % R)
-    b.record()
-    b.synchronize()
-    eager_ms = a.elapsed_time(b) / args.steps
+    def steps_eager():
+        for i in range(K):
+            step(i)
 
-    # graph: one replay = `passes` rotations over the input sets
+    eager = stats([t / K for t in time_replays(torch, steps_eager, args.repeats)])
     side = torch.cuda.Stream()
-    per = R * max(1, args.passes)
-    reps = max(1, args.steps // per)
-    step_ms = graph_time(torch, lambda: [step(i % R) for i in range(per)], reps, side) / per
-    attn_ms = graph_time(torch, lambda: [attn(i % R) for i in range(per)], reps, side) / per
-    steps_timed = reps * per
+    g_step = capture(torch, steps_eager, side)
+    graph = stats([t / K for t in time_replays(torch, g_step.replay, args.repeats)])
+    g_attn = capture(torch, lambda: [attn(i) for i in range(K)], side)
+    attn_st = stats([t / K for t in time_replays(torch, g_attn.replay, args.repeats)])
+    step_ms, attn_ms = graph["median"], attn_st["median"]
 
     peak_bytes = torch.cuda.max_memory_allocated(dev)
     value = alg["step_bytes"] / (step_ms * 1e-3) / 1e12
@@ -351,13 +399,17 @@ def main():
         "value": round(value, 4),
         "unit": "TB/s",
         "n_gpus": 1,
-        "steps": steps_timed,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 6),
         "us_per_step": round(step_ms * 1e3, 3),
+        "us_per_step_p10": round(graph["p10"] * 1e3, 3),
+        "us_per_step_p90": round(graph["p90"] * 1e3, 3),
         "tflops": round(alg["step_flops"] / (step_ms * 1e-3) / 1e12, 2),
         "cached_tokens_per_s": round(alg["tokens"] / (step_ms * 1e-3), 1),
-        "eager_us_per_step": round(eager_ms * 1e3, 3),
+        "eager_us_per_step": round(eager["median"] * 1e3, 3),
+        "eager_us_per_step_p10": round(eager["p10"] * 1e3, 3),
+        "eager_us_per_step_p90": round(eager["p90"] * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -376,7 +428,8 @@ def main():
                    "peak_allocated_bytes": peak_bytes,
                    "cache": "fp8 e4m3 rows, 656 B/token" if cfg.get("cache_dtype") == "fp8"
                    else f"bf16 rows, {2 * (cfg['kv_lora_rank'] + cfg['rope_dim'])} B/token",
-                   "timing": f"hip graph replay ({per} steps per replay), events on the launching stream"},
+                   "timing": f"{K} steps per hip graph replay, {args.repeats} replays, median "
+                             "per step (events on the launching stream)"},
         "roofline": narrow_roofline(alg, attn_ms) if narrow else {
             "kernel": "attn_decode_partials_kernel",
             "bound": "hbm",
@@ -386,6 +439,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_entry(args.workload),
             "kernel_us": round(attn_ms * 1e3, 3),
+            "kernel_us_p10": round(attn_st["p10"] * 1e3, 3),
+            "kernel_us_p90": round(attn_st["p90"] * 1e3, 3),
             "algorithmic_bytes_per_launch": alg["attn_bytes"],
             "mfma_tflops": round(alg["attn_flops"] / (attn_ms * 1e-3) / 1e12, 2),
             "mfma_frac": round(alg["attn_flops"] / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -97,6 +97,17 @@ typedef struct mla_config {
   int32_t kv_groups;    /* G >= 0: 0 = one W_UK and W_UV per head; else H % G
                            == 0 and heads g H/G .. (g+1) H/G - 1 share
                            W_UK[g], W_UV[g] (w_uk [G, Dn, R], w_uv [G, R, Dv])  */
+  int32_t split_workgroups; /* >= 0: workgroups per head group of the split-KV
+                           decode attention (kv_lora_rank 512 kernels), each
+                           taking an equal share of the batch's 32-token tiles;
+                           0 = one per compute unit in total; else a multiple
+                           of 8, at most 8192.  Results do not depend on it
+                           beyond float32 rounding (the partition is free).  */
+  int32_t prefill_attention; /* form of mla_prefill's attention: 0 = the one
+                           needing fewer FLOPs, 1 = on the latent rows
+                           (absorbed), 2 = through per-head keys and values
+                           (bf16, R = 512, Dr = 64, Dn = Dv = 128 only; an FP8
+                           cache takes 0 or 2).  Same result up to rounding. */
 } mla_config;
 
 /* ---- library information ------------------------------------------------ */
@@ -240,6 +251,13 @@ mla_status mla_cache_append(const mla_config* cfg, const void* x, const void* w_
  * as q_len).  Scratch only: no initial contents required. */
 mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int32_t q_len,
                                       int32_t max_context, size_t* bytes /* host out */);
+
+/* The attention form mla_prefill takes for q_len new tokens after
+ * max_start_pos cached ones under this config (prefill_attention, or with 0
+ * the one needing fewer FLOPs): *form = 1 on the latent rows (absorbed), 2
+ * through per-head keys and values.  Host only. */
+mla_status mla_prefill_attention_form(const mla_config* cfg, int32_t q_len, int32_t max_start_pos,
+                                      int32_t* form /* host out */);
 
 /* Forward of q_len new tokens per sequence through one MLA layer, absorbed
  * path ("GatedMLA" docs, "Build per-head Q, K and V" and "Observe logits,

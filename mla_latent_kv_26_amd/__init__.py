@@ -10,7 +10,7 @@ from .api import (  # noqa: F401
     mla_cache_bytes_per_token, mla_rope_table, mla_decode_workspace_size, mla_decode,
     mla_absorb_query, mla_latent_attention, mla_attention_partials, mla_combine_output,
     mla_output_projection,
-    mla_cache_append_workspace_size, mla_cache_append, mla_prefill_workspace_size, mla_prefill,
+    mla_cache_append_workspace_size, mla_cache_append, mla_prefill_workspace_size, mla_prefill_attention_form, mla_prefill,
     mla_output_gate_workspace_size, mla_output_gate_projection,
 )
 from .pool import LatentKVPool  # noqa: F401

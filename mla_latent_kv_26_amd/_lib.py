@@ -38,6 +38,8 @@ class MLAConfigC(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("cache_dtype", ctypes.c_int32),
         ("kv_groups", ctypes.c_int32),
+        ("split_workgroups", ctypes.c_int32),
+        ("prefill_attention", ctypes.c_int32),
     ]
 
 
@@ -89,6 +91,7 @@ SIGNATURES = {
     "mla_cache_append_workspace_size": (_I, [_CFG, _I, ctypes.POINTER(_SZ)]),
     "mla_cache_append": (_I, [_CFG, _P, _P, _FP, _FP, _I, _IP, _IP, _I, _P, _I, _P, _SZ, _P]),
     "mla_prefill_workspace_size": (_I, [_CFG, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "mla_prefill_attention_form": (_I, [_CFG, _I, _I, ctypes.POINTER(_I)]),
     "mla_output_gate_workspace_size": (_I, [_CFG, _I, ctypes.POINTER(_SZ)]),
     "mla_output_gate_projection": (_I, [_CFG, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "mla_prefill": (_I, [_CFG, _P, _P, _P, _FP, _P, _P, _FP, _P, _P, _FP, _I, _P, _I, _IP, _I,

@@ -19,6 +19,7 @@ from ._lib import lib, check, MLAConfigC
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _C_DTYPE = {"f32": _lib.DTYPE_F32, "bf16": _lib.DTYPE_BF16}
 _C_CACHE = {"same": _lib.CACHE_SAME, "fp8": _lib.CACHE_FP8_E4M3}
+_C_PREFILL = {"auto": 0, "latent": 1, "per_head": 2}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -38,6 +39,8 @@ class MLAConfig:
     dtype: str = "bf16"
     cache_dtype: str = "same"   # "same" (rows in dtype) or "fp8" (E4M3 latent, see mla.h)
     kv_groups: int = 0          # 0: W_UK, W_UV per head; G: heads share G matrices in order
+    split_workgroups: int = 0   # decode attention workgroups per head group (0: one per CU)
+    prefill_attention: str = "auto"   # "auto" (fewer FLOPs), "latent" (absorbed), "per_head"
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -73,7 +76,8 @@ class MLAConfig:
         return MLAConfigC(self.num_heads, self.kv_lora_rank, self.rope_dim, self.qk_nope_dim,
                           self.v_dim, self.d_model, self.q_lora_rank, self.block_size,
                           self.softmax_scale, self.rms_eps, self.rope_theta,
-                          _C_DTYPE[self.dtype], _C_CACHE[self.cache_dtype], self.kv_groups)
+                          _C_DTYPE[self.dtype], _C_CACHE[self.cache_dtype], self.kv_groups,
+                          self.split_workgroups, _C_PREFILL[self.prefill_attention])
 
     @classmethod
     def from_dict(cls, d: dict, **over) -> "MLAConfig":
@@ -177,6 +181,14 @@ def mla_prefill_workspace_size(cfg: MLAConfig, batch: int, q_len: int, max_conte
     check(lib.mla_prefill_workspace_size(_ref(cfg), batch, q_len, max_context, ctypes.byref(n)),
           "mla_prefill_workspace_size")
     return n.value
+
+
+def mla_prefill_attention_form(cfg: MLAConfig, q_len: int, max_start_pos: int = 0) -> str:
+    """"latent" or "per_head": the attention form mla_prefill takes."""
+    f = ctypes.c_int32()
+    check(lib.mla_prefill_attention_form(_ref(cfg), q_len, max_start_pos, ctypes.byref(f)),
+          "mla_prefill_attention_form")
+    return {1: "latent", 2: "per_head"}[f.value]
 
 
 # ---------------------------------------------------------------------------

@@ -234,34 +234,6 @@ void launch_bk(const void* A, const void* B, void* C, int M, int N, int K, long 
                            st);
 }
 
-// Each batch item through hipBLASLt, for a few items (sequences of a
-// prefill); many small ones (one per head) stay one batched tile launch.
-// False, with nothing launched, when the library does not take the first
-// item; an item after that which it refuses (not expected: same shape) goes
-// to the tile kernel on its own.
-bool blas_batched(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
-                  long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, bool bt,
-                  hipStream_t st) {
-  if (batch > 4) return false;
-  const size_t ec = c_f32 ? 4 : 2;
-  for (int b = 0; b < batch; ++b) {
-    const void* a = (const char*)A + (size_t)b * sA * 2;
-    const void* bb = (const char*)B + (size_t)b * sB * 2;
-    void* c = (char*)C + (size_t)b * sC * ec;
-    if (blas_gemm_bf16(a, bb, c, M, N, K, lda, ldb, ldc, alpha, c_f32 != 0, bt, st)) continue;
-    if (b == 0) return false;
-    if (gemm_tile256_fits(M, N, K, lda, ldb, ldc))
-      launch_gemm_tile256(a, bb, c, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, c_f32, bt, st);
-    else if (bt)
-      launch_bk<32, true>(a, bb, c, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, c_f32,
-                          Side{nullptr, 0, 0, nullptr, 0, nullptr}, st);
-    else
-      launch_bk<32, false>(a, bb, c, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, c_f32,
-                           Side{nullptr, 0, 0, nullptr, 0, nullptr}, st);
-  }
-  return true;
-}
-
 }  // namespace
 
 void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda,
@@ -269,9 +241,6 @@ void launch_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K
                       int c_f32, hipStream_t st, const void* side_src, long side_ld,
                       long side_sb, void* side_dst, int side_cols) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
-  if (!side_src &&
-      blas_batched(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, false, st))
-    return;
   if (!side_src && gemm_tile256_fits(M, N, K, lda, ldb, ldc)) {
     launch_gemm_tile256(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, false, st);
     return;
@@ -289,8 +258,6 @@ void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, i
                          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
                          int c_f32, hipStream_t st) {
   if (M <= 0 || N <= 0 || batch <= 0) return;
-  if (blas_batched(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, true, st))
-    return;
   if (gemm_tile256_fits(M, N, K, lda, ldb, ldc)) {
     launch_gemm_tile256(A, Bt, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, true, st);
     return;
@@ -307,12 +274,6 @@ void launch_gemm_bf16_bt(const void* A, const void* Bt, void* C, int M, int N, i
 void launch_gemm_bf16_gated(const void* A, const void* B, void* C, int M, int N, int K, long lda,
                             long ldb, long ldc, float alpha, const void* gmul, hipStream_t st) {
   if (M <= 0 || N <= 0) return;
-  // the library GEMM, then the gate as its own elementwise pass (contiguous C)
-  if (ldc == N && N % 8 == 0 &&
-      blas_gemm_bf16(A, B, C, M, N, K, lda, ldb, ldc, alpha, false, false, st)) {
-    launch_gate_mul_bf16(C, gmul, (long)M * N, st);
-    return;
-  }
   if (gemm_tile256_fits(M, N, K, lda, ldb, ldc)) {
     launch_gemm_tile256(A, B, C, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, alpha, 0, false, st, 0, 0,
                         gmul);

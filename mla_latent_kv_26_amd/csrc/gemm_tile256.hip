@@ -412,12 +412,14 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
 // column tiles side by side (C1's first) give n_nt tiles per 256-row tile.
 // All but the last column are whole tiles, one per workgroup, with the
 // row-group-per-XCD mapping above; the last column tile of each row tile is
-// split along k into S = n_nt - 1 parts, one per workgroup, whose float32
-// partial tiles a second kernel adds in a fixed order (deterministic).  The
-// split parts are as long as a whole tile's k loop divided by S, so when the
-// whole tiles take exactly one round of all CUs, the parts take one short
-// round more instead of a second full one.  (The prefill's x [W_DQ | W_DKV]
-// at 8192 rows: 256 whole tiles and 32 last-column tiles, split 8 ways.)
+// split along k into S parts, one per workgroup, whose float32 partial
+// tiles a second kernel adds in a fixed order (deterministic).  S is chosen
+// so that the split parts of all row tiles take exactly one round of the
+// CUs (S = CUs / row tiles), and the launch is used only when the whole
+// tiles take a whole number of rounds too: then no round of the CUs is left
+// partly idle.  (The prefill's x [W_DQ | W_DKV] at 8192 rows: 32 row tiles,
+// 8 whole column tiles = one round of 256 CUs; 32 last-column tiles split
+// 8 ways = one more, short round.)  Other shapes take two tile launches.
 // ---------------------------------------------------------------------------
 struct PairGemm {
   const bf16* A;
@@ -526,9 +528,12 @@ bool gemm_tile256_fits(int M, int N, int K, long lda, long ldb, long ldc) {
          ldb % 8 == 0 && ldc % 4 == 0;
 }
 
-size_t gemm_pair_scratch_bytes(int M, int N1, int N2) {
-  const int n_mt = (M + kTM - 1) / kTM, n_nt = N1 / 256 + (N2 + 255) / 256;
-  return (size_t)(n_nt - 1) * n_mt * kTM * 256 * sizeof(float);
+size_t gemm_pair_scratch_bytes(int M, int N1, int N2, int num_cus) {
+  (void)N1;
+  (void)N2;
+  const int n_mt = (M + kTM - 1) / kTM;
+  const int S = num_cus / n_mt;
+  return (size_t)S * n_mt * kTM * 256 * sizeof(float);
 }
 
 bool launch_gemm_pair_f32(const void* A, int M, int K, long lda, const void* B1, int N1,
@@ -559,14 +564,17 @@ bool launch_gemm_pair_f32(const void* A, int M, int K, long lda, const void* B1,
   g.n_nt = g.n_nt1 + (N2 + 255) / 256;
   g.n_mt = (M + kTM - 1) / kTM;
   g.m_per = g.n_mt / 8;
-  g.S = g.n_nt - 1;
   g.nk = K / kTK;
-  // the whole tiles must take exactly one round of the CUs (8 row groups of
-  // m_per row tiles, one per XCD), the split parts at least two k stages each
-  if (g.n_mt % 8 != 0 || g.S < 2 || 8 * g.m_per * g.S != num_cus || g.nk < 2 * g.S ||
-      scratch_bytes < gemm_pair_scratch_bytes(M, N1, N2))
+  // the split parts fill the CUs once (8 row groups of m_per row tiles, one
+  // per XCD, S parts each), the whole tiles a whole number of times, and
+  // every part gets at least two k stages
+  if (g.n_mt % 8 != 0 || num_cus % g.n_mt != 0) return false;
+  g.S = num_cus / g.n_mt;
+  const long whole = (long)g.n_mt * (g.n_nt - 1);
+  if (g.S < 2 || g.n_nt < 2 || whole % num_cus != 0 || g.nk < 2 * g.S ||
+      scratch_bytes < gemm_pair_scratch_bytes(M, N1, N2, num_cus))
     return false;
-  gemm_pair_kernel<<<8 * g.m_per * 2 * g.S, kTThreads, 0, st>>>(g);
+  gemm_pair_kernel<<<8 * g.m_per * (g.n_nt - 1 + g.S), kTThreads, 0, st>>>(g);
   const long chunks = (long)g.n_mt * kTM * 64;
   gemm_pair_reduce_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(g);
   return true;

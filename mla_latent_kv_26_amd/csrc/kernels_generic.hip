@@ -52,26 +52,6 @@ void launch_gate_mul_f32(float* g, const float* h, long n, hipStream_t st) {
   gate_mul_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, h, n);
 }
 
-// bf16: 8 values per thread (16-byte loads and stores), float32 math; n a
-// multiple of 8, 16-byte aligned arrays.
-__global__ void __launch_bounds__(256) gate_mul_bf16_kernel(bf16x8* __restrict__ g,
-                                                            const bf16x8* __restrict__ h, long n8) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const bf16x8 gv = g[i], hv = h[i];
-  bf16x8 o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)hv[e] * sigmoid_f((float)gv[e]));
-  g[i] = o;
-}
-
-void launch_gate_mul_bf16(void* g, const void* h, long n, hipStream_t st) {
-  if (n <= 0) return;
-  const long n8 = n / 8;
-  gate_mul_bf16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((bf16x8*)g,
-                                                                    (const bf16x8*)h, n8);
-}
-
 // ---------------------------------------------------------------------------
 // Block-wide sum over 256 threads.
 // ---------------------------------------------------------------------------

@@ -55,17 +55,6 @@ void launch_attention_f32(const float* q_full, const float* pool, const int* blo
 
 // g[i] = h[i] * sigmoid(g[i]) for i < n (float32 output gate).
 void launch_gate_mul_f32(float* g, const float* h, long n, hipStream_t st);
-// The same in bf16 (float32 math), n a multiple of 8, 16-byte aligned arrays.
-void launch_gate_mul_bf16(void* g, const void* h, long n, hipStream_t st);
-
-// Row-major C [M, N] = alpha A [M, K] B through hipBLASLt (blas_lt.cpp): A
-// bf16 (row stride lda), B bf16 row-major [K, N] or, when b_transposed,
-// [N, K] (row stride ldb), C bf16 or float32 (row stride ldc), float32
-// accumulation.  Returns false, having launched nothing, when the library is
-// unavailable or switched off (MLA_GEMM=tile), the shape is small (M < 256,
-// N < 128 or K < 32) or it has no algorithm for it.
-bool blas_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
-                    long ldc, float alpha, bool c_f32, bool b_transposed, hipStream_t st);
 
 // ---- bf16 MFMA kernels (gfx950) ----
 
@@ -86,13 +75,15 @@ void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, in
                          int c_f32, bool b_transposed, hipStream_t st, int nb = 0, long sBn = 0,
                          const void* gmul = nullptr);
 // Two float32 GEMMs that share A, C1 = alpha A B1 ([M, N1]) and C2 = alpha
-// A B2 ([M, N2]), B row-major, as one launch that fills the CUs when their
-// whole tiles make exactly one round (the last column tile split along k
-// into partial tiles in `scratch`, gemm_pair_scratch_bytes of it, added in a
-// fixed order by a second launch).  Returns false, having launched nothing,
-// for other shapes (N1 a multiple of 256, M a multiple of 2048, K of 32,
-// 16-byte rows) or a smaller scratch.
-size_t gemm_pair_scratch_bytes(int M, int N1, int N2);
+// A B2 ([M, N2]), B row-major, as one launch: the whole column tiles one per
+// workgroup, the last column tile of each row tile split along k into
+// num_cus / row-tiles parts (partial tiles in `scratch`,
+// gemm_pair_scratch_bytes of it, added in a fixed order by a second launch).
+// Returns false, having launched nothing, unless the split parts fill the
+// CUs once and the whole tiles a whole number of times (N1 a multiple of
+// 256, M a multiple of 2048, K of 32, 16-byte rows), or when the scratch is
+// smaller.
+size_t gemm_pair_scratch_bytes(int M, int N1, int N2, int num_cus);
 bool launch_gemm_pair_f32(const void* A, int M, int K, long lda, const void* B1, int N1,
                           long ldb1, float* C1, long ldc1, const void* B2, int N2, long ldb2,
                           float* C2, long ldc2, float alpha, int num_cus, void* scratch,

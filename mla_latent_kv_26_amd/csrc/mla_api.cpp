@@ -33,6 +33,8 @@ struct Dims {
   bool fp8;          // FP8 cache rows
   size_t row_bytes;  // bytes per cache row
   int G, gs;         // W_UK / W_UV matrices, heads per matrix
+  int split_wg;      // requested decode workgroups per head group (0: one per CU)
+  int prefill_form;  // 0 fewer FLOPs, 1 latent rows, 2 per-head keys and values
 };
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -77,6 +79,13 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
   if (c->kv_groups < 0 || (c->kv_groups > 0 && c->num_heads % c->kv_groups))
     return fail(MLA_ERR_INVALID_ARG, "kv_groups (%d) must be 0 or divide num_heads (%d)",
                 c->kv_groups, c->num_heads);
+  if (c->split_workgroups < 0 || c->split_workgroups > 8192 || c->split_workgroups % 8)
+    return fail(MLA_ERR_INVALID_ARG,
+                "split_workgroups (%d) must be 0 or a multiple of 8 up to 8192",
+                c->split_workgroups);
+  if (c->prefill_attention < 0 || c->prefill_attention > 2)
+    return fail(MLA_ERR_INVALID_ARG, "prefill_attention (%d) must be 0, 1 or 2",
+                c->prefill_attention);
   if (d) {
     d->H = c->num_heads;
     d->R = c->kv_lora_rank;
@@ -98,6 +107,8 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
     d->row_bytes = d->fp8 ? (size_t)d->R + 2 * (size_t)d->Dr + 16 : (size_t)d->W * d->esz;
     d->G = c->kv_groups > 0 ? c->kv_groups : d->H;
     d->gs = d->H / d->G;
+    d->split_wg = c->split_workgroups;
+    d->prefill_form = c->prefill_attention;
   }
   return MLA_OK;
 }
@@ -172,7 +183,7 @@ DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
     const int cus = num_cus();
     w.heads = mla::decode_heads_per_wg(d.H, batch, max_seq_len, cus);
     w.hgc = d.H / w.heads;
-    w.n_wg = mla::decode_num_wg(w.hgc, cus);
+    w.n_wg = d.split_wg > 0 ? d.split_wg : mla::decode_num_wg(w.hgc, cus);
     const size_t slots = mla::decode_partial_slots(batch, w.n_wg);
     w.prefix = off;
     off = up256(off + (size_t)(batch + 1) * 4);
@@ -206,8 +217,8 @@ bool prefill_naive_shapes(const Dims& d) {
 // An FP8 cache always takes the naive path: its gather widens the stored
 // rows to bf16, and everything after it is the bf16 path.
 bool prefill_naive(const Dims& d, int q_len, int max_start_pos) {
-  if (!prefill_naive_shapes(d)) return false;
-  if (d.fp8) return true;
+  if (!prefill_naive_shapes(d) || d.prefill_form == 1) return false;
+  if (d.fp8 || d.prefill_form == 2) return true;
   const double T = q_len, S = max_start_pos;
   const double pairs = T * (S + (T + 1) / 2);
   const double latent = (2.0 * d.R + d.Dr) * pairs;
@@ -733,6 +744,19 @@ mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t batch, int3
   return MLA_OK;
 }
 
+mla_status mla_prefill_attention_form(const mla_config* cfg, int32_t q_len, int32_t max_start_pos,
+                                      int32_t* form) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_cfg(cfg, &d);
+  if (s != MLA_OK) return s;
+  if (q_len <= 0 || max_start_pos < 0)
+    return fail(MLA_ERR_INVALID_ARG, "q_len must be positive and max_start_pos >= 0");
+  if (!form) return fail(MLA_ERR_INVALID_ARG, "form is NULL");
+  *form = prefill_naive(d, q_len, max_start_pos) ? 2 : 1;
+  return MLA_OK;
+}
+
 mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, const void* w_dq,
                        const float* q_norm_w, const void* w_uq, const void* w_dkv,
                        const float* kv_norm_w, const void* w_uk, const void* w_uv,
@@ -753,6 +777,14 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   if (d.fp8 && !prefill_naive_shapes(d))
     return fail(MLA_ERR_UNSUPPORTED,
                 "prefill over an FP8 cache needs bf16 with kv_lora_rank 512, rope_dim 64 and "
+                "qk_nope_dim = v_dim = 128");
+  if (d.fp8 && d.prefill_form == 1)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "prefill over an FP8 cache runs through per-head keys and values (prefill_attention "
+                "0 or 2)");
+  if (d.prefill_form == 2 && !prefill_naive_shapes(d))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "per-head prefill attention needs bf16 with kv_lora_rank 512, rope_dim 64 and "
                 "qk_nope_dim = v_dim = 128");
   if (batch <= 0 || q_len <= 0)
     return fail(MLA_ERR_INVALID_ARG, "batch and q_len must be positive (got %d, %d)", batch, q_len);
@@ -799,22 +831,18 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   //    both read x, and together they fill the CUs)
   float* z = (float*)at(workspace, w.z);
   float* cq32 = d.Rq > 0 ? (float*)at(workspace, w.cq32) : nullptr;
-  // x W_DQ by the library GEMM when it takes the shape; otherwise, when the
-  // shapes allow, x W_DQ and x W_DKV as one launch of the tile kernel (the
-  // query buffer, not yet written, holds its split partial tiles)
-  const bool lib_q = d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
-                     mla::blas_gemm_bf16(x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 1.0f,
-                                         true, false, st);
+  // with a q rank, x W_DQ and x W_DKV as one launch of the tile kernel when
+  // the shapes allow (the query buffer, not yet written, holds its split
+  // partial tiles); otherwise two launches
   const bool paired =
-      !lib_q && d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
+      d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
       mla::launch_gemm_pair_f32(x, (int)n, d.M, d.M, w_dq, d.Rq, d.Rq, cq32, d.Rq, w_dkv, d.W,
                                 d.W, z, d.W, 1.0f, num_cus(), at(workspace, w.q),
                                 (size_t)n * d.H * (d.Dn + d.Dr) * d.esz, st);
   void* cq = d.Rq > 0 ? at(workspace, w.cq) : nullptr;
-  const bool have_cq = lib_q || paired;
-  if (have_cq)  // normalise c_q while it is still in the cache
+  if (paired)  // normalise c_q while it is still in the cache
     mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
-  if (!paired)
+  else
     gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
   mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
                                 max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
@@ -822,7 +850,7 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   // 2. queries
   void* q = at(workspace, w.q);
   if (d.Rq > 0) {
-    if (!have_cq) {
+    if (!paired) {
       gemm(d, x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 0, 0, 0, 1, 1.0f, true, st);
       mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
     }

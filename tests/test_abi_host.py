@@ -36,7 +36,7 @@ def test_every_header_symbol_is_exported_and_bound():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.mla_abi_version() == 3
+    assert lib.mla_abi_version() == 4
     for s, name in _lib.STATUS_NAMES.items():
         assert lib.mla_status_string(s).decode() == name
 
@@ -61,7 +61,8 @@ def test_rope_table_matches_oracle_angles():
 @pytest.mark.parametrize("field,value", [
     ("num_heads", 0), ("kv_lora_rank", -1), ("rope_dim", 63), ("qk_nope_dim", 0), ("v_dim", 0),
     ("block_size", 0), ("softmax_scale", -1.0), ("rms_eps", -1e-6), ("rope_theta", 0.0),
-    ("d_model", -5)])
+    ("d_model", -5), ("split_workgroups", -8), ("split_workgroups", 12),
+    ("split_workgroups", 8200)])
 def test_invalid_config_rejected(field, value):
     import dataclasses
     bad = dataclasses.replace(KIMI, **{field: value})
@@ -69,6 +70,16 @@ def test_invalid_config_rejected(field, value):
         m.mla_validate_config(bad)
     assert e.value.status == _lib.MLA_ERR_INVALID_ARG
     assert _lib.last_error()
+
+
+def test_split_workgroups_sizes_the_workspace():
+    """The decode workspace holds one partial per (workgroup, sequence) slot:
+    more split workgroups need more of it; 0 is the library's own choice."""
+    import dataclasses
+    sizes = [m.mla_decode_workspace_size(dataclasses.replace(KIMI, split_workgroups=n), 32, 4096)
+             for n in (8, 64, 512)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    m.mla_validate_config(dataclasses.replace(KIMI, split_workgroups=8192))
 
 
 def test_latent_ranks_must_be_below_model_width():

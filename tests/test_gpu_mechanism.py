@@ -111,6 +111,26 @@ def test_shared_weights_on_the_tuned_kernels(m):
     check(m, cfg, [1, 64, 65, 1000, 4097])
 
 
+def test_shared_weights_many_rows_r512(m):
+    """kv_groups with more than 32 rows: 64 heads sharing 8 matrices at
+    kv_lora_rank 512 over 72 sequences, so the absorption and the W_UV product
+    run as per-group batched GEMMs (batch stride 0 on the shared matrix) with
+    the scaled q_rope copy as its own pass."""
+    cfg = dict(workloads.WORKLOADS["paged_ragged_h128_b64"], num_heads=64, kv_groups=8,
+               lengths="explicit", seed=75)
+    rng = np.random.default_rng(75)
+    check(m, cfg, rng.integers(1, 1500, size=72), sample=[0, 1, 35, 70, 71])
+
+
+def test_shared_weights_many_rows_narrow(m):
+    """The mechanism widths (16 heads, 4 shared matrices, latent 256) over 64
+    sequences: per-group GEMMs instead of the small-row kernels."""
+    cfg = dict(workloads.WORKLOADS["mechanism_h16_g4_r256_l512"], lengths="explicit",
+               paged=True, seed=76)
+    rng = np.random.default_rng(76)
+    check(m, cfg, rng.integers(1, 1200, size=64))
+
+
 def test_staged_calls_refuse_what_they_lack(m):
     """Split partials exist for the 512-wide kernels only, and their merge
     applies per-head W_UV only: both refuse before any launch."""

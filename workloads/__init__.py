@@ -67,6 +67,11 @@ WORKLOADS["longctx_h64_b4_l131072_fp8"] = dict(WORKLOADS["longctx_h64_b4_l131072
                                                cache_dtype="fp8")
 WORKLOADS["prefill_d7168_b2_t4096_fp8"] = dict(WORKLOADS["prefill_d7168_b2_t4096"],
                                                cache_dtype="fp8")
+# The prefill workload with its attention forced onto the latent rows (the
+# absorbed form; the default takes whichever form needs fewer FLOPs, at this
+# size the per-head keys and values).
+WORKLOADS["prefill_d7168_b2_t4096_absorbed"] = dict(WORKLOADS["prefill_d7168_b2_t4096"],
+                                                    prefill_attention="latent")
 # The tutorial's mechanism experiment widths ("ARCH-MLA. Multihead Latent
 # Attention", 5.1): 16 query heads sharing 4 W_UK / W_UV matrices, head
 # width 64, latent 256, rope 64, bf16; one sequence per history length
