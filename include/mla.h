@@ -173,6 +173,26 @@ mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_r
                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* mla_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and arguments without the workspace, which
+ * here is a device array inside the library's code object, one per GPU,
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB) large, held from the first call on that
+ * GPU until the process ends.  The call allocates nothing.  A call whose
+ * workspace (mla_decode_workspace_size) would exceed that size returns
+ * MLA_ERR_WORKSPACE before anything is enqueued: at H = 64 up to about 250
+ * sequences of any length fit, at H = 128 about 100.  Every call on one GPU
+ * uses the same array and leaves its contents behind; no call needs it
+ * cleared (a call reads only what it wrote).  Calls that may overlap on one
+ * GPU (different streams, or host threads without ordering) race on it:
+ * order them on one stream. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                              const void* w_uk, const void* w_uv, const void* kv_pool,
+                              int32_t num_blocks, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                              int32_t max_seq_len, void* out, void* stream);
+
 /* Stage 1 of decode: query absorption (modeldna "MLA" module, "Under the
  * hood": W_UK absorbed into the query).  For n_rows query rows:
  *   q_full[n, h, 0:R]    = scale * log2(e) * q_nope[n, h, :] W_UK[h]

@@ -8,6 +8,7 @@ from ._lib import MLAError, LIB_PATH  # noqa: F401  (raises ImportError if not b
 from .api import (  # noqa: F401
     MLAConfig, mla_abi_version, mla_validate_config, mla_cache_row_elems,
     mla_cache_bytes_per_token, mla_rope_table, mla_decode_workspace_size, mla_decode,
+    mla_decode_noalloc,
     mla_absorb_query, mla_latent_attention, mla_attention_partials, mla_combine_output,
     mla_output_projection,
     mla_cache_append_workspace_size, mla_cache_append, mla_prefill_workspace_size, mla_prefill_attention_form, mla_prefill,

@@ -83,6 +83,7 @@ SIGNATURES = {
     "mla_rope_table": (_I, [_CFG, _I, ctypes.POINTER(ctypes.c_float)]),
     "mla_decode_workspace_size": (_I, [_CFG, _I, _I, ctypes.POINTER(_SZ)]),
     "mla_decode": (_I, [_CFG, _P, _P, _P, _P, _P, _I, _IP, _I, _IP, _I, _I, _P, _P, _SZ, _P]),
+    "mla_decode_noalloc": (_I, [_CFG, _P, _P, _P, _P, _P, _I, _IP, _I, _IP, _I, _I, _P, _P]),
     "mla_absorb_query": (_I, [_CFG, _P, _P, _P, _I, _P, _P]),
     "mla_latent_attention": (_I, [_CFG, _P, _P, _I, _IP, _I, _IP, _I, _I, _P, _P, _SZ, _P]),
     "mla_attention_partials": (_I, [_CFG, _P, _P, _I, _IP, _I, _IP, _I, _I, _P, _SZ, _P]),

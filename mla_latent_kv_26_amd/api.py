@@ -226,6 +226,26 @@ def mla_decode(cfg: MLAConfig, q_nope, q_rope, w_uk, w_uv, kv_pool, block_table,
     return out
 
 
+def mla_decode_noalloc(cfg: MLAConfig, q_nope, q_rope, w_uk, w_uv, kv_pool, block_table,
+                       seq_lens, max_seq_len: int, out, stream=None) -> torch.Tensor:
+    """mla_decode without a workspace (see mla_decode_noalloc in
+    include/mla.h): out [B, H, Dv] must be given."""
+    dt = cfg.torch_dtype
+    B, H = q_nope.shape[0], cfg.num_heads
+    _dev(q_nope, "q_nope", dt, (B, H, cfg.qk_nope_dim))
+    _dev(q_rope, "q_rope", dt, (B, H, cfg.rope_dim))
+    _dev(w_uk, "w_uk", dt, (cfg.uk_heads, cfg.qk_nope_dim, cfg.kv_lora_rank))
+    _dev(w_uv, "w_uv", dt, (cfg.uk_heads, cfg.kv_lora_rank, cfg.v_dim))
+    nb, mb = _pool_args(cfg, kv_pool, block_table, B)
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    _dev(out, "out", dt, (B, H, cfg.v_dim))
+    check(lib.mla_decode_noalloc(_ref(cfg), q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(),
+                                 w_uv.data_ptr(), kv_pool.data_ptr(), nb, block_table.data_ptr(),
+                                 mb, seq_lens.data_ptr(), B, int(max_seq_len), out.data_ptr(),
+                                 _stream(stream)), "mla_decode_noalloc")
+    return out
+
+
 def mla_absorb_query(cfg: MLAConfig, q_nope, q_rope, w_uk, q_full=None, stream=None):
     """q_full [n, H, R + Dr] = scale*log2(e)*[q_nope W_UK | q_rope]."""
     dt = cfg.torch_dtype

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -484,6 +485,34 @@ static mla_status enqueue_latent(const Dims& d, const void* q_full, const void* 
   return MLA_OK;
 }
 
+// Validation shared by mla_decode and mla_decode_noalloc (everything but
+// the workspace); fills *d.
+static mla_status check_decode_call(const mla_config* cfg, Dims* d, const void* q_nope,
+                                    const void* q_rope, const void* w_uk, const void* w_uv,
+                                    const void* kv_pool, int32_t num_blocks,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                    void* out) {
+  mla_status s = check_cfg(cfg, d);
+  if (s != MLA_OK) return s;
+  s = check_decode_common(*d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                          max_seq_len);
+  if (s != MLA_OK) return s;
+  return check_ptrs16(*d, {q_nope, q_rope, w_uk, w_uv, out}, "q_nope, q_rope, w_uk, w_uv, out");
+}
+
+static void enqueue_decode(const Dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
+                           const void* w_uv, const void* kv_pool, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
+                           void* workspace, hipStream_t st) {
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
+  void* q_full = at(workspace, w.q_full);
+  enqueue_absorb(d, q_nope, q_rope, w_uk, batch, q_full, st);
+  enqueue_latent(d, q_full, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                 max_seq_len, w_uv, out, workspace, st);
+}
+
 mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_rope,
                       const void* w_uk, const void* w_uv, const void* kv_pool, int32_t num_blocks,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -491,23 +520,18 @@ mla_status mla_decode(const mla_config* cfg, const void* q_nope, const void* q_r
                       void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   g_err.clear();
-  mla_status s = check_cfg(cfg, &d);
-  if (s != MLA_OK) return s;
-  s = check_decode_common(d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
-                          max_seq_len);
-  if (s != MLA_OK) return s;
-  s = check_ptrs16(d, {q_nope, q_rope, w_uk, w_uv, out}, "q_nope, q_rope, w_uk, w_uv, out");
+  mla_status s = check_decode_call(cfg, &d, q_nope, q_rope, w_uk, w_uv, kv_pool, num_blocks,
+                                   block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                                   out);
   if (s != MLA_OK) return s;
   const DecodeWs w = decode_ws(d, batch, max_seq_len);
   if (!workspace || workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", w.total, workspace_bytes,
                 workspace ? "" : ", NULL");
   if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
-  void* q_full = at(workspace, w.q_full);
-  enqueue_absorb(d, q_nope, q_rope, w_uk, batch, q_full, st);
-  enqueue_latent(d, q_full, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
-                 w_uv, out, workspace, st);
+  enqueue_decode(d, q_nope, q_rope, w_uk, w_uv, kv_pool, num_blocks, block_table,
+                 max_blocks_per_seq, seq_lens, batch, max_seq_len, out, workspace,
+                 (hipStream_t)stream);
   return launched("mla_decode");
 }
 
@@ -912,6 +936,70 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   gemm(d, o_lat, w_uv, out, (int)n, d.Dv, d.R, (long)d.H * d.R, d.Dv, (long)d.H * d.Dv, d.R,
        (long)d.R * d.Dv, d.Dv, d.H, 1.0f, false, st);
   return launched("mla_prefill");
+}
+
+// ---------------------------------------------------------------------------
+// Decode for callers that cannot allocate.  The workspace lives in `scratch`,
+// one array per GPU in the code object's device memory (held until the
+// process ends); host code reaches it only through the address
+// hipGetSymbolAddress returns on that device.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// The current device's address of `scratch`, looked up on its first use on
+// that device (with the device current) and kept.
+mla_status scratch_on_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MLA_ERR_UNSUPPORTED, "device index %d above 63", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_noalloc(const mla_config* cfg, const void* q_nope, const void* q_rope,
+                              const void* w_uk, const void* w_uv, const void* kv_pool,
+                              int32_t num_blocks, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                              int32_t max_seq_len, void* out, void* stream) {
+  Dims d;
+  g_err.clear();
+  mla_status s = check_decode_call(cfg, &d, q_nope, q_rope, w_uk, w_uv, kv_pool, num_blocks,
+                                   block_table, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                                   out);
+  if (s != MLA_OK) return s;
+  const DecodeWs w = decode_ws(d, batch, max_seq_len);
+  if (w.total > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE,
+                "this decode needs %zu bytes of scratch; mla_decode_noalloc has %zu (call "
+                "mla_decode with a workspace instead)",
+                w.total, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  s = scratch_on_device(&ws);
+  if (s != MLA_OK) return s;
+  enqueue_decode(d, q_nope, q_rope, w_uk, w_uv, kv_pool, num_blocks, block_table,
+                 max_blocks_per_seq, seq_lens, batch, max_seq_len, out, ws, (hipStream_t)stream);
+  return launched("mla_decode_noalloc");
 }
 
 }  // extern "C"
