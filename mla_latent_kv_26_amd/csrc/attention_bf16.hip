@@ -356,27 +356,40 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
     const uint32_t buf = tile_buf<kFp8>(lds, k);
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
-      auto frag = [&](int ks, int tb) {
-        return lds_read_b128(buf + ((ks & 1) ? s_odd : s_even) +
-                             (uint32_t)((ks >> 1) * 128 + tb * 16 * kCh * 16));
-      };
-      // Fragments are read kSAhead steps ahead of their MFMAs; the
-      // scheduling barriers keep the compiler from sinking the reads next
-      // to their uses (it otherwise waits for every pair in turn, and the
-      // loop runs at LDS latency instead of MFMA rate).
+      // Fragments (ks, tb = 0 and 1) are read kSAhead steps ahead of their
+      // MFMAs, from inline assembly without a wait, and each pair is
+      // completed by a wait that allows the later pairs to stay in flight
+      // (LDS reads complete in order) and names its registers.  Reads the
+      // compiler issues itself are completed by full drains of the LDS
+      // queue, which expose the whole read latency several times a tile.
+      // The scheduling barriers keep each step's reads, wait and MFMAs in
+      // this order.
       constexpr int NK = kW / 32;
+      const uint32_t be = buf + s_even, bo = buf + s_odd;
+      auto issue = [&](int ks, bf16x8(&f)[2]) {
+        const uint32_t ad = ((ks & 1) ? bo : be) + (uint32_t)((ks >> 1) * 128);
+        ds_b128_nowait<0>(f[0], ad);
+        ds_b128_nowait<16 * kCh * 16>(f[1], ad);
+      };
+      // waits until at most 2 * later LDS reads of this wave are pending
+      auto settle = [&](bf16x8(&f)[2], int later) {
+        switch (later) {
+          case 0: lds_settle<0>(f[0], f[1]); break;
+          case 1: lds_settle<2>(f[0], f[1]); break;
+          case 2: lds_settle<4>(f[0], f[1]); break;
+          case 3: lds_settle<6>(f[0], f[1]); break;
+          default: lds_settle<8>(f[0], f[1]); break;
+        }
+      };
+      static_assert(kSAhead <= 4, "lgkmcnt range of the settle switch");
       bf16x8 fr[kSAhead + 1][2];
 #pragma unroll
-      for (int i = 0; i < kSAhead; ++i) {
-        fr[i][0] = frag(i, 0);
-        fr[i][1] = frag(i, 1);
-      }
+      for (int i = 0; i < kSAhead; ++i) issue(i, fr[i]);
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        if (ks + kSAhead < NK) {
-          fr[(ks + kSAhead) % (kSAhead + 1)][0] = frag(ks + kSAhead, 0);
-          fr[(ks + kSAhead) % (kSAhead + 1)][1] = frag(ks + kSAhead, 1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + kSAhead < NK) issue(ks + kSAhead, fr[(ks + kSAhead) % (kSAhead + 1)]);
+        settle(fr[ks % (kSAhead + 1)], min(kSAhead, NK - 1 - ks));
         __builtin_amdgcn_sched_barrier(0);
         sacc[0] = mfma16(fr[ks % (kSAhead + 1)][0], qf[ks], sacc[0]);
         sacc[1] = mfma16(fr[ks % (kSAhead + 1)][1], qf[ks], sacc[1]);

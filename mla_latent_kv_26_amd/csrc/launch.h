@@ -74,20 +74,24 @@ void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, in
                          long ldb, long ldc, long sA, long sB, long sC, int batch, float alpha,
                          int c_f32, bool b_transposed, hipStream_t st, int nb = 0, long sBn = 0,
                          const void* gmul = nullptr);
-// Two float32 GEMMs that share A, C1 = alpha A B1 ([M, N1]) and C2 = alpha
-// A B2 ([M, N2]), B row-major, as one launch: the whole column tiles one per
-// workgroup, the last column tile of each row tile split along k into
-// num_cus / row-tiles parts (partial tiles in `scratch`,
-// gemm_pair_scratch_bytes of it, added in a fixed order by a second launch).
-// Returns false, having launched nothing, unless the split parts fill the
-// CUs once and the whole tiles a whole number of times (N1 a multiple of
-// 256, M a multiple of 2048, K of 32, 16-byte rows), or when the scratch is
-// smaller.
-size_t gemm_pair_scratch_bytes(int M, int N1, int N2, int num_cus);
-bool launch_gemm_pair_f32(const void* A, int M, int K, long lda, const void* B1, int N1,
-                          long ldb1, float* C1, long ldc1, const void* B2, int N2, long ldb2,
-                          float* C2, long ldc2, float alpha, int num_cus, void* scratch,
-                          size_t scratch_bytes, hipStream_t st);
+// Cache append fused into the down-projection (append_gemm.hip), bf16 with
+// R = 512, Dr = 64: rows of z = x W_DKV ([n, K] x [K, 576]) are normalised
+// (RMSNorm on the latent with gain, eps), the rope key rotated by the table
+// row of its position, and stored to the pool in bf16 or as FP8 rows,
+// without z leaving the CU.  append_gemm: token t has position pos[t] and
+// slot slot[t] (negative: skipped).  project_append: token t = b T + i of a
+// prefill sits at start_pos[b] + i through the page table; when w_q is set,
+// the same launch also computes c = x w_q (float32 [n, N], row stride ldc,
+// w_q [K, N] row-major, ldb; n >= 256, N >= 128 and a multiple of 8).
+bool append_gemm_fits(int R, int Dr, int K, long ldx);
+void launch_append_gemm(const void* x, long ldx, int n, int K, const void* w_dkv,
+                        const float* gain, const float* rope, const int* pos, const int* slot,
+                        void* pool, bool fp8, float eps, hipStream_t st);
+void launch_project_append(const void* x, long ldx, int batch, int T, int K, const void* w_dkv,
+                           const float* gain, const float* rope, const int* start_pos,
+                           const int* block_table, int max_blocks, int block_size, void* pool,
+                           bool fp8, float eps, const void* w_q, int N, long ldb, float* c,
+                           long ldc, hipStream_t st);
 // Gated GEMM (bf16 out, batch 1): C = gmul * sigmoid(alpha A B), gmul [M, N]
 // laid out as C (row stride ldc).
 void launch_gemm_bf16_gated(const void* A, const void* B, void* C, int M, int N, int K, long lda,

@@ -715,7 +715,9 @@ mla_status mla_cache_append_workspace_size(const mla_config* cfg, int32_t n_toke
   if (s != MLA_OK) return s;
   if (n_tokens <= 0) return fail(MLA_ERR_INVALID_ARG, "n_tokens must be positive");
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = up256(256 + (size_t)n_tokens * d.W * 4);
+  // the fused down-projection keeps z on chip; the other shapes stage it
+  const bool fused = d.dt == MLA_DTYPE_BF16 && mla::append_gemm_fits(d.R, d.Dr, d.M, d.M);
+  *bytes = fused ? 256 : up256(256 + (size_t)n_tokens * d.W * 4);
   return MLA_OK;
 }
 
@@ -746,6 +748,12 @@ mla_status mla_cache_append(const mla_config* cfg, const void* x, const void* w_
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if (!al16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
+  if (d.dt == MLA_DTYPE_BF16 && mla::append_gemm_fits(d.R, d.Dr, d.M, d.M)) {
+    // down-projection, RMSNorm, RoPE and the store in one launch
+    mla::launch_append_gemm(x, d.M, n_tokens, d.M, w_dkv, kv_norm_w, rope_table, positions,
+                            slot_mapping, kv_pool, d.fp8, d.eps, st);
+    return launched("mla_cache_append");
+  }
   float* z = (float*)at(workspace, 256);
   gemm(d, x, w_dkv, z, n_tokens, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
   mla::launch_append_rows(z, d.W, kv_norm_w, rope_table, positions, slot_mapping, kv_pool, n_tokens,
@@ -851,33 +859,30 @@ mla_status mla_prefill(const mla_config* cfg, const void* x, const void* w_q, co
   hipStream_t st = (hipStream_t)stream;
   const int QW = d.H * (d.Dn + d.Dr);
   const float alpha = d.scale * 1.4426950408889634f;
-  // 1. cache rows (with a q rank, x W_DQ goes in the same launch as x W_DKV:
-  //    both read x, and together they fill the CUs)
-  float* z = (float*)at(workspace, w.z);
+  // 1. cache rows: the down-projection with the RMSNorm, RoPE and store in
+  //    its epilogue (bf16, R = 512, Dr = 64); with a q rank, x W_DQ goes in
+  //    the same launch (both read x, and together they fill the CUs)
   float* cq32 = d.Rq > 0 ? (float*)at(workspace, w.cq32) : nullptr;
-  // with a q rank, x W_DQ and x W_DKV as one launch of the tile kernel when
-  // the shapes allow (the query buffer, not yet written, holds its split
-  // partial tiles); otherwise two launches
-  const bool paired =
-      d.Rq > 0 && d.dt == MLA_DTYPE_BF16 &&
-      mla::launch_gemm_pair_f32(x, (int)n, d.M, d.M, w_dq, d.Rq, d.Rq, cq32, d.Rq, w_dkv, d.W,
-                                d.W, z, d.W, 1.0f, num_cus(), at(workspace, w.q),
-                                (size_t)n * d.H * (d.Dn + d.Dr) * d.esz, st);
   void* cq = d.Rq > 0 ? at(workspace, w.cq) : nullptr;
-  if (paired)  // normalise c_q while it is still in the cache
-    mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
-  else
+  bool have_cq = false;
+  if (d.dt == MLA_DTYPE_BF16 && mla::append_gemm_fits(d.R, d.Dr, d.M, d.M)) {
+    have_cq = d.Rq > 0 && mla::gemm_tile256_fits((int)n, d.Rq, d.M, d.M, d.Rq, d.Rq);
+    mla::launch_project_append(x, d.M, batch, q_len, d.M, w_dkv, kv_norm_w, rope_table, start_pos,
+                               block_table, max_blocks_per_seq, d.bs, kv_pool, d.fp8, d.eps,
+                               have_cq ? w_dq : nullptr, d.Rq, d.Rq, cq32, d.Rq, st);
+  } else {
+    float* z = (float*)at(workspace, w.z);
     gemm(d, x, w_dkv, z, (int)n, d.W, d.M, d.M, d.W, d.W, 0, 0, 0, 1, 1.0f, true, st);
-  mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
-                                max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
-                                d.fp8 ? 2 : d.dt, st);
+    mla::launch_append_rows_paged(z, d.W, kv_norm_w, rope_table, start_pos, block_table,
+                                  max_blocks_per_seq, d.bs, kv_pool, batch, q_len, d.R, d.Dr, d.eps,
+                                  d.fp8 ? 2 : d.dt, st);
+  }
   // 2. queries
   void* q = at(workspace, w.q);
   if (d.Rq > 0) {
-    if (!paired) {
+    if (!have_cq)
       gemm(d, x, w_dq, cq32, (int)n, d.Rq, d.M, d.M, d.Rq, d.Rq, 0, 0, 0, 1, 1.0f, true, st);
-      mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
-    }
+    mla::launch_rms_norm_rows(cq32, d.Rq, q_norm_w, cq, d.Rq, (int)n, d.Rq, d.eps, d.dt, st);
     gemm(d, cq, w_uq, q, (int)n, QW, d.Rq, d.Rq, QW, QW, 0, 0, 0, 1, 1.0f, false, st);
   } else {
     gemm(d, x, w_q, q, (int)n, QW, d.M, d.M, QW, QW, 0, 0, 0, 1, 1.0f, false, st);

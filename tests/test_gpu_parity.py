@@ -351,18 +351,57 @@ def _pool_rows(pool_np, table, L):
     return pool_np[table[j // bs], j % bs]
 
 
+def bf16_ulp(v):
+    """Spacing of bf16 numbers at |v| (8 significant bits): 2^(e - 7) for
+    |v| in [2^e, 2^(e+1))."""
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
 def check_rows(got, ref, what):
     """Stored bf16 rows: each element within one bf16 step of the oracle's
-    stored value (2^-7 relative covers one ulp anywhere in a binade; the two
-    sides round different float32/float64 sums, so a value next to a rounding
-    boundary can land one step apart), or within 1e-4 absolute where the
-    value is near zero (the float32 sum over d_model products carries ~1e-5
-    absolute error before the store); plus the bf16 relative-L2 bar."""
-    bound = np.maximum(2.0 ** -7 * np.abs(ref), 1e-4)
+    stored value (the two sides round different float32/float64 sums, so a
+    value next to a rounding boundary can land one step apart; the step is
+    taken at the larger of the two magnitudes), or within 1e-4 absolute where
+    the value is near zero (the float32 sum over d_model products carries
+    ~1e-5 absolute error before the store); plus the bf16 relative-L2 bar."""
+    bound = np.maximum(bf16_ulp(np.maximum(np.abs(got), np.abs(ref))), 1e-4)
     worst = np.max(np.abs(got - ref) / bound)
     assert worst <= 1.0, f"{what}: worst element at {worst:.2f} of its bound"
     e = assert_bf16(got, ref, what)
     print(what, "exact fraction", float(np.mean(got == ref)), e)
+
+
+@pytest.mark.parametrize("d_model,n", [(7168, 300), (640, 129)])
+def test_cache_append_bf16_rows(m, d_model, n):
+    """mla_cache_append in bf16 (the down-projection with RMSNorm, RoPE and
+    the store fused in one launch): panels of 128 tokens with a ragged last
+    one, permuted slots, every 7th token skipped, jittered gains, positions
+    out of order; every written row within one bf16 step of the oracle,
+    skipped and unused slots untouched."""
+    import torch
+    rng = np.random.default_rng(d_model + n)
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=d_model, q_lora_rank=0)
+    mc = m.MLAConfig.from_dict(cfg)
+    R, Dr, bs = cfg["kv_lora_rank"], cfg["rope_dim"], cfg["block_size"]
+    x = workloads.normal_tensor((n, d_model), seed=d_model + 1)
+    w_dkv = workloads.normal_tensor((d_model, R + Dr), seed=d_model + 2, std=1.0 / np.sqrt(d_model))
+    gain = (1.0 + 0.1 * rng.standard_normal(R)).astype(np.float32)
+    pos = rng.permutation(4 * n)[:n].astype(np.int32)
+    nb = -(-2 * n // bs)
+    slots = rng.permutation(nb * bs)[:n].astype(np.int32)
+    slots[::7] = -1
+    pool = torch.full((nb, bs, R + Dr), 7.0, dtype=torch.bfloat16, device="cuda")
+    m.mla_cache_append(mc, to_dev(x), to_dev(w_dkv), to_dev(gain), to_dev(pos), to_dev(slots),
+                       pool)
+    sync()
+    flat = to_host_f64(pool).reshape(nb * bs, R + Dr)
+    keep = slots >= 0
+    w64 = {"w_dkv": to_f64(w_dkv), "kv_norm_w": gain.astype(np.float64)}
+    ref = oracle.append_rows(to_f64(x)[keep], pos[keep], w64, cfg, storage="bf16")
+    check_rows(flat[slots[keep]], ref, f"append d_model {d_model}")
+    untouched = np.setdiff1d(np.arange(nb * bs), slots[keep])
+    assert np.all(flat[untouched] == 7.0)
 
 
 def test_prefill_small_bf16_with_query_rank_and_continuation(m):
