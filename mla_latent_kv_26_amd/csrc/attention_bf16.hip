@@ -1114,40 +1114,6 @@ __global__ void __launch_bounds__(kCThreads) combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: one workgroup per (query row, head group); whole causal range.
-// Rows are processed longest first.
-// ---------------------------------------------------------------------------
-template <int HEADS>
-__global__ void __launch_bounds__(kThreads, 1) attn_prefill_kernel(
-    const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
-    const int* __restrict__ block_table, int max_blocks, int shift,
-    const int* __restrict__ start_pos, int T_len, int n_rows, int H, bf16* __restrict__ o_lat) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  const uint32_t lds = lds_addr(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hgc = H / HEADS;
-  const int hg = blockIdx.x % hgc;
-  const int r = blockIdx.x / hgc;
-  // longest rows first: t descending, sequences interleaved
-  const int nb = n_rows / T_len;
-  const int t = T_len - 1 - r / nb;
-  const int b = r % nb;
-  const int n = b * T_len + t;
-  const int len = start_pos[b] + t + 1;
-  (void)tid;
-  SegArgs a{q_full + ((long)n * H + hg * HEADS) * kW, pool, block_table + (long)b * max_blocks,
-            max_blocks, shift, len, 0, (len + kTok - 1) / kTok, nullptr, false};
-  bf16* dst = o_lat + ((long)n * H + hg * HEADS) * kR;
-  if (wave < 4) {
-    bf16x8 qf[kW / 32];
-    float m, tot;
-    score_segment<HEADS, false>(a, lds, dst, wave, lane, qf, false, m, tot);
-  } else {
-    pv_segment<HEADS, false>(a, lds, dst, wave, lane);
-  }
-}
-
-// ---------------------------------------------------------------------------
 size_t decode_partial_slots(int batch, int n_wg) { return (size_t)n_wg + (size_t)batch; }
 
 int decode_heads_per_wg(int H, int batch, int max_seq_len, int num_cus) {
@@ -1227,20 +1193,6 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
     wide ? go(combine_kernel<true, 16>, w_uv) : go(combine_kernel<true, 8>, w_uv);
   else
     wide ? go(combine_kernel<false, 16>, nullptr) : go(combine_kernel<false, 8>, nullptr);
-}
-
-void launch_attention_prefill_bf16(const void* q_full, const void* pool, const int* block_table,
-                                   int max_blocks, int block_shift, const int* start_pos, int T,
-                                   int batch, int H, void* o_lat, hipStream_t st) {
-  const int n_rows = batch * T;
-  if (H % 64 == 0)
-    attn_prefill_kernel<64><<<n_rows * (H / 64), kThreads, 0, st>>>(
-        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, start_pos, T,
-        n_rows, H, (bf16*)o_lat);
-  else
-    attn_prefill_kernel<32><<<n_rows * (H / 32), kThreads, 0, st>>>(
-        (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_shift, start_pos, T,
-        n_rows, H, (bf16*)o_lat);
 }
 
 }  // namespace mla

@@ -458,6 +458,74 @@ def test_prefill_per_head_path_with_continuation(m):
         assert_bf16(got[b], ref, f"per-head path b={b}", per_row_axis=0)
 
 
+@pytest.mark.parametrize("heads,t1,t2,bs", [(64, 77, 51, 64), (32, 93, 30, 128), (64, 1, 1, 64)])
+def test_prefill_latent_form_edges(m, heads, t1, t2, bs):
+    """Attention on the latent rows forced: token counts that leave a partial
+    block of query tokens (2 per workgroup at 64 heads, 4 at 32), a
+    continuation whose first position is not on a 32-key tile boundary, and
+    128-row pages; outputs and cache rows of both calls against the oracle."""
+    import torch
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=128,
+               num_heads=heads, block_size=bs, prefill_attention="latent", seed=51 + heads)
+    mc = m.MLAConfig.from_dict(cfg)
+    T = t1 + t2
+    inp = workloads.prefill_inputs(cfg, q_len=T, batch=2, gain_jitter=0.1)
+    w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+    w64 = {k: (None if v is None else to_f64(v)) for k, v in vars(inp.weights).items()}
+    pool = torch.zeros((inp.num_blocks, bs, mc.row), dtype=torch.bfloat16, device="cuda")
+    table = to_dev(inp.block_table)
+    x = to_dev(inp.x)
+    out1 = m.mla_prefill(mc, x[:, :t1].contiguous(), w, pool, table,
+                         torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+    out2 = m.mla_prefill(mc, x[:, t1:].contiguous(), w, pool, table,
+                         torch.full((2,), t1, dtype=torch.int32, device="cuda"), t1)
+    sync()
+    got = np.concatenate([to_host_f64(out1), to_host_f64(out2)], axis=1)
+    pool_np = to_host_f64(pool)
+    for b in range(2):
+        ref, rows = oracle.layer_forward(to_f64(inp.x[b]), w64, cfg, storage="bf16")
+        check_rows(_pool_rows(pool_np, inp.block_table[b], T), rows, f"rows b={b}")
+        assert_bf16(got[b], ref, f"latent form H={heads} b={b}", per_row_axis=0)
+
+
+def test_prefill_latent_form_large_late_score(m):
+    """Token 80's hidden state scaled by 50: its rope key (not normalised)
+    gives later queries scores up to about 150 (log2 units) above the maximum
+    of their first key tile, so weights taken relative to that maximum would
+    overflow; the latent-form kernel then takes those workgroups' key range a
+    second time with the row maxima as references.  Both attention forms run.
+    Scores this large carry absolute errors of about |s| 2^-8 from the bf16
+    queries and rows, so the bound here is rel-L2 <= 1e-2, max abs <= 0.25,
+    cosine >= 0.9999, and the latent form within 25 % of the per-head form's
+    rel-L2 (the per-head kernel rescales its output lazily instead)."""
+    import torch
+    T = 150
+    errs = {}
+    for form in ("latent", "per_head"):
+        cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=640, q_lora_rank=128,
+                   prefill_attention=form, seed=61)
+        mc = m.MLAConfig.from_dict(cfg)
+        inp = workloads.prefill_inputs(cfg, q_len=T, batch=2)
+        xs = to_f64(inp.x)
+        xs[:, 80] *= 50.0
+        x_big = workloads.bf16_bits(xs.astype(np.float32))
+        w = {k: to_dev(v) for k, v in vars(inp.weights).items() if v is not None}
+        w64 = {k: (None if v is None else to_f64(v)) for k, v in vars(inp.weights).items()}
+        pool = torch.zeros((inp.num_blocks, 64, mc.row), dtype=torch.bfloat16, device="cuda")
+        out = m.mla_prefill(mc, to_dev(x_big), w, pool, to_dev(inp.block_table),
+                            torch.zeros(2, dtype=torch.int32, device="cuda"), 0)
+        sync()
+        got = to_host_f64(out)
+        assert np.all(np.isfinite(got)), f"{form}: non-finite output"
+        ref = np.stack([oracle.layer_forward(to_f64(x_big[b]), w64, cfg, storage="bf16")[0]
+                        for b in range(2)])
+        e = errors(got, ref)
+        print("large late score", form, e)
+        assert e["rel_l2"] <= 1e-2 and e["max_abs"] <= 0.25 and e["cosine"] >= 0.9999, (form, e)
+        errs[form] = e["rel_l2"]
+    assert errs["latent"] <= 1.25 * errs["per_head"] + 1e-4, errs
+
+
 @pytest.mark.parametrize("form", ["auto", "latent"])
 def test_prefill_d7168_b2_t4096_full(m, form):
     """Full-size prefill (d_model 7168, q rank 1536, 2 x 4096 new tokens):
