@@ -446,9 +446,66 @@ def main():
             "mfma_frac": round(alg["attn_flops"] / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
     }
+    if cfg.get("kv_groups"):
+        line["forms"] = mechanism_forms(args, torch, m, cfg, mc, sets, max_len, step_ms, alg)
     if not args.no_cpu_baseline and args.workload == workloads.HEADLINE:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def mechanism_forms(args, torch, m, cfg, mc, sets, max_len, latent_ms, alg):
+    """The tutorial's mechanism comparison (5.1, 5.4) between the two forms
+    of the same decode step: attention on the latent rows (absorbed) and
+    through per-head keys and values rebuilt from them for the step
+    (reconstruction).  Per form: time per step (graph replay, median), the
+    bytes of rebuilt keys and values, the workspace the form needs (the
+    library allocates nothing else) and the peak memory torch saw while one
+    step ran; the outputs' cosine against each other (the cosine of each
+    against the oracle is printed by the parity tests)."""
+    import dataclasses
+    dev = torch.device("cuda", 0)
+    B, H = len(sets[0]["seq_lens"]), cfg["num_heads"]
+    G = cfg.get("kv_groups") or H
+    tokens = alg["tokens"]
+    rec = {}
+    outs = {}
+    for form in ("latent", "per_head"):
+        fc = dataclasses.replace(mc, decode_attention=form)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        wsb = m.mla_decode_workspace_size(fc, B, max_len)
+        ws = [torch.zeros(wsb, dtype=torch.uint8, device=dev)]
+        out = torch.empty((B, H, cfg["v_dim"]), dtype=torch.bfloat16, device=dev)
+
+        def step(i, fc=fc, ws=ws, out=out):
+            s = sets[i % len(sets)]
+            m.mla_decode(fc, s["q_nope"], s["q_rope"], s["w_uk"], s["w_uv"], s["pool"],
+                         s["block_table"], s["seq_lens"], max_len, out=out,
+                         workspace=ws[i % len(sets)])
+
+        step(0)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base   # one step: workspace + output
+        outs[form] = out.float().clone()
+        ws += [torch.zeros(wsb, dtype=torch.uint8, device=dev) for _ in sets[1:]]
+        if form == "latent":
+            ms = latent_ms
+        else:
+            for i in range(args.warmup):
+                step(i)
+            g = capture(torch, lambda: [step(i) for i in range(args.steps)], torch.cuda.Stream())
+            ms = stats([t / args.steps for t in time_replays(torch, g.replay, args.repeats)])["median"]
+        rebuilt = 0 if form == "latent" else \
+            tokens * G * (cfg["qk_nope_dim"] + cfg["rope_dim"] + cfg["v_dim"]) * 2
+        rec[form] = {"us_per_step": round(ms * 1e3, 3), "rebuilt_kv_bytes": rebuilt,
+                     "workspace_bytes": wsb, "peak_extra_bytes": int(peak),
+                     "cache_bytes": alg["attn_bytes"]}
+        del ws
+    a, b = outs["latent"].flatten(), outs["per_head"].flatten()
+    rec["cosine_between_forms"] = round(float(torch.dot(a, b) / (a.norm() * b.norm())), 7)
+    rec["max_abs_between_forms"] = round(float((a - b).abs().max()), 6)
+    return rec
 
 
 if __name__ == "__main__":

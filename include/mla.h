@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -108,6 +108,16 @@ typedef struct mla_config {
                            (absorbed), 2 = through per-head keys and values
                            (bf16, R = 512, Dr = 64, Dn = Dv = 128 only; an FP8
                            cache takes 0 or 2).  Same result up to rounding. */
+  int32_t decode_attention; /* form of mla_decode's attention: 0 or 1 = on the
+                           latent rows (absorbed: W_UK folded into the query,
+                           W_UV applied after), 2 = through per-head keys and
+                           values rebuilt from the latent rows for the step
+                           (K_nope = c W_UK^T, V = c W_UV per kv group, then
+                           grouped attention over them; bf16, Dn = Dv = 64,
+                           Dr = 64, at most 16 query heads per kv group).  The
+                           reconstruction form of the tutorial's mechanism
+                           experiment ("ARCH-MLA", 5.1); same result up to
+                           rounding, more memory and bytes moved.            */
 } mla_config;
 
 /* ---- library information ------------------------------------------------ */

@@ -40,6 +40,7 @@ class MLAConfigC(ctypes.Structure):
         ("kv_groups", ctypes.c_int32),
         ("split_workgroups", ctypes.c_int32),
         ("prefill_attention", ctypes.c_int32),
+        ("decode_attention", ctypes.c_int32),
     ]
 
 

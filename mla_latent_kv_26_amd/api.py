@@ -20,6 +20,7 @@ _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _C_DTYPE = {"f32": _lib.DTYPE_F32, "bf16": _lib.DTYPE_BF16}
 _C_CACHE = {"same": _lib.CACHE_SAME, "fp8": _lib.CACHE_FP8_E4M3}
 _C_PREFILL = {"auto": 0, "latent": 1, "per_head": 2}
+_C_DECODE = {"auto": 0, "latent": 1, "per_head": 2}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -41,6 +42,7 @@ class MLAConfig:
     kv_groups: int = 0          # 0: W_UK, W_UV per head; G: heads share G matrices in order
     split_workgroups: int = 0   # decode attention workgroups per head group (0: one per CU)
     prefill_attention: str = "auto"   # "auto" (fewer FLOPs), "latent" (absorbed), "per_head"
+    decode_attention: str = "latent"  # "latent" (absorbed) or "per_head" (keys, values rebuilt)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -77,7 +79,8 @@ class MLAConfig:
                           self.v_dim, self.d_model, self.q_lora_rank, self.block_size,
                           self.softmax_scale, self.rms_eps, self.rope_theta,
                           _C_DTYPE[self.dtype], _C_CACHE[self.cache_dtype], self.kv_groups,
-                          self.split_workgroups, _C_PREFILL[self.prefill_attention])
+                          self.split_workgroups, _C_PREFILL[self.prefill_attention],
+                          _C_DECODE[self.decode_attention])
 
     @classmethod
     def from_dict(cls, d: dict, **over) -> "MLAConfig":

@@ -1129,7 +1129,7 @@ int decode_heads_per_wg(int H, int batch, int max_seq_len, int num_cus) {
 
 int decode_num_wg(int head_groups, int num_cus) {
   // one workgroup per CU in total; a multiple of 8 per head group (XCD pairing)
-  int n = num_cus / head_groups;
+  int n = num_cus / (head_groups > 0 ? head_groups : 1);
   n = (n / 8) * 8;
   return n < 8 ? 8 : n;
 }

@@ -7,81 +7,98 @@
 // q_full already scaled by softmax_scale * log2(e), softmax over each
 // sequence's tokens, weights applied to c.
 //
-// One workgroup (8 waves) takes 16 heads of one sequence over one chunk of
-// its tokens, 64-token tiles staged in LDS (two buffers; the next tile's
-// global loads are in flight while the current one is used).  Wave w owns
-// heads 2w, 2w+1: lane n scores token n of the tile (bf16 dot2 products,
-// float32 sums), the wave keeps the running max and sum of its heads, and for
-// the weighted sum lane n owns R/64 latent columns of those heads.  Each
-// chunk writes an unnormalised partial (m, l, O) in float32; a second kernel
-// merges the chunks of a sequence.  Vector-ALU work: at these widths one
-// token costs 2 * 16 * (2R + 64) flops against (R + 64) * 2 bytes.
+// One workgroup (4 waves) takes 16 heads of one sequence over one chunk of
+// its tokens in 64-token steps; wave w owns tokens 16 w .. 16 w + 15 of each
+// step and keeps its own running maximum, sum and output, so the waves never
+// wait for one another until the chunk ends.  Per step a wave stages its 16
+// rows in its own LDS buffer (rows padded to W + 8 values: 16 consecutive
+// rows of one column, and the 4 x 4 pieces of a transposing read, hit
+// distinct banks) and runs
+//   S^T [16 tok x 16 h]  = T [16 x W] Q^T        16x16x32 MFMAs, W / 32 of them
+//   O^T [R x 16 h]      += T[:, :R]^T P^T        16x16x16 MFMAs, R / 16 of them
+// with the queries (B of the first product) in registers and P (B of the
+// second) straight from the score accumulators: lane l holds tokens
+// 4 (l/16) .. + 3 of head l % 16 in both layouts.  The column fragments of
+// the second product come from transposing LDS reads.  At the chunk's end
+// the four waves' partials are merged through LDS and written once
+// (float32 (m, l, O), m in log2 units); merge_generic_kernel combines the
+// chunks of a sequence.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
 namespace {
 
-constexpr int kGT = 64;   // tokens per tile
+constexpr int kGT = 64;   // tokens per workgroup step (16 per wave)
 constexpr int kGH = 16;   // heads per workgroup
+constexpr float kNarrowSlack = 8.0f;  // lazy rescale threshold (log2 units)
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-__device__ __forceinline__ float lo_bf16(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t v) {
-  return __builtin_bit_cast(float, v & 0xffff0000u);
+__device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
-template <int R, int kWaves>
-__global__ void __launch_bounds__(64 * kWaves) attention_generic_kernel(
+// Rows of RW values; scores over values SOFF .. SOFF + SW - 1 of a row
+// (queries of SW values), the weighted sum over values 0 .. VW - 1.  Latent
+// rows: RW = SW = R + 64, SOFF = 0, VW = R.  Reconstructed per-head rows
+// [V | K_nope | k_rope]: RW = Dv + Dn + Dr, SOFF = Dv, SW = Dn + Dr, VW = Dv.
+template <int RW, int SOFF, int SW, int VW>
+__global__ void __launch_bounds__(256) attention_generic_kernel(
     const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
     const int* __restrict__ block_table, int max_blocks, int block_size,
     const int* __restrict__ seq_lens, int H, int chunk, int n_split, float* __restrict__ part_ml,
     float* __restrict__ part_o) {
-  constexpr int W = R + 64;           // row width (values)
-  constexpr int kRow = W * 2 + 16;    // LDS row stride (bytes), padded
-  constexpr int kChunks = W / 8;      // 16-byte pieces per row
-  constexpr int kThreads = 64 * kWaves;
-  constexpr int kHW = kGH / kWaves;   // heads per wave
-  constexpr int kLoads = kGT * kChunks / kThreads;
-  constexpr int kC = R / 64;          // latent columns per lane
-  static_assert(kGT * kChunks % kThreads == 0, "tile pieces must split evenly over the block");
-  static_assert(kHW == 2 || kHW == 4, "two or four heads per wave");
-  __shared__ __align__(16) unsigned char tile[2][kGT * kRow];
-  __shared__ __align__(16) unsigned char qs[kGH * W * 2];
-  __shared__ __align__(16) float ps[kGT * kGH];
+  constexpr int W = RW;                // row width (values)
+  constexpr int R = VW;                // output width
+  constexpr int kRowE = W + 8;         // LDS row stride (values)
+  constexpr int kChunks = W / 8;       // 16-byte pieces per row
+  constexpr int kLoads = 16 * kChunks / 64;  // per lane and step
+  constexpr int kKS = SW / 32;         // score k-steps
+  constexpr int kCB = R / 16;          // column blocks of O^T
+  static_assert(SW % 32 == 0 && R % 16 == 0 && SOFF + SW <= W && R <= W, "row layout");
+  static_assert(16 * kChunks % 64 == 0, "a wave's rows split evenly over its lanes");
+  constexpr int kBufE = 16 * kRowE;    // one wave's buffer (values)
+  // per wave: one row buffer; at the end, O^T of the four waves (float)
+  constexpr int kTileBytes = 4 * kBufE * 2;
+  constexpr int kMergeBytes = 4 * kGH * R * 4;
+  __shared__ __align__(16) unsigned char smem[kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes];
+  __shared__ float mls[4][2][kGH];
 
   const int split = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
   const int len = seq_lens[b];
   const int begin = split * chunk;
   const int end = min(len, begin + chunk);
-  const long slot = ((long)b * n_split + split) * H + hb * kGH + kHW * w;
+  const long slot = ((long)b * n_split + split) * H + hb * kGH;
   if (begin >= end) {  // nothing in this chunk: an empty partial (uniform per block)
-    if (lane < kHW) {
-      part_ml[(slot + lane) * 2] = -INFINITY;
-      part_ml[(slot + lane) * 2 + 1] = 0.f;
+    if (tid < kGH) {
+      part_ml[(slot + tid) * 2] = -INFINITY;
+      part_ml[(slot + tid) * 2 + 1] = 0.f;
     }
     // zero O too, so the merge reads every chunk's O without a branch
-    for (int i = lane; i < kHW * R; i += 64) part_o[slot * R + i] = 0.f;
+    for (int i = tid; i < kGH * R; i += 256) part_o[slot * R + i] = 0.f;
     return;
   }
 
-  // queries of the 16 heads
-  const bf16* qsrc = q_full + ((long)b * H + hb * kGH) * W;
-  for (int i = tid; i < kGH * kChunks; i += kThreads)
-    *(uint4*)(qs + i * 16) = *(const uint4*)(qsrc + i * 8);
+  // queries (B of the score product): head li, values 32 ks + 8 lg .. + 7
+  bf16x8 qf[kKS];
+  {
+    const bf16* q = q_full + ((long)b * H + hb * kGH + li) * SW + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
+  }
+  bf16* buf = (bf16*)smem + w * kBufE;
 
+  // this wave's rows of the step at t0: tokens t0 + 16 w + r (r < 16), piece
+  // c = lane + 64 i of the wave's 16 x kChunks pieces; zero past the chunk
   uint4 pre[kLoads];
   auto load = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + kThreads * i, r = c / kChunks, k = c - r * kChunks;
-      const int j = t0 + r;
+      const int c = lane + 64 * i, r = c / kChunks, k = c - r * kChunks;
+      const int j = t0 + 16 * w + r;
       uint4 v = {0u, 0u, 0u, 0u};
       if (j < end) {
         const long page = block_table[(long)b * max_blocks + j / block_size];
@@ -90,116 +107,107 @@ __global__ void __launch_bounds__(64 * kWaves) attention_generic_kernel(
       pre[i] = v;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + kThreads * i, r = c / kChunks, k = c - r * kChunks;
-      *(uint4*)(tile[buf] + r * kRow + k * 16) = pre[i];
+      const int c = lane + 64 * i, r = c / kChunks, k = c - r * kChunks;
+      *(uint4*)(buf + r * kRowE + k * 8) = pre[i];
     }
   };
 
-  float m[kHW], l[kHW], acc[kHW][kC];
+  float m = -INFINITY, l = 0.f;  // for head li (identical in the four lane groups)
+  f32x4 acc[kCB];
 #pragma unroll
-  for (int j = 0; j < kHW; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kC; ++c) acc[j][c] = 0.f;
-  }
+  for (int cb = 0; cb < kCB; ++cb) acc[cb] = f32x4{};
 
+  const int n_steps = (end - begin + kGT - 1) / kGT;
   load(begin);
-  store(0);
-  __syncthreads();
-  const int n_tiles = (end - begin + kGT - 1) / kGT;
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = 0; t < n_steps; ++t) {
     const int t0 = begin + t * kGT;
-    const bool more = t + 1 < n_tiles;
-    if (more) load(t0 + kGT);
-    const unsigned char* tb = tile[t & 1];
-
-    // scores of token `lane` for heads kHW w .. kHW w + kHW - 1
-    float s[kHW];
+    // the previous step's reads of the buffer are done (this wave's own
+    // program order), so it can take this step's rows
+    store();
+    if (t + 1 < n_steps) load(t0 + kGT);
+    // S^T: A = rows li (16 tokens), values 32 ks + 8 lg .. + 7
+    f32x4 s = f32x4{};
 #pragma unroll
-    for (int j = 0; j < kHW; ++j) s[j] = 0.f;
-    const unsigned char* rowp = tb + lane * kRow;
-    const unsigned char* qp = qs + (kHW * w) * W * 2;
-#pragma unroll 4
-    for (int k = 0; k < kChunks; ++k) {
-      const uint4 rv = *(const uint4*)(rowp + k * 16);
-#pragma unroll
-      for (int j = 0; j < kHW; ++j) {
-        const uint4 qv = *(const uint4*)(qp + j * W * 2 + k * 16);
-        s[j] = dot2(rv.x, qv.x, s[j]);
-        s[j] = dot2(rv.y, qv.y, s[j]);
-        s[j] = dot2(rv.z, qv.z, s[j]);
-        s[j] = dot2(rv.w, qv.w, s[j]);
-      }
+    for (int ks = 0; ks < kKS; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(buf + li * kRowE + SOFF + 32 * ks + 8 * lg);
+      s = mfma16(a, qf[ks], s);
     }
-    const bool valid = t0 + lane < end;
-    float p[kHW];
+    // register v <-> token t0 + 16 w + 4 lg + v, head li
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kHW; ++j) {
-      const float sj = valid ? s[j] : -INFINITY;
-      const float mn = fmaxf(m[j], wave_max(sj));   // finite: the tile has a valid token
-      const float corr = exp2f(m[j] - mn);          // 0 on the first tile
-      p[j] = valid ? exp2f(sj - mn) : 0.f;
-      l[j] = l[j] * corr + wave_sum(p[j]);
-      m[j] = mn;
-#pragma unroll
-      for (int c = 0; c < kC; ++c) acc[j][c] *= corr;
+    for (int v = 0; v < 4; ++v) {
+      if (t0 + 16 * w + 4 * lg + v >= end) s[v] = -INFINITY;
+      tmax = fmaxf(tmax, s[v]);
     }
-    if constexpr (kHW == 4)
-      *(f32x4*)(ps + lane * kGH + 4 * w) = f32x4{p[0], p[1], p[2], p[3]};
-    else
-      *(f32x2*)(ps + lane * kGH + 2 * w) = f32x2{p[0], p[1]};
-    __syncthreads();
-
-    // weighted sum: lane owns latent columns kC*lane .. kC*lane + kC - 1
-#pragma unroll 4
-    for (int n = 0; n < kGT; ++n) {
-      float pn[kHW];
-      if constexpr (kHW == 4) {
-        const f32x4 v = *(const f32x4*)(ps + n * kGH + 4 * w);
-        pn[0] = v[0], pn[1] = v[1], pn[2] = v[2], pn[3] = v[3];
-      } else {
-        const f32x2 v = *(const f32x2*)(ps + n * kGH + 2 * w);
-        pn[0] = v[0], pn[1] = v[1];
-      }
-      float cv[kC];
-      if constexpr (kC == 4) {
-        const uint2 raw = *(const uint2*)(tb + n * kRow + lane * 8);
-        cv[0] = lo_bf16(raw.x);
-        cv[1] = hi_bf16(raw.x);
-        cv[2] = lo_bf16(raw.y);
-        cv[3] = hi_bf16(raw.y);
-      } else {
-        const uint32_t raw = *(const uint32_t*)(tb + n * kRow + lane * 4);
-        cv[0] = lo_bf16(raw);
-        cv[1] = hi_bf16(raw);
-      }
+    tmax = max_xor32(max_xor16(tmax));
+    // lazy reference: moved only when a step exceeds it by more than the slack
+    const bool grow = tmax > m + kNarrowSlack;
+    const float m_new = grow ? tmax : m;
+    if (__ballot(grow) != 0ull) {
+      const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;  // 0 on the first step
 #pragma unroll
-      for (int j = 0; j < kHW; ++j)
-#pragma unroll
-        for (int c = 0; c < kC; ++c) acc[j][c] = fmaf(pn[j], cv[c], acc[j][c]);
+      for (int cb = 0; cb < kCB; ++cb) acc[cb] *= alpha;
+      l *= alpha;
     }
-    if (more) store((t + 1) & 1);
-    __syncthreads();
-  }
-
-  if (lane == 0) {
+    m = m_new;
+    bf16x4 p;
+    float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < kHW; ++j) {
-      part_ml[(slot + j) * 2] = m[j];
-      part_ml[(slot + j) * 2 + 1] = l[j];
+    for (int v = 0; v < 4; ++v) {
+      // a wave whose tokens are all past the chunk's end has m = -inf
+      const bf16 pv = (bf16)(m == -INFINITY ? 0.f : fast_exp2(s[v] - m));
+      p[v] = pv;
+      psum += (float)pv;
+    }
+    l += psum;
+    // O^T += T[:, cols]^T P^T: A = columns 16 cb + li, tokens 4 lg .. + 3 (a
+    // transposing read: lane 4 a + c of the group reads row 4 lg + a, columns
+    // 16 cb + 4 c .. + 3)
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const bf16x4 a = lds_read_tr(lds_addr(buf) +
+                                   ((4 * lg + (li >> 2)) * kRowE + 16 * cb + 4 * (li & 3)) * 2);
+      acc[cb] = mfma16k16(a, p, acc[cb]);
     }
   }
+
+  // ---- merge the four waves' partials of the chunk, then write it ----
+  l = sum_xor32(sum_xor16(l));
+  __syncthreads();  // every wave is done with its row buffer
+  float* ob = (float*)smem;
+  if (lg == 0) {
+    mls[w][0][li] = m;
+    mls[w][1][li] = l;
+  }
+  // O^T register v of block cb <-> column 16 cb + 4 lg + v, head li
 #pragma unroll
-  for (int j = 0; j < kHW; ++j) {
-    float* dst = part_o + (slot + j) * R + kC * lane;
-    if constexpr (kC == 4)
-      *(f32x4*)dst = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-    else
-      *(f32x2*)dst = f32x2{acc[j][0], acc[j][1]};
+  for (int cb = 0; cb < kCB; ++cb)
+    *(f32x4*)(ob + ((w * kGH + li) * R + 16 * cb + 4 * lg)) = acc[cb];
+  __syncthreads();
+  // thread (head hh, column block) combines the four waves with weights
+  // 2^(m_w - M) (M: the largest m; waves that saw no token have m = -inf)
+  for (int e = tid; e < kGH * (R / 4); e += 256) {
+    const int hh = e / (R / 4), c4 = (e % (R / 4)) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, mls[v][0][hh]);
+    f32x4 o = f32x4{};
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float mw = mls[v][0][hh];
+      const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      o += wt * *(const f32x4*)(ob + (v * kGH + hh) * R + c4);
+      L += wt * mls[v][1][hh];
+    }
+    *(f32x4*)(part_o + (slot + hh) * R + c4) = o;
+    if (c4 == 0) {
+      part_ml[(slot + hh) * 2] = M;
+      part_ml[(slot + hh) * 2 + 1] = L;
+    }
   }
 }
 
@@ -277,31 +285,39 @@ void generic_split(int batch, int H, int max_seq_len, int num_cus, int* chunk, i
   *n_split = (tiles + per - 1) / per;   // <= splits
 }
 
+template <int RW, int SOFF, int SW, int VW>
+void launch_narrow(const void* q_full, const void* pool, const int* block_table, int max_blocks,
+                   int block_size, const int* seq_lens, int batch, int H, int chunk, int n_split,
+                   float* part_ml, float* part_o, void* o_lat, bool o_f32, hipStream_t st) {
+  const dim3 grid(n_split, H / kGH, batch);
+  attention_generic_kernel<RW, SOFF, SW, VW><<<grid, 256, 0, st>>>(
+      (const bf16*)q_full, (const bf16*)pool, block_table, max_blocks, block_size, seq_lens, H,
+      chunk, n_split, part_ml, part_o);
+  const dim3 mg(H, batch);
+  if (o_f32)
+    merge_generic_kernel<VW, float><<<mg, 256, 0, st>>>(part_ml, part_o, H, n_split, (float*)o_lat);
+  else
+    merge_generic_kernel<VW, bf16><<<mg, 256, 0, st>>>(part_ml, part_o, H, n_split, (bf16*)o_lat);
+}
+
 void launch_attention_generic(const void* q_full, const void* pool, const int* block_table,
                               int max_blocks, int block_size, const int* seq_lens, int batch,
                               int H, int R, int chunk, int n_split, float* part_ml, float* part_o,
                               void* o_lat, bool o_f32, hipStream_t st) {
-  const dim3 grid(n_split, H / kGH, batch);
   if (R == 256)
-    attention_generic_kernel<256, 8><<<grid, 512, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
-                                                       block_table, max_blocks, block_size,
-                                                       seq_lens, H, chunk, n_split, part_ml, part_o);
+    launch_narrow<320, 0, 320, 256>(q_full, pool, block_table, max_blocks, block_size, seq_lens,
+                                    batch, H, chunk, n_split, part_ml, part_o, o_lat, o_f32, st);
   else
-    attention_generic_kernel<128, 8><<<grid, 512, 0, st>>>((const bf16*)q_full, (const bf16*)pool,
-                                                       block_table, max_blocks, block_size,
-                                                       seq_lens, H, chunk, n_split, part_ml, part_o);
-  const dim3 mg(H, batch);
-  if (R == 256) {
-    if (o_f32)
-      merge_generic_kernel<256, float><<<mg, 256, 0, st>>>(part_ml, part_o, H, n_split, (float*)o_lat);
-    else
-      merge_generic_kernel<256, bf16><<<mg, 256, 0, st>>>(part_ml, part_o, H, n_split, (bf16*)o_lat);
-  } else {
-    if (o_f32)
-      merge_generic_kernel<128, float><<<mg, 256, 0, st>>>(part_ml, part_o, H, n_split, (float*)o_lat);
-    else
-      merge_generic_kernel<128, bf16><<<mg, 256, 0, st>>>(part_ml, part_o, H, n_split, (bf16*)o_lat);
-  }
+    launch_narrow<192, 0, 192, 128>(q_full, pool, block_table, max_blocks, block_size, seq_lens,
+                                    batch, H, chunk, n_split, part_ml, part_o, o_lat, o_f32, st);
+}
+
+void launch_attention_perhead(const void* q, const void* rows, const int* table, int row_block,
+                              const int* seq_lens, int batch, int chunk, int n_split,
+                              float* part_ml, float* part_o, void* o, hipStream_t st) {
+  // rows [V (64) | K_nope (64) | k_rope (64)]; scores over values 64 .. 191
+  launch_narrow<192, 64, 128, 64>(q, rows, table, 1, row_block, seq_lens, batch, kGH, chunk,
+                                  n_split, part_ml, part_o, o, false, st);
 }
 
 }  // namespace mla

@@ -483,3 +483,98 @@ void launch_project_small(const void* o_lat, const void* w_uv, int n, int H, int
 }
 
 }  // namespace mla
+
+// ---------------------------------------------------------------------------
+// Decode through per-head keys and values rebuilt for the step (Dn = Dv = Dr
+// = 64): the gather of the latent rows, the grouped queries and the output
+// reordering around two batched GEMMs and the narrow attention kernel.
+// ---------------------------------------------------------------------------
+namespace mla {
+namespace {
+
+// One block of 64 threads per (sequence b, position t < lpad): the latent
+// part of row t (R values) to cg[b lpad + t], its rope key (64 values) to
+// value columns 128 .. 191 of rows[g][b lpad + t] for every group g; zeros
+// past the sequence's length.  Block (b, 0) also writes seq2 and tab2.
+__global__ void __launch_bounds__(64) perhead_gather_kernel(
+    const bf16* __restrict__ pool, const int* __restrict__ block_table, int max_blocks,
+    int block_size, const int* __restrict__ seq_lens, int batch, int G, int R, int lpad,
+    bf16* __restrict__ cg, bf16* __restrict__ rows, int* __restrict__ seq2,
+    int* __restrict__ tab2) {
+  const int t = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int len = seq_lens[b];
+  if (t == 0)
+    for (int g = lane; g < G; g += 64) {
+      seq2[g * batch + b] = len;
+      tab2[g * batch + b] = g * batch + b;
+    }
+  const long row = (long)b * lpad + t;
+  const int W = R + 64;
+  const bf16* src = nullptr;
+  if (t < len) {
+    const long page = block_table[(long)b * max_blocks + t / block_size];
+    src = pool + (page * block_size + t % block_size) * W;
+  }
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  for (int c = lane; c < R / 8; c += 64)
+    *(uint4*)(cg + row * R + c * 8) = src ? *(const uint4*)(src + c * 8) : zero;
+  for (int e = lane; e < 8 * G; e += 64) {
+    const int g = e / 8, c = e % 8;
+    *(uint4*)(rows + ((long)g * batch * lpad + row) * 192 + 128 + c * 8) =
+        src ? *(const uint4*)(src + R + c * 8) : zero;
+  }
+}
+
+// q2[g B + b, i] = alpha [q_nope[b, g gs + i] | q_rope[b, g gs + i]] (i <
+// gs), zero for gs <= i < 16; one block of 256 threads per (b, g), 8 values
+// per thread.
+__global__ void __launch_bounds__(256) perhead_query_kernel(
+    const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope, int batch, int H, int G,
+    float alpha, bf16* __restrict__ q2) {
+  const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int gs = H / G, i = t / 16, c = (t % 16) * 8;
+  bf16x8 v;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = (bf16)0.f;
+  if (i < gs) {
+    const long h = (long)b * H + g * gs + i;
+    const bf16x8 s = c < 64 ? *(const bf16x8*)(q_nope + h * 64 + c)
+                            : *(const bf16x8*)(q_rope + h * 64 + c - 64);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (bf16)(alpha * (float)s[k]);
+  }
+  *(bf16x8*)(q2 + (((long)g * batch + b) * 16 + i) * 128 + c) = v;
+}
+
+// out[b, g gs + i] = o2[g B + b, i] for i < gs (64 values); one block of 64
+// threads per (b, g), 8 values per thread.
+__global__ void __launch_bounds__(128) perhead_out_kernel(const bf16* __restrict__ o2, int batch,
+                                                          int H, int G, bf16* __restrict__ out) {
+  const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int gs = H / G, i = t / 8, c = (t % 8) * 8;
+  if (i < gs)
+    *(bf16x8*)(out + ((long)b * H + g * gs + i) * 64 + c) =
+        *(const bf16x8*)(o2 + (((long)g * batch + b) * 16 + i) * 64 + c);
+}
+
+}  // namespace
+
+void launch_perhead_gather(const void* pool, const int* block_table, int max_blocks,
+                           int block_size, const int* seq_lens, int batch, int G, int R, int lpad,
+                           void* cg, void* rows, int* seq2, int* tab2, hipStream_t st) {
+  perhead_gather_kernel<<<dim3(lpad, batch), 64, 0, st>>>(
+      (const bf16*)pool, block_table, max_blocks, block_size, seq_lens, batch, G, R, lpad,
+      (bf16*)cg, (bf16*)rows, seq2, tab2);
+}
+
+void launch_perhead_query(const void* q_nope, const void* q_rope, int batch, int H, int G,
+                          float alpha, void* q2, hipStream_t st) {
+  perhead_query_kernel<<<dim3(batch, G), 256, 0, st>>>((const bf16*)q_nope, (const bf16*)q_rope,
+                                                       batch, H, G, alpha, (bf16*)q2);
+}
+
+void launch_perhead_out(const void* o2, int batch, int H, int G, void* out, hipStream_t st) {
+  perhead_out_kernel<<<dim3(batch, G), 128, 0, st>>>((const bf16*)o2, batch, H, G, (bf16*)out);
+}
+
+}  // namespace mla

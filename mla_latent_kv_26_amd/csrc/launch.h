@@ -154,6 +154,26 @@ void launch_attention_generic(const void* q_full, const void* pool, const int* b
                               int H, int R, int chunk, int n_split, float* part_ml, float* part_o,
                               void* o_lat, bool o_f32, hipStream_t st);
 
+// Decode through per-head keys and values rebuilt for the step, for Dn = Dv
+// = Dr = 64 (kernels_generic.hip, attention_generic.hip).  Sequence b' =
+// g B + b of the grouped attention is (kv group g, sequence b).
+// gather: cg [B, lpad, R] = the latent part of each sequence's rows 0 ..
+// len-1 (zero after), rows[g][b lpad + t][128 .. 191] = its rope key; also
+// seq2[b'] = len(b), tab2[b'] = b'.  query: q2 [G B, 16, 128] = alpha
+// [q_nope | q_rope] of the group's gs heads (zero rows after gs).  out:
+// out[b, g gs + i] = o2[g B + b, i] (i < gs), 64 values.  attention: as
+// launch_attention_generic over rows [G B lpad, 192] of one row_block-row
+// page per sequence b', 16 heads, outputs o [G B, 16, 64] bf16.
+void launch_perhead_gather(const void* pool, const int* block_table, int max_blocks,
+                           int block_size, const int* seq_lens, int batch, int G, int R, int lpad,
+                           void* cg, void* rows, int* seq2, int* tab2, hipStream_t st);
+void launch_perhead_query(const void* q_nope, const void* q_rope, int batch, int H, int G,
+                          float alpha, void* q2, hipStream_t st);
+void launch_perhead_out(const void* o2, int batch, int H, int G, void* out, hipStream_t st);
+void launch_attention_perhead(const void* q, const void* rows, const int* table, int row_block,
+                              const int* seq_lens, int batch, int chunk, int n_split,
+                              float* part_ml, float* part_o, void* o, hipStream_t st);
+
 // Per-head projections of a few rows (rows <= 32, Dn, R, Dv <= 1024)
 // with W_UK / W_UV shared by gs consecutive heads: q_full [n, H, R + Dr] =
 // alpha [q_nope W_UK[h / gs] | q_rope]; out [n, H, Dv] = o_lat W_UV[h / gs].

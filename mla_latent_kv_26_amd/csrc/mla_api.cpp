@@ -36,6 +36,7 @@ struct Dims {
   int G, gs;         // W_UK / W_UV matrices, heads per matrix
   int split_wg;      // requested decode workgroups per head group (0: one per CU)
   int prefill_form;  // 0 fewer FLOPs, 1 latent rows, 2 per-head keys and values
+  int decode_form;   // 0, 1 latent rows, 2 per-head keys and values rebuilt per step
 };
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -87,6 +88,9 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
   if (c->prefill_attention < 0 || c->prefill_attention > 2)
     return fail(MLA_ERR_INVALID_ARG, "prefill_attention (%d) must be 0, 1 or 2",
                 c->prefill_attention);
+  if (c->decode_attention < 0 || c->decode_attention > 2)
+    return fail(MLA_ERR_INVALID_ARG, "decode_attention (%d) must be 0, 1 or 2",
+                c->decode_attention);
   if (d) {
     d->H = c->num_heads;
     d->R = c->kv_lora_rank;
@@ -110,12 +114,26 @@ mla_status check_cfg(const mla_config* c, Dims* d) {
     d->gs = d->H / d->G;
     d->split_wg = c->split_workgroups;
     d->prefill_form = c->prefill_attention;
+    d->decode_form = c->decode_attention;
   }
   return MLA_OK;
 }
 
+// Decode through per-head keys and values rebuilt for the step.
+bool perhead_decode(const Dims& d) { return d.decode_form == 2; }
+
 // Shape support of the kernels (after the config itself is valid).
 mla_status check_decode_kernels(const Dims& d, int batch) {
+  if (perhead_decode(d)) {
+    if (d.dt != MLA_DTYPE_BF16 || d.fp8 || d.Dn != 64 || d.Dv != 64 || d.Dr != 64 ||
+        d.gs > 16 || d.R % 8)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "decode_attention 2 (per-head keys and values) needs bf16 rows, qk_nope_dim = "
+                  "v_dim = rope_dim = 64, at most 16 heads per kv group and kv_lora_rank %% 8 == 0 "
+                  "(got %d, %d, %d, %d heads per group, rank %d)",
+                  d.Dn, d.Dv, d.Dr, d.gs, d.R);
+    return MLA_OK;
+  }
   if (d.dt == MLA_DTYPE_F32) {
     if (d.R > 1024)
       return fail(MLA_ERR_UNSUPPORTED, "float32 path supports kv_lora_rank <= 1024 (got %d)", d.R);
@@ -165,6 +183,9 @@ struct DecodeWs {
   size_t prefix, part_ml, part_o, q_full, o_lat, total;
   int n_wg, hgc, heads;
   int chunk, n_split;  // narrow-latent kernels
+  // per-head form: latent part, rebuilt rows, grouped queries, lengths, table
+  size_t cg, rows, q2, seq2, tab2;
+  int lpad;
 };
 // bf16 shapes that go to the narrow-latent kernels instead of the tuned ones
 bool generic_decode(const Dims& d) { return d.dt == MLA_DTYPE_BF16 && d.R != 512; }
@@ -172,6 +193,30 @@ bool generic_decode(const Dims& d) { return d.dt == MLA_DTYPE_BF16 && d.R != 512
 DecodeWs decode_ws(const Dims& d, int batch, int max_seq_len) {
   DecodeWs w{};
   size_t off = 256;  // reserved
+  if (perhead_decode(d)) {
+    const size_t nb2 = (size_t)d.G * batch;
+    w.lpad = (max_seq_len + 15) / 16 * 16;
+    mla::generic_split((int)nb2, 16, max_seq_len, num_cus(), &w.chunk, &w.n_split);
+    w.cg = off;
+    off = up256(off + (size_t)batch * w.lpad * d.R * 2);
+    w.rows = off;
+    off = up256(off + nb2 * w.lpad * 192 * 2);
+    w.q2 = off;
+    off = up256(off + nb2 * 16 * 128 * 2);
+    w.seq2 = off;
+    off = up256(off + nb2 * 4);
+    w.tab2 = off;
+    off = up256(off + nb2 * 4);
+    w.part_ml = off;
+    off = up256(off + nb2 * w.n_split * 16 * 2 * 4);
+    w.part_o = off;
+    off = up256(off + nb2 * w.n_split * 16 * 64 * 4);
+    w.o_lat = off;
+    off = up256(off + nb2 * 16 * 64 * 2);
+    w.q_full = off;
+    w.total = off;
+    return w;
+  }
   if (generic_decode(d)) {
     mla::generic_split(batch, d.H, max_seq_len, num_cus(), &w.chunk, &w.n_split);
     w.part_ml = off;
@@ -430,6 +475,10 @@ mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32
   if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be positive (got %d)", batch);
   if (max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be positive");
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  // the layout follows the kernels the call would take: none for a shape
+  // they do not cover
+  s = check_decode_kernels(d, batch);
+  if (s != MLA_OK) return s;
   *bytes = decode_ws(d, batch, max_seq_len).total;
   return MLA_OK;
 }
@@ -507,6 +556,30 @@ static void enqueue_decode(const Dims& d, const void* q_nope, const void* q_rope
                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* out,
                            void* workspace, hipStream_t st) {
   const DecodeWs w = decode_ws(d, batch, max_seq_len);
+  if (perhead_decode(d)) {
+    // keys and values of every kv group rebuilt from the latent rows
+    // (K_nope = c W_UK[g]^T, V = c W_UV[g], rows [V | K_nope | k_rope]),
+    // then grouped attention over them; nothing is applied after
+    const int M = batch * w.lpad, G = d.G;
+    void* cg = at(workspace, w.cg);
+    uint16_t* rows = (uint16_t*)at(workspace, w.rows);
+    const long sC = (long)M * 192;
+    mla::launch_perhead_gather(kv_pool, block_table, max_blocks_per_seq, d.bs, seq_lens, batch, G,
+                               d.R, w.lpad, cg, rows, (int*)at(workspace, w.seq2),
+                               (int*)at(workspace, w.tab2), st);
+    mla::launch_gemm_bf16_bt(cg, w_uk, rows + 64, M, 64, d.R, d.R, d.R, 192, 0, 64L * d.R, sC, G,
+                             1.0f, 0, st);
+    mla::launch_gemm_bf16(cg, w_uv, rows, M, 64, d.R, d.R, 64, 192, 0, 64L * d.R, sC, G, 1.0f, 0,
+                          st);
+    mla::launch_perhead_query(q_nope, q_rope, batch, d.H, G, d.scale * 1.4426950408889634f,
+                              at(workspace, w.q2), st);
+    mla::launch_attention_perhead(at(workspace, w.q2), rows, (const int*)at(workspace, w.tab2),
+                                  w.lpad, (const int*)at(workspace, w.seq2), G * batch, w.chunk,
+                                  w.n_split, (float*)at(workspace, w.part_ml),
+                                  (float*)at(workspace, w.part_o), at(workspace, w.o_lat), st);
+    mla::launch_perhead_out(at(workspace, w.o_lat), batch, d.H, G, out, st);
+    return;
+  }
   void* q_full = at(workspace, w.q_full);
   enqueue_absorb(d, q_nope, q_rope, w_uk, batch, q_full, st);
   enqueue_latent(d, q_full, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
@@ -560,6 +633,10 @@ mla_status mla_latent_attention(const mla_config* cfg, const void* q_full, const
   g_err.clear();
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
+  if (perhead_decode(d))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "the staged decode calls run on the latent rows; decode_attention 2 applies to "
+                "mla_decode only");
   s = check_decode_common(d, kv_pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
                           max_seq_len);
   if (s != MLA_OK) return s;
@@ -592,6 +669,10 @@ mla_status mla_attention_partials(const mla_config* cfg, const void* q_full, con
   g_err.clear();
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
+  if (perhead_decode(d))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "the staged decode calls run on the latent rows; decode_attention 2 applies to "
+                "mla_decode only");
   if (d.dt != MLA_DTYPE_BF16 || generic_decode(d))
     return fail(MLA_ERR_UNSUPPORTED,
                 "split partials exist for the bf16 kernels at kv_lora_rank 512 only; use "
@@ -619,6 +700,10 @@ mla_status mla_combine_output(const mla_config* cfg, const void* w_uv, int32_t b
   g_err.clear();
   mla_status s = check_cfg(cfg, &d);
   if (s != MLA_OK) return s;
+  if (perhead_decode(d))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "the staged decode calls run on the latent rows; decode_attention 2 applies to "
+                "mla_decode only");
   if (d.dt != MLA_DTYPE_BF16 || generic_decode(d))
     return fail(MLA_ERR_UNSUPPORTED,
                 "split partials exist for the bf16 kernels at kv_lora_rank 512 only; use "

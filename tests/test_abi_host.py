@@ -36,7 +36,7 @@ def test_every_header_symbol_is_exported_and_bound():
 
 
 def test_abi_version_and_status_strings():
-    assert lib.mla_abi_version() == 4
+    assert lib.mla_abi_version() == 5
     for s, name in _lib.STATUS_NAMES.items():
         assert lib.mla_status_string(s).decode() == name
 
@@ -127,6 +127,45 @@ def test_decode_rejects_unsupported_shapes():
                  dict(kv_lora_rank=256, cache_dtype="fp8")):
         cfg = dataclasses.replace(KIMI, **over)
         assert _decode(cfg, max_len=64) == _lib.MLA_ERR_UNSUPPORTED, over
+
+
+MECH = m.MLAConfig(num_heads=16, kv_lora_rank=256, rope_dim=64, qk_nope_dim=64, v_dim=64,
+                   kv_groups=4)
+
+
+def test_decode_attention_field():
+    """decode_attention: 0..2 accepted, others rejected; the per-head form
+    takes its own workspace, refuses shapes outside Dn = Dv = Dr = 64 or more
+    than 16 heads per group, and the staged (latent-form) calls refuse it."""
+    import dataclasses
+    for v, st in ((0, _lib.MLA_OK), (1, _lib.MLA_OK), (2, _lib.MLA_OK),
+                  (3, _lib.MLA_ERR_INVALID_ARG), (-1, _lib.MLA_ERR_INVALID_ARG)):
+        c = MECH.c()
+        c.decode_attention = v
+        assert lib.mla_validate_config(ctypes.byref(c)) == st, v
+    ph = dataclasses.replace(MECH, decode_attention="per_head")
+    lat = m.mla_decode_workspace_size(MECH, 1, 8192)
+    per = m.mla_decode_workspace_size(ph, 1, 8192)
+    # the rebuilt rows alone: 4 groups x 8192 tokens x 192 values x 2 bytes
+    assert per > 4 * 8192 * 192 * 2 > lat
+    assert _decode(dataclasses.replace(KIMI, decode_attention="per_head"), max_len=64) == \
+        _lib.MLA_ERR_UNSUPPORTED                                   # Dn = Dv = 128
+    assert _decode(dataclasses.replace(ph, num_heads=32, kv_groups=1), max_len=64) == \
+        _lib.MLA_ERR_UNSUPPORTED                                   # 32 heads in one group
+    assert _decode(dataclasses.replace(ph, cache_dtype="fp8"), max_len=64) == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_latent_attention(ctypes.byref(ph.c()), FAKE, FAKE, 100, FAKE, 64, FAKE, 1, 64,
+                                    FAKE, FAKE, 1 << 40, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert "mla_decode only" in _lib.last_error()
+
+
+def test_workspace_size_of_unsupported_shape_is_an_error():
+    """A shape no decode kernel takes (16 heads on the latent-512 kernels)
+    gets MLA_ERR_UNSUPPORTED from the workspace query too."""
+    import dataclasses
+    with pytest.raises(m.MLAError) as e:
+        m.mla_decode_workspace_size(dataclasses.replace(KIMI, num_heads=16), 1, 64)
+    assert e.value.status == _lib.MLA_ERR_UNSUPPORTED
 
 
 def test_kv_groups_must_divide_heads():

@@ -151,3 +151,50 @@ def test_staged_calls_refuse_what_they_lack(m):
     with pytest.raises(m.MLAError) as e:
         m.mla_combine_output(mb, 1, 64, wsb, w_uv=w_uv)
     assert e.value.status == 2
+
+
+# ---------------------------------------------------------------------------
+# The reconstruction form (decode_attention "per_head"): per-head keys and
+# values rebuilt from the latent rows for the step, then grouped attention,
+# against the oracle's naive path (keys and values rebuilt in float64).
+# ---------------------------------------------------------------------------
+def check_per_head(m, cfg, lengths=None, seed=None):
+    cfg = dict(cfg, decode_attention="per_head")
+    lens = None if lengths is None else np.asarray(lengths, np.int32)
+    inp = workloads.decode_inputs(cfg, seed=seed, lengths=lens)
+    got = run_decode(m, cfg, inp)
+    ids = list(range(len(inp.seq_lens)))
+    refs = []
+    for b, (pages, table, ln) in zip(ids, compact_sequences(inp, ids)):
+        o, _ = oracle.decode(workloads.to_f64(inp.q_nope[b:b + 1]),
+                             workloads.to_f64(inp.q_rope[b:b + 1]), workloads.to_f64(inp.w_uk),
+                             workloads.to_f64(inp.w_uv), pages, table, ln, cfg, path="naive")
+        refs.append(o[0])
+    e = assert_bf16(got, np.stack(refs), f"per-head {list(inp.seq_lens[:8])}", per_row_axis=0)
+    # the latent form of the same step agrees with it to the same bar
+    lat = run_decode(m, dict(cfg, decode_attention="latent"), inp)
+    assert_bf16(got, lat, "per-head vs latent form", per_row_axis=0)
+    return e
+
+
+@pytest.mark.parametrize("L", [512, 2048, 8192])
+def test_mechanism_widths_per_head_form(m, L):
+    """The tutorial's reconstruction leg at its widths: 16 query heads over 4
+    rebuilt key/value heads of width 64 (rope 64), latent 256."""
+    e = check_per_head(m, workloads.WORKLOADS[f"mechanism_h16_g4_r256_l{L}"])
+    print(f"per-head form mechanism_h16_g4_r256_l{L}", e)
+
+
+def test_per_head_form_paged_ragged(m):
+    """Several sequences of ragged lengths (1 token up to past a tile) over
+    16-token pages of a permuted pool; 32 heads in 8 groups; latent 128."""
+    cfg = dict(workloads.WORKLOADS["mechanism_h16_g4_r256_l512"], num_heads=32, kv_groups=8,
+               kv_lora_rank=128, block_size=16, paged=True, lengths="explicit", seed=81)
+    check_per_head(m, cfg, [1, 2, 15, 16, 17, 63, 64, 65, 129, 700])
+
+
+def test_per_head_form_one_head_per_group_and_rank_512(m):
+    """32 heads with their own matrices (no sharing) over latent-512 rows."""
+    cfg = dict(workloads.WORKLOADS["mechanism_h16_g4_r256_l512"], num_heads=32, kv_groups=32,
+               kv_lora_rank=512, lengths="explicit", paged=True, seed=83)
+    check_per_head(m, cfg, [300, 1, 1024, 77])
