@@ -311,6 +311,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the device's HBM read and bf16 MFMA ceilings with the "
+                         "library's probes (include/mla.h) and print them")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (10 times), as the "
                          "known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -336,6 +339,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 10}))
         return
     import mla_latent_kv_26_amd as m
+    if args.ceilings:
+        return ceilings_main(args, torch, m)
     if "q_len" in workloads.WORKLOADS[args.workload]:
         return prefill_main(args, torch, m)
     if "rows" in workloads.WORKLOADS[args.workload]:
@@ -450,6 +455,54 @@ def main():
         line["forms"] = mechanism_forms(args, torch, m, cfg, mc, sets, max_len, step_ms, alg)
     if not args.no_cpu_baseline and args.workload == workloads.HEADLINE:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def ceilings_main(args, torch, m):
+    """The ceilings the kernels are measured against, on this device: HBM
+    reads of a 2 GiB buffer (8x the 256 MB Infinity Cache) through 16-byte
+    vector loads and through direct-to-LDS loads of 36 KB pieces (the decode
+    attention's way), and back-to-back bf16 32x32x16 MFMAs.  Median of
+    --repeats launches each, HIP events on the launching stream."""
+    dev = torch.device("cuda", 0)
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    sink = m.mla_probe_sink(dev)
+    st = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.repeats):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return stats(ts)
+
+    nbytes = buf.numel()
+    dma_bytes = (nbytes // 36864) * 36864
+    vec = timed(lambda: m.mla_probe_hbm_read(buf, 0, sink))
+    dma = timed(lambda: m.mla_probe_hbm_read(buf, 1, sink))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs, iters = 4 * cus, 4000
+    flops = wgs * 4 * iters * 4 * 32768
+    mf = timed(lambda: m.mla_probe_mfma(wgs, iters, sink))
+    gbs = lambda b, t: b / (t * 1e-3) / 1e9
+    line = {
+        "metric": "device ceilings: HBM read GB/s, bf16 MFMA TFLOP/s",
+        "hbm_read_vector_GBs": round(gbs(nbytes, vec["median"]), 1),
+        "hbm_read_direct_to_lds_GBs": round(gbs(dma_bytes, dma["median"]), 1),
+        "hbm_peak_GBs": HBM_PEAK_GBS,
+        "mfma_bf16_TFLOPs": round(flops / (mf["median"] * 1e-3) / 1e12, 1),
+        "mfma_bf16_peak_TFLOPs": BF16_PEAK_TFLOPS,
+        "buffer_bytes": nbytes, "repeats": args.repeats,
+        "mfma_workgroups": wgs, "mfma_iterations": iters, "compute_units": cus,
+        "ms": {"vector": round(vec["median"], 4), "direct_to_lds": round(dma["median"], 4),
+               "mfma": round(mf["median"], 4)},
+    }
     print(json.dumps(line), flush=True)
 
 

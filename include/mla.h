@@ -350,6 +350,27 @@ mla_status mla_output_gate_projection(const mla_config* cfg, const void* x, cons
                                       const void* w_g, const void* w_o, int32_t n_rows, void* out,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- measurement probes (not part of the method) ------------------------
+ * The ceilings this library's kernels are measured against, taken on the
+ * device at hand: the caller times each launch on `stream`.
+ * mla_probe_sink_bytes: bytes of device memory `sink` must hold.
+ * mla_probe_hbm_read: reads bytes (>= 36864) of buf (device, 16-byte
+ *   aligned) once and writes one value per thread to sink.  mode 0: 16-byte
+ *   vector loads by 8 workgroups of 512 threads per compute unit; mode 1:
+ *   whole 36864-byte pieces (bytes rounded down) through direct-to-LDS loads
+ *   into four rotating LDS buffers by one 512-thread workgroup per compute
+ *   unit, the way the decode attention moves its tiles.
+ * mla_probe_mfma: workgroups x 4 waves each run iterations x 4 independent
+ *   32x32x16 bf16 MFMAs on register operands (32768 FLOP each; workgroups of
+ *   256 threads); one value per thread to sink.
+ * Errors: MLA_ERR_INVALID_ARG for NULL or misaligned pointers, a too small
+ * buffer, an unknown mode or non-positive counts; MLA_ERR_HIP if the launch
+ * fails.  Nothing is allocated. */
+size_t mla_probe_sink_bytes(void);
+mla_status mla_probe_hbm_read(const void* buf, size_t bytes, int32_t mode, void* sink,
+                              void* stream);
+mla_status mla_probe_mfma(int32_t workgroups, int32_t iterations, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -98,6 +98,9 @@ SIGNATURES = {
     "mla_output_gate_projection": (_I, [_CFG, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "mla_prefill": (_I, [_CFG, _P, _P, _P, _FP, _P, _P, _FP, _P, _P, _FP, _I, _P, _I, _IP, _I,
                          _IP, _I, _I, _I, _P, _P, _SZ, _P]),
+    "mla_probe_sink_bytes": (_SZ, []),
+    "mla_probe_hbm_read": (_I, [_P, _SZ, _I, _P, _P]),
+    "mla_probe_mfma": (_I, [_I, _I, _P, _P]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():

@@ -438,3 +438,29 @@ def mla_output_gate_projection(cfg: MLAConfig, x, head_out, w_o, w_g=None, out=N
                                          out.data_ptr(), ws_ptr, ws_len, _stream(stream)),
           "mla_output_gate_projection")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Measurement probes (include/mla.h): the HBM read and bf16 MFMA ceilings.
+# ---------------------------------------------------------------------------
+def mla_probe_sink(device=None) -> torch.Tensor:
+    """A device buffer large enough for the probes' per-thread outputs."""
+    return torch.empty(lib.mla_probe_sink_bytes(), dtype=torch.uint8,
+                       device=device or torch.device("cuda"))
+
+
+def mla_probe_hbm_read(buf: torch.Tensor, mode: int, sink: torch.Tensor, stream=None) -> None:
+    """Read all of `buf` (device) once: mode 0 vector loads, mode 1
+    direct-to-LDS loads of 36864-byte pieces."""
+    _dev(buf, "buf", buf.dtype, tuple(buf.shape))
+    _dev(sink, "sink", torch.uint8, (lib.mla_probe_sink_bytes(),))
+    check(lib.mla_probe_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(), mode,
+                                 sink.data_ptr(), _stream(stream)), "mla_probe_hbm_read")
+
+
+def mla_probe_mfma(workgroups: int, iterations: int, sink: torch.Tensor, stream=None) -> int:
+    """Run the MFMA probe; returns the FLOPs it executes."""
+    _dev(sink, "sink", torch.uint8, (lib.mla_probe_sink_bytes(),))
+    check(lib.mla_probe_mfma(workgroups, iterations, sink.data_ptr(), _stream(stream)),
+          "mla_probe_mfma")
+    return workgroups * 4 * iterations * 4 * 32768
