@@ -11,10 +11,12 @@ Timing: after --warmup untimed steps, exactly --steps steps (rotating over
 the input sets) are captured in one HIP graph; the graph is replayed
 --repeats times, each replay bracketed by HIP events on the launching
 stream, and the median replay (with p10 and p90) divided by --steps is the
-step time.  The same steps issued eagerly from Python are timed the same
-way and reported beside it.  The split-KV attention kernel alone is timed
-the same way for the roofline entry.  The oracle is timed on the host cores
-on a bounded sample of the same workload.
+step time.  Unless --repeats is given, the replay count is chosen so that
+about 6000 steps are timed (at least 20 replays).  The same steps issued
+eagerly from Python are timed the same way and reported beside it.  The
+split-KV attention kernel alone is timed the same way for the roofline
+entry.  The oracle is timed on the host cores on a bounded sample of the
+same workload.
 """
 import argparse
 import hashlib
@@ -304,8 +306,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--repeats", type=int, default=20,
-                    help="graph replays of --steps steps each; the median is reported")
+    ap.add_argument("--repeats", type=int, default=0,
+                    help="graph replays of --steps steps each; the median is reported "
+                         "(default: enough replays for about 6000 timed steps, at least 20)")
     ap.add_argument("--workload", default=workloads.HEADLINE,
                     choices=[k for k, v in workloads.WORKLOADS.items() if v["dtype"] == "bf16"])
     ap.add_argument("--rotate", type=int, default=3)
@@ -324,9 +327,14 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.repeats < 1:
-        print("--steps and --repeats must be positive", file=sys.stderr)
+    if args.steps < 1 or args.repeats < 0:
+        print("--steps must be positive and --repeats not negative", file=sys.stderr)
         sys.exit(2)
+    if args.repeats == 0:
+        # Replays of a few steps last about a millisecond each, where clock and
+        # power management move single replays by 10 % and more: time enough of
+        # them that the median rests on several thousand steps.
+        args.repeats = max(20, -(-6000 // args.steps))
 
     import torch
     if args.copy_calibration_mb:
