@@ -137,21 +137,31 @@ __device__ __forceinline__ void issue_part(const bf16* rows, int valid, uint32_t
 
 // FP8 cache rows (R E4M3 codes | Dr bf16 rope values | float32 scale | 12
 // zero bytes, 656 bytes = 41 chunks; the softved article's advice to
-// quantize the cache, in a format it leaves open).  The tile loop is the same
-// as for bf16 rows: the P*C waves turn each staged tile into the bf16 tile
-// layout one step before the score waves use it, so the fragment reads and
-// MFMAs are unchanged, and HBM moves 656 instead of 1152 bytes per token.
-// LDS: two bf16 tile buffers (ping-pong) and three staging slots of 24 KB.
+// quantize the cache, in a format it leaves open).  Tiles stay FP8 in LDS:
+// the score waves widen the codes of their fragments in registers (scale 1)
+// and apply each row's power-of-two scale to its score, s = scale (q_lat .
+// code) + q_rope . k_rope; the P*C waves read the codes transposed and take
+// P scaled by the row's scale (exact in bf16), so O = sum P scale code.  HBM
+// and LDS move 656 instead of 1152 bytes per token, and six 24 KB staging
+// slots keep four tiles in flight.
 // A staged tile comes by 24 direct-to-LDS instructions of 1 KB, 3 per wave:
-// slot s < 1280 holds chunk s % 40 of row s / 40 (codes, rope key), slots
-// 1280 .. 1535 the scale chunk of row (s - 1280) % 32 (eight copies).  Rows
-// past `valid` repeat the last valid row.
+// slot s < 1280 is position s % 40 of row s / 40 (rows of 640 bytes: 32
+// code chunks, then 8 rope chunks), slots 1280 .. 1535 hold the scale chunk
+// of row (s - 1280) % 32 (eight copies).  Chunk c of row t sits at position
+// 8 (c / 8) + ((c % 8) ^ s8(t)): the 16 rows x 16 bytes of a score fragment
+// read and the 8 rows x 2 chunks of a transposing read (32 lanes each) then
+// fall on distinct bank slots.  Rows past `valid` repeat the last valid row.
 constexpr int kF8Row = kR + 2 * kDr + 16;               // 656 bytes
 constexpr int kF8Data = (kR + 2 * kDr) / 16;            // 40 data chunks per row
+constexpr int kF8RowBytes = kF8Data * 16;               // 640 bytes per staged row
+constexpr int kF8ScaleOff = kTok * kF8RowBytes;         // scale chunks of the slot
 constexpr int kF8Loads = 3;                             // per wave and tile
 constexpr int kF8StageBytes = 8 * kF8Loads * 1024;      // 24 KB
+constexpr int kF8Slots = 6;                             // tiles k-1, k and four in flight
 static_assert(kTok * kF8Data + kTok <= kF8StageBytes / 16, "staging slots");
-static_assert(2 * kTileBytes + 3 * kF8StageBytes <= kOffP, "FP8 LDS layout");
+static_assert(kF8Slots * kF8StageBytes <= kOffP, "FP8 LDS layout");
+
+__device__ __forceinline__ uint32_t s8(uint32_t t) { return (((t >> 1) & 3u) << 1) | ((t >> 3) & 1u); }
 
 __device__ __forceinline__ void issue_part_fp8(const unsigned char* rows, int valid, uint32_t stg,
                                                uint32_t j0, int lane) {
@@ -162,7 +172,8 @@ __device__ __forceinline__ void issue_part_fp8(const unsigned char* rows, int va
     uint32_t t, c;
     if (s < (uint32_t)(kTok * kF8Data)) {
       t = s / kF8Data;
-      c = s - t * kF8Data;
+      const uint32_t p = s - t * kF8Data;
+      c = (p & ~7u) | ((p & 7u) ^ s8(t));
     } else {
       t = (s - kTok * kF8Data) & (kTok - 1);
       c = kF8Data;
@@ -170,43 +181,6 @@ __device__ __forceinline__ void issue_part_fp8(const unsigned char* rows, int va
     const uint32_t tt = min(t, (uint32_t)(valid - 1));
     g2lds16(rows + tt * kF8Row + c * 16, stg + j * 1024u);
   }
-}
-
-// P*C wave pw turns a staged tile into the bf16 tile layout for its own
-// columns 128 pw .. 128 pw + 127 (the only ones it reads there, so it may
-// overwrite them right after its own P*C reads of the previous tile) and for
-// rows 8 pw .. 8 pw + 7 of the rope key (read by the score waves only, one
-// step later).  value = scale * code is exact in bf16 (a power-of-two scale,
-// 3 mantissa bits).  Staging reads: lanes 8 apart are consecutive rows, 640
-// bytes apart, so 16 lanes cover a 256-byte window once.
-__device__ __forceinline__ void convert_tile_fp8(uint32_t stg, uint32_t buf, int pw, int lane) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8v;
-  typedef __attribute__((address_space(3))) float lds_f32v;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t t = 8u * p + (uint32_t)(lane >> 3), i = 8u * pw + (uint32_t)(lane & 7);
-    const u32x4 raw = *(const lds_u32x4*)(uintptr_t)(stg + (t * kF8Data + i) * 16u);
-    const float sc = *(const lds_f32v*)(uintptr_t)(stg + (kTok * kF8Data + t) * 16u);
-    bf16x8 half[2];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      // dword d holds the codes of columns 16 i + 4 d .. 16 i + 4 d + 3
-      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[d], sc, false);
-      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[d], sc, true);
-      half[d >> 1][4 * (d & 1) + 0] = lo[0];
-      half[d >> 1][4 * (d & 1) + 1] = lo[1];
-      half[d >> 1][4 * (d & 1) + 2] = hi[0];
-      half[d >> 1][4 * (d & 1) + 3] = hi[1];
-    }
-    const uint32_t sw = swz(t);
-    *(lds_bf16x8v*)(uintptr_t)(buf + (t * kCh + ((2 * i) ^ sw)) * 16u) = half[0];
-    *(lds_bf16x8v*)(uintptr_t)(buf + (t * kCh + ((2 * i + 1) ^ sw)) * 16u) = half[1];
-  }
-  const uint32_t t = 8u * pw + (uint32_t)(lane >> 3), r = (uint32_t)(lane & 7);
-  const bf16x8 kr = *(const lds_bf16x8v*)(uintptr_t)(stg + (t * kF8Data + kR / 16 + r) * 16u);
-  *(lds_bf16x8v*)(uintptr_t)(buf + (t * kCh + ((kR / 8 + r) ^ swz(t))) * 16u) = kr;
 }
 
 // One segment: a query row (HEADS heads at q_rows, row stride kW) against
@@ -220,20 +194,12 @@ struct SegArgs {
   bool tile0_issued;      // tile0's loads already in flight into buffer 0
 };
 
-// Where the loads of local tile x go, and where the score and P*C waves read
-// it: the same buffer for bf16 rows (four, round robin); a staging slot
-// (three) and then one of two bf16 buffers for FP8 rows.
+// Where the loads of local tile x go and the waves read it: four bf16 tile
+// buffers or six FP8 staging slots, round robin.
 template <bool kFp8>
 __device__ __forceinline__ uint32_t load_slot(uint32_t lds, int x) {
   if constexpr (kFp8)
-    return lds + 2u * kTileBytes + (uint32_t)(x % 3) * kF8StageBytes;
-  else
-    return lds + (uint32_t)(x % kNBuf) * kTileBytes;
-}
-template <bool kFp8>
-__device__ __forceinline__ uint32_t tile_buf(uint32_t lds, int x) {
-  if constexpr (kFp8)
-    return lds + (uint32_t)(x & 1) * kTileBytes;
+    return lds + (uint32_t)(x % kF8Slots) * kF8StageBytes;
   else
     return lds + (uint32_t)(x % kNBuf) * kTileBytes;
 }
@@ -275,17 +241,14 @@ __device__ __forceinline__ void seg_start(const SegArgs& a, PageCursor& pc, uint
   if (!a.tile0_issued) issue_tile<kFp8, NL>(a, pc, a.tile0, load_slot<kFp8>(lds, 0), j0, lane);
 }
 
-// Step-top synchronisation shared by both wave roles: wait for this wave's
-// loads of tile k (tile k+1 may stay in flight), barrier, then issue tile
-// k+2 into the buffer tile k-2 used.  FP8 rows run one step ahead (steps
-// from -1): the loads of tile k+1 land for the P*C waves to convert during
-// step k, and tile k+3 goes into the staging slot tile k left.
-template <bool kFp8, int NL>
+// Step-top synchronisation shared by both wave roles (bf16 rows): wait for
+// this wave's loads of tile k (tile k+1 may stay in flight), barrier, then
+// issue tile k+2 into the buffer tile k-2 used.
+template <int NL>
 __device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint32_t lds,
                                           uint32_t j0, int k, int n, int lane) {
-  constexpr int A = kFp8 ? 1 : 0;
-  if (k + A < n) {
-    if (k + A + 1 < n)
+  if (k < n) {
+    if (k + 1 < n)
       wait_vmcnt<NL>();
     else
       wait_vmcnt<0>();
@@ -296,8 +259,7 @@ __device__ __forceinline__ void step_sync(const SegArgs& a, PageCursor& pc, uint
   // it reads a page id).
   asm volatile("" : "+v"(pc.cur), "+v"(pc.nxt));
   lds_barrier();
-  if (k + 2 + A < n)
-    issue_tile<kFp8, NL>(a, pc, a.tile0 + k + 2 + A, load_slot<kFp8>(lds, k + 2 + A), j0, lane);
+  if (k + 2 < n) issue_tile<false, NL>(a, pc, a.tile0 + k + 2, load_slot<false>(lds, k + 2), j0, lane);
 }
 
 // Queries of head 16 sw + lane%16, chunks 4 ks + lane/16 (the B operand of
@@ -314,24 +276,24 @@ __device__ __forceinline__ void load_queries(const bf16* q_rows, int sw, int lan
 // 16 sw + lane.  Inactive score waves (sw >= SW) only take part in loads and
 // barriers.  qf: the segment's queries when q_ready (loaded before the
 // segment's tiles), else loaded here.
-template <int HEADS, bool kFp8>
+template <int HEADS>
 __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int sw, int lane,
                                            bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,
                                            float& l_out) {
   using G = Geo<HEADS>;
   const bool active = sw < G::SW;
   const int n = a.tile1 - a.tile0;
-  constexpr int NL = tile_loads<kFp8>(true);
-  const uint32_t j0 = first_load<kFp8>(sw);
+  constexpr int NL = tile_loads<false>(true);
+  const uint32_t j0 = first_load<false>(sw);
   PageCursor pc;
-  seg_start<kFp8, NL>(a, pc, lds, j0, lane);
+  seg_start<false, NL>(a, pc, lds, j0, lane);
 
   const int h = 16 * sw + (lane & 15);
   const uint32_t kq = lane >> 4;
   if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
   // tile 0 and the queries (issued before tile 1) land; tile 1 may stay in flight
   if (n > 1) {
-    issue_tile<kFp8, NL>(a, pc, a.tile0 + 1, load_slot<kFp8>(lds, 1), j0, lane);
+    issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
     wait_vmcnt<NL>();
   } else {
     wait_vmcnt<0>();
@@ -350,10 +312,10 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
   const uint32_t pw_base = lds + kOffP + (h * kPStride + 4 * kq) * 2;
 
   float m = -INFINITY, l = 0.f;
-  for (int k = kFp8 ? -1 : 0; k <= n; ++k) {
-    step_sync<kFp8, NL>(a, pc, lds, j0, k, n, lane);
-    if (k < 0 || k == n || !active) continue;
-    const uint32_t buf = tile_buf<kFp8>(lds, k);
+  for (int k = 0; k <= n; ++k) {
+    step_sync<NL>(a, pc, lds, j0, k, n, lane);
+    if (k == n || !active) continue;
+    const uint32_t buf = load_slot<false>(lds, k);
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
       // Fragments (ks, tb = 0 and 1) are read kSAhead steps ahead of their
@@ -443,16 +405,16 @@ struct OAcc {
   f32x16 o[Geo<HEADS>::HB][4];
 };
 
-template <int HEADS, bool kFp8>
+template <int HEADS>
 __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, int lane,
                                         OAcc<HEADS>& acc) {
   using G = Geo<HEADS>;
   const int n = a.tile1 - a.tile0;
-  constexpr int NL = tile_loads<kFp8>(false);
-  const uint32_t j0 = first_load<kFp8>(4 + pw);
+  constexpr int NL = tile_loads<false>(false);
+  const uint32_t j0 = first_load<false>(4 + pw);
   PageCursor pc;
-  seg_start<kFp8, NL>(a, pc, lds, j0, lane);
-  if (n > 1) issue_tile<kFp8, NL>(a, pc, a.tile0 + 1, load_slot<kFp8>(lds, 1), j0, lane);
+  seg_start<false, NL>(a, pc, lds, j0, lane);
+  if (n > 1) issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
 #pragma unroll
   for (int hb = 0; hb < G::HB; ++hb)
 #pragma unroll
@@ -478,21 +440,11 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
   const uint32_t pa_base = lds + kOffP + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
   const uint32_t al_base = lds + kOffAlpha + (lane & 31) * 4;
 
-  for (int k = kFp8 ? -1 : 0; k <= n; ++k) {
-    step_sync<kFp8, NL>(a, pc, lds, j0, k, n, lane);
-    if constexpr (kFp8) {
-      // the FP8 tile the score waves take next, once this step's P*C reads
-      // of the buffer it replaces are done (in this wave's program order)
-      if (k < 1) {
-        if (k + 1 < n)
-          convert_tile_fp8(load_slot<true>(lds, k + 1), tile_buf<true>(lds, k + 1), pw, lane);
-        continue;
-      }
-    } else {
-      if (k == 0) continue;
-    }
+  for (int k = 0; k <= n; ++k) {
+    step_sync<NL>(a, pc, lds, j0, k, n, lane);
+    if (k == 0) continue;
     const int kp = k - 1;  // tile whose P is ready
-    const uint32_t buf = tile_buf<kFp8>(lds, kp);
+    const uint32_t buf = load_slot<false>(lds, kp);
     const uint32_t par = (uint32_t)(kp & 1);
     const f32x4 f = lds_ld4(lds + kOffFlag + par * 16);
     float fs = f[0] + f[1];
@@ -531,9 +483,350 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
         for (int hb = 0; hb < G::HB; ++hb) acc.o[hb][cb] = mfma32(bv, pa[hb], acc.o[hb][cb]);
       }
     }
-    if constexpr (kFp8) {
-      if (k + 1 < n)
-        convert_tile_fp8(load_slot<true>(lds, k + 1), tile_buf<true>(lds, k + 1), pw, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 rows: the tile loop on the staged codes (see the FP8 section above).
+// ---------------------------------------------------------------------------
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// LDS reads without a wait (completed by an lds_settle naming the registers).
+template <int OFF>
+__device__ __forceinline__ void ds_b64_nowait(u32x2& o, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+// Transposing 8-bit read: within each group of 16 lanes, output lane i byte j
+// is byte i % 8 of the 8 bytes addressed by lane 2 j + i / 8 of the group.
+template <int OFF>
+__device__ __forceinline__ void ds_tr8_nowait(u32x2& o, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_b32_nowait(float& o, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_b128f_nowait(f32x4& o, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(o) : "v"(a), "i"(OFF));
+}
+// Eight E4M3 codes (byte j is element j) as bf16, without a scale (exact).
+__device__ __forceinline__ bf16x8 widen8(const u32x2& c) {
+  bf16x8 r;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[d], 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[d], 1.0f, true);
+    r[4 * d + 0] = lo[0];
+    r[4 * d + 1] = lo[1];
+    r[4 * d + 2] = hi[0];
+    r[4 * d + 3] = hi[1];
+  }
+  return r;
+}
+
+// Step-top synchronisation for FP8 rows.  A segment starts with tiles 0 and
+// 1 in flight (seg_start, then the caller); step 0 waits for tile 0 and
+// issues tiles 2 .. 4; step k > 0 waits for tile k (tiles k+1 .. k+3 may
+// stay in flight) and issues tile k+4 into the slot tile k-2 left.
+template <int NL>
+__device__ __forceinline__ void step_sync_f8(const SegArgs& a, PageCursor& pc, uint32_t lds,
+                                             uint32_t j0, int k, int n, int lane) {
+  if (k < n) {
+    const int ahead = min(n - 1 - k, k == 0 ? 1 : 3);  // tiles issued after tile k
+    if (ahead >= 3)
+      wait_vmcnt<3 * NL>();
+    else if (ahead == 2)
+      wait_vmcnt<2 * NL>();
+    else if (ahead == 1)
+      wait_vmcnt<NL>();
+    else
+      wait_vmcnt<0>();
+  }
+  asm volatile("" : "+v"(pc.cur), "+v"(pc.nxt));  // landed before the tile loads
+  lds_barrier();
+  auto tile = [&](int x) {
+    if (x < n) issue_tile<true, NL>(a, pc, a.tile0 + x, load_slot<true>(lds, x), j0, lane);
+  };
+  if (k == 0) {
+    tile(2);
+    tile(3);
+  }
+  tile(k + 4);
+}
+
+// Score wave `sw` on FP8 rows: as score_role, with the fragments of the 512
+// latent columns read as codes (8 per lane) and widened in registers, the
+// two rope steps read as bf16, and s = scale (q_lat . code) + q_rope . k_rope.
+template <int HEADS>
+__device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, int sw, int lane,
+                                              bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,
+                                              float& l_out) {
+  using G = Geo<HEADS>;
+  const bool active = sw < G::SW;
+  const int n = a.tile1 - a.tile0;
+  constexpr int NL = kF8Loads;
+  const uint32_t j0 = first_load<true>(sw);
+  PageCursor pc;
+  seg_start<true, NL>(a, pc, lds, j0, lane);
+  const int h = 16 * sw + (lane & 15);
+  const uint32_t kq = lane >> 4;
+  if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
+  // tile 0 and the queries land; tile 1 may stay in flight
+  if (n > 1) {
+    issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
+    wait_vmcnt<NL>();
+  } else {
+    wait_vmcnt<0>();
+  }
+#pragma unroll
+  for (int ks = 0; ks < kW / 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+
+  // Fragment (ks, tb) of the latent: row t = lane%16 + 16 tb, codes 32 ks +
+  // 8 kq .. +7, i.e. chunk 2 ks + kq/2 (position by s8(t); s8(t + 16) =
+  // s8(t)), half kq%2.  Rope steps r = 0, 1: bf16 chunk 32 + 4 r + kq.
+  const uint32_t t0 = lane & 15, sx = s8(t0);
+  uint32_t lat_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    lat_off[i] = t0 * kF8RowBytes + (((2u * i + (kq >> 1)) ^ sx) * 16u) + 8u * (kq & 1u);
+  uint32_t rope_off[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) rope_off[r] = t0 * kF8RowBytes + (32u + ((4u * r + kq) ^ sx)) * 16u;
+  const uint32_t sc_off = kF8ScaleOff + 64u * kq;  // scale chunk of token 4 kq
+  const uint32_t pw_base = lds + kOffP + (h * kPStride + 4 * kq) * 2;
+  constexpr uint32_t kTb = 16 * kF8RowBytes;       // rows 16 .. 31
+
+  float m = -INFINITY, l = 0.f;
+  for (int k = 0; k <= n; ++k) {
+    step_sync_f8<NL>(a, pc, lds, j0, k, n, lane);
+    if (k == n || !active) continue;
+    const uint32_t stg = load_slot<true>(lds, k);
+    f32x4 sl[2] = {f32x4{}, f32x4{}}, sr[2] = {f32x4{}, f32x4{}};
+    // scales of tokens 16 tb + 4 kq + v, read first (LDS reads complete in order)
+    float sc[2][4];
+    {
+      const uint32_t sa = stg + sc_off;
+      ds_b32_nowait<0>(sc[0][0], sa);
+      ds_b32_nowait<16>(sc[0][1], sa);
+      ds_b32_nowait<32>(sc[0][2], sa);
+      ds_b32_nowait<48>(sc[0][3], sa);
+      ds_b32_nowait<256>(sc[1][0], sa);
+      ds_b32_nowait<272>(sc[1][1], sa);
+      ds_b32_nowait<288>(sc[1][2], sa);
+      ds_b32_nowait<304>(sc[1][3], sa);
+    }
+    {
+      // Reads go kSAhead steps ahead of their MFMAs; each step's fragments
+      // are settled and widened one step ahead, so the conversions of step
+      // ks + 1 issue while the MFMAs of step ks run.
+      constexpr int NK = kW / 32;  // 16 latent steps, then 2 rope steps
+      constexpr int A = kSAhead;
+      u32x2 lat[A + 1][2];
+      bf16x8 rope[2][2];
+      bf16x8 w[2][2];  // widened fragments of steps ks (index ks % 2), tb
+      auto issue = [&](int ks) {
+        if (ks < 16) {
+          const uint32_t ad = stg + lat_off[ks & 3] + 128u * (uint32_t)(ks >> 2);
+          ds_b64_nowait<0>(lat[ks % (A + 1)][0], ad);
+          ds_b64_nowait<kTb>(lat[ks % (A + 1)][1], ad);
+        } else {
+          const uint32_t ad = stg + rope_off[ks - 16];
+          ds_b128_nowait<0>(rope[ks - 16][0], ad);
+          ds_b128_nowait<kTb>(rope[ks - 16][1], ad);
+        }
+      };
+      // waits for step ks's reads (2 later reads per later step may stay
+      // in flight) and widens them
+      auto ready = [&](int ks, int later) {
+        if (ks < 16) {
+          u32x2(&f)[2] = lat[ks % (A + 1)];
+          switch (later) {
+            case 0: lds_settle<0>(f[0], f[1]); break;
+            case 1: lds_settle<2>(f[0], f[1]); break;
+            case 2: lds_settle<4>(f[0], f[1]); break;
+            default: lds_settle<6>(f[0], f[1]); break;
+          }
+          w[ks & 1][0] = widen8(f[0]);
+          w[ks & 1][1] = widen8(f[1]);
+        } else {
+          bf16x8(&f)[2] = rope[ks - 16];
+          switch (later) {
+            case 0: lds_settle<0>(f[0], f[1]); break;
+            default: lds_settle<2>(f[0], f[1]); break;
+          }
+          w[ks & 1][0] = f[0];
+          w[ks & 1][1] = f[1];
+        }
+      };
+      static_assert(A == 4, "settle counts of ready()");
+#pragma unroll
+      for (int i = 0; i < A; ++i) issue(i);
+      // the scales (issued first) have landed once at most 2 A reads remain
+      asm volatile("s_waitcnt lgkmcnt(%8)"
+                   : "+v"(sc[0][0]), "+v"(sc[0][1]), "+v"(sc[0][2]), "+v"(sc[0][3]),
+                     "+v"(sc[1][0]), "+v"(sc[1][1]), "+v"(sc[1][2]), "+v"(sc[1][3])
+                   : "i"(2 * A));
+      ready(0, A - 1);
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        if (ks + A < NK) issue(ks + A);
+        if (ks + 1 < NK) ready(ks + 1, min(A - 1, NK - 2 - ks));
+        if (ks < 16) {
+          sl[0] = mfma16(w[ks & 1][0], qf[ks], sl[0]);
+          sl[1] = mfma16(w[ks & 1][1], qf[ks], sl[1]);
+        } else {
+          sr[0] = mfma16(w[ks & 1][0], qf[ks], sr[0]);
+          sr[1] = mfma16(w[ks & 1][1], qf[ks], sr[1]);
+        }
+      }
+    }
+    // register v of block tb <-> token 16 tb + 4 kq + v, head h
+    const int valid = a.len - (a.tile0 + k) * kTok;
+    float s[2][4];
+    float hmax = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        s[tb][v] = 16 * tb + 4 * (int)kq + v >= valid ? -INFINITY
+                                                      : fmaf(sl[tb][v], sc[tb][v], sr[tb][v]);
+        hmax = fmaxf(hmax, s[tb][v]);
+      }
+    hmax = max_xor32(max_xor16(hmax));
+    const bool grow = hmax > m + kRescaleSlack;
+    const float m_new = grow ? hmax : m;
+    const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
+    const bool any = __ballot(grow) != 0ull;
+    const uint32_t pb = pw_base + (uint32_t)(k & 1) * (kMaxHG * kPStride * 2);
+    float psum = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      bf16x4 pk;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bf16 p = (bf16)fast_exp2(s[tb][v] - m_new);
+        psum += (float)p;
+        pk[v] = (bf16)((float)p * sc[tb][v]);  // exact: a power-of-two scale
+      }
+      lds_st(pb + tb * 32, pk);
+    }
+    l = l * alpha + psum;
+    m = m_new;
+    if (lane < 16) lds_st(lds + kOffAlpha + ((k & 1) * kMaxHG + h) * 4, alpha);
+    if (lane == 0) lds_st(lds + kOffFlag + ((k & 1) * 4 + sw) * 4, any ? 1.0f : 0.0f);
+  }
+  l = sum_xor32(sum_xor16(l));
+  m_out = m;
+  l_out = l;
+}
+
+// P*C wave `pw` on FP8 rows: as pv_role, with the A fragments (32 columns x
+// 16 tokens) read from the codes by one transposing 8-bit read each and
+// widened in registers; P carries the row scales.
+template <int HEADS>
+__device__ __forceinline__ void pv_role_f8(const SegArgs& a, uint32_t lds, int pw, int lane,
+                                           OAcc<HEADS>& acc) {
+  using G = Geo<HEADS>;
+  const int n = a.tile1 - a.tile0;
+  constexpr int NL = kF8Loads;
+  const uint32_t j0 = first_load<true>(4 + pw);
+  PageCursor pc;
+  seg_start<true, NL>(a, pc, lds, j0, lane);
+  if (n > 1) issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
+#pragma unroll
+  for (int hb = 0; hb < G::HB; ++hb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc.o[hb][cb] = f32x16{};
+
+  // Group g4 = lane/16 of the fragment for (ks, cb) holds columns 128 pw +
+  // 32 cb + 16 (g4 % 2) + 0..15 of tokens 16 ks + 8 (g4 / 2) + 0..7; lane li
+  // of the group addresses row 16 ks + 8 (g4 / 2) + li / 2, chunk 8 pw + 2 cb
+  // + g4 % 2, half li % 2 (s8 of the row does not depend on ks).
+  const uint32_t g4 = lane >> 4, li = lane & 15;
+  const uint32_t row = 8u * (g4 >> 1) + (li >> 1), sx = s8(row);
+  uint32_t tr_off[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    tr_off[cb] = row * kF8RowBytes + (8u * pw + ((2u * cb + (g4 & 1u)) ^ sx)) * 16u + 8u * (li & 1u);
+  constexpr uint32_t kKs = 16 * kF8RowBytes;  // tokens 16 .. 31
+  // P fragments (B operand of 32x32x16): head 32 hb + lane%32, tokens 16 ks + 8 (lane/32)
+  const uint32_t pa_base = lds + kOffP + ((lane & 31) * kPStride + 8 * (lane >> 5)) * 2;
+  const uint32_t al_base = lds + kOffAlpha + (lane & 31) * 4;
+  constexpr uint32_t kPHb = 32 * kPStride * 2;  // next 32 heads of P
+
+  for (int k = 0; k <= n; ++k) {
+    step_sync_f8<NL>(a, pc, lds, j0, k, n, lane);
+    if (k == 0) continue;
+    const int kp = k - 1;  // tile whose P is ready
+    const uint32_t stg = load_slot<true>(lds, kp);
+    const uint32_t par = (uint32_t)(kp & 1);
+    const uint32_t pbase = pa_base + par * (kMaxHG * kPStride * 2);
+    f32x4 f;
+    ds_b128f_nowait<0>(f, lds + kOffFlag + par * 16);
+    float al[G::HB];
+#pragma unroll
+    for (int hb = 0; hb < G::HB; ++hb) ds_b32_nowait<0>(al[hb], al_base + (par * kMaxHG + 32 * hb) * 4);
+    // both token blocks' reads: P (HB) and codes (4) of ks 0, then of ks 1
+    bf16x8 pa[2][G::HB];
+    u32x2 cr[2][4];
+#pragma unroll
+    for (int hb = 0; hb < G::HB; ++hb) ds_b128_nowait<0>(pa[0][hb], pbase + hb * kPHb);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) ds_tr8_nowait<0>(cr[0][cb], stg + tr_off[cb]);
+#pragma unroll
+    for (int hb = 0; hb < G::HB; ++hb) ds_b128_nowait<32>(pa[1][hb], pbase + hb * kPHb);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) ds_tr8_nowait<kKs>(cr[1][cb], stg + tr_off[cb]);
+    // flags and factors (issued first) have landed once the 2 (HB + 4) reads remain
+    constexpr int kLater = 2 * (G::HB + 4);
+    if constexpr (G::HB == 2)
+      asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(f), "+v"(al[0]), "+v"(al[1]) : "i"(kLater));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f), "+v"(al[0]) : "i"(kLater));
+    float fs = f[0] + f[1];
+    if (G::SW > 2) fs += f[2] + f[3];
+    if (fs != 0.0f) {
+#pragma unroll
+      for (int hb = 0; hb < G::HB; ++hb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc.o[hb][cb][v] *= al[hb];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks == 0) {
+        if constexpr (G::HB == 2)
+          asm volatile("s_waitcnt lgkmcnt(%6)"
+                       : "+v"(pa[0][0]), "+v"(pa[0][1]), "+v"(cr[0][0]), "+v"(cr[0][1]),
+                         "+v"(cr[0][2]), "+v"(cr[0][3])
+                       : "i"(G::HB + 4));
+        else
+          asm volatile("s_waitcnt lgkmcnt(%5)"
+                       : "+v"(pa[0][0]), "+v"(cr[0][0]), "+v"(cr[0][1]), "+v"(cr[0][2]),
+                         "+v"(cr[0][3])
+                       : "i"(G::HB + 4));
+      } else {
+        if constexpr (G::HB == 2)
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(pa[1][0]), "+v"(pa[1][1]), "+v"(cr[1][0]), "+v"(cr[1][1]),
+                         "+v"(cr[1][2]), "+v"(cr[1][3]));
+        else
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(pa[1][0]), "+v"(cr[1][0]), "+v"(cr[1][1]), "+v"(cr[1][2]),
+                         "+v"(cr[1][3]));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const bf16x8 bv = widen8(cr[ks][cb]);
+#pragma unroll
+        for (int hb = 0; hb < G::HB; ++hb) acc.o[hb][cb] = mfma32(bv, pa[ks][hb], acc.o[hb][cb]);
+      }
     }
   }
 }
@@ -561,7 +854,10 @@ __device__ __forceinline__ void score_segment(const SegArgs& a, uint32_t lds, bf
                                               int lane, bf16x8 (&qf)[kW / 32], bool q_ready,
                                               float& m_out, float& l_out) {
   using G = Geo<HEADS>;
-  score_role<HEADS, kFp8>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
+  if constexpr (kFp8)
+    score_role_f8<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
+  else
+    score_role<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
   if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
   lds_barrier();
   lds_barrier();
@@ -574,7 +870,10 @@ __device__ __forceinline__ void pv_segment(const SegArgs& a, uint32_t lds, bf16*
   using G = Geo<HEADS>;
   const int pw = wave - 4;
   OAcc<HEADS> acc;
-  pv_role<HEADS, kFp8>(a, lds, pw, lane, acc);
+  if constexpr (kFp8)
+    pv_role_f8<HEADS>(a, lds, pw, lane, acc);
+  else
+    pv_role<HEADS>(a, lds, pw, lane, acc);
   lds_barrier();
   // lane: head 32 hb + lane%32; register v of o[hb][cb]: column
   // 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 (runs of 4 -> 8-byte stores)
