@@ -1125,9 +1125,10 @@ __device__ __forceinline__ bool decode_attention_wg(
 // have in the equal-length layout (guessed from max_seq_len) before the
 // prefix sums (scalar loads) arrive, and reloaded only when the real layout
 // differs.  W_UV[h] (128 KB) streams into LDS with direct-to-LDS loads
-// issued after them, so it takes no registers and does not delay them; the
-// merge touches no LDS until its row is written, so nothing waits for W_UV
-// before that.  A piece is read only if its workgroup's range is non-empty
+// issued between the statistics and the piece values (it takes no
+// registers): the step is bound by the bytes it moves, so the values land
+// last whatever the order, and W_UV issued first is in LDS when the merged
+// rows are, instead of trailing them.  A piece is read only if its workgroup's range is non-empty
 // (with fewer tiles than workgroups some write nothing), so stale workspace
 // contents never enter the merge.
 // ---------------------------------------------------------------------------
@@ -1210,12 +1211,19 @@ __device__ __forceinline__ void combine_wg(const int* prefix, const float* __res
   constexpr int kStatPieces = 64 * kStats;
   bf16x8 v[kChunk];
   f32x2 ml_raw[kStats];
-  auto first_chunk = [&](const SeqPieces& q) {
+  auto first_stats = [&](const SeqPieces& q) {
     const int last = max(q.n, 1) - 1;
 #pragma unroll
     for (int i = 0; i < kStats; ++i) ml_raw[i] = ld_ml(q.slot0, min(64 * i + lane, last));
+  };
+  auto first_values = [&](const SeqPieces& q) {
+    const int last = max(q.n, 1) - 1;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) v[u] = ld_o(q.slot0, min(part + wps * u, last));
+  };
+  auto first_chunk = [&](const SeqPieces& q) {
+    first_stats(q);
+    first_values(q);
   };
   auto settle_first_chunk = [&]() {
     wait_vmcnt<0>();
@@ -1233,8 +1241,12 @@ __device__ __forceinline__ void combine_wg(const int* prefix, const float* __res
     g.n = gsplit.owner((bw0 + 1) * guess_tiles - 1) - g.f + 1;
   }
   g.slot0 = (long)hg * n_slots + g.f + min(bw0, batch - 1);
-  first_chunk(g);
+  // statistics, then W_UV, then the piece values: the values arrive last in
+  // any order (the bytes are bound by HBM), and W_UV is then in LDS by the
+  // time the merged rows are
+  first_stats(g);
   if constexpr (kProject) issue_w_uv(w_uv + (long)h * kR * Dv, Dv, wb, wave, lane);
+  first_values(g);
 
   const StreamSplit split(prefix[batch], n_wg);
   auto pieces = [&](int b) {
