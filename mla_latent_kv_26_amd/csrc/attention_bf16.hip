@@ -192,6 +192,7 @@ struct SegArgs {
   int max_blocks, shift, len, tile0, tile1;
   const PageCursor* pre;  // page ids already loaded for tile0's page, or null
   bool tile0_issued;      // tile0's loads already in flight into buffer 0
+  bool tile1_issued;      // and tile0 + 1's into buffer 1
 };
 
 // Where the loads of local tile x go and the waves read it: four bf16 tile
@@ -293,7 +294,7 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
   if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
   // tile 0 and the queries (issued before tile 1) land; tile 1 may stay in flight
   if (n > 1) {
-    issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
+    if (!a.tile1_issued) issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
     wait_vmcnt<NL>();
   } else {
     wait_vmcnt<0>();
@@ -414,7 +415,8 @@ __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, 
   const uint32_t j0 = first_load<false>(4 + pw);
   PageCursor pc;
   seg_start<false, NL>(a, pc, lds, j0, lane);
-  if (n > 1) issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
+  if (n > 1 && !a.tile1_issued)
+    issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
 #pragma unroll
   for (int hb = 0; hb < G::HB; ++hb)
 #pragma unroll
@@ -578,7 +580,7 @@ __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, in
   if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
   // tile 0 and the queries land; tile 1 may stay in flight
   if (n > 1) {
-    issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
+    if (!a.tile1_issued) issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
     wait_vmcnt<NL>();
   } else {
     wait_vmcnt<0>();
@@ -737,7 +739,8 @@ __device__ __forceinline__ void pv_role_f8(const SegArgs& a, uint32_t lds, int p
   const uint32_t j0 = first_load<true>(4 + pw);
   PageCursor pc;
   seg_start<true, NL>(a, pc, lds, j0, lane);
-  if (n > 1) issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
+  if (n > 1 && !a.tile1_issued)
+    issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
 #pragma unroll
   for (int hb = 0; hb < G::HB; ++hb)
 #pragma unroll
@@ -1002,9 +1005,12 @@ __device__ __forceinline__ bool decode_attention_wg(
   // chunk now, in parallel with the lengths, and keep it if the guess holds.
   // As soon as the ids land, the guessed first tile (as a full tile) goes in
   // flight into buffer 0, then the guessed sequence's queries (score waves),
-  // overlapping the prefix sums and the range search; a page id outside the
-  // pool is never dereferenced.  (Issuing three tiles there measured slower:
-  // the opening burst delays every workgroup's first tile.)
+  // then the guessed second tile into buffer 1, overlapping the prefix sums
+  // and the range search; a page id outside the pool is never dereferenced.
+  // (The first step waits for the second tile too: the queries are registers
+  // loaded before direct-to-LDS loads, which the compiler completes by
+  // draining every load in flight.  Issuing a third tile here measured
+  // slower: the opening burst delays every workgroup's first tiles.)
   const StreamSplit gsplit(batch * guess_tiles, n_wg);
   const int xg = gsplit.start(w);
   const int bg = min(xg / guess_tiles, batch - 1);
@@ -1014,25 +1020,32 @@ __device__ __forceinline__ bool decode_attention_wg(
   spec.start(block_table + (long)bg * max_blocks, max_blocks, pg0, lane);
   bf16x8 qf[kW / 32];  // score waves: the queries of sequence qb
   int qb = -1;
-  bool spec_issued = false;
+  bool spec_issued = false, spec2 = false;
+  // guessed tile tg0 + t (as a full tile) into buffer t; false if its page
+  // id is outside the pool (then nothing is issued)
+  auto spec_tile = [&](int t) {
+    const int tok = (tg0 + t) * kTok;
+    const int page = spec.page(tok >> shift, lane);  // page index pg0 or pg0 + 1
+    if (page < 0 || page >= num_blocks) return false;
+    const long row = (long)page * (1 << shift) + (tok & ((1 << shift) - 1));
+    if constexpr (kFp8)
+      issue_part_fp8((const unsigned char*)pool + row * kF8Row, kTok, load_slot<true>(lds, t),
+                     first_load<true>(wave), lane);
+    else if (wave < 4)
+      issue_part<kSLoads>(pool + row * kW, kTok, load_slot<false>(lds, t), first_load<false>(wave),
+                          lane);
+    else
+      issue_part<kPLoads>(pool + row * kW, kTok, load_slot<false>(lds, t), first_load<false>(wave),
+                          lane);
+    return true;
+  };
   auto early = [&]() {
-    const int page = spec.page(pg0, lane);
-    if (page >= 0 && page < num_blocks) {
-      const int tok = tg0 * kTok;
-      const long row = (long)page * (1 << shift) + (tok & ((1 << shift) - 1));
-      if constexpr (kFp8)
-        issue_part_fp8((const unsigned char*)pool + row * kF8Row, kTok, load_slot<true>(lds, 0),
-                       first_load<true>(wave), lane);
-      else if (wave < 4)
-        issue_part<kSLoads>(pool + row * kW, kTok, lds, first_load<false>(wave), lane);
-      else
-        issue_part<kPLoads>(pool + row * kW, kTok, lds, first_load<false>(wave), lane);
-      spec_issued = true;
-    }
+    spec_issued = spec_tile(0);
     if (wave < Geo<HEADS>::SW) {
       load_queries(q_full + ((long)bg * H + hg * HEADS) * kW, wave, lane, qf);
       qb = bg;
     }
+    if (spec_issued && tg0 + 1 < guess_tiles) spec2 = spec_tile(1);
   };
 
   tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo, early);
@@ -1078,11 +1091,13 @@ __device__ __forceinline__ bool decode_attention_wg(
       // the speculative tile is this segment's tile 0 only if it is the same
       // tile and a full one (a partial tile repeats its last row instead)
       const bool reuse = spec_issued && guessed && tile0 == tg0 && (tile0 + 1) * kTok <= len;
-      if (spec_issued && !reuse) wait_vmcnt<0>();  // its loads land before buffer 0 is refilled
+      const bool reuse2 = reuse && spec2 && tile1 - tile0 >= 2 && (tile0 + 2) * kTok <= len;
+      // speculative loads not taken over land before their buffers are refilled
+      if (spec_issued && !(reuse && (reuse2 || !spec2))) wait_vmcnt<0>();
       const SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool,
                       block_table + (long)b * max_blocks, max_blocks, shift, len, tile0, tile1,
-                      guessed ? &spec : nullptr, reuse};
-      spec_issued = false;
+                      guessed ? &spec : nullptr, reuse, reuse2};
+      spec_issued = spec2 = false;
       segment(a, b, slot);
       x = seg_end;
       ++b;
