@@ -561,13 +561,117 @@ __device__ __forceinline__ void step_sync_f8(const SegArgs& a, PageCursor& pc, u
   tile(k + 4);
 }
 
-// Score wave `sw` on FP8 rows: as score_role, with the fragments of the 512
-// latent columns read as codes (8 per lane) and widened in registers, the
-// two rope steps read as bf16, and s = scale (q_lat . code) + q_rope . k_rope.
+// Query split for the FP8 score MFMAs: a bf16 value has 8 significant
+// bits and an e4m3 code 4, so two e4m3 terms hold it (hi = e4m3(q / 2^e1),
+// lo = e4m3((q - 2^e1 hi) / 2^e2), one power-of-two scale per head and
+// term); what is left is below 2^-20 of the head's largest value.
+typedef int v8i __attribute__((ext_vector_type(8)));
+// smallest e with amax / 2^e <= 448 (exact: amax = m 2^E, m in [0.5, 1))
+__device__ __forceinline__ int e4m3_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float m = frexpf(amax, &E);
+  return max(-127, min(127, m <= 0.875f ? E - 9 : E - 8));
+}
+// e4m3 codes of a / s .. d / s (round to nearest even) in one dword
+__device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d, float s) {
+  typedef short __attribute__((ext_vector_type(2))) short2v;
+  const short2v lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2v{0, 0}, a, b, s, false);
+  const short2v pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c, d, s, true);
+  return __builtin_bit_cast(int, pk);
+}
+// A score wave's queries in the form its FP8 MFMAs take: the latent part as
+// hi and lo terms in the byte order of the code fragments (step kc, byte
+// 8 i + j holds qf[4 kc + i][j]) with their E8M0 scale bytes eb1, eb2 (127 +
+// e), the rope part as bf16.
+struct QSplit {
+  v8i qh[4], ql[4];
+  bf16x8 qr[2];
+  int eb1, eb2;
+};
+__device__ __forceinline__ void split_queries(bf16x8 (&qf)[kW / 32], QSplit& qs) {
+  v8i(&qh)[4] = qs.qh;
+  v8i(&ql)[4] = qs.ql;
+  // Three passes over the 128 values; between them the inputs are handed on
+  // through empty asm statements, so each pass converts its values again
+  // instead of keeping all of them live in registers.
+  auto launder = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+v"(qf[ks]));
+  };
+  float amax = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)qf[ks][j]));
+  amax = max_xor32(max_xor16(amax));  // the head's four lanes
+  const int e1 = e4m3_exp(amax);
+  const float s1 = ldexpf(1.0f, e1);
+  launder();
+  float rmax = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const bf16x8& q = qf[4 * kc + (d >> 1)];
+      const int j = 4 * (d & 1);
+      const float v0 = (float)q[j], v1 = (float)q[j + 1], v2 = (float)q[j + 2], v3 = (float)q[j + 3];
+      qh[kc][d] = pack4_e4m3(v0, v1, v2, v3, s1);
+      const auto f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((unsigned)qh[kc][d], s1, false);
+      const auto f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((unsigned)qh[kc][d], s1, true);
+      rmax = fmaxf(rmax, fmaxf(fmaxf(fabsf(v0 - f01[0]), fabsf(v1 - f01[1])),
+                               fmaxf(fabsf(v2 - f23[0]), fabsf(v3 - f23[1]))));
+    }
+  rmax = max_xor32(max_xor16(rmax));
+  const int e2 = e4m3_exp(rmax);
+  const float s2 = ldexpf(1.0f, e2);
+  launder();
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) asm volatile("" : "+v"(qh[kc]));
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const bf16x8& q = qf[4 * kc + (d >> 1)];
+      const int j = 4 * (d & 1);
+      const auto f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((unsigned)qh[kc][d], s1, false);
+      const auto f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((unsigned)qh[kc][d], s1, true);
+      ql[kc][d] = pack4_e4m3((float)q[j] - f01[0], (float)q[j + 1] - f01[1],
+                             (float)q[j + 2] - f23[0], (float)q[j + 3] - f23[1], s2);
+    }
+  qs.eb1 = 127 + e1;
+  qs.eb2 = 127 + e2;
+  qs.qr[0] = qf[16];
+  qs.qr[1] = qf[17];
+}
+// Waits until at most N LDS operations of this wave are outstanding and
+// hands the four named registers on as written here.
+template <int N>
+__device__ __forceinline__ void lds_settle4(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+__device__ __forceinline__ v8i cat4(const u32x2& a, const u32x2& b, const u32x2& c,
+                                    const u32x2& d) {
+  return v8i{(int)a[0], (int)a[1], (int)b[0], (int)b[1], (int)c[0], (int)c[1], (int)d[0], (int)d[1]};
+}
+// 16x16x128 e4m3 MFMA with E8M0 scales (the A scale of row r is taken from
+// the lanes holding row r, the B scale of column n from the lanes holding
+// column n; each is the same in all four of them here, so how the blocks of
+// 32 map to lanes does not matter).  Same accumulator layout as mfma16.
+__device__ __forceinline__ f32x4 mfma_f8(const v8i& a, const v8i& b, const f32x4& c, int sa,
+                                         int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Score wave `sw` on FP8 rows: the codes of the 512 latent columns go into
+// e4m3 MFMAs as they are, with the row's scale as the A scale and the
+// split queries (hi and lo terms) as B: s = scale (q_lat . code) + q_rope .
+// k_rope in one accumulator (the rope steps are bf16 MFMAs).  A fragment
+// (step kc, tb): row t = lane%16 + 16 tb, codes 128 kc + 32 i + 8 kq .. +7
+// for i = 0 .. 3 (four 8-byte reads, the byte order of the split queries).
 template <int HEADS>
 __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, int sw, int lane,
-                                              bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,
-                                              float& l_out) {
+                                              float& m_out, float& l_out) {
   using G = Geo<HEADS>;
   const bool active = sw < G::SW;
   const int n = a.tile1 - a.tile0;
@@ -577,7 +681,9 @@ __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, in
   seg_start<true, NL>(a, pc, lds, j0, lane);
   const int h = 16 * sw + (lane & 15);
   const uint32_t kq = lane >> 4;
-  if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
+  // this segment's queries (bf16), split once they land
+  bf16x8 qt[kW / 32];
+  if (active) load_queries(a.q_rows, sw, lane, qt);
   // tile 0 and the queries land; tile 1 may stay in flight
   if (n > 1) {
     if (!a.tile1_issued) issue_tile<true, NL>(a, pc, a.tile0 + 1, load_slot<true>(lds, 1), j0, lane);
@@ -585,12 +691,16 @@ __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, in
   } else {
     wait_vmcnt<0>();
   }
+  QSplit qs;
+  if (active) {
 #pragma unroll
-  for (int ks = 0; ks < kW / 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+    for (int ks = 0; ks < kW / 32; ++ks) asm volatile("" : "+v"(qt[ks]));
+    split_queries(qt, qs);
+  }
 
-  // Fragment (ks, tb) of the latent: row t = lane%16 + 16 tb, codes 32 ks +
-  // 8 kq .. +7, i.e. chunk 2 ks + kq/2 (position by s8(t); s8(t + 16) =
-  // s8(t)), half kq%2.  Rope steps r = 0, 1: bf16 chunk 32 + 4 r + kq.
+  // Code reads of step ks (i = ks % 4 of group kc = ks / 4): chunk 2 ks +
+  // kq/2 of row t (position by s8(t); s8(t + 16) = s8(t)), half kq%2.  Rope
+  // steps r = 0, 1: bf16 chunk 32 + 4 r + kq.
   const uint32_t t0 = lane & 15, sx = s8(t0);
   uint32_t lat_off[4];
 #pragma unroll
@@ -599,18 +709,24 @@ __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, in
   uint32_t rope_off[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) rope_off[r] = t0 * kF8RowBytes + (32u + ((4u * r + kq) ^ sx)) * 16u;
-  const uint32_t sc_off = kF8ScaleOff + 64u * kq;  // scale chunk of token 4 kq
+  const uint32_t sc_off = kF8ScaleOff + 64u * kq;   // scale chunk of token 4 kq
+  const uint32_t rs_off = kF8ScaleOff + 16u * t0;   // scale chunk of row t0
   const uint32_t pw_base = lds + kOffP + (h * kPStride + 4 * kq) * 2;
-  constexpr uint32_t kTb = 16 * kF8RowBytes;       // rows 16 .. 31
+  constexpr uint32_t kTb = 16 * kF8RowBytes;        // rows 16 .. 31
 
   float m = -INFINITY, l = 0.f;
   for (int k = 0; k <= n; ++k) {
     step_sync_f8<NL>(a, pc, lds, j0, k, n, lane);
     if (k == n || !active) continue;
     const uint32_t stg = load_slot<true>(lds, k);
-    f32x4 sl[2] = {f32x4{}, f32x4{}}, sr[2] = {f32x4{}, f32x4{}};
-    // scales of tokens 16 tb + 4 kq + v, read first (LDS reads complete in order)
-    float sc[2][4];
+    // the hi terms (with the rope steps) and the lo terms accumulate apart:
+    // four independent MFMA chains instead of two
+    f32x4 sacc[2] = {f32x4{}, f32x4{}}, slo[2] = {f32x4{}, f32x4{}};
+    // scales of tokens 16 tb + 4 kq + v (for P), of rows t0 and t0 + 16
+    // (the A scales) and the rope fragments, read first (LDS reads complete
+    // in order)
+    float sc[2][4], rs[2];
+    bf16x8 rope[2][2];
     {
       const uint32_t sa = stg + sc_off;
       ds_b32_nowait<0>(sc[0][0], sa);
@@ -621,83 +737,76 @@ __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, in
       ds_b32_nowait<272>(sc[1][1], sa);
       ds_b32_nowait<288>(sc[1][2], sa);
       ds_b32_nowait<304>(sc[1][3], sa);
+      ds_b32_nowait<0>(rs[0], stg + rs_off);
+      ds_b32_nowait<256>(rs[1], stg + rs_off);
+      ds_b128_nowait<0>(rope[0][0], stg + rope_off[0]);
+      ds_b128_nowait<kTb>(rope[0][1], stg + rope_off[0]);
+      ds_b128_nowait<0>(rope[1][0], stg + rope_off[1]);
+      ds_b128_nowait<kTb>(rope[1][1], stg + rope_off[1]);
     }
     {
-      // Reads go kSAhead steps ahead of their MFMAs; each step's fragments
-      // are settled and widened one step ahead, so the conversions of step
-      // ks + 1 issue while the MFMAs of step ks run.
-      constexpr int NK = kW / 32;  // 16 latent steps, then 2 rope steps
-      constexpr int A = kSAhead;
-      u32x2 lat[A + 1][2];
-      bf16x8 rope[2][2];
-      bf16x8 w[2][2];  // widened fragments of steps ks (index ks % 2), tb
-      auto issue = [&](int ks) {
-        if (ks < 16) {
-          const uint32_t ad = stg + lat_off[ks & 3] + 128u * (uint32_t)(ks >> 2);
-          ds_b64_nowait<0>(lat[ks % (A + 1)][0], ad);
-          ds_b64_nowait<kTb>(lat[ks % (A + 1)][1], ad);
+      // groups g = 0 .. 7 (kc = g / 2, tb = g % 2) of four 8-byte reads,
+      // one group ahead of its MFMAs
+      constexpr int NG = 8, A = 1;
+      u32x2 grp[A + 1][4];
+      auto issue = [&](int g) {
+        const uint32_t ad = stg + 128u * (uint32_t)(g >> 1);
+        u32x2(&f)[4] = grp[g % (A + 1)];
+        if (g & 1) {
+          ds_b64_nowait<kTb>(f[0], ad + lat_off[0]);
+          ds_b64_nowait<kTb>(f[1], ad + lat_off[1]);
+          ds_b64_nowait<kTb>(f[2], ad + lat_off[2]);
+          ds_b64_nowait<kTb>(f[3], ad + lat_off[3]);
         } else {
-          const uint32_t ad = stg + rope_off[ks - 16];
-          ds_b128_nowait<0>(rope[ks - 16][0], ad);
-          ds_b128_nowait<kTb>(rope[ks - 16][1], ad);
+          ds_b64_nowait<0>(f[0], ad + lat_off[0]);
+          ds_b64_nowait<0>(f[1], ad + lat_off[1]);
+          ds_b64_nowait<0>(f[2], ad + lat_off[2]);
+          ds_b64_nowait<0>(f[3], ad + lat_off[3]);
         }
       };
-      // waits for step ks's reads (2 later reads per later step may stay
-      // in flight) and widens them
-      auto ready = [&](int ks, int later) {
-        if (ks < 16) {
-          u32x2(&f)[2] = lat[ks % (A + 1)];
-          switch (later) {
-            case 0: lds_settle<0>(f[0], f[1]); break;
-            case 1: lds_settle<2>(f[0], f[1]); break;
-            case 2: lds_settle<4>(f[0], f[1]); break;
-            default: lds_settle<6>(f[0], f[1]); break;
-          }
-          w[ks & 1][0] = widen8(f[0]);
-          w[ks & 1][1] = widen8(f[1]);
-        } else {
-          bf16x8(&f)[2] = rope[ks - 16];
-          switch (later) {
-            case 0: lds_settle<0>(f[0], f[1]); break;
-            default: lds_settle<2>(f[0], f[1]); break;
-          }
-          w[ks & 1][0] = f[0];
-          w[ks & 1][1] = f[1];
-        }
-      };
-      static_assert(A == 4, "settle counts of ready()");
 #pragma unroll
-      for (int i = 0; i < A; ++i) issue(i);
-      // the scales (issued first) have landed once at most 2 A reads remain
-      asm volatile("s_waitcnt lgkmcnt(%8)"
+      for (int g = 0; g < A; ++g) issue(g);
+      // the scales and rope fragments (issued first) have landed once at
+      // most 4 A reads remain
+      asm volatile("s_waitcnt lgkmcnt(%14)"
                    : "+v"(sc[0][0]), "+v"(sc[0][1]), "+v"(sc[0][2]), "+v"(sc[0][3]),
-                     "+v"(sc[1][0]), "+v"(sc[1][1]), "+v"(sc[1][2]), "+v"(sc[1][3])
-                   : "i"(2 * A));
-      ready(0, A - 1);
+                     "+v"(sc[1][0]), "+v"(sc[1][1]), "+v"(sc[1][2]), "+v"(sc[1][3]), "+v"(rs[0]),
+                     "+v"(rs[1]), "+v"(rope[0][0]), "+v"(rope[0][1]), "+v"(rope[1][0]),
+                     "+v"(rope[1][1])
+                   : "i"(4 * A));
+      // E8M0 bytes of the row scales (a power of two: its exponent field)
+      const int rb0 = (int)((__builtin_bit_cast(unsigned, rs[0]) >> 23) & 255u);
+      const int rb1 = (int)((__builtin_bit_cast(unsigned, rs[1]) >> 23) & 255u);
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        if (ks + A < NK) issue(ks + A);
-        if (ks + 1 < NK) ready(ks + 1, min(A - 1, NK - 2 - ks));
-        if (ks < 16) {
-          sl[0] = mfma16(w[ks & 1][0], qf[ks], sl[0]);
-          sl[1] = mfma16(w[ks & 1][1], qf[ks], sl[1]);
-        } else {
-          sr[0] = mfma16(w[ks & 1][0], qf[ks], sr[0]);
-          sr[1] = mfma16(w[ks & 1][1], qf[ks], sr[1]);
-        }
+      for (int r = 0; r < 2; ++r) {
+        sacc[0] = mfma16(rope[r][0], qs.qr[r], sacc[0]);
+        sacc[1] = mfma16(rope[r][1], qs.qr[r], sacc[1]);
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g + A < NG) issue(g + A);
+        u32x2(&f)[4] = grp[g % (A + 1)];
+        if (g + 1 < NG)
+          lds_settle4<4 * A>(f[0], f[1], f[2], f[3]);
+        else
+          lds_settle4<0>(f[0], f[1], f[2], f[3]);
+        const v8i av = cat4(f[0], f[1], f[2], f[3]);
+        const int tb = g & 1, kc = g >> 1;
+        sacc[tb] = mfma_f8(av, qs.qh[kc], sacc[tb], tb ? rb1 : rb0, qs.eb1);
+        slo[tb] = mfma_f8(av, qs.ql[kc], slo[tb], tb ? rb1 : rb0, qs.eb2);
       }
     }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) sacc[tb] += slo[tb];
     // register v of block tb <-> token 16 tb + 4 kq + v, head h
     const int valid = a.len - (a.tile0 + k) * kTok;
-    float s[2][4];
     float hmax = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        s[tb][v] = 16 * tb + 4 * (int)kq + v >= valid ? -INFINITY
-                                                      : fmaf(sl[tb][v], sc[tb][v], sr[tb][v]);
-        hmax = fmaxf(hmax, s[tb][v]);
+        if (16 * tb + 4 * (int)kq + v >= valid) sacc[tb][v] = -INFINITY;
+        hmax = fmaxf(hmax, sacc[tb][v]);
       }
     hmax = max_xor32(max_xor16(hmax));
     const bool grow = hmax > m + kRescaleSlack;
@@ -711,7 +820,7 @@ __device__ __forceinline__ void score_role_f8(const SegArgs& a, uint32_t lds, in
       bf16x4 pk;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const bf16 p = (bf16)fast_exp2(s[tb][v] - m_new);
+        const bf16 p = (bf16)fast_exp2(sacc[tb][v] - m_new);
         psum += (float)p;
         pk[v] = (bf16)((float)p * sc[tb][v]);  // exact: a power-of-two scale
       }
@@ -858,7 +967,7 @@ __device__ __forceinline__ void score_segment(const SegArgs& a, uint32_t lds, bf
                                               float& m_out, float& l_out) {
   using G = Geo<HEADS>;
   if constexpr (kFp8)
-    score_role_f8<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
+    score_role_f8<HEADS>(a, lds, wave, lane, m_out, l_out);
   else
     score_role<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
   if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
@@ -1041,7 +1150,7 @@ __device__ __forceinline__ bool decode_attention_wg(
   };
   auto early = [&]() {
     spec_issued = spec_tile(0);
-    if (wave < Geo<HEADS>::SW) {
+    if (!kFp8 && wave < Geo<HEADS>::SW) {  // FP8: each segment loads and splits its own
       load_queries(q_full + ((long)bg * H + hg * HEADS) * kW, wave, lane, qf);
       qb = bg;
     }
