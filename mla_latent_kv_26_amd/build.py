@@ -2,7 +2,8 @@
 
 Compiles every source under csrc/ for gfx950 with hipcc (one process per
 source, in parallel), then links them.  Packed-fp32 VALU instructions are
-disabled for all device code.
+disabled for all device code; kernel arguments are preloaded into scalar
+registers where the hardware supports it.
 """
 import os
 import subprocess
@@ -18,6 +19,9 @@ ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # leading kernel arguments arrive in scalar registers at wave
+         # launch instead of through a scalar load each kernel starts with
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

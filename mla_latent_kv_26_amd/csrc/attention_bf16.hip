@@ -1046,17 +1046,19 @@ struct StreamSplit {
 // Prefix sums of tiles per sequence into LDS prefix[0..batch] (2 sequences
 // per thread, then a scan); optionally (len - 1) % kTok per sequence into
 // lenlo, so a length needs no further global read.  All kThreads threads
-// call it; ends with a barrier.  `early` runs once the lengths have landed
-// and before the scan: loads it issues overlap the rest (the barriers here
-// are LDS-only, so they do not wait for them).
-template <typename Early>
+// call it; ends with a barrier.  `issued` runs once the length loads are in
+// flight and before they are waited for.  `early` runs once the lengths have
+// landed and before the scan: loads it issues overlap the rest (the barriers
+// here are LDS-only, so they do not wait for them).
+template <typename Issued, typename Early>
 __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, int batch,
                                             int* prefix, int* scan, unsigned char* lenlo,
-                                            Early&& early) {
+                                            Issued&& issued, Early&& early) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int lens[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) lens[i] = tid * 2 + i < batch ? seq_lens[tid * 2 + i] : 0;
+  issued();
   // the lengths are plain values from here on: no wait below is tied to them
   asm volatile("" : "+v"(lens[0]), "+v"(lens[1]));
   early();
@@ -1097,10 +1099,10 @@ __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, in
 // along the stream).  Returns whether this workgroup wrote any piece.
 template <int HEADS, bool kFp8>
 __device__ __forceinline__ bool decode_attention_wg(
-    char* smem, int blk, const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
-    const int* __restrict__ block_table, int max_blocks, int shift, int num_blocks,
-    const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
-    int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
+    char* smem, int blk, const int* __restrict__ seq_lens, const int* __restrict__ block_table,
+    const bf16* __restrict__ pool, int H, int n_wg, int batch, int guess_tiles, int max_blocks,
+    int shift, int num_blocks, const bf16* __restrict__ q_full, int* __restrict__ prefix_out,
+    float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   const uint32_t lds = lds_addr(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hgc = H / HEADS;
@@ -1157,7 +1159,17 @@ __device__ __forceinline__ bool decode_attention_wg(
     if (spec_issued && tg0 + 1 < guess_tiles) spec2 = spec_tile(1);
   };
 
-  tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo, early);
+  // The arguments past the ones the hardware preloads into scalar registers
+  // are scalar loads from the argument segment, which the compiler would
+  // issue and wait for where first used (the queries, the epilogue): fetched
+  // here, their round trip overlaps that of the lengths and page ids.
+  auto issued = [&]() {
+    fetch_arg(q_full);
+    fetch_arg(prefix_out);
+    fetch_arg(part_ml);
+    fetch_arg(part_o);
+  };
+  tile_prefix(seq_lens, batch, prefix, (int*)(smem + kOffScan), lenlo, issued, early);
   const int T = prefix[batch];
   if (blk == 0)
     for (int b = tid; b <= batch; b += kThreads) prefix_out[b] = prefix[b];
@@ -1371,11 +1383,23 @@ __device__ __forceinline__ void combine_wg(const int* prefix, const float* __res
   first_stats(g);
   if constexpr (kProject) issue_w_uv(w_uv + (long)h * kR * Dv, Dv, wb, wave, lane);
   first_values(g);
+  // The prefix sums are scalar loads, and a scalar load is waited for with
+  // lgkmcnt(0) at its first use: hoisted above the loads just issued, they
+  // would hold their issue back by a whole round trip.  The output pointer
+  // (an argument past the preloaded ones) is fetched here too, not in the
+  // epilogue.
+  fetch_arg(out);
+  asm volatile("" ::: "memory");
 
-  const StreamSplit split(prefix[batch], n_wg);
+  // the first sequence's prefix sums load with the total (one round trip)
+  const int T = prefix[batch];
+  const int first_p0 = bw0 < batch ? prefix[bw0] : 0, first_p1 = bw0 < batch ? prefix[bw0 + 1] : 0;
+  const StreamSplit split(T, n_wg);
   auto pieces = [&](int b) {
     SeqPieces q{0, 0, 0};
-    const int p0 = b < batch ? prefix[b] : 0, p1 = b < batch ? prefix[b + 1] : 0;
+    const bool first = b == bw0;
+    const int p0 = first ? first_p0 : b < batch ? prefix[b] : 0;
+    const int p1 = first ? first_p1 : b < batch ? prefix[b + 1] : 0;
     if (p1 > p0) {
       q.f = split.owner(p0);
       q.n = split.owner(p1 - 1) - q.f + 1;
@@ -1524,24 +1548,29 @@ __device__ __forceinline__ void combine_wg(const int* prefix, const float* __res
 // ---------------------------------------------------------------------------
 // Split-KV attention partials only (the staged call).
 // ---------------------------------------------------------------------------
+// The arguments are ordered by when the workgroup needs them: the first 14
+// dwords (up to num_blocks) are the ones the prologue uses before its first
+// loads land, which the hardware preloads into scalar registers.
 template <int HEADS, bool kFp8>
 __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
-    const bf16* __restrict__ q_full, const bf16* __restrict__ pool,
-    const int* __restrict__ block_table, int max_blocks, int shift, int num_blocks,
-    const int* __restrict__ seq_lens, int batch, int H, int n_wg, int guess_tiles,
-    int* __restrict__ prefix_out, float* __restrict__ part_ml, bf16* __restrict__ part_o) {
+    const int* __restrict__ seq_lens, const int* __restrict__ block_table,
+    const bf16* __restrict__ pool, int H, int n_wg, int batch, int guess_tiles, int max_blocks,
+    int shift, int num_blocks, const bf16* __restrict__ q_full, int* __restrict__ prefix_out,
+    float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  decode_attention_wg<HEADS, kFp8>(smem, blockIdx.x, q_full, pool, block_table, max_blocks,
-                                   shift, num_blocks, seq_lens, batch, H, n_wg, guess_tiles,
-                                   prefix_out, part_ml, part_o);
+  decode_attention_wg<HEADS, kFp8>(smem, blockIdx.x, seq_lens, block_table, pool, H, n_wg, batch,
+                                   guess_tiles, max_blocks, shift, num_blocks, q_full, prefix_out,
+                                   part_ml, part_o);
 }
 
 // Combine of the partials (the staged call): grid (H, ceil(batch / S)).
+// Arguments in the order the workgroup needs them (the first 14 dwords are
+// preloaded into scalar registers).
 template <bool kProject, int kChunk>
 __global__ void __launch_bounds__(kCThreads) combine_kernel(
-    const int* __restrict__ prefix, const float* __restrict__ part_ml,
-    const bf16* __restrict__ part_o, int batch, int H, int hg_heads, int n_wg, int guess_tiles,
-    int S, const bf16* __restrict__ w_uv, int Dv, bf16* __restrict__ out) {
+    const float* __restrict__ part_ml, const bf16* __restrict__ part_o,
+    const bf16* __restrict__ w_uv, int batch, int H, int hg_heads, int n_wg, int guess_tiles,
+    int S, int Dv, const int* __restrict__ prefix, bf16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char smem[kCWBytes + kCOBytes];
   const uint32_t wb = lds_addr(smem), ob = wb + kCWBytes;
   combine_wg<kProject, kChunk>(prefix, part_ml, part_o, batch, H, hg_heads, n_wg, guess_tiles, S,
@@ -1578,9 +1607,10 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
   const int hgc = H / heads_per_wg;
   const int guess_tiles = (max_seq_len + kTok - 1) / kTok;
   auto go = [&](auto kernel) {
-    kernel<<<n_wg * hgc, kThreads, 0, st>>>((const bf16*)q_full, (const bf16*)pool, block_table,
-                                            max_blocks, block_shift, num_blocks, seq_lens, batch,
-                                            H, n_wg, guess_tiles, prefix, part_ml, (bf16*)part_o);
+    kernel<<<n_wg * hgc, kThreads, 0, st>>>(seq_lens, block_table, (const bf16*)pool, H, n_wg,
+                                            batch, guess_tiles, max_blocks, block_shift,
+                                            num_blocks, (const bf16*)q_full, prefix, part_ml,
+                                            (bf16*)part_o);
   };
   if (heads_per_wg == 64)
     fp8 ? go(attn_decode_partials_kernel<64, true>) : go(attn_decode_partials_kernel<64, false>);
@@ -1620,8 +1650,8 @@ void launch_combine(const int* prefix, const float* part_ml, const void* part_o,
   const int wps = S < kCWaves ? kCWaves / S : 1;
   const bool wide = (n_max + wps - 1) / wps > 8;
   auto go = [&](auto kernel, const void* w) {
-    kernel<<<grid, kCThreads, 0, st>>>(prefix, part_ml, (const bf16*)part_o, batch, H,
-                                       heads_per_wg, n_wg, guess_tiles, S, (const bf16*)w, Dv,
+    kernel<<<grid, kCThreads, 0, st>>>(part_ml, (const bf16*)part_o, (const bf16*)w, batch, H,
+                                       heads_per_wg, n_wg, guess_tiles, S, Dv, prefix,
                                        (bf16*)out);
   };
   if (w_uv)

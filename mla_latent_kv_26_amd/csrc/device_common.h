@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of this library.
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -110,6 +111,20 @@ __device__ __forceinline__ void lds_st(uint32_t a, const bf16x4& v) { *(lds_bf16
 // Address of a __shared__ object in the LDS aperture.
 template <typename T> __device__ __forceinline__ uint32_t lds_addr(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+}
+
+// A kernel argument past the ones preloaded into scalar registers is a
+// scalar load from the argument segment, which the compiler issues and waits
+// for where the argument is first used.  fetch_arg makes it a value at this
+// point instead (placed where other loads are in flight, its round trip
+// overlaps theirs).  The pointer stays a global one, so the accesses through
+// it remain global (not flat) loads and stores.
+template <typename P> __device__ __forceinline__ void fetch_arg(P& p) {
+  typedef std::remove_reference_t<decltype(*p)> T;
+  typedef __attribute__((address_space(1))) T gT;
+  gT* g = (gT*)p;
+  asm volatile("" : "+s"(g));
+  p = (T*)g;
 }
 
 // Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes land at
