@@ -315,7 +315,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceilings", action="store_true",
-                    help="only measure the device's HBM read and bf16 MFMA ceilings with the "
+                    help="only measure the device's HBM read, bf16 MFMA and LDS read ceilings with the "
                          "library's probes (include/mla.h) and print them")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (10 times), as the "
@@ -470,7 +470,8 @@ def ceilings_main(args, torch, m):
     """The ceilings the kernels are measured against, on this device: HBM
     reads of a 2 GiB buffer (8x the 256 MB Infinity Cache) through 16-byte
     vector loads and through direct-to-LDS loads of 36 KB pieces (the decode
-    attention's way), and back-to-back bf16 32x32x16 MFMAs.  Median of
+    attention's way), back-to-back bf16 32x32x16 MFMAs, and conflict-free
+    LDS reads of 16 and 8 bytes per lane on every CU.  Median of
     --repeats launches each, HIP events on the launching stream."""
     dev = torch.device("cuda", 0)
     buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
@@ -498,18 +499,25 @@ def ceilings_main(args, torch, m):
     wgs, iters = 4 * cus, 4000
     flops = wgs * 4 * iters * 4 * 32768
     mf = timed(lambda: m.mla_probe_mfma(wgs, iters, sink))
+    lds_iters = 20000
+    lds_bytes = {w: cus * 8 * lds_iters * 8 * 64 * w for w in (16, 8)}
+    lds = {w: timed(lambda w=w: m.mla_probe_lds_read(w, lds_iters, sink)) for w in (16, 8)}
     gbs = lambda b, t: b / (t * 1e-3) / 1e9
     line = {
-        "metric": "device ceilings: HBM read GB/s, bf16 MFMA TFLOP/s",
+        "metric": "device ceilings: HBM read GB/s, bf16 MFMA TFLOP/s, LDS read GB/s per CU",
         "hbm_read_vector_GBs": round(gbs(nbytes, vec["median"]), 1),
         "hbm_read_direct_to_lds_GBs": round(gbs(dma_bytes, dma["median"]), 1),
         "hbm_peak_GBs": HBM_PEAK_GBS,
         "mfma_bf16_TFLOPs": round(flops / (mf["median"] * 1e-3) / 1e12, 1),
         "mfma_bf16_peak_TFLOPs": BF16_PEAK_TFLOPS,
         "buffer_bytes": nbytes, "repeats": args.repeats,
+        "lds_read_b128_GBs_per_cu": round(gbs(lds_bytes[16], lds[16]["median"]) / cus, 1),
+        "lds_read_b64_GBs_per_cu": round(gbs(lds_bytes[8], lds[8]["median"]) / cus, 1),
         "mfma_workgroups": wgs, "mfma_iterations": iters, "compute_units": cus,
+        "lds_iterations": lds_iters,
         "ms": {"vector": round(vec["median"], 4), "direct_to_lds": round(dma["median"], 4),
-               "mfma": round(mf["median"], 4)},
+               "mfma": round(mf["median"], 4), "lds_b128": round(lds[16]["median"], 4),
+               "lds_b64": round(lds[8]["median"], 4)},
     }
     print(json.dumps(line), flush=True)
 

@@ -363,13 +363,18 @@ mla_status mla_output_gate_projection(const mla_config* cfg, const void* x, cons
  * mla_probe_mfma: workgroups x 4 waves each run iterations x 4 independent
  *   32x32x16 bf16 MFMAs on register operands (32768 FLOP each; workgroups of
  *   256 threads); one value per thread to sink.
+ * mla_probe_lds_read: one workgroup of 8 waves per compute unit; every wave
+ *   runs iterations x 8 bank-conflict-free LDS reads of width (16 or 8)
+ *   bytes per lane, i.e. CUs x 8 x iterations x 8 x 64 x width bytes in all;
+ *   one value per thread to sink.
  * Errors: MLA_ERR_INVALID_ARG for NULL or misaligned pointers, a too small
- * buffer, an unknown mode or non-positive counts; MLA_ERR_HIP if the launch
- * fails.  Nothing is allocated. */
+ * buffer, an unknown mode or width or non-positive counts; MLA_ERR_HIP if
+ * the launch fails.  Nothing is allocated. */
 size_t mla_probe_sink_bytes(void);
 mla_status mla_probe_hbm_read(const void* buf, size_t bytes, int32_t mode, void* sink,
                               void* stream);
 mla_status mla_probe_mfma(int32_t workgroups, int32_t iterations, void* sink, void* stream);
+mla_status mla_probe_lds_read(int32_t width, int32_t iterations, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

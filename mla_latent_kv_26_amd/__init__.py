@@ -13,6 +13,6 @@ from .api import (  # noqa: F401
     mla_output_projection,
     mla_cache_append_workspace_size, mla_cache_append, mla_prefill_workspace_size, mla_prefill_attention_form, mla_prefill,
     mla_output_gate_workspace_size, mla_output_gate_projection,
-    mla_probe_sink, mla_probe_hbm_read, mla_probe_mfma,
+    mla_probe_sink, mla_probe_hbm_read, mla_probe_mfma, mla_probe_lds_read,
 )
 from .pool import LatentKVPool  # noqa: F401

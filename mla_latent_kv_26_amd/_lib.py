@@ -101,6 +101,7 @@ SIGNATURES = {
     "mla_probe_sink_bytes": (_SZ, []),
     "mla_probe_hbm_read": (_I, [_P, _SZ, _I, _P, _P]),
     "mla_probe_mfma": (_I, [_I, _I, _P, _P]),
+    "mla_probe_lds_read": (_I, [_I, _I, _P, _P]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():

@@ -441,7 +441,8 @@ def mla_output_gate_projection(cfg: MLAConfig, x, head_out, w_o, w_g=None, out=N
 
 
 # ---------------------------------------------------------------------------
-# Measurement probes (include/mla.h): the HBM read and bf16 MFMA ceilings.
+# Measurement probes (include/mla.h): the HBM read, bf16 MFMA and LDS read
+# ceilings.
 # ---------------------------------------------------------------------------
 def mla_probe_sink(device=None) -> torch.Tensor:
     """A device buffer large enough for the probes' per-thread outputs."""
@@ -464,3 +465,13 @@ def mla_probe_mfma(workgroups: int, iterations: int, sink: torch.Tensor, stream=
     check(lib.mla_probe_mfma(workgroups, iterations, sink.data_ptr(), _stream(stream)),
           "mla_probe_mfma")
     return workgroups * 4 * iterations * 4 * 32768
+
+
+def mla_probe_lds_read(width: int, iterations: int, sink: torch.Tensor, stream=None) -> int:
+    """Run the LDS read probe (16- or 8-byte reads per lane, one workgroup
+    per compute unit); returns the bytes it reads."""
+    _dev(sink, "sink", torch.uint8, (lib.mla_probe_sink_bytes(),))
+    check(lib.mla_probe_lds_read(width, iterations, sink.data_ptr(), _stream(stream)),
+          "mla_probe_lds_read")
+    cus = torch.cuda.get_device_properties(sink.device).multi_processor_count
+    return cus * 8 * iterations * 8 * 64 * width

@@ -8,7 +8,10 @@
 //                     tiles (one workgroup per CU, 512 threads);
 //   mfma_kernel:      back-to-back independent 32x32x16 bf16 MFMAs on
 //                     register operands (one 256-thread workgroup per CU
-//                     slot, four accumulators per wave).
+//                     slot, four accumulators per wave);
+//   lds_read_kernel:  LDS reads of 16 or 8 bytes per lane, eight in flight
+//                     per wave, bank-conflict free, by one 512-thread
+//                     workgroup per CU (the decode attention's shape).
 #include "device_common.h"
 #include "mla.h"
 
@@ -102,6 +105,41 @@ __global__ void __launch_bounds__(256) mfma_kernel(int iters, float* __restrict_
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Each wave reads rows of 64 x W bytes (W = 16 or 8) at consecutive
+// addresses, eight per iteration, all below 64 KB of a 96 KB allocation
+// (which keeps the workgroup alone on its CU); 64 consecutive lanes of one
+// read touch every bank equally, so the reads are conflict free.
+constexpr int kProbeLds = 96 * 1024;
+template <int W>
+__global__ void __launch_bounds__(512, 1) lds_read_kernel(int iters, uint32_t* __restrict__ sink) {
+  typedef unsigned v4 __attribute__((ext_vector_type(4)));
+  typedef unsigned v2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v4 lds_v4;
+  typedef __attribute__((address_space(3))) v2 lds_v2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kProbeLds];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kProbeLds / 4; i += 512) ((uint32_t*)smem)[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const uint32_t base = lds_addr(smem) + (uint32_t)wave * 8192u + (uint32_t)lane * W;
+  uint32_t x = 0;
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (W == 16) {
+      v4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *(volatile lds_v4*)(uintptr_t)(base + j * 1024u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x ^= v[j][0] + v[j][1] + v[j][2] + v[j][3];
+    } else {
+      v2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *(volatile lds_v2*)(uintptr_t)(base + j * 512u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x ^= v[j][0] + v[j][1];
+    }
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -126,6 +164,22 @@ mla_status mla_probe_hbm_read(const void* buf, size_t bytes, int32_t mode, void*
   else
     mla::dma_read_kernel<<<cus, 512, 0, st>>>((const unsigned char*)buf,
                                               bytes / mla::kProbeTile, (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_probe_lds_read(int32_t width, int32_t iterations, void* sink, void* stream) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (cus <= 0 || cus > 1024) cus = 256;
+  if (!sink || iterations <= 0 || (width != 16 && width != 8) ||
+      (size_t)cus * 512 * 4 > mla_probe_sink_bytes())
+    return MLA_ERR_INVALID_ARG;
+  if (width == 16)
+    mla::lds_read_kernel<16><<<cus, 512, 0, (hipStream_t)stream>>>(iterations, (uint32_t*)sink);
+  else
+    mla::lds_read_kernel<8><<<cus, 512, 0, (hipStream_t)stream>>>(iterations, (uint32_t*)sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -193,6 +193,17 @@ def test_prefill_and_append_reject_invalid_calls():
                                 FAKE, 4, FAKE, 10, FAKE, 1 << 30, None) == _lib.MLA_ERR_INVALID_ARG
 
 
+def test_probes_reject_invalid_calls():
+    """The measurement probes validate before any launch."""
+    bad = _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_lds_read(4, 10, FAKE, None) == bad      # width 16 or 8 only
+    assert lib.mla_probe_lds_read(16, 0, FAKE, None) == bad
+    assert lib.mla_probe_lds_read(8, 10, None, None) == bad
+    assert lib.mla_probe_mfma(0, 10, FAKE, None) == bad
+    assert lib.mla_probe_hbm_read(FAKE, 1024, 0, FAKE, None) == bad   # below one 36864-byte piece
+    assert lib.mla_probe_hbm_read(FAKE, 1 << 20, 2, FAKE, None) == bad
+
+
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(2, 64, 128, dtype=torch.bfloat16)
