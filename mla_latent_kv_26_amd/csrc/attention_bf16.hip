@@ -235,10 +235,18 @@ __device__ __forceinline__ void issue_tile(const SegArgs& a, PageCursor& pc, int
 template <bool kFp8, int NL>
 __device__ __forceinline__ void seg_start(const SegArgs& a, PageCursor& pc, uint32_t lds,
                                           uint32_t j0, int lane) {
-  if (a.pre)
+  if (a.pre) {
     pc = *a.pre;
-  else
+  } else {
     pc.start(a.table, a.max_blocks, (a.tile0 * kTok) >> a.shift, lane);
+    // Tile 0's address needs the page ids at once; waited for here, before
+    // any tile load, they become plain values.  (Registers loaded before
+    // direct-to-LDS loads are otherwise completed by the compiler with a
+    // drain of every load in flight, placed where the tile loop starts and
+    // so paid on every step.)
+    wait_vmcnt<0>();
+    asm volatile("" : "+v"(pc.cur), "+v"(pc.nxt));
+  }
   if (!a.tile0_issued) issue_tile<kFp8, NL>(a, pc, a.tile0, load_slot<kFp8>(lds, 0), j0, lane);
 }
 
@@ -271,12 +279,62 @@ __device__ __forceinline__ void step_issue(const SegArgs& a, PageCursor& pc, uin
 }
 
 // Queries of head 16 sw + lane%16, chunks 4 ks + lane/16 (the B operand of
-// the score MFMAs), from the segment's query rows.
+// the score MFMAs), from the segment's query rows.  FP8 rows: loaded into
+// registers (the split into e4m3 terms follows).
 __device__ __forceinline__ void load_queries(const bf16* q_rows, int sw, int lane,
                                              bf16x8 (&qf)[kW / 32]) {
   const bf16* q = q_rows + (16 * sw + (lane & 15)) * kW + 8 * (lane >> 4);
 #pragma unroll
   for (int ks = 0; ks < kW / 32; ++ks) qf[ks] = *(const bf16x8*)(q + 32 * ks);
+}
+// bf16 rows: staged through LDS.  Score wave sw's 18 KB go by direct-to-LDS
+// loads into tile buffers 2 and 3, load ks filling 1 KB at q_stage(sw) +
+// 1024 ks with lane l's 16 bytes, and come back into registers by 16-byte
+// LDS reads before the segment's first barrier (tile 2 is issued into
+// buffer 2 only after it, tile 3 into buffer 3 a step later).  Loaded into
+// registers by vector loads instead, the queries make the compiler complete
+// them by draining every load in flight, so the first step waits for tile 1
+// as well as tile 0 (measured 0.4 us per step at 32 x 4096 tokens; for FP8
+// rows staging measured no faster).
+constexpr uint32_t kQStage = (kW / 32) * 1024;  // 18 KB per score wave
+static_assert(4 * kQStage <= 2 * kTileBytes, "staged queries fit tile buffers 2 and 3");
+__device__ __forceinline__ uint32_t q_stage(uint32_t lds, int sw) {
+  return lds + 2u * kTileBytes + (uint32_t)sw * kQStage;
+}
+__device__ __forceinline__ void stage_queries(const bf16* q_rows, int sw, int lane, uint32_t lds) {
+  const bf16* q = q_rows + (16 * sw + (lane & 15)) * kW + 8 * (lane >> 4);
+  const uint32_t dst = q_stage(lds, sw);
+#pragma unroll
+  for (int ks = 0; ks < kW / 32; ++ks) g2lds16(q + 32 * ks, dst + (uint32_t)ks * 1024u);
+}
+// The staged queries into registers (after the wave's wait for them).
+__device__ __forceinline__ void read_staged_queries(uint32_t lds, int sw, int lane,
+                                                    bf16x8 (&qf)[kW / 32]) {
+  static_assert(kW / 32 == 18, "eighteen query fragments");
+  const uint32_t a = q_stage(lds, sw) + 16u * (uint32_t)lane;
+  ds_b128_nowait<0 * 1024>(qf[0], a);
+  ds_b128_nowait<1 * 1024>(qf[1], a);
+  ds_b128_nowait<2 * 1024>(qf[2], a);
+  ds_b128_nowait<3 * 1024>(qf[3], a);
+  ds_b128_nowait<4 * 1024>(qf[4], a);
+  ds_b128_nowait<5 * 1024>(qf[5], a);
+  ds_b128_nowait<6 * 1024>(qf[6], a);
+  ds_b128_nowait<7 * 1024>(qf[7], a);
+  ds_b128_nowait<8 * 1024>(qf[8], a);
+  ds_b128_nowait<9 * 1024>(qf[9], a);
+  ds_b128_nowait<10 * 1024>(qf[10], a);
+  ds_b128_nowait<11 * 1024>(qf[11], a);
+  ds_b128_nowait<12 * 1024>(qf[12], a);
+  ds_b128_nowait<13 * 1024>(qf[13], a);
+  ds_b128_nowait<14 * 1024>(qf[14], a);
+  ds_b128_nowait<15 * 1024>(qf[15], a);
+  ds_b128_nowait<16 * 1024>(qf[16], a);
+  ds_b128_nowait<17 * 1024>(qf[17], a);
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
+                 "+v"(qf[6]), "+v"(qf[7]), "+v"(qf[8]), "+v"(qf[9]), "+v"(qf[10]), "+v"(qf[11]),
+                 "+v"(qf[12]), "+v"(qf[13]), "+v"(qf[14]), "+v"(qf[15]), "+v"(qf[16]),
+                 "+v"(qf[17]));
 }
 
 // Score wave `sw` (heads 16 sw .. 16 sw + 15): runs the segment's steps and
@@ -298,7 +356,7 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
 
   const int h = 16 * sw + (lane & 15);
   const uint32_t kq = lane >> 4;
-  if (active && !q_ready) load_queries(a.q_rows, sw, lane, qf);
+  if (active && !q_ready) stage_queries(a.q_rows, sw, lane, lds);
   // tile 0 and the queries (issued before tile 1) land; tile 1 may stay in flight
   if (n > 1) {
     if (!a.tile1_issued) issue_tile<false, NL>(a, pc, a.tile0 + 1, load_slot<false>(lds, 1), j0, lane);
@@ -306,11 +364,9 @@ __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int s
   } else {
     wait_vmcnt<0>();
   }
-  // The queries have landed (only tile 1 may still be in flight).  Hand them
-  // on as plain register values, so that no wait inside the loop is tied to
-  // their loads.
-#pragma unroll
-  for (int ks = 0; ks < kW / 32; ++ks) asm volatile("" : "+v"(qf[ks]));
+  // the staged queries into registers, before the first barrier frees
+  // their buffers for tiles 2 and 3
+  if (active) read_staged_queries(lds, sw, lane, qf);
 
   // S fragment (ks, tb): row tr0 + 16 tb, chunk 4 ks + kq at position
   // 8 (ks/2) + ((4 (ks%2) + kq) ^ swz(tr0)); swz depends on lane%16 only.
@@ -1130,13 +1186,11 @@ __device__ __forceinline__ bool decode_attention_wg(
   // guess_tiles tiles (the common equal-length batch): load that page-id
   // chunk now, in parallel with the lengths, and keep it if the guess holds.
   // As soon as the ids land, the guessed first tile (as a full tile) goes in
-  // flight into buffer 0, then the guessed sequence's queries (score waves),
-  // then the guessed second tile into buffer 1, overlapping the prefix sums
-  // and the range search; a page id outside the pool is never dereferenced.
-  // (The first step waits for the second tile too: the queries are registers
-  // loaded before direct-to-LDS loads, which the compiler completes by
-  // draining every load in flight.  Issuing a third tile here measured
-  // slower: the opening burst delays every workgroup's first tiles.)
+  // flight into buffer 0, then the guessed sequence's queries (score waves,
+  // staged in LDS), then the guessed second tile into buffer 1, overlapping
+  // the prefix sums and the range search; a page id outside the pool is never
+  // dereferenced.  (Issuing a third tile here measured slower: the opening
+  // burst delays every workgroup's first tiles.)
   const StreamSplit gsplit(batch * guess_tiles, n_wg);
   const int xg = gsplit.start(w);
   const int bg = min(xg / guess_tiles, batch - 1);
@@ -1147,6 +1201,7 @@ __device__ __forceinline__ bool decode_attention_wg(
   bf16x8 qf[kW / 32];  // score waves: the queries of sequence qb
   int qb = -1;
   bool spec_issued = false, spec2 = false;
+  bool q_spec = false;  // queries of sequence qb staged in LDS before the range was known
   // guessed tile tg0 + t (as a full tile) into buffer t; false if its page
   // id is outside the pool (then nothing is issued)
   auto spec_tile = [&](int t) {
@@ -1168,8 +1223,9 @@ __device__ __forceinline__ bool decode_attention_wg(
   auto early = [&]() {
     spec_issued = spec_tile(0);
     if (!kFp8 && wave < Geo<HEADS>::SW) {  // FP8: each segment loads and splits its own
-      load_queries(q_full + ((long)bg * H + hg * HEADS) * kW, wave, lane, qf);
+      stage_queries(q_full + ((long)bg * H + hg * HEADS) * kW, wave, lane, lds);
       qb = bg;
+      q_spec = true;
     }
     if (spec_issued && tg0 + 1 < guess_tiles) spec2 = spec_tile(1);
   };
@@ -1228,12 +1284,13 @@ __device__ __forceinline__ bool decode_attention_wg(
       // tile and a full one (a partial tile repeats its last row instead)
       const bool reuse = spec_issued && guessed && tile0 == tg0 && (tile0 + 1) * kTok <= len;
       const bool reuse2 = reuse && spec2 && tile1 - tile0 >= 2 && (tile0 + 2) * kTok <= len;
-      // speculative loads not taken over land before their buffers are refilled
-      if (spec_issued && !(reuse && (reuse2 || !spec2))) wait_vmcnt<0>();
+      // speculative loads (tiles, staged queries) not taken over land before
+      // their buffers are refilled
+      if ((spec_issued || q_spec) && !(reuse && (reuse2 || !spec2))) wait_vmcnt<0>();
       const SegArgs a{q_full + ((long)b * H + hg * HEADS) * kW, pool,
                       block_table + (long)b * max_blocks, max_blocks, shift, len, tile0, tile1,
                       guessed ? &spec : nullptr, reuse, reuse2};
-      spec_issued = spec2 = false;
+      spec_issued = spec2 = q_spec = false;
       segment(a, b, slot);
       x = seg_end;
       ++b;
@@ -1256,7 +1313,7 @@ __device__ __forceinline__ bool decode_attention_wg(
       pv_segment<HEADS, kFp8>(a, lds, part_o + slot * HEADS * kR, wave, lane);
     });
   }
-  if (spec_issued) wait_vmcnt<0>();
+  if (spec_issued || q_spec) wait_vmcnt<0>();
   return true;
 }
 
