@@ -32,7 +32,10 @@
  *     MLA_ERR_WORKSPACE), enqueues nothing, writes nothing, and
  *     mla_last_error() says why.  Device-resident integers (page tables,
  *     sequence lengths, positions, slots) are trusted: the caller keeps them
- *     within the sizes passed.  A failed launch returns MLA_ERR_HIP.
+ *     within the sizes passed.  Page-table entries past the pages a sequence
+ *     uses may hold any value: they are read (the decode prologue guesses
+ *     pages from them) but never followed outside [0, num_blocks).  A failed
+ *     launch returns MLA_ERR_HIP.
  *   - Cache pool: [num_blocks, block_size, R + Dr].  Logical token j of
  *     sequence b lives at page block_table[b * max_blocks_per_seq + j / block_size],
  *     offset j % block_size (the ticket "MLA + KV cache (Tier 3 #5)",

@@ -340,8 +340,9 @@ __device__ __forceinline__ void read_staged_queries(uint32_t lds, int sw, int la
 // Score wave `sw` (heads 16 sw .. 16 sw + 15): runs the segment's steps and
 // returns (in lanes 0..15) the reference max and full row sum of head
 // 16 sw + lane.  Inactive score waves (sw >= SW) only take part in loads and
-// barriers.  qf: the segment's queries when q_ready (loaded before the
-// segment's tiles), else loaded here.
+// barriers.  qf receives the segment's queries from their LDS staging:
+// staged with the guessed tiles when q_ready, else staged here (after tile 0,
+// before tile 1).
 template <int HEADS>
 __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int sw, int lane,
                                            bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,

@@ -342,6 +342,25 @@ def test_garbage_beyond_sequence_end_is_ignored(m):
     assert_bf16(got, ref, "NaN padding")
 
 
+@pytest.mark.parametrize("filler", [-1, 1 << 30, "pool_size"])
+def test_unused_block_table_entries_outside_the_pool(m, filler):
+    """Block-table entries past each sequence's pages point outside the pool
+    (negative, huge, or exactly the pool size).  The equal-length guess of the
+    decode prologue (every sequence 4096 tokens long) lands on such entries
+    for the short sequences: the guessed tiles must be skipped and the queries
+    staged for the guess replaced, with no effect on the output."""
+    cfg = bf16_decode_cfg(seed=19)
+    lens = np.array([4096, 64, 2000, 4096, 33, 4096, 1, 700], np.int32)
+    inp = workloads.decode_inputs(cfg, lengths=lens)
+    bs = inp.pool.shape[1]
+    fill = inp.pool.shape[0] if filler == "pool_size" else filler
+    for b, L in enumerate(lens):
+        inp.block_table[b, -(-int(L) // bs):] = fill
+    got = gpu_decode(m, cfg, inp)
+    ref = oracle_decode(cfg, inp, range(len(lens)))
+    assert_bf16(got, ref, f"unused entries = {filler}", per_row_axis=0)
+
+
 # ---------------------------------------------------------------------------
 # bf16 prefill
 # ---------------------------------------------------------------------------
