@@ -30,8 +30,7 @@
 // for every direct-to-LDS load in flight.
 //
 // In the prefill with a query rank, x W_DQ (256 x 256 tiles of the tile GEMM)
-// runs in the same launch: at 8192 rows, 64 workgroups of two panels each
-// and 192 tiles are one round of 256 CUs, each a similar amount of work.
+// runs in the same launch: at 8192 rows, 128 panel workgroups and 192 tiles.
 #include "launch.h"
 #include "tile_gemm.h"
 
@@ -430,16 +429,16 @@ void launch_project_append(const void* x, long ldx, int batch, int T, int K, con
   d.T = T;
   d.max_blocks = max_blocks;
   d.block_size = block_size;
-  // with the q-rank tiles, two panels per workgroup (a panel is about half
-  // a tile's work); alone, one
+  // one panel per workgroup, also beside the q-rank tiles: a panel streams
+  // all of W_DKV, so two panels per workgroup (one round of the CUs with the
+  // tiles) measured 4 % slower than a partial second round
   const int np = (n + kPM - 1) / kPM;
-  int np8 = (np + 7) / 8 * 8;
+  const int np8 = (np + 7) / 8 * 8;
   int tiles = 0, m_per = 0;
   if (w_q) {
     const int n_mt = (n + kTM - 1) / kTM, n_nt = (N + 255) / 256;
     m_per = (n_mt + 7) / 8;
     tiles = 8 * m_per * n_nt;
-    np8 = ((np + 1) / 2 + 7) / 8 * 8;
   }
   project_append_kernel<<<np8 + tiles, kPThreads, 0, st>>>(
       (const bf16*)x, ldx, n, K, (const bf16*)w_dkv, d, np8, (const bf16*)w_q, N, ldb, c, ldc,
