@@ -83,6 +83,15 @@ def test_fp8_decode_h128_ragged_sample(m):
     check_fp8_decode(m, cfg, sample=[0, 5, 15])
 
 
+@pytest.mark.parametrize("heads", [32, 96])
+def test_fp8_decode_heads_not_a_multiple_of_64(m, heads):
+    """The 32-heads-per-workgroup FP8 kernels (H = 32, and 96 in three head
+    groups), ragged lengths over permuted pages."""
+    cfg = dict(workloads.WORKLOADS["paged_ragged_h128_b64"], num_heads=heads, lengths="explicit",
+               paged=True, seed=33 + heads)
+    check_fp8_decode(m, cfg, [1, 31, 32, 33, 700, 4096, 2049, 65])
+
+
 def test_fp8_decode_single_long_sequence(m):
     """One 20,000-token sequence: 625 tiles over all workgroups."""
     cfg = dict(workloads.WORKLOADS["paged_ragged_h128_b64"], num_heads=64, lengths="explicit",

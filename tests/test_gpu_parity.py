@@ -205,6 +205,15 @@ def test_decode_h128_ragged(m):
     check_decode(m, bf16_decode_cfg(num_heads=128, seed=13), [1, 100, 4096, 5000, 16384])
 
 
+@pytest.mark.parametrize("heads", [32, 96])
+def test_decode_heads_not_a_multiple_of_64(m, heads):
+    """H = 32 and 96 run the 32-heads-per-workgroup kernels (two active score
+    waves, two that only load; 96 heads are three head groups sharing every
+    tile): ragged lengths over permuted pages against the oracle."""
+    check_decode(m, bf16_decode_cfg(num_heads=heads, seed=29 + heads),
+                 [1, 31, 32, 33, 700, 4096, 2049, 65])
+
+
 def test_paged_ragged_h128_b64_full(m):
     """H=128, 64 ragged sequences (512..16384 tokens) over a permuted pool:
     every sequence against the oracle."""
