@@ -83,6 +83,13 @@ def test_fp8_decode_h128_ragged_sample(m):
     check_fp8_decode(m, cfg, sample=[0, 5, 15])
 
 
+def test_fp8_decode_larger_pages(m):
+    """FP8 rows in 256-token pages (8 tiles per page), ragged lengths."""
+    cfg = dict(workloads.WORKLOADS["paged_ragged_h128_b64"], num_heads=64, lengths="explicit",
+               paged=True, block_size=256, seed=41)
+    check_fp8_decode(m, cfg, [1, 255, 256, 257, 799, 4096, 3000])
+
+
 @pytest.mark.parametrize("heads", [32, 96])
 def test_fp8_decode_heads_not_a_multiple_of_64(m, heads):
     """The 32-heads-per-workgroup FP8 kernels (H = 32, and 96 in three head

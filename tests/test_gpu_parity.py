@@ -205,6 +205,15 @@ def test_decode_h128_ragged(m):
     check_decode(m, bf16_decode_cfg(num_heads=128, seed=13), [1, 100, 4096, 5000, 16384])
 
 
+@pytest.mark.parametrize("block_size", [128, 1024])
+def test_decode_larger_pages(m, block_size):
+    """Pages of 128 and 1024 tokens (4 and 32 tiles per page: the page-id
+    cursor and the guessed first tiles index pages by shifts), ragged lengths
+    at page and tile edges over a permuted pool."""
+    check_decode(m, bf16_decode_cfg(block_size=block_size, seed=37 + block_size),
+                 [1, block_size - 1, block_size, block_size + 1, 3 * block_size + 31, 4096, 5000])
+
+
 @pytest.mark.parametrize("heads", [32, 96])
 def test_decode_heads_not_a_multiple_of_64(m, heads):
     """H = 32 and 96 run the 32-heads-per-workgroup kernels (two active score
