@@ -1,19 +1,28 @@
 // Large bf16 GEMM on MFMA (gfx950): C[z] = alpha * A[z] * B[z] (or A Bt^T),
 // float32 accumulate, bf16 or float32 output, in 256 x (256|128) tiles; the
 // main loop, LDS layouts and epilogue are in tile_gemm.h.
+//
+// Two shapes of launch: one workgroup per CU with 256 x 256 (or 256 x 128)
+// tiles and four stages, and for short K (at most kShortK) two workgroups
+// per CU with 256 x 128 tiles and three stages (72 KB of LDS and at most
+// 256 registers per lane each), so one workgroup's pipeline fill and
+// stores run beside the other's MFMAs.  Measured on MI355X: the per-head
+// key and value products of the prefill (M 4096 per sequence, N 8192,
+// K 512) 124 -> 117 us; at K = 1536 (c_q W_UQ) the short-K shape is slower.
 #include "launch.h"
 #include "tile_gemm.h"
 
 namespace mla {
 namespace {
 
-template <int BN, bool kBT, bool kOutF32>
-__global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
+template <int BN, bool kBT, bool kOutF32, int NS, int OCC>
+__global__ void __launch_bounds__(kTThreads, OCC) gemm_tile256_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* __restrict__ Cv, int M, int N,
     int K, long lda, long ldb, long ldc, long sA, long sB, long sC, int batch, int m_per,
     float alpha, int nb, long sBn, const bf16* __restrict__ gmul) {
   using Cf = TileCfg<BN>;
-  __shared__ __attribute__((aligned(16))) char smem[kTStages * Cf::STAGE];
+  static_assert(OCC * NS * Cf::STAGE <= 160 * 1024, "LDS of the resident workgroups");
+  __shared__ __attribute__((aligned(16))) char smem[NS * Cf::STAGE];
   const uint32_t lds = lds_addr(smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
@@ -36,7 +45,7 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jb = 0; jb < Cf::FN; ++jb) acc[i][jb] = f32x16{};
-  tile_mainloop<BN, kBT>(lds, src, 0, K / kTK, acc);
+  tile_mainloop<BN, kBT, NS>(lds, src, 0, K / kTK, acc);
   if constexpr (kOutF32)
     tile_epilogue<BN, true, false>(acc, (float*)Cv + z * sC, M, N, ldc, m0, n0, alpha, nullptr);
   else
@@ -44,7 +53,7 @@ __global__ void __launch_bounds__(kTThreads, 1) gemm_tile256_kernel(
                                     gmul ? gmul + z * sC : nullptr);
 }
 
-template <int BN, bool kBT>
+template <int BN, bool kBT, int NS = kTStages, int OCC = 1>
 void launch_tile(const void* A, const void* B, void* C, int M, int N, int K, long lda, long ldb,
                  long ldc, long sA, long sB, long sC, int batch, float alpha, int c_f32, int nb,
                  long sBn, const void* gmul, hipStream_t st) {
@@ -53,16 +62,18 @@ void launch_tile(const void* A, const void* B, void* C, int M, int N, int K, lon
   const int m_per = (rows_total + 7) / 8;
   const int grid = 8 * m_per * n_nt;
   if (c_f32)
-    gemm_tile256_kernel<BN, kBT, true><<<grid, kTThreads, 0, st>>>(
+    gemm_tile256_kernel<BN, kBT, true, NS, OCC><<<grid, kTThreads, 0, st>>>(
         (const bf16*)A, (const bf16*)B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, m_per, alpha,
         nb, sBn, (const bf16*)gmul);
   else
-    gemm_tile256_kernel<BN, kBT, false><<<grid, kTThreads, 0, st>>>(
+    gemm_tile256_kernel<BN, kBT, false, NS, OCC><<<grid, kTThreads, 0, st>>>(
         (const bf16*)A, (const bf16*)B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, m_per, alpha,
         nb, sBn, (const bf16*)gmul);
 }
 
 }  // namespace
+
+constexpr int kShortK = 512;  // longest K that takes the two-workgroup launch
 
 bool gemm_tile256_fits(int M, int N, int K, long lda, long ldb, long ldc) {
   // 16-byte aligned rows and chunks, whole 32-wide k steps, vector stores of 4
@@ -80,6 +91,15 @@ void launch_gemm_tile256(const void* A, const void* B, void* C, int M, int N, in
     sBn = 0;
   }
   const bool wide = N >= 256;
+  if (K <= kShortK) {
+    if (b_transposed)
+      launch_tile<128, true, 3, 2>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha,
+                                   c_f32, nb, sBn, gmul, st);
+    else
+      launch_tile<128, false, 3, 2>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha,
+                                    c_f32, nb, sBn, gmul, st);
+    return;
+  }
   if (b_transposed) {
     if (wide)
       launch_tile<256, true>(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, alpha, c_f32, nb,

@@ -180,10 +180,13 @@ __device__ __forceinline__ void tile_sources(TileSrc<BN, kBT>& t, const bf16* A,
 }
 
 // acc += the product over k stages [kt0, kt1) of the tile whose sources are
-// `src` (kt1 > kt0).  The LDS buffers are free on entry and on return.
-template <int BN, bool kBT>
+// `src` (kt1 > kt0), through NS stage buffers (the loads of stage kt + NS go
+// into stage kt's buffer; the description above is for NS = 4).  The LDS
+// buffers are free on entry and on return.
+template <int BN, bool kBT, int NS = kTStages>
 __device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kBT>& src, int kt0,
                                               int kt1, f32x16 (&acc)[4][TileCfg<BN>::FN]) {
+  static_assert(NS >= 2 && NS <= kTStages, "stage count");
   using Cf = TileCfg<BN>;
   constexpr int FN = Cf::FN, T = Cf::T, L = Cf::LOADS;
   constexpr int NR = kBT ? 4 + FN : 4 + 2 * FN;  // fragment reads per half step
@@ -194,7 +197,7 @@ __device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kB
 
   // load q (0 .. L-1) of stage kt
   auto issue_one = [&](int kt, int q) {
-    const uint32_t st = lds + (uint32_t)(kt % kTStages) * Cf::STAGE;
+    const uint32_t st = lds + (uint32_t)(kt % NS) * Cf::STAGE;
     if (q < Cf::A_LOADS) {
       g2lds16(src.a[q] + (long)kt * kTK, st + (uint32_t)(wave * Cf::A_LOADS + q) * 1024u);
     } else {
@@ -260,12 +263,12 @@ __device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kB
   Frag<FN, kBT> f0, f1;
   // Iteration kt: half step (kt, 0) on f0 while f1 = (kt, 1) is read; the
   // barrier that publishes stage kt + 1 (and frees stage kt's buffer); half
-  // step (kt, 1) on f1 while f0 = (kt + 1, 0) is read and stage kt + 4 is
+  // step (kt, 1) on f1 while f0 = (kt + 1, 0) is read and stage kt + NS is
   // loaded into kt's buffer.
   auto body = [&](int kt, auto load_c, auto next_c) {
-    constexpr bool LOAD = decltype(load_c)::value;  // stage kt + 4 exists
+    constexpr bool LOAD = decltype(load_c)::value;  // stage kt + NS exists
     constexpr bool NEXT = decltype(next_c)::value;  // stage kt + 1 exists
-    const uint32_t st = lds + (uint32_t)(kt % kTStages) * Cf::STAGE;
+    const uint32_t st = lds + (uint32_t)(kt % NS) * Cf::STAGE;
 #pragma unroll
     for (int e = 0; e < T; ++e) {
       mfma_one(f0, e);
@@ -279,10 +282,10 @@ __device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kB
     }
     settle(f1);
     if constexpr (NEXT) {
-      wait_stages<L>(min(kt1 - 2 - kt, kTStages - 2));
+      wait_stages<L>(min(kt1 - 2 - kt, NS - 2));
       lds_barrier();
     }
-    const uint32_t sn = lds + (uint32_t)((kt + 1) % kTStages) * Cf::STAGE;
+    const uint32_t sn = lds + (uint32_t)((kt + 1) % NS) * Cf::STAGE;
 #pragma unroll
     for (int e = 0; e < T; ++e) {
       mfma_one(f1, e);
@@ -298,7 +301,7 @@ __device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kB
         if (e >= kDOff) {
 #pragma unroll
           for (int q = (e - kDOff) * L / (T - kDOff); q < (e - kDOff + 1) * L / (T - kDOff); ++q)
-            issue_one(kt + kTStages, q);
+            issue_one(kt + NS, q);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -306,19 +309,19 @@ __device__ __forceinline__ void tile_mainloop(uint32_t lds, const TileSrc<BN, kB
     if constexpr (NEXT) settle(f0);
   };
 
-  for (int kt = kt0; kt < min(kt1, kt0 + kTStages); ++kt)
+  for (int kt = kt0; kt < min(kt1, kt0 + NS); ++kt)
 #pragma unroll
     for (int q = 0; q < L; ++q) issue_one(kt, q);
-  wait_stages<L>(min(kt1 - kt0 - 1, kTStages - 1));
+  wait_stages<L>(min(kt1 - kt0 - 1, NS - 1));
   lds_barrier();
   {
-    const uint32_t st = lds + (uint32_t)(kt0 % kTStages) * Cf::STAGE;
+    const uint32_t st = lds + (uint32_t)(kt0 % NS) * Cf::STAGE;
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_one(st, 0, r, f0);
   }
   settle(f0);
   int kt = kt0;
-  for (; kt + kTStages < kt1; ++kt) body(kt, std::true_type{}, std::true_type{});
+  for (; kt + NS < kt1; ++kt) body(kt, std::true_type{}, std::true_type{});
   for (; kt + 1 < kt1; ++kt) body(kt, std::false_type{}, std::true_type{});
   body(kt, std::false_type{}, std::false_type{});
   lds_barrier();  // every wave is done with the buffers
