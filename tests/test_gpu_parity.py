@@ -638,6 +638,18 @@ def test_output_gate_bf16_decode_rows(m):
         assert_bf16(got, ref, f"gate={gated}", per_row_axis=0)
 
 
+def test_output_gate_bf16_short_k(m):
+    """bf16, 300 rows, d_model 352, 4 heads of 128: both products have
+    K <= 512, so they take the two-workgroups-per-CU tile launch (256 x 128
+    tiles) with a ragged last row tile; x W_G carries the gate in its
+    epilogue, and W_O's 352 columns leave a partial column tile."""
+    cfg = dict(workloads.WORKLOADS["prefill_d7168_b2_t4096"], d_model=352, q_lora_rank=0,
+               kv_lora_rank=256, num_heads=4)
+    for gated in (True, False):
+        got, ref = run_gate(m, cfg, 300, 97, gated)
+        assert_bf16(got, ref, f"gate={gated}", per_row_axis=0)
+
+
 def test_output_gate_bf16_many_rows(m):
     """bf16, 600 rows (the 256-row tile GEMM, ragged last row tile), d_model
     1024, 16 heads of 128."""
