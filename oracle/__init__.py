@@ -27,7 +27,7 @@ Sources (cited in each function by page title and section):
     geometry and stored weights; Build per-head Q, K and V; Observe logits,
     then compute causal attention; Output projection and optional gate).
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
   RoPE pairs element i with i + Dr/2 (half split), frequency theta^(-2i/Dr),
   angle = absolute 0-based position * frequency; RMSNorm eps = 1e-6 on the
   latent part only; W_DKV output order [c | k_pe]; per-head query order

@@ -6,8 +6,7 @@ The softved article ("Multi-Head Latent Attention...", "Practical
 Implementation Tips for MLA in LLM Serving") advises applying quantization on
 top of MLA to cut the cache further, and its "Understanding KV Cache" section
 counts quantization among the techniques that only partly relieve the cache;
-neither names a format or a scale.  Reading taken here (also listed in
-DESIGN.md):
+neither names a format or a scale.  Reading taken here:
 
 * The latent part c (R values) of a cached row is stored in FP8 E4M3 as the
   OCP 8-bit floating point specification defines it: 1 sign bit, 4 exponent
