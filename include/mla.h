@@ -30,9 +30,10 @@
  *   - Validation runs on the host before anything is enqueued.  An invalid
  *     call returns MLA_ERR_INVALID_ARG (or MLA_ERR_UNSUPPORTED /
  *     MLA_ERR_WORKSPACE), enqueues nothing, writes nothing, and
- *     mla_last_error() says why.  Device-resident integers (page tables,
- *     sequence lengths, positions, slots) are trusted: the caller keeps them
- *     within the sizes passed.  Page-table entries past the pages a sequence
+ *     mla_last_error() says why.  Counts (batch, n_tokens, q_len, n_rows)
+ *     must be positive: an empty call is MLA_ERR_INVALID_ARG, not a no-op.
+ *     Device-resident integers (page tables, sequence lengths, positions,
+ *     slots) are trusted: the caller keeps them within the sizes passed.  Page-table entries past the pages a sequence
  *     uses may hold any value: they are read (the decode prologue guesses
  *     pages from them) but never followed outside [0, num_blocks).  A failed
  *     launch returns MLA_ERR_HIP.

@@ -193,6 +193,27 @@ def test_prefill_and_append_reject_invalid_calls():
                                 FAKE, 4, FAKE, 10, FAKE, 1 << 30, None) == _lib.MLA_ERR_INVALID_ARG
 
 
+def test_empty_calls_are_rejected():
+    """A zero count is MLA_ERR_INVALID_ARG on every entry point (checked on the
+    host before anything is enqueued), never a silent no-op."""
+    bad = _lib.MLA_ERR_INVALID_ARG
+    cfg = m.MLAConfig(64, 512, 64, 128, 128, d_model=7168, q_lora_rank=1536)
+    c = ctypes.byref(cfg.c())
+    assert _decode(KIMI, batch=0) == bad
+    args = [c, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 128, FAKE,
+            64, FAKE, 0, 2, 4096, FAKE, FAKE, 1 << 40, None]
+    for idx in (18, 19):  # batch, q_len
+        a = list(args)
+        a[idx] = 0
+        assert lib.mla_prefill(*a) == bad, idx
+    assert lib.mla_cache_append(c, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 0, FAKE, 10, FAKE,
+                                1 << 30, None) == bad
+    assert lib.mla_output_projection(c, FAKE, FAKE, 0, FAKE, None) == bad
+    assert lib.mla_output_gate_projection(c, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 30,
+                                          None) == bad
+    assert "positive" in _lib.last_error()
+
+
 def test_probes_reject_invalid_calls():
     """The measurement probes validate before any launch."""
     bad = _lib.MLA_ERR_INVALID_ARG
