@@ -49,6 +49,16 @@ constexpr int kTileLoads = kTileBytes / 1024;           // 36 1-KB load instruct
 constexpr int kSLoads = 4, kPLoads = 5;                 // per score wave / per P*C wave
 constexpr int kSAhead = 4;  // score fragment pairs read ahead of their MFMAs
 static_assert(4 * kSLoads + 4 * kPLoads == kTileLoads, "every slot loaded once");
+// The tile loads can also all go to the P*C waves (SL = 0 score-wave loads,
+// 9 per P*C wave): that takes the load issue off the score waves' chain,
+// which sets the tile step where HBM does not (two head groups of 64 heads,
+// each tile read by two workgroups: 3-4 % off the attention at H=128), and
+// costs where the stream binds (4 x 131,072 tokens 1-2 % slower).
+template <int SL>
+__device__ __forceinline__ constexpr int p_loads() {
+  static_assert(SL >= 0 && 4 * SL <= kTileLoads && (kTileLoads - 4 * SL) % 4 == 0, "load split");
+  return (kTileLoads - 4 * SL) / 4;
+}
 constexpr int kMaxHG = 64;                              // heads per workgroup, at most
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -205,14 +215,14 @@ __device__ __forceinline__ uint32_t load_slot(uint32_t lds, int x) {
     return lds + (uint32_t)(x % kNBuf) * kTileBytes;
 }
 // Loads per wave and tile, and the first load index of wave `wave`.
-template <bool kFp8>
+template <bool kFp8, int SL = kSLoads>
 __device__ __forceinline__ constexpr int tile_loads(bool score) {
-  return kFp8 ? kF8Loads : score ? kSLoads : kPLoads;
+  return kFp8 ? kF8Loads : score ? SL : p_loads<SL>();
 }
-template <bool kFp8>
+template <bool kFp8, int SL = kSLoads>
 __device__ __forceinline__ uint32_t first_load(int wave) {
   if constexpr (kFp8) return (uint32_t)wave * kF8Loads;
-  return wave < 4 ? (uint32_t)wave * kSLoads : 4u * kSLoads + (uint32_t)(wave - 4) * kPLoads;
+  return wave < 4 ? (uint32_t)wave * SL : 4u * SL + (uint32_t)(wave - 4) * p_loads<SL>();
 }
 
 // This wave's share of the loads of segment tile `tile` into `dst`.
@@ -343,15 +353,15 @@ __device__ __forceinline__ void read_staged_queries(uint32_t lds, int sw, int la
 // barriers.  qf receives the segment's queries from their LDS staging:
 // staged with the guessed tiles when q_ready, else staged here (after tile 0,
 // before tile 1).
-template <int HEADS>
+template <int HEADS, int SL>
 __device__ __forceinline__ void score_role(const SegArgs& a, uint32_t lds, int sw, int lane,
                                            bf16x8 (&qf)[kW / 32], bool q_ready, float& m_out,
                                            float& l_out) {
   using G = Geo<HEADS>;
   const bool active = sw < G::SW;
   const int n = a.tile1 - a.tile0;
-  constexpr int NL = tile_loads<false>(true);
-  const uint32_t j0 = first_load<false>(sw);
+  constexpr int NL = tile_loads<false, SL>(true);
+  const uint32_t j0 = first_load<false, SL>(sw);
   PageCursor pc;
   seg_start<false, NL>(a, pc, lds, j0, lane);
 
@@ -477,13 +487,13 @@ struct OAcc {
   f32x16 o[Geo<HEADS>::HB][4];
 };
 
-template <int HEADS>
+template <int HEADS, int SL>
 __device__ __forceinline__ void pv_role(const SegArgs& a, uint32_t lds, int pw, int lane,
                                         OAcc<HEADS>& acc) {
   using G = Geo<HEADS>;
   const int n = a.tile1 - a.tile0;
-  constexpr int NL = tile_loads<false>(false);
-  const uint32_t j0 = first_load<false>(4 + pw);
+  constexpr int NL = tile_loads<false, SL>(false);
+  const uint32_t j0 = first_load<false, SL>(4 + pw);
   PageCursor pc;
   seg_start<false, NL>(a, pc, lds, j0, lane);
   if (n > 1 && !a.tile1_issued)
@@ -1033,7 +1043,7 @@ __device__ __forceinline__ void copy_out(uint32_t lds, bf16* dst) {
   lds_barrier();
 }
 
-template <int HEADS, bool kFp8>
+template <int HEADS, bool kFp8, int SL>
 __device__ __forceinline__ void score_segment(const SegArgs& a, uint32_t lds, bf16* dst, int wave,
                                               int lane, bf16x8 (&qf)[kW / 32], bool q_ready,
                                               float& m_out, float& l_out) {
@@ -1041,14 +1051,14 @@ __device__ __forceinline__ void score_segment(const SegArgs& a, uint32_t lds, bf
   if constexpr (kFp8)
     score_role_f8<HEADS>(a, lds, wave, lane, m_out, l_out);
   else
-    score_role<HEADS>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
+    score_role<HEADS, SL>(a, lds, wave, lane, qf, q_ready, m_out, l_out);
   if (wave < G::SW && lane < 16) lds_st(lds + kOffInv + (16 * wave + lane) * 4, 1.0f / l_out);
   lds_barrier();
   lds_barrier();
   copy_out<HEADS>(lds, dst);
 }
 
-template <int HEADS, bool kFp8>
+template <int HEADS, bool kFp8, int SL>
 __device__ __forceinline__ void pv_segment(const SegArgs& a, uint32_t lds, bf16* dst, int wave,
                                            int lane) {
   using G = Geo<HEADS>;
@@ -1057,7 +1067,7 @@ __device__ __forceinline__ void pv_segment(const SegArgs& a, uint32_t lds, bf16*
   if constexpr (kFp8)
     pv_role_f8<HEADS>(a, lds, pw, lane, acc);
   else
-    pv_role<HEADS>(a, lds, pw, lane, acc);
+    pv_role<HEADS, SL>(a, lds, pw, lane, acc);
   lds_barrier();
   // lane: head 32 hb + lane%32; register v of o[hb][cb]: column
   // 128 pw + 32 cb + 8 (v/4) + 4 (lane/32) + v%4 (runs of 4 -> 8-byte stores)
@@ -1169,7 +1179,7 @@ __device__ __forceinline__ void tile_prefix(const int* __restrict__ seq_lens, in
 // One decode workgroup of the tile stream (block `blk`): every (workgroup,
 // sequence) piece writes one partial into slot w + b (unique: w + b grows
 // along the stream).  Returns whether this workgroup wrote any piece.
-template <int HEADS, bool kFp8>
+template <int HEADS, bool kFp8, int SL>
 __device__ __forceinline__ bool decode_attention_wg(
     char* smem, int blk, const int* __restrict__ seq_lens, const int* __restrict__ block_table,
     const bf16* __restrict__ pool, int H, int n_wg, int batch, int guess_tiles, int max_blocks,
@@ -1214,10 +1224,11 @@ __device__ __forceinline__ bool decode_attention_wg(
       issue_part_fp8((const unsigned char*)pool + row * kF8Row, kTok, load_slot<true>(lds, t),
                      first_load<true>(wave), lane);
     else if (wave < 4)
-      issue_part<kSLoads>(pool + row * kW, kTok, load_slot<false>(lds, t), first_load<false>(wave),
+      issue_part<SL>(pool + row * kW, kTok, load_slot<false>(lds, t), first_load<false, SL>(wave),
                           lane);
     else
-      issue_part<kPLoads>(pool + row * kW, kTok, load_slot<false>(lds, t), first_load<false>(wave),
+      issue_part<p_loads<SL>()>(pool + row * kW, kTok, load_slot<false>(lds, t),
+                                first_load<false, SL>(wave),
                           lane);
     return true;
   };
@@ -1300,7 +1311,7 @@ __device__ __forceinline__ bool decode_attention_wg(
   if (wave < 4) {
     walk([&](const SegArgs& a, int b, long slot) {
       float m, tot;
-      score_segment<HEADS, kFp8>(a, lds, part_o + slot * HEADS * kR, wave, lane, qf, qb == b, m,
+      score_segment<HEADS, kFp8, SL>(a, lds, part_o + slot * HEADS * kR, wave, lane, qf, qb == b, m,
                                  tot);
       qb = b;
       if (wave < Geo<HEADS>::SW && lane < 16) {
@@ -1311,7 +1322,7 @@ __device__ __forceinline__ bool decode_attention_wg(
     });
   } else {
     walk([&](const SegArgs& a, int, long slot) {
-      pv_segment<HEADS, kFp8>(a, lds, part_o + slot * HEADS * kR, wave, lane);
+      pv_segment<HEADS, kFp8, SL>(a, lds, part_o + slot * HEADS * kR, wave, lane);
     });
   }
   if (spec_issued || q_spec) wait_vmcnt<0>();
@@ -1624,16 +1635,16 @@ __device__ __forceinline__ void combine_wg(const int* prefix, const float* __res
 // The arguments are ordered by when the workgroup needs them: the first 14
 // dwords (up to num_blocks) are the ones the prologue uses before its first
 // loads land, which the hardware preloads into scalar registers.
-template <int HEADS, bool kFp8>
+template <int HEADS, bool kFp8, int SL>
 __global__ void __launch_bounds__(kThreads, 1) attn_decode_partials_kernel(
     const int* __restrict__ seq_lens, const int* __restrict__ block_table,
     const bf16* __restrict__ pool, int H, int n_wg, int batch, int guess_tiles, int max_blocks,
     int shift, int num_blocks, const bf16* __restrict__ q_full, int* __restrict__ prefix_out,
     float* __restrict__ part_ml, bf16* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  decode_attention_wg<HEADS, kFp8>(smem, blockIdx.x, seq_lens, block_table, pool, H, n_wg, batch,
-                                   guess_tiles, max_blocks, shift, num_blocks, q_full, prefix_out,
-                                   part_ml, part_o);
+  decode_attention_wg<HEADS, kFp8, SL>(smem, blockIdx.x, seq_lens, block_table, pool, H, n_wg,
+                                       batch, guess_tiles, max_blocks, shift, num_blocks, q_full,
+                                       prefix_out, part_ml, part_o);
 }
 
 // Combine of the partials (the staged call): grid (H, ceil(batch / S)).
@@ -1685,10 +1696,16 @@ void launch_attention_partials_bf16(const void* q_full, const void* pool, int nu
                                             num_blocks, (const bf16*)q_full, prefix, part_ml,
                                             (bf16*)part_o);
   };
-  if (heads_per_wg == 64)
-    fp8 ? go(attn_decode_partials_kernel<64, true>) : go(attn_decode_partials_kernel<64, false>);
+  // bf16 rows over several 64-head groups: every tile load on the P*C waves
+  if (heads_per_wg == 64 && fp8)
+    go(attn_decode_partials_kernel<64, true, kSLoads>);
+  else if (heads_per_wg == 64 && hgc > 1)
+    go(attn_decode_partials_kernel<64, false, 0>);
+  else if (heads_per_wg == 64)
+    go(attn_decode_partials_kernel<64, false, kSLoads>);
   else
-    fp8 ? go(attn_decode_partials_kernel<32, true>) : go(attn_decode_partials_kernel<32, false>);
+    fp8 ? go(attn_decode_partials_kernel<32, true, kSLoads>)
+        : go(attn_decode_partials_kernel<32, false, kSLoads>);
 }
 
 int combine_rows_per_wg(int H, int batch, int num_cus) {
